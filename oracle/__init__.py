@@ -1,0 +1,13 @@
+"""CPU oracle (test infrastructure only; see ``sketch_oracle``)."""
+from .sketch_oracle import (  # noqa: F401
+    backward_dlut,
+    backward_dlut_loop,
+    backward_dx,
+    dequantize,
+    forward,
+    group_of_column,
+    pack_indices,
+    rel_err,
+    unpack_indices,
+    weight_gradient,
+)

@@ -1,0 +1,173 @@
+"""CPU oracle for the sketched-weight matrix multiply (float64, numpy).
+
+TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module. The library itself never
+calls it, and this module imports nothing from the library: it shares no code,
+tables or constants with the HIP path.
+
+What is computed, and where the pages define it
+------------------------------------------------
+Sources: "SpaLLM: Unified Compressive Adaptation of Large Language Models with
+Sketching" (arXiv 2410.06364v1; called *SpaLLM* below) and the OpenReview
+discussion of the same method, "Sketch to Adapt: Fine-Tunable Sketches for
+Efficient LLM Adaptation" (called *Sketch to Adapt* below).
+
+* Row-wise sketch (SpaLLM, section 2.2, Eq. (1)): a weight row theta in R^d is
+  approximated as Pi w, where w in R^k is the sketched parameter (the lookup
+  table) and Pi in R^{d x k} has one-hot rows. Storing the position of the one
+  in each row of Pi as a b-bit integer gives ``idx[i, j]`` with k = 2^b, so
+  ``W[i, j] = w_i[idx[i, j]]``.
+* Groups per row (SpaLLM, section 2.2, "Scaling up learning power ..."; Sketch
+  to Adapt, reply W2 on sub-rows): each row is cut into ``gpr`` contiguous,
+  non-overlapping sub-rows of ``d / gpr`` columns, each with its own table, so
+  ``W[i, j] = LUT[i, j // (d / gpr), idx[i, j]]``.
+* Forward (SpaLLM, abstract and section 2.3: a single compressed matmul per
+  layer; Sketch to Adapt, reply on Eq. (6): y = w M X): with tokens as rows of
+  X, ``Y = X W^T``.
+* Gradient of the tables (Sketch to Adapt, corrected Eq. (6)):
+  dL/dw = dL/dy (M X)^T. For row i this sums ``dW[i, j] = sum_t dY[t, i]
+  X[t, j]`` over the columns that map to each table entry:
+  ``dLUT[i, g, c] = sum_{j in g, idx[i, j] = c} dW[i, j]``. The mapping Pi is
+  frozen (SpaLLM, section 2.3), so there is no gradient for the indices.
+* Gradient of the input: the chain rule through ``Y = X W^T`` gives
+  ``dX = dY W``; the pages use it implicitly to train lower layers.
+
+Readings where the pages leave a step open (listed with the design notes):
+the packed bit order is little-endian (field j at bits b*j .. b*j+b-1 of the
+row's byte stream, LSB first); gradients of shared entries are summed, as the
+chain rule of the corrected Eq. (6) gives, not averaged.
+
+Every function here is pinned in ``tests/test_oracle_pins.py`` against facts
+the pages or plain mathematics fix (the identity example, a dense special case,
+finite differences, invariants, brute force on tiny inputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# index stream
+# ---------------------------------------------------------------------------
+
+def unpack_indices(idx_packed: np.ndarray, d: int, b: int) -> np.ndarray:
+    """b-bit little-endian fields of each row's byte stream -> int64 ``[n][d]``.
+
+    Bit p of a row's stream is bit ``p % 8`` of byte ``p // 8``; field j is the
+    integer whose bit q is stream bit ``b*j + q``.
+    """
+    packed = np.ascontiguousarray(idx_packed, dtype=np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] * 8 < d * b:
+        raise ValueError("packed rows too short for d*b bits")
+    bits = np.unpackbits(packed, axis=1, bitorder="little")[:, : d * b]
+    fields = bits.reshape(n, d, b).astype(np.int64)
+    weights = (1 << np.arange(b, dtype=np.int64))
+    return fields @ weights
+
+
+def pack_indices(idx: np.ndarray, b: int) -> np.ndarray:
+    """Inverse of :func:`unpack_indices`: int ``[n][d]`` in ``[0, 2^b)`` -> uint8 stream."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    if idx.min(initial=0) < 0 or idx.max(initial=0) >= (1 << b):
+        raise ValueError("index out of range for b bits")
+    if (d * b) % 8:
+        raise ValueError("d*b must be a multiple of 8")
+    bits = ((idx[:, :, None] >> np.arange(b, dtype=np.int64)) & 1).astype(np.uint8)
+    return np.packbits(bits.reshape(n, d * b), axis=1, bitorder="little")
+
+
+# ---------------------------------------------------------------------------
+# dequantisation (SpaLLM Eq. (1) with groups per row)
+# ---------------------------------------------------------------------------
+
+def group_of_column(d: int, gpr: int) -> np.ndarray:
+    """g(j) = floor(j / (d / gpr)): contiguous, equal, non-overlapping sub-rows."""
+    if gpr < 1 or d % gpr:
+        raise ValueError("d must be a multiple of gpr")
+    return np.arange(d, dtype=np.int64) // (d // gpr)
+
+
+def dequantize(idx_packed: np.ndarray, lut: np.ndarray, d: int, b: int, gpr: int) -> np.ndarray:
+    """W[i, j] = LUT[i, g(j), idx[i, j]] in float64 (exact for f32/f16/bf16 tables)."""
+    lut = np.asarray(lut, dtype=np.float64)
+    n = lut.shape[0]
+    if lut.shape != (n, gpr, 1 << b):
+        raise ValueError(f"lut shape {lut.shape} != {(n, gpr, 1 << b)}")
+    idx = unpack_indices(idx_packed, d, b)
+    g = group_of_column(d, gpr)
+    rows = np.arange(n, dtype=np.int64)[:, None]
+    return lut[rows, g[None, :], idx]
+
+
+# ---------------------------------------------------------------------------
+# forward and backward
+# ---------------------------------------------------------------------------
+
+def forward(X: np.ndarray, idx_packed: np.ndarray, lut: np.ndarray, b: int, gpr: int) -> np.ndarray:
+    """Y[t, i] = sum_j X[t, j] W[i, j]  (float64)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = dequantize(idx_packed, lut, X.shape[1], b, gpr)
+    return X @ W.T
+
+
+def backward_dx(dY: np.ndarray, idx_packed: np.ndarray, lut: np.ndarray, d: int, b: int, gpr: int) -> np.ndarray:
+    """dX[t, j] = sum_i dY[t, i] W[i, j]  (float64)."""
+    dY = np.asarray(dY, dtype=np.float64)
+    W = dequantize(idx_packed, lut, d, b, gpr)
+    return dY @ W
+
+
+def weight_gradient(dY: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """Gradient of every virtual parameter: dW[i, j] = sum_t dY[t, i] X[t, j]."""
+    return np.asarray(dY, dtype=np.float64).T @ np.asarray(X, dtype=np.float64)
+
+
+def backward_dlut_loop(dY: np.ndarray, X: np.ndarray, idx_packed: np.ndarray, b: int, gpr: int) -> np.ndarray:
+    """dLUT by an explicit loop over every virtual parameter (tiny shapes only).
+
+    Each virtual parameter W[i, j] hands its gradient to the table entry it is
+    mapped to; entries shared by several columns receive the sum.
+    """
+    dW = weight_gradient(dY, X)
+    n, d = dW.shape
+    idx = unpack_indices(idx_packed, d, b)
+    g = group_of_column(d, gpr)
+    out = np.zeros((n, gpr, 1 << b), dtype=np.float64)
+    for i in range(n):
+        for j in range(d):
+            out[i, g[j], idx[i, j]] += dW[i, j]
+    return out
+
+
+def backward_dlut(dY: np.ndarray, X: np.ndarray, idx_packed: np.ndarray, b: int, gpr: int) -> np.ndarray:
+    """Same sum as :func:`backward_dlut_loop`, binned row by row with ``np.bincount``."""
+    dW = weight_gradient(dY, X)
+    n, d = dW.shape
+    k = 1 << b
+    idx = unpack_indices(idx_packed, d, b)
+    g = group_of_column(d, gpr)
+    out = np.empty((n, gpr, k), dtype=np.float64)
+    for i in range(n):
+        out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# scoring
+# ---------------------------------------------------------------------------
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| (0 when both are all zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch {got.shape} vs {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got - ref)))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den

@@ -1,0 +1,294 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes an object ``o`` exposing the oracle API (the real oracle
+module, or a copy with a planted mistake) and raises ``AssertionError`` when
+``o`` disagrees with the fact it checks. The facts are:
+
+* hand-worked bitstreams (``tests/golden/bitstream_*.txt``) and an
+  independent big-integer field extractor for the index layout;
+* the identity example of SpaLLM section 2.4 (``tests/golden/identity_two_values.txt``);
+* a dense special case (group width == k and idx[i, j] = j mod k), where the
+  sketch reproduces an arbitrary matrix and the forward pass must equal the
+  textbook product ``X @ W.T`` and each table entry's gradient must equal the
+  single virtual parameter's gradient;
+* a second formulation of the forward pass (bin the inputs, then multiply by
+  the table: sum_{g,c} LUT[i,g,c] * sum_{j in g, idx=c} x_j);
+* central finite differences of L = <dY, Y(X, LUT)> (exact up to rounding,
+  since Y is linear in X and in LUT);
+* invariants: bins partition a group (sum over c of dLUT equals the group's sum
+  of dW), adjointness <dY, X W^T> = <dY W, X>, entry-permutation invariance;
+* exact integer histograms for selection inputs.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            out[key.strip()] = val.strip()
+    return out
+
+
+def _ints(s):
+    return [int(t, 0) for t in s.split()]
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bigint_fields(row_bytes, d, b):
+    """Independent extractor: read the row as one little-endian integer."""
+    s = 0
+    for q, byte in enumerate(row_bytes):
+        s |= int(byte) << (8 * q)
+    mask = (1 << b) - 1
+    return [(s >> (b * j)) & mask for j in range(d)]
+
+
+def _random_case(seed, n, d, b, gpr, m):
+    r = _rng(seed)
+    k = 1 << b
+    idx = r.integers(0, k, size=(n, d))
+    lut = np.sort(r.normal(0.0, 0.02, size=(n, gpr, k)), axis=-1)
+    X = r.normal(size=(m, d))
+    dY = r.normal(size=(m, n))
+    return idx, lut, X, dY
+
+
+# ---------------------------------------------------------------------------
+# index layout
+# ---------------------------------------------------------------------------
+
+def pin_bitstream_golden(o):
+    g3 = _read_golden("bitstream_b3_0to7.txt")
+    packed = np.array([_ints(g3["bytes"])], dtype=np.uint8)
+    want = _ints(g3["indices"])
+    assert list(o.unpack_indices(packed, int(g3["d"]), int(g3["b"]))[0]) == want
+    assert list(o.pack_indices(np.array([want]), 3)[0]) == _ints(g3["bytes"])
+    g = _read_golden("bitstream_b4_b2.txt")
+    for b, ik, bk in ((4, "b4_indices", "b4_bytes"), (2, "b2_indices", "b2_bytes")):
+        ind, byt = _ints(g[ik]), _ints(g[bk])
+        assert list(o.unpack_indices(np.array([byt], dtype=np.uint8), len(ind), b)[0]) == ind
+        assert list(o.pack_indices(np.array([ind]), b)[0]) == byt
+
+
+def pin_unpack_bigint(o):
+    r = _rng(1)
+    for b in (2, 3, 4):
+        for d in (8, 16, 24, 64, 96):
+            if (d * b) % 8:
+                continue
+            packed = r.integers(0, 256, size=(3, d * b // 8), dtype=np.uint8)
+            got = o.unpack_indices(packed, d, b)
+            for i in range(3):
+                assert list(got[i]) == _bigint_fields(packed[i], d, b), (b, d, i)
+
+
+def pin_unpack_exhaustive_b3(o):
+    # every value 0..7 at every field position modulo 8 (fields that straddle bytes)
+    d = 64
+    for v in range(8):
+        for start in range(8):
+            idx = np.zeros((1, d), dtype=np.int64)
+            idx[0, start::8] = v
+            packed = o.pack_indices(idx, 3)
+            assert _bigint_fields(packed[0], d, 3) == list(idx[0])
+            assert np.array_equal(o.unpack_indices(packed, d, 3), idx)
+
+
+# ---------------------------------------------------------------------------
+# dequantisation
+# ---------------------------------------------------------------------------
+
+def pin_identity(o):
+    """SpaLLM section 2.4: the identity is exact with two shared values."""
+    _read_golden("identity_two_values.txt")
+    for b, gpr, n in ((2, 1, 32), (3, 2, 64), (4, 4, 64)):
+        k = 1 << b
+        lut = np.full((n, gpr, k), 7.25)
+        lut[:, :, 0] = 0.0
+        lut[:, :, 1] = 1.0
+        idx = np.eye(n, dtype=np.int64)
+        packed = o.pack_indices(idx, b)
+        W = o.dequantize(packed, lut, n, b, gpr)
+        assert np.array_equal(W, np.eye(n))
+        X = _rng(2).normal(size=(5, n))
+        dY = _rng(3).normal(size=(5, n))
+        assert np.array_equal(o.forward(X, packed, lut, b, gpr), X)
+        assert np.array_equal(o.backward_dx(dY, packed, lut, n, b, gpr), dY)
+        dl = o.backward_dlut(dY, X, packed, b, gpr)
+        want = np.zeros_like(dl)
+        G = n // gpr
+        for i in range(n):
+            for j in range(n):
+                # the diagonal maps to slot 1, every other column to the shared 0 in slot 0
+                want[i, j // G, 1 if i == j else 0] += float(np.dot(dY[:, i], X[:, j]))
+        assert np.allclose(dl, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_dense_special_case(o):
+    """Group width == k and idx = j mod k: every W is representable."""
+    r = _rng(4)
+    for b in (2, 3, 4):
+        k = 1 << b
+        n, gpr, m = 6, 4, 3
+        d = gpr * k
+        W = r.normal(size=(n, d))
+        lut = W.reshape(n, gpr, k).copy()
+        idx = np.tile(np.arange(d) % k, (n, 1))
+        packed = o.pack_indices(idx, b)
+        assert np.array_equal(o.dequantize(packed, lut, d, b, gpr), W)
+        X = r.normal(size=(m, d))
+        dY = r.normal(size=(m, n))
+        assert np.allclose(o.forward(X, packed, lut, b, gpr), X @ W.T, rtol=1e-12, atol=1e-12)
+        assert np.allclose(o.backward_dx(dY, packed, lut, d, b, gpr), dY @ W, rtol=1e-12, atol=1e-12)
+        dW = dY.T @ X
+        assert np.allclose(o.backward_dlut(dY, X, packed, b, gpr), dW.reshape(n, gpr, k), rtol=1e-12, atol=1e-12)
+        assert np.allclose(o.backward_dlut_loop(dY, X, packed, b, gpr), dW.reshape(n, gpr, k),
+                           rtol=1e-12, atol=1e-12)
+
+
+def pin_dequant_elementwise(o):
+    """Direct element-by-element read of the definition on a tiny case."""
+    b, gpr, n, d = 3, 2, 3, 16
+    idx, lut, _, _ = _random_case(5, n, d, b, gpr, 1)
+    W = o.dequantize(o.pack_indices(idx, b), lut, d, b, gpr)
+    G = d // gpr
+    for i in range(n):
+        for j in range(d):
+            assert W[i, j] == lut[i, j // G, idx[i, j]]
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def pin_forward_binned(o):
+    """Bin the inputs first, then multiply by the table entries."""
+    for b, gpr in ((2, 1), (3, 2), (4, 4)):
+        n, d, m = 5, 32, 3
+        k = 1 << b
+        idx, lut, X, _ = _random_case(6 + b, n, d, b, gpr, m)
+        G = d // gpr
+        want = np.zeros((m, n))
+        for t in range(m):
+            for i in range(n):
+                S = np.zeros((gpr, k))
+                for j in range(d):
+                    S[j // G, idx[i, j]] += X[t, j]
+                want[t, i] = float(np.sum(lut[i] * S))
+        got = o.forward(X, o.pack_indices(idx, b), lut, b, gpr)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def pin_permutation_invariance(o):
+    b, gpr, n, d, m = 4, 2, 4, 32, 2
+    k = 1 << b
+    idx, lut, X, _ = _random_case(9, n, d, b, gpr, m)
+    perm = _rng(10).permutation(k)
+    inv = np.argsort(perm)
+    lut_p = lut[:, :, perm]             # new slot s holds old entry perm[s]
+    idx_p = inv[idx]                    # old entry c now lives at slot inv[c]
+    y0 = o.forward(X, o.pack_indices(idx, b), lut, b, gpr)
+    y1 = o.forward(X, o.pack_indices(idx_p, b), lut_p, b, gpr)
+    assert np.allclose(y0, y1, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def _loss(o, X, packed, lut, dY, b, gpr):
+    return float(np.sum(dY * o.forward(X, packed, lut, b, gpr)))
+
+
+def pin_finite_difference(o):
+    for b, gpr in ((2, 2), (3, 1), (4, 2)):
+        n, d, m = 4, 32, 3
+        idx, lut, X, dY = _random_case(11 + b, n, d, b, gpr, m)
+        packed = o.pack_indices(idx, b)
+        h = 0.5  # L is linear in X and in LUT: the central difference is exact
+        dX = o.backward_dx(dY, packed, lut, d, b, gpr)
+        for (t, j) in ((0, 0), (1, 17), (2, 31), (0, 9)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[t, j] += h
+            Xm[t, j] -= h
+            fd = (_loss(o, Xp, packed, lut, dY, b, gpr) - _loss(o, Xm, packed, lut, dY, b, gpr)) / (2 * h)
+            assert abs(fd - dX[t, j]) <= 1e-10 * max(1.0, abs(fd)), (b, t, j, fd, dX[t, j])
+        dl = o.backward_dlut(dY, X, packed, b, gpr)
+        k = 1 << b
+        for (i, g, c) in ((0, 0, 0), (1, gpr - 1, k - 1), (3, 0, k // 2), (2, gpr - 1, 1)):
+            Lp, Lm = lut.copy(), lut.copy()
+            Lp[i, g, c] += h
+            Lm[i, g, c] -= h
+            fd = (_loss(o, X, packed, Lp, dY, b, gpr) - _loss(o, X, packed, Lm, dY, b, gpr)) / (2 * h)
+            assert abs(fd - dl[i, g, c]) <= 1e-10 * max(1.0, abs(fd)), (b, i, g, c, fd, dl[i, g, c])
+
+
+def pin_bins_partition_group(o):
+    b, gpr, n, d, m = 4, 4, 6, 64, 5
+    idx, lut, X, dY = _random_case(20, n, d, b, gpr, m)
+    packed = o.pack_indices(idx, b)
+    dl = o.backward_dlut(dY, X, packed, b, gpr)
+    dW = dY.T @ X
+    G = d // gpr
+    for i in range(n):
+        for g in range(gpr):
+            assert np.isclose(dl[i, g].sum(), dW[i, g * G:(g + 1) * G].sum(), rtol=1e-12, atol=1e-12)
+
+
+def pin_adjoint(o):
+    b, gpr, n, d, m = 3, 2, 7, 64, 4
+    idx, lut, X, dY = _random_case(21, n, d, b, gpr, m)
+    packed = o.pack_indices(idx, b)
+    lhs = float(np.sum(dY * o.forward(X, packed, lut, b, gpr)))
+    rhs = float(np.sum(o.backward_dx(dY, packed, lut, d, b, gpr) * X))
+    assert np.isclose(lhs, rhs, rtol=1e-12, atol=1e-13)
+
+
+def pin_histogram(o):
+    """X = identity (m = d), dY = 1: dLUT counts each (row, group) bin exactly."""
+    for b, gpr in ((2, 2), (3, 4), (4, 1)):
+        n, d = 5, 32
+        k = 1 << b
+        idx = _rng(30 + b).integers(0, k, size=(n, d))
+        packed = o.pack_indices(idx, b)
+        X = np.eye(d)
+        dY = np.ones((d, n))
+        dl = o.backward_dlut(dY, X, packed, b, gpr)
+        G = d // gpr
+        for i in range(n):
+            for g in range(gpr):
+                counts = np.zeros(k)
+                for j in range(g * G, (g + 1) * G):
+                    counts[idx[i, j]] += 1
+                assert np.array_equal(dl[i, g], counts)
+
+
+def pin_loop_vs_bincount(o):
+    b, gpr, n, d, m = 3, 2, 4, 32, 3
+    idx, lut, X, dY = _random_case(40, n, d, b, gpr, m)
+    packed = o.pack_indices(idx, b)
+    assert np.allclose(o.backward_dlut_loop(dY, X, packed, b, gpr),
+                       o.backward_dlut(dY, X, packed, b, gpr), rtol=1e-13, atol=1e-15)
+
+
+ALL_PINS = [
+    pin_bitstream_golden, pin_unpack_bigint, pin_unpack_exhaustive_b3,
+    pin_identity, pin_dense_special_case, pin_dequant_elementwise,
+    pin_forward_binned, pin_permutation_invariance,
+    pin_finite_difference, pin_bins_partition_group, pin_adjoint, pin_histogram,
+    pin_loop_vs_bincount,
+]

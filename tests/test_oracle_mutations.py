@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in a copy of the oracle; some pin must catch each.
+
+The mistakes are planted in the oracle's source text on the CPU (a flipped bit
+order, interleaved instead of contiguous groups, a transposed operand, an
+averaged instead of summed gradient, ...). A mutation that no pin catches
+would mean the pins do not fix that part of the oracle.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "sketch_oracle.py")
+
+MUTATIONS = {
+    "big_endian_bits": ('bitorder="little"', 'bitorder="big"'),
+    "msb_first_fields": ("weights = (1 << np.arange(b, dtype=np.int64))",
+                         "weights = (1 << np.arange(b, dtype=np.int64)[::-1])"),
+    "interleaved_groups": ("return np.arange(d, dtype=np.int64) // (d // gpr)",
+                           "return np.arange(d, dtype=np.int64) % gpr"),
+    "reversed_groups": ("return lut[rows, g[None, :], idx]", "return lut[rows, (gpr - 1 - g)[None, :], idx]"),
+    "index_off_by_one": ("return lut[rows, g[None, :], idx]",
+                         "return lut[rows, g[None, :], (idx + 1) % lut.shape[2]]"),
+    "forward_transposed": ("return X @ W.T", "return X @ W"),
+    "forward_dropped_group": ("return X @ W.T", "return X[:, : W.shape[1] // 2] @ W[:, : W.shape[1] // 2].T"),
+    "dx_sign": ("return dY @ W", "return -(dY @ W)"),
+    "dx_transposed": ("return dY @ W", "return dY @ W.T"),
+    "dw_transposed": ("return np.asarray(dY, dtype=np.float64).T @ np.asarray(X, dtype=np.float64)",
+                      "return (np.asarray(X, dtype=np.float64).T @ np.asarray(dY, dtype=np.float64)).T[:, ::-1]"),
+    "dlut_overwrite": ("out[i, g[j], idx[i, j]] += dW[i, j]", "out[i, g[j], idx[i, j]] = dW[i, j]"),
+    "dlut_average": (
+        "out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)",
+        "out[i] = (np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k)"
+        " / np.maximum(1, np.bincount(g * k + idx[i], minlength=gpr * k))).reshape(gpr, k)"),
+}
+
+
+def _load_mutant(old, new):
+    text = open(SRC).read()
+    assert old in text, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(text.replace(old, new), SRC + "[mutant]", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name):
+    mutant = _load_mutant(*MUTATIONS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as e:  # AssertionError, or a shape error from the mistake
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutation {name}"
+
+
+def test_unmutated_copy_passes():
+    text = open(SRC).read()
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(text, SRC, "exec"), mod.__dict__)
+    for pin in ALL_PINS:
+        pin(mod)
