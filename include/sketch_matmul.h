@@ -1,0 +1,147 @@
+/*
+ * sketch_matmul.h - C ABI of the sketched-weight matrix multiply for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method ("SpaLLM: Unified Compressive Adaptation of Large Language Models
+ * with Sketching", section 2.2, Eq. (1), and "Sketch to Adapt: Fine-Tunable
+ * Sketches for Efficient LLM Adaptation", reply W2 on sub-rows) stores each
+ * weight row of an n x d layer as gpr contiguous groups of G = d / gpr columns.
+ * Every (row, group) owns a lookup table of k = 2^b values and every weight
+ * stores a b-bit index into its group's table:
+ *
+ *     W[i][j] = lut[i][j / G][idx[i][j]]                         (dequantise)
+ *     Y[t][i] = sum_j X[t][j] * W[i][j]                          (forward)
+ *     dX[t][j] = sum_i dY[t][i] * W[i][j]                        (input grad)
+ *     dLUT[i][g][c] = sum_{j in g, idx[i][j] == c} sum_t dY[t][i] * X[t][j]
+ *                                                                (table grad,
+ *                     corrected Eq. (6) of the Sketch to Adapt discussion)
+ *
+ * Data layout (all row-major, all pointers are DEVICE pointers):
+ *   idx_packed  uint8 [n][d*b/8]   row i's indices as one little-endian
+ *                                  bitstream: index j occupies bits
+ *                                  b*j .. b*j+b-1, stream bit p is bit p%8 of
+ *                                  byte p/8 (b=4: low nibble = even column;
+ *                                  b=3: contiguous 3-bit stream).
+ *   lut         [n][gpr][2^b]      table values, dtype lut_dtype.
+ *   X           [m][d]             activations, dtype x_dtype.
+ *   Y           [m][n]             forward output, dtype x_dtype, rounded to
+ *                                  nearest-even from an fp32 accumulator.
+ *   dY          [m][n]             output gradient, dtype io_dtype.
+ *   dX          [m][d]   fp32      input gradient.
+ *   dLUT        [n][gpr][2^b] fp32 table gradient.
+ *
+ * Supported shapes: b in {2,3,4}; gpr >= 1 with d % gpr == 0 and
+ * (d / gpr) % 32 == 0; n >= 1; m >= 0 (m == 0 is a no-op that returns OK).
+ * Supported dtype pairs (x_dtype, lut_dtype): (F32,F32) fp32 path with fp32
+ * products; (F16,F16), (BF16,F16), (F16,BF16), (BF16,BF16) matrix-core path
+ * whose operands are in the lut dtype (activations are converted to it) with
+ * fp32 accumulation. The table gradient's dY^T X product always uses the
+ * activations' own dtype.
+ *
+ * Alignment: every pointer must be 16-byte aligned.
+ *
+ * Ownership and threading: the caller allocates and owns every buffer; the
+ * library never allocates, frees or keeps device memory and holds no mutable
+ * global state, so calls are thread-safe. Work is enqueued on `stream`
+ * (NULL = the default stream) and runs asynchronously; no call synchronises.
+ *
+ * Errors: argument checks run on the host before anything is launched; a
+ * failed check returns its status and launches nothing. A launch failure
+ * returns SKM_EHIP. Device-side faults surface at the caller's next
+ * synchronisation of `stream`.
+ */
+#ifndef SKETCH_MATMUL_H
+#define SKETCH_MATMUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKM_F32 = 0,
+  SKM_F16 = 1,
+  SKM_BF16 = 2
+} skm_dtype;
+
+typedef enum {
+  SKM_OK = 0,
+  SKM_EINVAL = -1,        /* bad size, bit width, group count or NULL pointer */
+  SKM_EUNSUPPORTED = -2,  /* dtype combination not provided                   */
+  SKM_EALIGN = -3,        /* a pointer is not 16-byte aligned                  */
+  SKM_EWORKSPACE = -4,    /* workspace smaller than sketch_matmul_bwd_workspace */
+  SKM_EHIP = -5,          /* the HIP runtime reported a launch error           */
+  SKM_EALIAS = -6         /* an output buffer overlaps an input buffer         */
+} skm_status;
+
+/*
+ * Forward pass Y = X * W^T (SpaLLM abstract and section 2.3: one compressed
+ * matrix multiplication per layer; W is never materialised).
+ *   X          [m][d] x_dtype     idx_packed [n][d*b/8]   lut [n][gpr][2^b]
+ *   Y          [m][n] x_dtype (written, must not overlap any input)
+ * Decode-sized m streams the indices once; larger m runs a tiled matrix-core
+ * GEMM. Returns SKM_OK or an error status (see above).
+ */
+int sketch_matmul_fwd(const void* X, int x_dtype,
+                      const uint8_t* idx_packed,
+                      const void* lut, int lut_dtype,
+                      int64_t m, int64_t n, int64_t d, int b, int gpr,
+                      void* Y, hipStream_t stream);
+
+/*
+ * Backward pass (the mapping is frozen, SpaLLM section 2.3, so there is no
+ * index gradient):
+ *   dX   = dY * W                      [m][d] fp32, NULL = skip
+ *   dLUT = table gradient (see top)    [n][gpr][2^b] fp32, NULL = skip;
+ *          accumulate == 0 overwrites dLUT, accumulate == 1 adds to it.
+ *   dY [m][n] and X [m][d] are in io_dtype; X may be NULL when dLUT is NULL.
+ * workspace/workspace_bytes: device scratch of at least
+ * sketch_matmul_bwd_workspace(...) bytes (may be NULL when that is 0).
+ * Gradients are sums over the columns that share an entry (chain rule of the
+ * corrected Eq. (6)), not averages. With m == 0 and accumulate == 0 the
+ * requested gradients are written as zeros.
+ */
+int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype,
+                      const uint8_t* idx_packed,
+                      const void* lut, int lut_dtype,
+                      int64_t m, int64_t n, int64_t d, int b, int gpr,
+                      float* dX,
+                      float* dLUT, int accumulate,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Bytes of device workspace sketch_matmul_bwd needs for these sizes (>= 0). */
+size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr,
+                                   int io_dtype, int lut_dtype);
+
+/*
+ * Dequantise W[i][j] = lut[i][j/G][idx[i][j]] into a dense [n][d] array of
+ * lut_dtype (SpaLLM Eq. (1) with groups per row). A checking aid: the matmul
+ * entry points never build W.
+ */
+int sketch_dequant(const uint8_t* idx_packed, const void* lut, int lut_dtype,
+                   int64_t n, int64_t d, int b, int gpr,
+                   void* W, hipStream_t stream);
+
+/*
+ * Unpack the b-bit index stream into one uint8 per weight: idx [n][d].
+ * A checking aid for the bit layout described at the top of this file.
+ */
+int sketch_unpack_indices(const uint8_t* idx_packed, int64_t n, int64_t d, int b,
+                          uint8_t* idx, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* sketch_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int sketch_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKETCH_MATMUL_H */

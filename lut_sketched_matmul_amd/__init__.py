@@ -1,0 +1,20 @@
+"""Sketched-weight (LUT + one-hot mapping) matrix multiply for AMD MI355X.
+
+The compute lives in the HIP library ``libsketchmm.so`` (C ABI:
+``include/sketch_matmul.h``); this package holds its ctypes binding, the
+build script and the synthetic workload generators.
+"""
+from ._lib import (  # noqa: F401
+    SKM_BF16,
+    SKM_F16,
+    SKM_F32,
+    SketchError,
+    header_functions,
+    lib,
+    sketch_dequant,
+    sketch_matmul_bwd,
+    sketch_matmul_fwd,
+    sketch_unpack_indices,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,183 @@
+"""ctypes binding of ``libsketchmm.so`` (the C ABI in ``include/sketch_matmul.h``).
+
+Argument marshalling only: every step of the sketched matmul runs in the HIP
+library. PyTorch provides device memory (``tensor.data_ptr()``) and the
+current HIP stream; nothing here computes on the host, and there is no
+fallback: when the library is missing or its call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libsketchmm.so")
+HEADER = os.path.join(ROOT, "include", "sketch_matmul.h")
+
+SKM_F32, SKM_F16, SKM_BF16 = 0, 1, 2
+STATUS = {
+    0: "SKM_OK", -1: "SKM_EINVAL", -2: "SKM_EUNSUPPORTED", -3: "SKM_EALIGN",
+    -4: "SKM_EWORKSPACE", -5: "SKM_EHIP", -6: "SKM_EALIAS",
+}
+
+
+class SketchError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_vp = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "sketch_matmul_fwd": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
+                                   _c_vp, _c_vp]),
+    "sketch_matmul_bwd": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
+                                   _c_vp, _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
+    "sketch_matmul_bwd_workspace": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "sketch_dequant": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp]),
+    "sketch_unpack_indices": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "sketch_status_str": (ctypes.c_char_p, [_c_int]),
+    "sketch_version": (_c_int, []),
+}
+
+
+def library_path() -> str:
+    return os.environ.get("SKETCHMM_LIB", LIB_PATH)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found: build it with `python -m lut_sketched_matmul_amd.build`")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/sketch_matmul.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sketch_\w+)\s*\(", text)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SketchError(fn, status, lib().sketch_status_str(status).decode())
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: SKM_F32, torch.float16: SKM_F16, torch.bfloat16: SKM_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=None):
+    """Y = X W^T with W[i, j] = lut[i, j // (d/gpr), idx[i, j]].
+
+    X [m, d] (f32/f16/bf16), idx_packed [n, d*b/8] uint8, lut [n, gpr, 2^b].
+    Returns Y [m, n] in X's dtype.
+    """
+    torch = _torch()
+    _require_device(X, idx_packed, lut, out)
+    m, d = X.shape
+    n = idx_packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=X.dtype, device=X.device)
+    st = lib().sketch_matmul_fwd(X.data_ptr(), dtype_code(X), idx_packed.data_ptr(), lut.data_ptr(),
+                                 dtype_code(lut), m, n, d, b, gpr, out.data_ptr() if out.numel() else None,
+                                 _stream_ptr(stream))
+    _check("sketch_matmul_fwd", st)
+    return out
+
+
+def sketch_matmul_bwd(dY, X, idx_packed, lut, b: int, gpr: int, d: Optional[int] = None,
+                      need_dx: bool = True, need_dlut: bool = True, dlut_out=None, accumulate: bool = False,
+                      workspace=None, stream=None) -> Tuple[object, object]:
+    """(dX, dLUT) of the sketched matmul; both fp32. dLUT sums shared entries."""
+    torch = _torch()
+    _require_device(dY, X, idx_packed, lut, dlut_out)
+    m, n = dY.shape
+    if d is None:
+        d = X.shape[1]
+    K = 1 << b
+    dX = torch.empty((m, d), dtype=torch.float32, device=dY.device) if need_dx else None
+    dL = None
+    if need_dlut:
+        dL = dlut_out if dlut_out is not None else torch.empty((n, gpr, K), dtype=torch.float32, device=dY.device)
+    ws_bytes = lib().sketch_matmul_bwd_workspace(m, n, d, b, gpr, dtype_code(dY), dtype_code(lut))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dY.device)
+    st = lib().sketch_matmul_bwd(
+        dY.data_ptr() if dY.numel() else None, X.data_ptr() if (X is not None and X.numel()) else None,
+        dtype_code(dY), idx_packed.data_ptr(), lut.data_ptr(), dtype_code(lut), m, n, d, b, gpr,
+        dX.data_ptr() if (dX is not None and dX.numel()) else None, dL.data_ptr() if dL is not None else None,
+        1 if accumulate else 0, workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_ptr(stream))
+    _check("sketch_matmul_bwd", st)
+    return dX, dL
+
+
+def sketch_dequant(idx_packed, lut, d: int, b: int, gpr: int, stream=None):
+    """Dense W [n, d] in the table dtype (a checking aid)."""
+    torch = _torch()
+    _require_device(idx_packed, lut)
+    n = idx_packed.shape[0]
+    W = torch.empty((n, d), dtype=lut.dtype, device=lut.device)
+    st = lib().sketch_dequant(idx_packed.data_ptr(), lut.data_ptr(), dtype_code(lut), n, d, b, gpr, W.data_ptr(),
+                              _stream_ptr(stream))
+    _check("sketch_dequant", st)
+    return W
+
+
+def sketch_unpack_indices(idx_packed, d: int, b: int, stream=None):
+    """One uint8 per weight: idx [n, d] (a checking aid)."""
+    torch = _torch()
+    _require_device(idx_packed)
+    n = idx_packed.shape[0]
+    out = torch.empty((n, d), dtype=torch.uint8, device=idx_packed.device)
+    st = lib().sketch_unpack_indices(idx_packed.data_ptr(), n, d, b, out.data_ptr(), _stream_ptr(stream))
+    _check("sketch_unpack_indices", st)
+    return out

@@ -1,0 +1,164 @@
+// C ABI of the sketched-weight matmul: argument checks and kernel selection.
+// The formulas, layouts and error rules are documented in sketch_matmul.h.
+#include "sketch_matmul.h"
+
+#include "skm_common.h"
+#include "skm_launch.h"
+
+namespace {
+
+using skm::Problem;
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dt) { return dt == SKM_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == SKM_F32 || dt == SKM_F16 || dt == SKM_BF16; }
+
+// (activation dtype, table dtype) pairs with a kernel
+bool supported_pair(int x_dt, int lut_dt) {
+  if (!valid_dtype(x_dt) || !valid_dtype(lut_dt)) return false;
+  if (x_dt == SKM_F32 || lut_dt == SKM_F32) return x_dt == SKM_F32 && lut_dt == SKM_F32;
+  return true;
+}
+
+int check_shape(int64_t m, int64_t n, int64_t d, int b, int gpr) {
+  if (b < 2 || b > 4) return SKM_EINVAL;
+  if (m < 0 || n < 1 || d < 32 || gpr < 1) return SKM_EINVAL;
+  if (d % gpr != 0) return SKM_EINVAL;
+  if ((d / gpr) % 32 != 0) return SKM_EINVAL;
+  // indices of one launch are addressed with 32-bit table offsets and 64-bit
+  // element offsets; keep every dimension well inside those ranges
+  if (n > (int64_t(1) << 31) || d > (int64_t(1) << 31) || m > (int64_t(1) << 31)) return SKM_EINVAL;
+  return SKM_OK;
+}
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SKM_OK : SKM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sketch_version(void) { return kVersion; }
+
+const char* sketch_status_str(int status) {
+  switch (status) {
+    case SKM_OK: return "ok";
+    case SKM_EINVAL: return "invalid argument (size, bit width, group count or NULL pointer)";
+    case SKM_EUNSUPPORTED: return "unsupported dtype combination";
+    case SKM_EALIGN: return "pointer not 16-byte aligned";
+    case SKM_EWORKSPACE: return "workspace too small";
+    case SKM_EHIP: return "HIP runtime error at launch";
+    case SKM_EALIAS: return "output buffer overlaps an input buffer";
+    default: return "unknown status";
+  }
+}
+
+int sketch_unpack_indices(const uint8_t* idx_packed, int64_t n, int64_t d, int b, uint8_t* idx,
+                          hipStream_t stream) {
+  int st = check_shape(0, n, d, b, 1);
+  if (st != SKM_OK) return st;
+  if (!idx_packed || !idx) return SKM_EINVAL;
+  if (!aligned16(idx_packed) || !aligned16(idx)) return SKM_EALIGN;
+  if (overlap({idx, n * d}, {idx_packed, n * d * b / 8})) return SKM_EALIAS;
+  const Problem p{0, n, d, b, 1};
+  return status_of(skm::launch_unpack(idx_packed, p, idx, stream));
+}
+
+int sketch_dequant(const uint8_t* idx_packed, const void* lut, int lut_dtype, int64_t n, int64_t d, int b, int gpr,
+                   void* W, hipStream_t stream) {
+  int st = check_shape(0, n, d, b, gpr);
+  if (st != SKM_OK) return st;
+  if (!valid_dtype(lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!idx_packed || !lut || !W) return SKM_EINVAL;
+  if (!aligned16(idx_packed) || !aligned16(lut) || !aligned16(W)) return SKM_EALIGN;
+  const int es = elem_bytes(lut_dtype);
+  const Range out{W, n * d * es};
+  if (overlap(out, {idx_packed, n * d * b / 8}) || overlap(out, {lut, n * gpr * (int64_t(1) << b) * es}))
+    return SKM_EALIAS;
+  const Problem p{0, n, d, b, gpr};
+  return status_of(skm::launch_dequant(idx_packed, lut, lut_dtype, p, W, stream));
+}
+
+int sketch_matmul_fwd(const void* X, int x_dtype, const uint8_t* idx_packed, const void* lut, int lut_dtype,
+                      int64_t m, int64_t n, int64_t d, int b, int gpr, void* Y, hipStream_t stream) {
+  int st = check_shape(m, n, d, b, gpr);
+  if (st != SKM_OK) return st;
+  if (!supported_pair(x_dtype, lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!idx_packed || !lut) return SKM_EINVAL;
+  if (m > 0 && (!X || !Y)) return SKM_EINVAL;
+  if (!aligned16(idx_packed) || !aligned16(lut) || (X && !aligned16(X)) || (Y && !aligned16(Y))) return SKM_EALIGN;
+  const int xs = elem_bytes(x_dtype), ls = elem_bytes(lut_dtype);
+  const Range out{Y, m * n * xs};
+  if (overlap(out, {X, m * d * xs}) || overlap(out, {idx_packed, n * d * b / 8}) ||
+      overlap(out, {lut, n * gpr * (int64_t(1) << b) * ls}))
+    return SKM_EALIAS;
+  if (m == 0) return SKM_OK;
+  const Problem p{m, n, d, b, gpr};
+  if (x_dtype == SKM_F32)
+    return status_of(skm::launch_fwd_f32((const float*)X, idx_packed, (const float*)lut, p, (float*)Y, stream));
+  if (skm::decode_supported(p))
+    return status_of(skm::launch_decode(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, stream));
+  return SKM_EUNSUPPORTED;
+}
+
+size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr, int io_dtype, int lut_dtype) {
+  (void)m; (void)n; (void)d; (void)b; (void)gpr; (void)io_dtype; (void)lut_dtype;
+  return 0;
+}
+
+int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t* idx_packed, const void* lut,
+                      int lut_dtype, int64_t m, int64_t n, int64_t d, int b, int gpr, float* dX, float* dLUT,
+                      int accumulate, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(m, n, d, b, gpr);
+  if (st != SKM_OK) return st;
+  if (!supported_pair(io_dtype, lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!idx_packed || !lut) return SKM_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return SKM_EINVAL;
+  if (m > 0 && !dY && (dX || dLUT)) return SKM_EINVAL;
+  if (m > 0 && dLUT && !X) return SKM_EINVAL;
+  if (!aligned16(idx_packed) || !aligned16(lut) || (dY && !aligned16(dY)) || (X && !aligned16(X)) ||
+      (dX && !aligned16(dX)) || (dLUT && !aligned16(dLUT)))
+    return SKM_EALIGN;
+  if (workspace_bytes < sketch_matmul_bwd_workspace(m, n, d, b, gpr, io_dtype, lut_dtype)) return SKM_EWORKSPACE;
+  (void)workspace;
+  const int xs = elem_bytes(io_dtype), ls = elem_bytes(lut_dtype);
+  const int64_t K = int64_t(1) << b;
+  const Range ins[4] = {{dY, m * n * xs}, {X, m * d * xs}, {idx_packed, n * d * b / 8}, {lut, n * gpr * K * ls}};
+  const Range odx{dX, m * d * 4}, odl{dLUT, n * gpr * K * 4};
+  for (const Range& r : ins)
+    if (overlap(odx, r) || overlap(odl, r)) return SKM_EALIAS;
+  if (overlap(odx, odl)) return SKM_EALIAS;
+
+  const Problem p{m, n, d, b, gpr};
+  if (m == 0) {
+    if (dLUT && !accumulate) return status_of(skm::launch_zero_f32(dLUT, n * gpr * K, stream));
+    return SKM_OK;
+  }
+  if (io_dtype == SKM_F32) {
+    if (dX) {
+      st = status_of(skm::launch_dx_f32((const float*)dY, idx_packed, (const float*)lut, p, dX, stream));
+      if (st != SKM_OK) return st;
+    }
+    if (dLUT)
+      return status_of(skm::launch_dlut_f32((const float*)dY, (const float*)X, idx_packed, p, dLUT, accumulate,
+                                            stream));
+    return SKM_OK;
+  }
+  return SKM_EUNSUPPORTED;
+}
+
+}  // extern "C"

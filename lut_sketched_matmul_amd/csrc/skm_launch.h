@@ -1,0 +1,46 @@
+// Host-side launchers of the sketched-matmul kernels. Internal to the library:
+// the public surface is the C ABI in include/sketch_matmul.h. Every launcher
+// assumes the arguments were validated by the ABI layer and only enqueues
+// work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace skm {
+
+struct Problem {
+  int64_t m, n, d;
+  int b, gpr;
+  int k() const { return 1 << b; }
+  int64_t group_cols() const { return d / gpr; }
+  int64_t units() const { return d / 32; }
+  int64_t row_bytes() const { return d * b / 8; }
+};
+
+// checking aids
+hipError_t launch_unpack(const uint8_t* idx_packed, const Problem& p, uint8_t* idx, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* idx_packed, const void* lut, int lut_dtype, const Problem& p, void* W,
+                          hipStream_t s);
+
+// fp32 path (fp32 activations and fp32 tables)
+hipError_t launch_fwd_f32(const float* X, const uint8_t* idx, const float* lut, const Problem& p, float* Y,
+                          hipStream_t s);
+hipError_t launch_dx_f32(const float* dY, const uint8_t* idx, const float* lut, const Problem& p, float* dX,
+                         hipStream_t s);
+hipError_t launch_dlut_f32(const float* dY, const float* X, const uint8_t* idx, const Problem& p, float* dLUT,
+                           int accumulate, hipStream_t s);
+
+// fill `count` floats with zero (used instead of hipMemsetAsync so that a
+// captured graph holds only kernel nodes)
+hipError_t launch_zero_f32(float* dst, int64_t count, hipStream_t s);
+
+// matrix-core paths (16-bit operands, fp32 accumulation)
+// decode: m <= decode_max_m(), tables of one 16-row block must fit in LDS
+int decode_max_m();
+bool decode_supported(const Problem& p);
+hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
+                         const Problem& p, void* Y, hipStream_t s);
+
+}  // namespace skm

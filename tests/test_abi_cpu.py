@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+function, and rejects bad arguments before launching anything (no GPU needed:
+every call below fails its argument checks on the host)."""
+import ctypes
+
+import pytest
+
+import lut_sketched_matmul_amd as skm
+from lut_sketched_matmul_amd import _lib
+
+EINVAL, EUNSUP, EALIGN, EWS, EALIAS = -1, -2, -3, -4, -6
+A = 0x10000          # fake, 16-byte aligned "device" addresses; never dereferenced
+B_ = 0x20000000
+C = 0x40000000
+Dp = 0x60000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert {"sketch_matmul_fwd", "sketch_matmul_bwd", "sketch_matmul_bwd_workspace", "sketch_dequant",
+            "sketch_unpack_indices", "sketch_status_str", "sketch_version"} <= set(names)
+    for nme in names:
+        assert hasattr(lib, nme), nme
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, 12345):
+        assert lib.sketch_status_str(code)
+    assert lib.sketch_version() >= 100
+
+
+def fwd(lib, X=A, xdt=1, idx=B_, lut=C, ldt=1, m=4, n=64, d=512, b=4, gpr=1, Y=Dp):
+    return lib.sketch_matmul_fwd(X, xdt, idx, lut, ldt, m, n, d, b, gpr, Y, None)
+
+
+def test_fwd_rejects_bad_shapes(lib):
+    assert fwd(lib, b=1) == EINVAL
+    assert fwd(lib, b=5) == EINVAL
+    assert fwd(lib, gpr=0) == EINVAL
+    assert fwd(lib, d=512, gpr=3) == EINVAL            # d % gpr != 0
+    assert fwd(lib, d=512, gpr=32) == EINVAL           # group of 16 columns
+    assert fwd(lib, d=48) == EINVAL
+    assert fwd(lib, m=-1) == EINVAL
+    assert fwd(lib, n=0) == EINVAL
+
+
+def test_fwd_rejects_bad_pointers_and_dtypes(lib):
+    assert fwd(lib, idx=0) == EINVAL
+    assert fwd(lib, lut=0) == EINVAL
+    assert fwd(lib, X=0) == EINVAL
+    assert fwd(lib, Y=0) == EINVAL
+    assert fwd(lib, X=A + 2) == EALIGN
+    assert fwd(lib, idx=B_ + 8) == EALIGN
+    assert fwd(lib, xdt=0, ldt=1) == EUNSUP           # fp32 activations need fp32 tables
+    assert fwd(lib, xdt=1, ldt=0) == EUNSUP
+    assert fwd(lib, xdt=7) == EUNSUP
+    assert fwd(lib, Y=A) == EALIAS                    # output over the input
+    assert fwd(lib, Y=C + 16) == EALIAS
+
+
+def test_fwd_empty_is_noop(lib):
+    assert fwd(lib, m=0, X=0, Y=0) == 0
+
+
+def bwd(lib, dY=A, X=Dp, dt=1, idx=B_, lut=C, ldt=1, m=4, n=64, d=512, b=4, gpr=1, dX=0x70000000,
+        dL=0x78000000, acc=0, ws=0, wsb=0):
+    return lib.sketch_matmul_bwd(dY, X, dt, idx, lut, ldt, m, n, d, b, gpr, dX, dL, acc, ws, wsb, None)
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert bwd(lib, b=6) == EINVAL
+    assert bwd(lib, acc=2) == EINVAL
+    assert bwd(lib, dY=0) == EINVAL
+    assert bwd(lib, X=0) == EINVAL                    # dLUT needs X
+    assert bwd(lib, dX=0x70000004) == EALIGN
+    assert bwd(lib, dt=0) == EUNSUP
+    assert bwd(lib, dX=A) == EALIAS
+    assert bwd(lib, dL=0x70000000) == EALIAS          # dX and dLUT overlap
+
+
+def test_dequant_and_unpack_reject(lib):
+    assert lib.sketch_dequant(B_, C, 1, 64, 512, 7, 1, A, None) == EINVAL
+    assert lib.sketch_dequant(B_, C, 9, 64, 512, 4, 1, A, None) == EUNSUP
+    assert lib.sketch_unpack_indices(B_, 64, 40, 4, A, None) == EINVAL
+    assert lib.sketch_unpack_indices(B_, 64, 512, 4, B_, None) == EALIAS
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setenv("SKETCHMM_LIB", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()

@@ -1,0 +1,164 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: unpacked indices, dequantised W, selection inputs (one-hot rows of
+X pick single weights), the identity example. Floating point: every output
+tensor scored as max|gpu - oracle| / max|oracle| <= 5e-3 for 16-bit I/O with
+fp32 accumulation and <= 1e-5 for the fp32 path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from lut_sketched_matmul_amd import synthetic as syn
+from lut_sketched_matmul_amd import workloads as wl
+
+from gpu_util import round_to, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL16 = 5e-3
+TOL32 = 1e-5
+
+
+def skm():
+    import lut_sketched_matmul_amd as m
+    return m
+
+
+def make_case(tag, n, d, b, gpr, m, x_dtype="f16", lut_dtype="f16", lut_sigma=0.02, dy_sigma=1.0):
+    idx = syn.random_packed_indices(f"{tag}/idx", n, d, b)
+    lut = syn.random_lut(f"{tag}/lut", n, gpr, b, lut_sigma, lut_dtype)
+    X = syn.random_normal(f"{tag}/X", (m, d), 1.0, x_dtype)
+    dY = syn.random_normal(f"{tag}/dY", (m, n), dy_sigma, x_dtype)
+    return idx, lut, X, dY
+
+
+# ---------------------------------------------------------------------------
+# bit-exact checking aids
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("n,d", [(5, 32), (37, 480), (64, 4096)])
+def test_unpack_bit_exact(b, n, d):
+    idx = syn.random_packed_indices(f"unpack/{b}/{n}/{d}", n, d, b)
+    got = skm().sketch_unpack_indices(to_dev(idx, "u8"), d, b).cpu().numpy()
+    assert np.array_equal(got.astype(np.int64), oracle.unpack_indices(idx, d, b))
+
+
+@pytest.mark.parametrize("lut_dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("b,gpr,n,d", [(2, 1, 16, 64), (3, 4, 33, 512), (4, 8, 40, 4096), (3, 8, 17, 11008)])
+def test_dequant_bit_exact(lut_dtype, b, gpr, n, d):
+    idx, lut, _, _ = make_case(f"deq/{lut_dtype}/{b}/{gpr}/{n}/{d}", n, d, b, gpr, 1, lut_dtype=lut_dtype)
+    W = skm().sketch_dequant(to_dev(idx, "u8"), to_dev(lut, lut_dtype), d, b, gpr)
+    want = oracle.dequantize(idx, syn.to_float64(lut, lut_dtype), d, b, gpr)
+    assert np.array_equal(to_f64(W), want)
+
+
+# ---------------------------------------------------------------------------
+# fp32 path (tiny single layer, forward and backward)
+# ---------------------------------------------------------------------------
+
+def _check_fp32(idx, lut, X, dY, b, gpr, d):
+    dev = dict(idx=to_dev(idx, "u8"), lut=to_dev(lut, "f32"), X=to_dev(X, "f32"), dY=to_dev(dY, "f32"))
+    Y = skm().sketch_matmul_fwd(dev["X"], dev["idx"], dev["lut"], b, gpr)
+    L64, X64, dY64 = lut.astype(np.float64), X.astype(np.float64), dY.astype(np.float64)
+    assert oracle.rel_err(to_f64(Y), oracle.forward(X64, idx, L64, b, gpr)) <= TOL32
+    dX, dL = skm().sketch_matmul_bwd(dev["dY"], dev["X"], dev["idx"], dev["lut"], b, gpr)
+    assert oracle.rel_err(to_f64(dX), oracle.backward_dx(dY64, idx, L64, d, b, gpr)) <= TOL32
+    assert oracle.rel_err(to_f64(dL), oracle.backward_dlut(dY64, X64, idx, b, gpr)) <= TOL32
+
+
+def test_tiny_workload_fp32():
+    w = wl.TINY
+    s = w.shapes[0]
+    t = w.make(s, 4, 4)
+    _check_fp32(t["idx_packed"], t["lut"], t["X"], t["dY"], 4, w.gpr, s.d)
+
+
+@pytest.mark.parametrize("b,gpr,n,d,m", [(2, 2, 19, 256, 3), (3, 1, 50, 96, 9), (4, 4, 7, 512, 1)])
+def test_fp32_ragged(b, gpr, n, d, m):
+    idx, lut, X, dY = make_case(f"f32r/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, "f32", "f32")
+    _check_fp32(idx, lut, X, dY, b, gpr, d)
+
+
+# ---------------------------------------------------------------------------
+# 16-bit forward
+# ---------------------------------------------------------------------------
+
+def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
+    Y = skm().sketch_matmul_fwd(to_dev(X, x_dtype), to_dev(idx, "u8"), to_dev(lut, lut_dtype), b, gpr)
+    got = to_f64(Y)
+    X64 = syn.to_float64(X, x_dtype)
+    L64 = syn.to_float64(lut, lut_dtype)
+    if rows is None:
+        return got, oracle.forward(X64, idx, L64, b, gpr)
+    return got[:, rows], oracle.forward(X64, idx[rows], L64[rows], b, gpr)
+
+
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 8, 4096, 4096, 1), (4, 1, 100, 160, 3), (2, 2, 257, 1024, 16), (3, 4, 77, 1536, 5),
+    (2, 8, 300, 11008, 4), (3, 8, 48, 11008, 16), (4, 4, 64, 8192, 2),
+])
+def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
+    idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
+                               x_dtype, lut_dtype)
+    got, want = _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+def _workload_rows(n, seed):
+    r = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(0, 32), np.arange(n - 32, n), r.choice(n, 448, replace=False)])
+    return np.unique(rows)
+
+
+@pytest.mark.parametrize("wname", [wl.LLAMA2_7B_ATTN.name, wl.LLAMA2_7B_MLP_LOWBIT.name, wl.LLAMA3_70B_MLP.name])
+def test_fwd_workloads(wname):
+    """Every (shape, b, m) of the forward workloads at full size; sampled rows."""
+    w = wl.BY_NAME[wname]
+    worst = 0.0
+    for s, b, m in wl.runs(w):
+        t = w.make(s, b, m)
+        rows = _workload_rows(s.n, s.n + m + b)
+        got, want = _fwd16(t["idx_packed"], t["lut"], t["X"], b, w.gpr, w.x_dtype, w.lut_dtype, rows)
+        e = oracle.rel_err(got, want)
+        worst = max(worst, e)
+        assert e <= w.tol, (s.name, b, m, e)
+    print(f"{wname}: worst rel err {worst:.3e}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("m", [1, 7, 16])
+def test_fwd_selection_bit_exact(dt, m):
+    """X rows are one-hot: Y[t, i] = W[i, j_t] exactly (one non-zero product)."""
+    b, gpr, n, d = 4, 8, 80, 4096
+    idx, lut, _, _ = make_case(f"sel/{dt}/{m}", n, d, b, gpr, 1, dt, dt)
+    cols = np.random.default_rng(m).choice(d, m, replace=False)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    Xs = syn.to_storage(X, dt)
+    Y = skm().sketch_matmul_fwd(to_dev(Xs, dt), to_dev(idx, "u8"), to_dev(lut, dt), b, gpr)
+    W = oracle.dequantize(idx, syn.to_float64(lut, dt), d, b, gpr)
+    assert np.array_equal(to_f64(Y), W[:, cols].T)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_fwd_identity_exact(b):
+    """SpaLLM section 2.4: the identity sketched with the two values 0 and 1."""
+    n, gpr, m = 256, 4, 5
+    k = 1 << b
+    lut = np.full((n, gpr, k), 0.5, dtype=np.float32)
+    lut[:, :, 0] = 0.0
+    lut[:, :, 1] = 1.0
+    idx = oracle.pack_indices(np.eye(n, dtype=np.int64), b)
+    X = syn.random_normal(f"ident/{b}", (m, n), 1.0, "f16")
+    Y = skm().sketch_matmul_fwd(to_dev(X, "f16"), to_dev(idx, "u8"), to_dev(syn.to_storage(lut, "f16"), "f16"), b, gpr)
+    assert np.array_equal(to_f64(Y), syn.to_float64(X, "f16"))
+
+
+def test_fwd_deterministic():
+    idx, lut, X, _ = make_case("det", 1000, 4096, 4, 8, 4)
+    a = skm().sketch_matmul_fwd(to_dev(X, "f16"), to_dev(idx, "u8"), to_dev(lut, "f16"), 4, 8)
+    b_ = skm().sketch_matmul_fwd(to_dev(X, "f16"), to_dev(idx, "u8"), to_dev(lut, "f16"), 4, 8)
+    assert bool((a == b_).all())
