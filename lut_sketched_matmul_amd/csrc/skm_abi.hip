@@ -112,6 +112,8 @@ int sketch_matmul_fwd(const void* X, int x_dtype, const uint8_t* idx_packed, con
     return status_of(skm::launch_fwd_f32((const float*)X, idx_packed, (const float*)lut, p, (float*)Y, stream));
   if (skm::decode_supported(p))
     return status_of(skm::launch_decode(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, stream));
+  if (skm::gemm_fwd_supported(p))
+    return status_of(skm::launch_gemm_fwd(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, stream));
   return SKM_EUNSUPPORTED;
 }
 
@@ -158,7 +160,13 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
                                             stream));
     return SKM_OK;
   }
-  return SKM_EUNSUPPORTED;
+  if (!skm::gemm_bwd_supported(p)) return SKM_EUNSUPPORTED;
+  if (dX) {
+    st = status_of(skm::launch_gemm_dx(dY, io_dtype, idx_packed, lut, lut_dtype, p, dX, stream));
+    if (st != SKM_OK) return st;
+  }
+  if (dLUT) return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, stream));
+  return SKM_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,545 @@
+// Matrix-core backward kernels of the sketched matmul (gfx950):
+//
+//   dX[t][j]      = sum_i dY[t][i] W[i][j]                      (k_gemm_dx)
+//   dLUT[i][g][c] = sum_{j in g, idx[i][j] = c} sum_t dY[t][i] X[t][j]
+//                                                              (k_gemm_dlut)
+//
+// The table gradient is the corrected Eq. (6) of the "Sketch to Adapt"
+// discussion (dL/dw = dL/dy (M X)^T) taken row by row: the gradient of every
+// virtual parameter W[i][j] is summed into the table entry it maps to. The
+// mapping is frozen ("SpaLLM", section 2.3), so there is no index gradient.
+// dX is the chain rule through Y = X W^T, needed to train lower layers.
+//
+// k_gemm_dx: M = tokens (256), N = columns of dX (128), K = weight rows (32
+// per step). The weight tile of 32 rows x 128 columns is dequantised once per
+// step and written transposed ([column][row]) so each MFMA B fragment is 8
+// consecutive rows of one column. Each step brings 32 new rows, so the tables
+// (up to 4 groups of the column tile, private copy per lane slot) are staged
+// every step, two steps ahead.
+//
+// k_gemm_dlut: one block owns 128 rows x one group. For each 128-column chunk
+// of the group it accumulates the dW = dY^T X tile over all tokens (K = 32
+// tokens per step, operands transposed into [row][token] / [column][token]
+// LDS tiles), then scatter-adds the tile into LDS bins [row][entry] using the
+// chunk's indices staged in LDS. Waves own disjoint (row, bin copy) pairs, so
+// the bins need no cross-wave atomics and the sums are deterministic; the
+// block stores each gradient entry exactly once (no global atomics).
+#include "skm_gemm_common.h"
+#include "skm_launch.h"
+
+namespace skm {
+
+namespace {
+
+using namespace mm;
+
+// ============================================================================
+// dX
+// ============================================================================
+constexpr int DX_BM = 256, DX_BN = 128, DX_BK = 32, DX_NG = 4;
+constexpr uint32_t DX_A = 0;                                   // [2][256][32] dY (compute dtype)
+constexpr uint32_t DX_B = 2u * DX_BM * DX_BK * 2u;             // 32768: [2][128 cols][32 rows]
+constexpr uint32_t DX_T = DX_B + 2u * DX_BN * DX_BK * 2u;      // 49152: tables [2][NG][T][64] dwords
+constexpr uint32_t DX_LDS = DX_T + 2u * DX_NG * 16u * 64u * 4u;  // 81920
+
+template <int B> struct DxIdx { uint32_t w[B == 3 ? 3 : (B == 4 ? 2 : 1)]; };
+
+template <int B>
+__device__ __forceinline__ void dx_load_idx(DxIdx<B>& I, const uint8_t* rowp, uint32_t u, int hh) {
+  if constexpr (B == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(rowp + u * 16u + hh * 8);
+    I.w[0] = v.x;
+    I.w[1] = v.y;
+  } else if constexpr (B == 2) {
+    I.w[0] = *reinterpret_cast<const uint32_t*>(rowp + u * 8u + hh * 4);
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(rowp + u * 12u);
+    I.w[0] = p[0];
+    I.w[1] = p[1];
+    I.w[2] = p[2];
+  }
+}
+
+// 16 weights of half hh of a unit -> 8 words of packed consecutive columns
+template <int B>
+__device__ __forceinline__ void dx_dequant(const DxIdx<B>& I, int hh, uint32_t gk, uint32_t lane4, uint32_t* o) {
+  const uint32_t gk4 = gk * 0x01010101u;
+  if constexpr (B == 4) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t ev = (I.w[j] & 0x0F0F0F0Fu) | gk4;
+      const uint32_t od = ((I.w[j] >> 4) & 0x0F0F0F0Fu) | gk4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[4 * j + t] = pack2(ld_h(gaddr(ev, lane4, t) + DX_T), ld_h(gaddr(od, lane4, t) + DX_T));
+    }
+  } else if constexpr (B == 2) {
+    const uint32_t ev = (I.w[0] & 0x0F0F0F0Fu) | gk4;
+    const uint32_t od = ((I.w[0] >> 4) & 0x0F0F0F0Fu) | gk4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o[2 * t] = ld_w(gaddr(ev, lane4, t) + DX_T);
+      o[2 * t + 1] = ld_w(gaddr(od, lane4, t) + DX_T);
+    }
+  } else {
+    if (hh) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t e0 = unit_field<3>(I.w, 16 + 2 * t), e1 = unit_field<3>(I.w, 17 + 2 * t);
+        o[t] = pack2(ld_h((((gk + e0) << 8) | lane4) + DX_T), ld_h((((gk + e1) << 8) | lane4) + DX_T));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t e0 = unit_field<3>(I.w, 2 * t), e1 = unit_field<3>(I.w, 1 + 2 * t);
+        o[t] = pack2(ld_h((((gk + e0) << 8) | lane4) + DX_T), ld_h((((gk + e1) << 8) | lane4) + DX_T));
+      }
+    }
+  }
+}
+
+// Tables of step rows k0..k0+31, groups glo..glo+ng-1, into buffer tb:
+// slot s (lane id) holds row k0 + s%32; wave w writes entries [w*T/4, (w+1)*T/4).
+template <int B> struct DxLut { uint32_t v[2]; };
+
+template <int B, typename TL>
+__device__ __forceinline__ void dx_load_lut(DxLut<B>& L, const TL* lut, int64_t row, bool row_ok, int gpr, uint32_t g,
+                                            int w) {
+  constexpr int K = 1 << B;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(lut) + ((int64_t)row * gpr + g) * K;
+  if (!row_ok) {
+    L.v[0] = L.v[1] = 0u;
+    return;
+  }
+  if constexpr (B == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src + 4 * w);
+    L.v[0] = v.x;
+    L.v[1] = v.y;
+  } else if constexpr (B == 3) {
+    L.v[0] = *reinterpret_cast<const uint32_t*>(src + 2 * w);
+    L.v[1] = 0u;
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+    L.v[0] = v.x;
+    L.v[1] = v.y;
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void dx_store_lut(const DxLut<B>& L, uint32_t tb, uint32_t gsel, int w, uint32_t lane4) {
+  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
+  const uint32_t base = (tb * DX_NG + gsel) * T;
+  if constexpr (B == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = (i & 1) ? (L.v[i >> 1] >> 16) : (L.v[i >> 1] & 0xFFFFu);
+      st_w(DX_T + ((base + 4u * w + i) << 8) + lane4, v);
+    }
+  } else if constexpr (B == 3) {
+    st_w(DX_T + ((base + 2u * w) << 8) + lane4, L.v[0] & 0xFFFFu);
+    st_w(DX_T + ((base + 2u * w + 1) << 8) + lane4, L.v[0] >> 16);
+  } else {
+    const uint32_t e[4] = {L.v[0] & 0xFFFFu, L.v[0] >> 16, L.v[1] & 0xFFFFu, L.v[1] >> 16};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pe = 4 * w + i;
+      st_w(DX_T + ((base + pe) << 8) + lane4, e[pe & 3] | (e[pe >> 2] << 16));
+    }
+  }
+}
+
+// dY tile row (32 weight rows starting at k0) of one token -> compute dtype
+template <typename TX, typename TC>
+__device__ __forceinline__ void dx_load_a(u32x4* a, const TX* dyrow, int64_t k0, int64_t n, bool vec) {
+  if (vec && k0 + 32 <= n) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(dyrow + k0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = p[c];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(dyrow);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i0 = k0 + 8 * c + 2 * q;
+        const uint32_t lo = i0 < n ? p[i0] : 0u;
+        const uint32_t hi = i0 + 1 < n ? p[i0 + 1] : 0u;
+        a[c][q] = lo | (hi << 16);
+      }
+  }
+}
+
+template <int B, typename TX, typename TL>
+__global__ void __launch_bounds__(256, 1)
+k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut, int64_t m,
+          int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX) {
+  typedef mfma32<TL> MF;
+  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
+  extern __shared__ uint32_t smem[];
+  (void)smem;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
+  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;   // token / column tile origins
+  const bool vec = (n % 8) == 0;
+
+  // dequant role: weight row r of the step, 16-column chunk c of the tile
+  const int r = t & 31;
+  const int c = t >> 5;
+  const int hh = c & 1;
+  const int64_t jc = n0 + 16 * c;                   // first column of the chunk
+  const bool col_ok = jc < d;
+  const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
+  const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
+  const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
+  const uint32_t ng = ghi - glo + 1;                // groups touched by the column tile (<= 4)
+  const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
+  // activation role: token row t
+  const int64_t gtok = (m0 + t < m) ? m0 + t : m - 1;
+  const TX* dyrow = dY + gtok * n;
+
+  const int64_t rb = d * B / 8;
+  const uint32_t KS = (uint32_t)((n + DX_BK - 1) / DX_BK);  // K-steps
+
+  auto stage_tables = [&](uint32_t ks, uint32_t tb) {
+    const int64_t row = (int64_t)ks * DX_BK + (lane & 31);
+    const bool ok = row < n;
+    for (uint32_t gs = 0; gs < ng; ++gs) {
+      DxLut<B> L;
+      dx_load_lut<B, TL>(L, lut, ok ? row : 0, ok, gpr, glo + gs, wave);
+      dx_store_lut<B>(L, tb, gs, wave, lane4);
+    }
+  };
+  auto dequant_step = [&](uint32_t ks, uint32_t buf) {
+    const int64_t row = (int64_t)ks * DX_BK + r;
+    const bool ok = row < n && col_ok;
+    uint32_t o[8];
+    DxIdx<B> I;
+    dx_load_idx<B>(I, idx_packed + (ok ? row : 0) * rb, u, hh);
+    dx_dequant<B>(I, hh, ((ks & 1u) * DX_NG + gsel) * T, lane4, o);
+    const uint32_t bb = DX_B + buf * (uint32_t)(DX_BN * DX_BK * 2);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const uint32_t v = ok ? ((f & 1) ? (o[f >> 1] >> 16) : (o[f >> 1] & 0xFFFFu)) : 0u;
+      st_h(bb + swz_elem((uint32_t)(16 * c + f), (uint32_t)r), v);
+    }
+  };
+  auto store_a = [&](const u32x4* a, uint32_t buf) {
+    const uint32_t ab = DX_A + buf * (uint32_t)(DX_BM * DX_BK * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st_q(ab + swz((uint32_t)t, (uint32_t)q), cvt_quad<TX, TL>(a[q]));
+  };
+
+  // ---- prologue
+  u32x4 a[4];
+  stage_tables(0, 0);
+  if (KS > 1) stage_tables(1, 1);
+  dx_load_a<TX, TL>(a, dyrow, 0, n, vec);
+  __syncthreads();
+  dequant_step(0, 0);
+  store_a(a, 0);
+  __syncthreads();
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zero16(acc[i][j]);
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
+  const uint32_t khalf = (uint32_t)(lane >> 5);
+
+  for (uint32_t k = 0; k < KS; ++k) {
+    const uint32_t cur = k & 1u;
+    const bool more = k + 1 < KS;
+    if (more) dx_load_a<TX, TL>(a, dyrow, (int64_t)(k + 1) * DX_BK, n, vec);
+    const uint32_t abase = DX_A + cur * (uint32_t)(DX_BM * DX_BK * 2);
+    const uint32_t bbase = DX_B + cur * (uint32_t)(DX_BN * DX_BK * 2);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+      u32x4 af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = ld_q(abase + swz(arow + 32u * i, ch));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = ld_q(bbase + swz(brow + 32u * j, ch));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(af[i], bf[j], acc[i][j]);
+    }
+    if (more) {
+      dequant_step(k + 1, cur ^ 1u);
+      store_a(a, cur ^ 1u);
+      if (k + 2 < KS) stage_tables(k + 2, cur);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + 64 * wn + 32 * j + (lane & 31);
+      if (col >= d) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (tok < m) dX[tok * d + col] = acc[i][j][e];
+      }
+    }
+}
+
+// ============================================================================
+// dLUT
+// ============================================================================
+constexpr int DL_BM = 128, DL_BN = 128, DL_BK = 32;
+constexpr uint32_t DL_A = 0;                                  // [2][128 rows][32 tokens]
+constexpr uint32_t DL_B = 2u * DL_BM * DL_BK * 2u;            // 16384: [2][128 cols][32 tokens]
+constexpr uint32_t DL_I = DL_B + 2u * DL_BN * DL_BK * 2u;     // 32768: packed indices [128 rows][16*B bytes]
+constexpr uint32_t DL_BINS = DL_I + 128u * 64u;               // 40960: [2][128 rows][16] fp32
+constexpr uint32_t DL_LDS = DL_BINS + 2u * 128u * 16u * 4u;   // 57344
+
+// 16 consecutive 16-bit values of row `rowp` starting at element e0 (zero past `lim`)
+template <typename TS>
+__device__ __forceinline__ void dl_load16(uint32_t* v, const TS* rowp, int64_t e0, int64_t lim, bool vec) {
+  if (vec && e0 + 16 <= lim) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(rowp + e0);
+    const u32x4 x0 = p[0], x1 = p[1];
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t i = e0 + 2 * q;
+      const uint32_t lo = i < lim ? p[i] : 0u;
+      const uint32_t hi = i + 1 < lim ? p[i + 1] : 0u;
+      v[q] = lo | (hi << 16);
+    }
+  }
+}
+
+// field j of the packed row staged at LDS byte address `row` (16*B bytes per row)
+template <int B>
+__device__ __forceinline__ uint32_t dl_field(uint32_t row, uint32_t j) {
+  const uint32_t bit = j * (uint32_t)B;
+  const uint32_t w = ld_w(row + ((bit >> 5) << 2));
+  const uint32_t off = bit & 31u;
+  if constexpr (B == 3) {
+    if (off > 29u) {
+      const uint32_t w2 = ld_w(row + ((bit >> 5) << 2) + 4u);
+      return __builtin_amdgcn_alignbit(w2, w, off) & 7u;
+    }
+  }
+  return (w >> off) & ((1u << B) - 1u);
+}
+
+template <int B, typename TX>
+__global__ void __launch_bounds__(256, 1)
+k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
+            int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
+  typedef mfma32<TX> MF;
+  constexpr int K = 1 << B;
+  extern __shared__ uint32_t smem[];
+  (void)smem;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int64_t i0 = (int64_t)(blockIdx.x / gpr) * DL_BM;
+  const int g = (int)(blockIdx.x % gpr);
+  const int64_t G = d / gpr;
+  const int64_t jg0 = (int64_t)g * G;              // first column of the group
+  const bool vy = (n % 8) == 0, vx = (d % 8) == 0;
+
+  // zero the bins
+  for (uint32_t q = (uint32_t)t; q < 2u * 128u * 16u; q += 256u) st_w(DL_BINS + q * 4u, 0u);
+
+  // operand staging role: token tt of the step, 16-element chunk rc
+  const int tt = t & 31;
+  const int rc = t >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t arow = (uint32_t)(64 * wm + (lane & 31));
+  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
+  const uint32_t khalf = (uint32_t)(lane >> 5);
+  const uint32_t KS = (uint32_t)((m + DL_BK - 1) / DL_BK);
+
+  auto load_step = [&](uint32_t ks, int64_t j0, uint32_t* ya, uint32_t* xb) {
+    const int64_t tok = (int64_t)ks * DL_BK + tt;
+    const bool tok_ok = tok < m;
+    const int64_t tr = tok_ok ? tok : 0;
+    // dY[tok][i0 + 16 rc ..], zero past row n or token m
+    dl_load16<TX>(ya, dY + tr * n, i0 + 16 * rc, tok_ok ? n : 0, vy);
+    // X[tok][j0 + 16 rc ..], zero past the group end
+    const int64_t jend = jg0 + G;
+    dl_load16<TX>(xb, X + tr * d, j0 + 16 * rc, tok_ok ? jend : 0, vx);
+  };
+  auto store_step = [&](uint32_t buf, const uint32_t* ya, const uint32_t* xb) {
+    const uint32_t ab = DL_A + buf * (uint32_t)(DL_BM * DL_BK * 2);
+    const uint32_t bb = DL_B + buf * (uint32_t)(DL_BN * DL_BK * 2);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const uint32_t yv = (f & 1) ? (ya[f >> 1] >> 16) : (ya[f >> 1] & 0xFFFFu);
+      const uint32_t xv = (f & 1) ? (xb[f >> 1] >> 16) : (xb[f >> 1] & 0xFFFFu);
+      st_h(ab + swz_elem((uint32_t)(16 * rc + f), (uint32_t)tt), yv);
+      st_h(bb + swz_elem((uint32_t)(16 * rc + f), (uint32_t)tt), xv);
+    }
+  };
+
+  for (int64_t j0 = jg0; j0 < jg0 + G; j0 += DL_BN) {
+    __syncthreads();  // the previous chunk's binning is done with the staged indices
+    // stage this chunk's packed indices: 128 rows x (128 * B / 8) bytes as dwords
+    {
+      const int row = t >> 1;
+      const int64_t grow = i0 + row < n ? i0 + row : n - 1;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
+      const int64_t avail_units = (jg0 + G - j0) / 32;  // units of the chunk inside the group
+      const int words = 4 * B;                           // dwords per 128 columns
+#pragma unroll
+      for (int q = 0; q < 2 * B; ++q) {
+        const int wd = (t & 1) * 2 * B + q;
+        const bool in = (wd / B) < avail_units;          // unit wd/B of the chunk exists
+        st_w(DL_I + (uint32_t)row * 64u + (uint32_t)wd * 4u, in ? src[wd] : 0u);
+      }
+      (void)words;
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) zero16(acc[a][b]);
+
+    uint32_t ya[8], xb[8];
+    load_step(0, j0, ya, xb);
+    store_step(0, ya, xb);
+    __syncthreads();
+    for (uint32_t k = 0; k < KS; ++k) {
+      const uint32_t cur = k & 1u;
+      const bool more = k + 1 < KS;
+      if (more) load_step(k + 1, j0, ya, xb);
+      const uint32_t abase = DL_A + cur * (uint32_t)(DL_BM * DL_BK * 2);
+      const uint32_t bbase = DL_B + cur * (uint32_t)(DL_BN * DL_BK * 2);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+        u32x4 af[2], bf[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) af[a] = ld_q(abase + swz(arow + 32u * a, ch));
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bf[b] = ld_q(bbase + swz(brow + 32u * b, ch));
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[a][b] = MF::run(af[a], bf[b], acc[a][b]);
+      }
+      if (more) store_step(cur ^ 1u, ya, xb);
+      __syncthreads();
+    }
+
+    // ---- scatter-add the finished dW tile into this wave's bins
+    // D[i][j] of tile (a, b): i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4, j = 64 wn + 32 b + lane%32
+    const uint32_t binbase = DL_BINS + (uint32_t)wn * (128u * 16u * 4u);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint32_t j = (uint32_t)(64 * wn + 32 * b + (lane & 31));
+        const bool j_ok = j0 + (int64_t)j < jg0 + G;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t i = (uint32_t)(64 * wm + 32 * a + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3));
+          if (j_ok && i0 + (int64_t)i < n) {
+            const uint32_t c = dl_field<B>(DL_I + i * 64u, j);
+            __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * 16u + c) * 4u), acc[a][b][e],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+      }
+  }
+  __syncthreads();
+
+  // ---- one store per gradient entry
+  for (uint32_t q = (uint32_t)t; q < 128u * (uint32_t)K; q += 256u) {
+    const uint32_t i = q / K, c = q % K;
+    if (i0 + (int64_t)i >= n) continue;
+    const float s = *(const lds_f32*)(uintptr_t)(DL_BINS + (i * 16u + c) * 4u) +
+                    *(const lds_f32*)(uintptr_t)(DL_BINS + 128u * 16u * 4u + (i * 16u + c) * 4u);
+    float* dst = dLUT + ((i0 + i) * gpr + g) * K + c;
+    *dst = accumulate ? *dst + s : s;
+  }
+}
+
+// ---- launchers ---------------------------------------------------------------
+
+uint32_t ug_magic_of(const Problem& p) {
+  const uint32_t ug = (uint32_t)(p.group_cols() / 32);
+  return ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
+}
+
+template <int B, typename TX, typename TL>
+hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+  const auto kern = k_gemm_dx<B, TX, TL>;
+  // more than 64 KB of LDS per block must be requested once per kernel
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, DX_LDS);
+  if (attr != hipSuccess) return attr;
+  const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
+  const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(256), DX_LDS, s, dY, idx, lut, p.m, p.n, p.d, p.gpr,
+                     ug_magic_of(p), mb, dX);
+  return hipGetLastError();
+}
+
+template <typename TX, typename TL>
+hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+  switch (p.b) {
+    case 2: return dx_b<2>(dY, idx, lut, p, dX, s);
+    case 3: return dx_b<3>(dY, idx, lut, p, dX, s);
+    default: return dx_b<4>(dY, idx, lut, p, dX, s);
+  }
+}
+
+template <int B, typename TX>
+hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
+                  hipStream_t s) {
+  const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
+  hipLaunchKernelGGL((k_gemm_dlut<B, TX>), dim3((unsigned)(rb * p.gpr)), dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n,
+                     p.d, p.gpr, dLUT, accumulate);
+  return hipGetLastError();
+}
+
+template <typename TX>
+hipError_t dlut_t(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
+                  hipStream_t s) {
+  switch (p.b) {
+    case 2: return dlut_b<2>(dY, X, idx, p, dLUT, accumulate, s);
+    case 3: return dlut_b<3>(dY, X, idx, p, dLUT, accumulate, s);
+    default: return dlut_b<4>(dY, X, idx, p, dLUT, accumulate, s);
+  }
+}
+
+}  // namespace
+
+bool gemm_bwd_supported(const Problem& p) { return p.d <= (int64_t(1) << 20); }
+
+hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
+                          const Problem& p, float* dX, hipStream_t s) {
+  if (io_dtype == DT_F16 && lut_dtype == DT_F16) return dx_t((const half_t*)dY, idx, (const half_t*)lut, p, dX, s);
+  if (io_dtype == DT_BF16 && lut_dtype == DT_F16) return dx_t((const bf16_t*)dY, idx, (const half_t*)lut, p, dX, s);
+  if (io_dtype == DT_F16 && lut_dtype == DT_BF16) return dx_t((const half_t*)dY, idx, (const bf16_t*)lut, p, dX, s);
+  return dx_t((const bf16_t*)dY, idx, (const bf16_t*)lut, p, dX, s);
+}
+
+hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
+                            float* dLUT, int accumulate, hipStream_t s) {
+  if (io_dtype == DT_F16) return dlut_t((const half_t*)dY, (const half_t*)X, idx, p, dLUT, accumulate, s);
+  return dlut_t((const bf16_t*)dY, (const bf16_t*)X, idx, p, dLUT, accumulate, s);
+}
+
+}  // namespace skm

@@ -1,0 +1,113 @@
+// Shared pieces of the tiled matrix-core kernels (forward GEMM, dX, dLUT):
+// LDS access by absolute address, the swizzled 64-byte row layout, MFMA
+// wrappers, activation conversion and the per-lane gather address.
+#pragma once
+
+#include "skm_common.h"
+
+namespace skm {
+namespace mm {
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// Kernels that use these helpers allocate only dynamic LDS, which therefore
+// starts at address 0, and address it with absolute byte offsets.
+__device__ __forceinline__ uint32_t ld_h(uint32_t a) { return *(const lds_u16*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t ld_w(uint32_t a) { return *(const lds_u32*)(uintptr_t)a; }
+__device__ __forceinline__ u32x4 ld_q(uint32_t a) { return *(const lds_u32x4*)(uintptr_t)a; }
+__device__ __forceinline__ void st_h(uint32_t a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (uint16_t)v; }
+__device__ __forceinline__ void st_w(uint32_t a, uint32_t v) { *(lds_u32*)(uintptr_t)a = v; }
+__device__ __forceinline__ void st_q(uint32_t a, u32x4 v) { *(lds_u32x4*)(uintptr_t)a = v; }
+
+// 64-byte rows of four 16-byte chunks; chunk c of row r is stored at
+// c ^ ((r >> 1) & 3) so that 8 consecutive rows read by one ds_read_b128 pass
+// cover all banks.
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
+}
+// byte offset of 16-bit element e (0..31) of row r in the same layout
+__device__ __forceinline__ uint32_t swz_elem(uint32_t row, uint32_t e) {
+  return swz(row, e >> 3) + ((e & 7u) << 1);
+}
+
+// gather address: lane slot in byte 0, entry number from byte-lane p of `ent`
+__device__ __forceinline__ uint32_t gaddr(uint32_t ent, uint32_t lane4, int p) {
+  return __builtin_amdgcn_perm(ent, lane4, 0x0C0C0400u | ((4u + (uint32_t)p) << 8));
+}
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <int B> struct tab_entries { static constexpr int value = (B == 2) ? 16 : (1 << B); };
+
+template <typename TC> struct mfma32;
+template <> struct mfma32<half_t> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  }
+};
+template <> struct mfma32<bf16_t> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  }
+};
+
+// Convert two 16-bit values packed in a word from storage TS to compute TC.
+// (Goes through 16-bit integers: this hipcc miscompiles a bit-cast of a vector
+// element to a 2 x f16 vector into a splat of element 0.)
+template <typename TS, typename TC>
+__device__ __forceinline__ uint32_t cvt_word(uint32_t w) {
+  if constexpr (__is_same(TS, TC)) {
+    return w;
+  } else {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    float lo, hi;
+    if constexpr (__is_same(TS, bf16_t)) {
+      lo = __builtin_bit_cast(float, w << 16);
+      hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    } else {
+      lo = (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xFFFFu));
+      hi = (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
+    }
+    if constexpr (__is_same(TC, half_t)) {
+      f16x2_t r;
+      r.x = (half_t)lo;
+      r.y = (half_t)hi;
+      return __builtin_bit_cast(uint32_t, r);
+    } else {
+      bf16x2_t r;
+      r.x = (bf16_t)lo;
+      r.y = (bf16_t)hi;
+      return __builtin_bit_cast(uint32_t, r);
+    }
+  }
+}
+
+template <typename TS, typename TC>
+__device__ __forceinline__ u32x4 cvt_quad(u32x4 v) {
+  if constexpr (__is_same(TS, TC)) {
+    return v;
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = cvt_word<TS, TC>(v[q]);
+    return o;
+  }
+}
+
+__device__ __forceinline__ void zero16(f32x16& a) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a[e] = 0.0f;
+}
+
+// group index of unit u: multiply-high by the host's magic (0 = one unit/group)
+__device__ __forceinline__ uint32_t group_of(uint32_t u, uint32_t magic) { return magic ? __umulhi(u, magic) : u; }
+
+}  // namespace mm
+}  // namespace skm

@@ -43,4 +43,16 @@ bool decode_supported(const Problem& p);
 hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
                          const Problem& p, void* Y, hipStream_t s);
 
+// prefill / training forward: m > 16, tiled matrix-core GEMM
+bool gemm_fwd_supported(const Problem& p);
+hipError_t launch_gemm_fwd(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
+                           const Problem& p, void* Y, hipStream_t s);
+
+// backward on the matrix cores (16-bit operands, fp32 results)
+bool gemm_bwd_supported(const Problem& p);
+hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
+                          const Problem& p, float* dX, hipStream_t s);
+hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
+                            float* dLUT, int accumulate, hipStream_t s);
+
 }  // namespace skm

@@ -107,6 +107,32 @@ def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     assert oracle.rel_err(got, want) <= TOL16
 
 
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 8, 200, 4096, 300), (4, 1, 64, 512, 17), (2, 8, 130, 11008, 40), (3, 4, 257, 1536, 513),
+    (2, 2, 96, 1024, 256), (3, 8, 128, 11008, 33), (4, 4, 300, 8192, 260),
+])
+def test_fwd16_gemm(x_dtype, lut_dtype, b, gpr, n, d, m):
+    """m > 16 runs the tiled matrix-core GEMM: ragged token and row tiles."""
+    idx, lut, X, _ = make_case(f"gemm16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
+                               x_dtype, lut_dtype)
+    got, want = _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_gemm_selection_bit_exact(dt):
+    """m > 16 one-hot rows through the GEMM: Y[t, i] = W[i, j_t] exactly."""
+    b, gpr, n, d, m = 4, 8, 150, 4096, 70
+    idx, lut, _, _ = make_case(f"gsel/{dt}", n, d, b, gpr, 1, dt, dt)
+    cols = np.random.default_rng(7).choice(d, m, replace=False)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    Y = skm().sketch_matmul_fwd(to_dev(syn.to_storage(X, dt), dt), to_dev(idx, "u8"), to_dev(lut, dt), b, gpr)
+    W = oracle.dequantize(idx, syn.to_float64(lut, dt), d, b, gpr)
+    assert np.array_equal(to_f64(Y), W[:, cols].T)
+
+
 def _workload_rows(n, seed):
     r = np.random.default_rng(seed)
     rows = np.concatenate([np.arange(0, 32), np.arange(n - 32, n), r.choice(n, 448, replace=False)])
@@ -162,3 +188,80 @@ def test_fwd_deterministic():
     a = skm().sketch_matmul_fwd(to_dev(X, "f16"), to_dev(idx, "u8"), to_dev(lut, "f16"), 4, 8)
     b_ = skm().sketch_matmul_fwd(to_dev(X, "f16"), to_dev(idx, "u8"), to_dev(lut, "f16"), 4, 8)
     assert bool((a == b_).all())
+
+
+# ---------------------------------------------------------------------------
+# 16-bit backward (dX and dLUT on the matrix cores)
+# ---------------------------------------------------------------------------
+
+def _bwd16(idx, lut, X, dY, b, gpr, d, io, lut_dtype, accumulate=False, dlut_init=None):
+    dl = None
+    if dlut_init is not None:
+        dl = to_dev(dlut_init.astype(np.float32), "f32")
+    dX, dL = skm().sketch_matmul_bwd(to_dev(dY, io), to_dev(X, io), to_dev(idx, "u8"), to_dev(lut, lut_dtype), b,
+                                     gpr, d=d, dlut_out=dl, accumulate=accumulate)
+    return to_f64(dX), to_f64(dL)
+
+
+@pytest.mark.parametrize("io,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 8, 200, 4096, 300), (2, 2, 130, 1024, 40), (3, 8, 96, 11008, 33), (4, 1, 257, 512, 17),
+    (3, 4, 300, 1536, 260), (2, 32, 64, 1024, 64), (4, 4, 33, 8192, 5),
+])
+def test_bwd16(io, lut_dtype, b, gpr, n, d, m):
+    idx, lut, X, dY = make_case(f"bwd16/{io}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, lut_dtype)
+    gdx, gdl = _bwd16(idx, lut, X, dY, b, gpr, d, io, lut_dtype)
+    L64, X64, dY64 = syn.to_float64(lut, lut_dtype), syn.to_float64(X, io), syn.to_float64(dY, io)
+    assert oracle.rel_err(gdx, oracle.backward_dx(dY64, idx, L64, d, b, gpr)) <= TOL16
+    assert oracle.rel_err(gdl, oracle.backward_dlut(dY64, X64, idx, b, gpr)) <= TOL16
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_dlut_bins_exact(b):
+    """Integer dY and one-hot X rows: every bin sum is an exact small integer."""
+    n, gpr, d, m = 130, 4, 2048, 96
+    idx, lut, _, _ = make_case(f"bins/{b}", n, d, b, gpr, 1, "bf16", "bf16")
+    cols = np.random.default_rng(b).choice(d, m, replace=False)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    dY = syn.random_int_valued(f"bins/{b}/dY", (m, n), -3, 3, "bf16")
+    Xs = syn.to_storage(X, "bf16")
+    _, gdl = _bwd16(idx, lut, Xs, dY, b, gpr, d, "bf16", "bf16")
+    want = oracle.backward_dlut(syn.to_float64(dY, "bf16"), X.astype(np.float64), idx, b, gpr)
+    assert np.array_equal(gdl, want)
+
+
+def test_bwd_accumulate_and_deterministic():
+    b, gpr, n, d, m = 4, 8, 160, 4096, 80
+    idx, lut, X, dY = make_case("bwdacc", n, d, b, gpr, m, "bf16", "f16")
+    a1 = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
+    a2 = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
+    assert np.array_equal(a1[0], a2[0]) and np.array_equal(a1[1], a2[1])
+    base = np.random.default_rng(3).normal(size=(n, gpr, 16)).astype(np.float32)
+    _, acc = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16", accumulate=True, dlut_init=base)
+    assert np.allclose(acc, base.astype(np.float64) + a1[1], rtol=0, atol=1e-6 * max(1.0, np.abs(a1[1]).max()))
+
+
+def test_finetune_workload_sampled():
+    """The 7B decoder layer's projections at full size (m = 8192): sampled outputs."""
+    w = wl.LLAMA2_7B_FINETUNE
+    r = np.random.default_rng(11)
+    for s in (w.shapes[0], w.shapes[4], w.shapes[6]):   # q, gate, down
+        t = w.make(s, 4, 8192)
+        X64 = syn.to_float64(t["X"], w.x_dtype)
+        dY64 = syn.to_float64(t["dY"], w.x_dtype)
+        L64 = syn.to_float64(t["lut"], w.lut_dtype)
+        gi, gl = to_dev(t["idx_packed"], "u8"), to_dev(t["lut"], w.lut_dtype)
+        gx, gdy = to_dev(t["X"], w.x_dtype), to_dev(t["dY"], w.x_dtype)
+        Y = to_f64(skm().sketch_matmul_fwd(gx, gi, gl, 4, w.gpr))
+        dX, dL = skm().sketch_matmul_bwd(gdy, gx, gi, gl, 4, w.gpr)
+        dX, dL = to_f64(dX), to_f64(dL)
+        rows = np.unique(np.concatenate([[0, s.n - 1], r.choice(s.n, 256, replace=False)]))
+        cols = np.unique(np.concatenate([[0, s.d - 1], r.choice(s.d, 256, replace=False)]))
+        toks = np.unique(np.concatenate([[0, 8191], r.choice(8192, 512, replace=False)]))
+        want_y = oracle.forward(X64[toks], t["idx_packed"][rows], L64[rows], 4, w.gpr)
+        assert oracle.rel_err(Y[np.ix_(toks, rows)], want_y) <= w.tol, s.name
+        W = oracle.dequantize(t["idx_packed"], L64, s.d, 4, w.gpr)
+        assert oracle.rel_err(dX[np.ix_(toks, cols)], dY64[toks] @ W[:, cols]) <= w.tol, s.name
+        want_dl = oracle.backward_dlut(dY64[:, rows], X64, t["idx_packed"][rows], 4, w.gpr)
+        assert oracle.rel_err(dL[rows], want_dl) <= w.tol, s.name
