@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--parts", default="all", help="comma list: decode,fwd16 (default all)")
+    ap.add_argument("--parts", default="all", help="comma list of decode,fwd16,prefill,finetune (default all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -66,55 +66,91 @@ class Rotation:
 
 
 def time_launches(torch, launch, steps, warmup):
-    """Per-launch and whole-run GPU times (ms) from HIP events on the launch stream.
+    """GPU time (ms) of `steps` back-to-back launches, from HIP events on the launch stream.
 
     The stream is held by a spin kernel while the host enqueues every timed
     launch, so the GPU then runs them back to back: the events measure the
-    kernels (and the gaps between them), not the host's submission time.
+    kernels and the dispatch gaps between them, not the host's submission time.
     """
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(SPIN_CYCLES_PER_LAUNCH * steps))
     first.record(stream)
-    for a, b in ev:
-        a.record(stream)
+    for _ in range(steps):
         launch()
-        b.record(stream)
     last.record(stream)
     torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev])
-    return per, first.elapsed_time(last)
+    return first.elapsed_time(last)
 
 
-def bench_fwd(torch, skm, w, shape, b, m, steps, warmup):
+def bench_fwd(torch, skm, w, shape, b, m, steps, warmup, rotate=True):
     from lut_sketched_matmul_amd import workloads as wl
     t = w.make(shape, b, m)
     X = dev(torch, t["X"], w.x_dtype)
     idx = dev(torch, t["idx_packed"], "u8")
     lut = dev(torch, t["lut"], w.lut_dtype)
     Y = torch.empty((m, shape.n), dtype=X.dtype, device="cuda:0")
-    rot = Rotation(torch, idx, lut)
+    rot = Rotation(torch, idx, lut) if rotate else None
 
     def launch():
-        i, l = rot.next()
+        i, l = rot.next() if rot else (idx, lut)
         skm.sketch_matmul_fwd(X, i, l, b, w.gpr, out=Y)
 
-    per, gpu_total = time_launches(torch, launch, steps, warmup)
+    total = time_launches(torch, launch, steps, warmup)
     xb = wl.DTYPE_BYTES[w.x_dtype]
     lb = wl.DTYPE_BYTES[w.lut_dtype]
     nbytes = wl.algorithmic_bytes_fwd(shape.n, shape.d, b, w.gpr, m, lb, xb)
     flops = wl.flops_pass(shape.n, shape.d, m)
-    ms = float(np.mean(per))
+    ms = total / steps
     return {
-        "n": shape.n, "d": shape.d, "b": b, "gpr": w.gpr, "m": m,
-        "ms_mean": ms, "ms_median": float(np.median(per)), "gpu_ms_per_step": gpu_total / steps,
-        "bytes": nbytes, "flops": flops,
+        "shape": f"{shape.name} {shape.n}x{shape.d}", "b": b, "gpr": w.gpr, "m": m,
+        "ms_per_launch": ms, "bytes": nbytes, "flops": flops,
         "GBps": nbytes / (ms * 1e-3) / 1e9, "TFLOPs": flops / (ms * 1e-3) / 1e12,
-        "rotation_copies": rot.count,
+        "rotation_copies": rot.count if rot else 1,
+    }
+
+
+def bench_finetune(torch, skm, steps, warmup):
+    """One fine-tuning step of a 7B decoder layer: forward, dX and dLUT of all seven projections."""
+    from lut_sketched_matmul_amd import workloads as wl
+    w = wl.LLAMA2_7B_FINETUNE
+    m = w.tokens[0]
+    projs = []
+    for s in w.shapes:
+        t = w.make(s, 4, m)
+        projs.append(dict(
+            s=s, X=dev(torch, t["X"], w.x_dtype), dY=dev(torch, t["dY"], w.x_dtype),
+            idx=dev(torch, t["idx_packed"], "u8"), lut=dev(torch, t["lut"], w.lut_dtype),
+            Y=torch.empty((m, s.n), dtype=torch.bfloat16, device="cuda:0"),
+            dL=torch.empty((s.n, w.gpr, 16), dtype=torch.float32, device="cuda:0")))
+        del t
+
+    def step():
+        for p in projs:
+            skm.sketch_matmul_fwd(p["X"], p["idx"], p["lut"], 4, w.gpr, out=p["Y"])
+            skm.sketch_matmul_bwd(p["dY"], p["X"], p["idx"], p["lut"], 4, w.gpr, dlut_out=p["dL"])
+
+    total = time_launches(torch, step, steps, warmup)
+    flops = sum(3 * wl.flops_pass(p["s"].n, p["s"].d, m) for p in projs)
+    ms = total / steps
+    # per-pass split, timed the same way on the largest projection (gate)
+    g = projs[4]
+    t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(g["X"], g["idx"], g["lut"], 4, w.gpr, out=g["Y"]),
+                          steps, warmup) / steps
+    t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(g["dY"], g["X"], g["idx"], g["lut"], 4, w.gpr,
+                                                               need_dlut=False), steps, warmup) / steps
+    t_dl = time_launches(torch, lambda: skm.sketch_matmul_bwd(g["dY"], g["X"], g["idx"], g["lut"], 4, w.gpr,
+                                                               need_dx=False, dlut_out=g["dL"]), steps, warmup) / steps
+    fg = wl.flops_pass(g["s"].n, g["s"].d, m)
+    return {
+        "workload": w.name, "m": m, "ms_per_step": ms, "flops": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "frac_mfma_peak": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "gate_11008x4096": {"fwd_TFLOPs": fg / (t_fwd * 1e-3) / 1e12, "dx_TFLOPs": fg / (t_dx * 1e-3) / 1e12,
+                            "dlut_TFLOPs": fg / (t_dl * 1e-3) / 1e12, "fwd_ms": t_fwd, "dx_ms": t_dx,
+                            "dlut_ms": t_dl},
     }
 
 
@@ -162,20 +198,32 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
+    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
-    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16"}
+    log = lambda msg: print("# " + msg, file=sys.stderr, flush=True)
 
     dec = bench_fwd(torch, skm, w, shape, 4, 1, args.steps, args.warmup)
     parts["decode_m1"] = dec
-    print(f"# decode 4096x4096 b=4 m=1: {dec['ms_mean'] * 1e3:.2f} us/launch, {dec['GBps']:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    log(f"decode 4096x4096 b=4 m=1: {dec['ms_per_launch'] * 1e3:.2f} us/launch, {dec['GBps']:.0f} GB/s")
     if "fwd16" in want:
         f16 = bench_fwd(torch, skm, w, shape, 4, 16, args.steps, args.warmup)
         parts["fwd_m16"] = f16
-        print(f"# forward 4096x4096 b=4 m=16: {f16['ms_mean'] * 1e3:.2f} us/launch, {f16['GBps']:.0f} GB/s",
-              file=sys.stderr, flush=True)
+        log(f"forward 4096x4096 b=4 m=16: {f16['ms_per_launch'] * 1e3:.2f} us/launch, {f16['GBps']:.0f} GB/s")
+    big_steps = max(2, min(args.steps, 10))
+    big_warm = max(1, min(args.warmup, 2))
+    if "prefill" in want:
+        w4 = wl.LLAMA3_70B_MLP
+        for s4 in w4.shapes:
+            r = bench_fwd(torch, skm, w4, s4, 4, 2048, big_steps, big_warm, rotate=False)
+            r["frac_mfma_peak"] = r["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+            parts[f"prefill_70b_{s4.name}_m2048"] = r
+            log(f"prefill 70B {s4.name} m=2048: {r['ms_per_launch']:.3f} ms, {r['TFLOPs']:.0f} TFLOP/s")
+    if "finetune" in want:
+        ft = bench_finetune(torch, skm, big_steps, big_warm)
+        parts["finetune_7b_layer"] = ft
+        log(f"fine-tune step 7B layer m=8192: {ft['ms_per_step']:.2f} ms, {ft['TFLOPs']:.0f} TFLOP/s")
 
     cpu = None if args.no_cpu else cpu_baseline(w, shape, 4, 1)
     value = dec["GBps"]
@@ -186,7 +234,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": dec["gpu_ms_per_step"],
+        "ms_per_step": dec["ms_per_launch"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
