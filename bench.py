@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--parts", default="all", help="comma list of decode,fwd16,prefill,finetune (default all)")
+    ap.add_argument("--parts", default="all",
+                    help="comma list of decode,fwd16,prefill,finetune,copy (default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -154,6 +155,22 @@ def bench_finetune(torch, skm, steps, warmup):
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(torch, steps, warmup):
+    """A plain streaming kernel (dst = src + 1, fp32, 1 GiB each way): the
+    practical HBM ceiling, and the known-size kernel that scales the FETCH_SIZE
+    / WRITE_SIZE counters."""
+    n = COPY_BYTES // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    total = time_launches(torch, lambda: torch.add(src, 1.0, out=dst), steps, warmup)
+    ms = total / steps
+    return {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "ms_per_launch": ms,
+            "GBps_read_plus_write": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, shape, b, m, budget_s=12.0):
     """The CPU oracle (float64 numpy) on the same decode workload."""
     import oracle
@@ -198,7 +215,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
-    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune"}
+    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune", "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -224,6 +241,11 @@ def main():
         ft = bench_finetune(torch, skm, big_steps, big_warm)
         parts["finetune_7b_layer"] = ft
         log(f"fine-tune step 7B layer m=8192: {ft['ms_per_step']:.2f} ms, {ft['TFLOPs']:.0f} TFLOP/s")
+
+    if "copy" in want:
+        cp = bench_copy(torch, big_steps, big_warm)
+        parts["copy_1GiB"] = cp
+        log(f"device copy 1 GiB: {cp['ms_per_launch']:.3f} ms, {cp['GBps_read_plus_write']:.0f} GB/s read+write")
 
     cpu = None if args.no_cpu else cpu_baseline(w, shape, 4, 1)
     value = dec["GBps"]

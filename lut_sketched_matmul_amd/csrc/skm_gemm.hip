@@ -14,21 +14,22 @@
 //   A  [2][256 tokens][32 cols] activations in the compute dtype
 //   Bt [2][128 rows][32 cols]   dequantised weights
 //   tables [2 groups][2 row halves][T entries][64 lanes] dwords
-// Rows of A and Bt are 64 bytes; the four 16-byte chunks of row r are stored
-// at chunk ^ ((r >> 1) & 3) so 8 consecutive rows read by one ds_read_b128
-// pass land in distinct banks.
+// Rows of A and Bt are 64 bytes with XOR-swizzled 16-byte chunks (mm::swz) so
+// the 16 rows of one ds_read_b128 pass land in distinct banks.
 //
 // Dequantisation roles: thread t owns weight row r = t % 128 and the column
 // half hh = t / 128 of each unit (16 weights per K-step). Its table copies sit
 // at lane slot t % 64 of its row half, entry-major, so the gathers of one wave
 // (64 distinct rows) are conflict-free; the gather address is built by one
 // v_perm_b32 as in the decode kernel. Tables are staged one group ahead.
-#include "skm_common.h"
+#include "skm_gemm_common.h"
 #include "skm_launch.h"
 
 namespace skm {
 
 namespace {
+
+using mm::swz;
 
 constexpr int G_BM = 256;
 constexpr int G_BN = 128;
@@ -60,9 +61,6 @@ template <> struct mfma32<bf16_t> {
   }
 };
 
-__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
-  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
-}
 
 __device__ __forceinline__ uint32_t lds_h(uint32_t a) { return *(const lds_u16*)(uintptr_t)a; }
 __device__ __forceinline__ uint32_t lds_w(uint32_t a) { return *(const lds_u32*)(uintptr_t)a; }

@@ -23,10 +23,13 @@ __device__ __forceinline__ void st_w(uint32_t a, uint32_t v) { *(lds_u32*)(uintp
 __device__ __forceinline__ void st_q(uint32_t a, u32x4 v) { *(lds_u32x4*)(uintptr_t)a = v; }
 
 // 64-byte rows of four 16-byte chunks; chunk c of row r is stored at
-// c ^ ((r >> 1) & 3) so that 8 consecutive rows read by one ds_read_b128 pass
-// cover all banks.
+// c ^ f(r) with f(r) = ((r >> 1) ^ (r >> 2)) & 3. gfx950's LDS serves a
+// ds_read_b128 / ds_write_b128 in passes of 16 lanes over 64 banks: rows r,
+// r+4, r+8, r+12 start on the same bank, and f gives them four different
+// chunks, so 16 consecutive rows at one chunk index touch 16 distinct 16-byte
+// bank groups (f is also conflict-free for passes of 8 lanes over 32 banks).
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
-  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
+  return row * 64u + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3u)) << 4);
 }
 // byte offset of 16-bit element e (0..31) of row r in the same layout
 __device__ __forceinline__ uint32_t swz_elem(uint32_t row, uint32_t e) {
