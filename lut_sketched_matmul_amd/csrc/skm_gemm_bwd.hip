@@ -297,34 +297,42 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
 // ============================================================================
 // dLUT
 // ============================================================================
+// Operand tiles are stored as loaded: Yt[token][row] (dY) and Xt[token][col]
+// (X), 128 values per token row plus 64 bytes of padding (row stride 320 B =
+// 16 dwords mod 64 banks), so the 4 rows x 2 column halves read by one
+// 32-lane pass of ds_read_b64_tr_b16 fall in distinct banks.
 constexpr int DL_BM = 128, DL_BN = 128, DL_BK = 32;
-constexpr uint32_t DL_A = 0;                                  // [2][128 rows][32 tokens]
-constexpr uint32_t DL_B = 2u * DL_BM * DL_BK * 2u;            // 16384: [2][128 cols][32 tokens]
-constexpr uint32_t DL_I = DL_B + 2u * DL_BN * DL_BK * 2u;     // 32768: packed indices [128 rows][16*B bytes]
-constexpr uint32_t DL_BINS = DL_I + 128u * 64u;               // 40960: [2][128 rows][16] fp32
-constexpr uint32_t DL_LDS = DL_BINS + 2u * 128u * 16u * 4u;   // 57344
+constexpr uint32_t DL_RS = 128u * 2u + 64u;                   // 320
+constexpr uint32_t DL_TILE = DL_BK * DL_RS;                   // 10240
+constexpr uint32_t DL_Y = 0;                                  // [2][32][RS] dY tiles
+constexpr uint32_t DL_X = 2u * DL_TILE;                       // 20480: [2][32][RS] X tiles
+constexpr uint32_t DL_I = DL_X + 2u * DL_TILE;                // 40960: packed indices [128 rows][64 B]
+constexpr uint32_t DL_BINS = DL_I + 128u * 64u;               // 49152: [2][128 rows][16] fp32
+constexpr uint32_t DL_LDS = DL_BINS + 2u * 128u * 16u * 4u;   // 65536
 
-// 16 consecutive 16-bit values of row `rowp` starting at element e0 (zero past `lim`)
-template <typename TS>
-__device__ __forceinline__ void dl_load16(uint32_t* v, const TS* rowp, int64_t e0, int64_t lim, bool vec) {
-  if (vec && e0 + 16 <= lim) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(rowp + e0);
-    const u32x4 x0 = p[0], x1 = p[1];
-    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-  } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t i = e0 + 2 * q;
-      const uint32_t lo = i < lim ? p[i] : 0u;
-      const uint32_t hi = i + 1 < lim ? p[i + 1] : 0u;
-      v[q] = lo | (hi << 16);
-    }
+// 8 consecutive 16-bit values p[e0 .. e0+7] (zero at or past `lim`).
+// VEC: rows are 16-byte aligned and `lim` is a multiple of 8, so a chunk is
+// either wholly inside (one 16-byte load) or wholly outside (zeros).
+template <bool VEC, typename TS>
+__device__ __forceinline__ u32x4 dl_load8(const TS* rowp, int64_t e0, int64_t lim) {
+  if constexpr (VEC) {
+    const bool in = e0 < lim;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(rowp + (in ? e0 : 0));
+    return in ? v : u32x4{0u, 0u, 0u, 0u};
   }
+  const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp);
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = e0 + 2 * q;
+    const uint32_t lo = i < lim ? p[i] : 0u;
+    const uint32_t hi = i + 1 < lim ? p[i + 1] : 0u;
+    v[q] = lo | (hi << 16);
+  }
+  return v;
 }
 
-// field j of the packed row staged at LDS byte address `row` (16*B bytes per row)
+// field j of the packed row staged at LDS byte address `row`
 template <int B>
 __device__ __forceinline__ uint32_t dl_field(uint32_t row, uint32_t j) {
   const uint32_t bit = j * (uint32_t)B;
@@ -339,8 +347,8 @@ __device__ __forceinline__ uint32_t dl_field(uint32_t row, uint32_t j) {
   return (w >> off) & ((1u << B) - 1u);
 }
 
-template <int B, typename TX>
-__global__ void __launch_bounds__(256, 1)
+template <int B, typename TX, bool VEC>
+__global__ void __launch_bounds__(256, 2)
 k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
             int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
   typedef mfma32<TX> MF;
@@ -349,64 +357,58 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   (void)smem;
 
   const int t = threadIdx.x;
-  const int lane = t & 63;
+  const uint32_t lane = (uint32_t)(t & 63);
   const int wave = t >> 6;
-  const int64_t i0 = (int64_t)(blockIdx.x / gpr) * DL_BM;
-  const int g = (int)(blockIdx.x % gpr);
+  // the gpr groups of one row block (same dY strip) share an XCD's L2
+  const uint32_t lb = xcd_block(blockIdx.x, gridDim.x);
+  const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
+  const int g = (int)(lb % (uint32_t)gpr);
   const int64_t G = d / gpr;
   const int64_t jg0 = (int64_t)g * G;              // first column of the group
-  const bool vy = (n % 8) == 0, vx = (d % 8) == 0;
+  const int64_t jend = jg0 + G;
 
-  // zero the bins
   for (uint32_t q = (uint32_t)t; q < 2u * 128u * 16u; q += 256u) st_w(DL_BINS + q * 4u, 0u);
 
-  // operand staging role: token tt of the step, 16-element chunk rc
-  const int tt = t & 31;
-  const int rc = t >> 5;
+  // staging role: 16-byte pieces c = t and t + 256 of a 32 x 128 tile
+  // (token c / 16, values 8 (c % 16) .. +7)
   const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(64 * wm + (lane & 31));
-  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
   const uint32_t KS = (uint32_t)((m + DL_BK - 1) / DL_BK);
 
-  auto load_step = [&](uint32_t ks, int64_t j0, uint32_t* ya, uint32_t* xb) {
-    const int64_t tok = (int64_t)ks * DL_BK + tt;
-    const bool tok_ok = tok < m;
-    const int64_t tr = tok_ok ? tok : 0;
-    // dY[tok][i0 + 16 rc ..], zero past row n or token m
-    dl_load16<TX>(ya, dY + tr * n, i0 + 16 * rc, tok_ok ? n : 0, vy);
-    // X[tok][j0 + 16 rc ..], zero past the group end
-    const int64_t jend = jg0 + G;
-    dl_load16<TX>(xb, X + tr * d, j0 + 16 * rc, tok_ok ? jend : 0, vx);
-  };
-  auto store_step = [&](uint32_t buf, const uint32_t* ya, const uint32_t* xb) {
-    const uint32_t ab = DL_A + buf * (uint32_t)(DL_BM * DL_BK * 2);
-    const uint32_t bb = DL_B + buf * (uint32_t)(DL_BN * DL_BK * 2);
+  auto load_step = [&](uint32_t ks, int64_t j0, u32x4* ya, u32x4* xb) {
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      const uint32_t yv = (f & 1) ? (ya[f >> 1] >> 16) : (ya[f >> 1] & 0xFFFFu);
-      const uint32_t xv = (f & 1) ? (xb[f >> 1] >> 16) : (xb[f >> 1] & 0xFFFFu);
-      st_h(ab + swz_elem((uint32_t)(16 * rc + f), (uint32_t)tt), yv);
-      st_h(bb + swz_elem((uint32_t)(16 * rc + f), (uint32_t)tt), xv);
+    for (int h = 0; h < 2; ++h) {
+      const int c = t + 256 * h;
+      const int64_t tok = (int64_t)ks * DL_BK + (c >> 4);
+      const bool ok = tok < m;
+      const int64_t tr = ok ? tok : 0;
+      ya[h] = dl_load8<VEC, TX>(dY + tr * n, i0 + 8 * (c & 15), ok ? n : 0);
+      xb[h] = dl_load8<VEC, TX>(X + tr * d, j0 + 8 * (c & 15), ok ? jend : 0);
+    }
+  };
+  auto store_step = [&](uint32_t buf, const u32x4* ya, const u32x4* xb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (uint32_t)(t + 256 * h);
+      const uint32_t off = (c >> 4) * DL_RS + (c & 15u) * 16u;
+      st_q(DL_Y + buf * DL_TILE + off, ya[h]);
+      st_q(DL_X + buf * DL_TILE + off, xb[h]);
     }
   };
 
-  for (int64_t j0 = jg0; j0 < jg0 + G; j0 += DL_BN) {
+  for (int64_t j0 = jg0; j0 < jend; j0 += DL_BN) {
     __syncthreads();  // the previous chunk's binning is done with the staged indices
-    // stage this chunk's packed indices: 128 rows x (128 * B / 8) bytes as dwords
     {
+      // this chunk's packed indices: 128 rows x (16 * B) bytes, as dwords
       const int row = t >> 1;
       const int64_t grow = i0 + row < n ? i0 + row : n - 1;
       const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
-      const int64_t avail_units = (jg0 + G - j0) / 32;  // units of the chunk inside the group
-      const int words = 4 * B;                           // dwords per 128 columns
+      const int64_t avail_units = (jend - j0) / 32;
 #pragma unroll
       for (int q = 0; q < 2 * B; ++q) {
         const int wd = (t & 1) * 2 * B + q;
-        const bool in = (wd / B) < avail_units;          // unit wd/B of the chunk exists
+        const bool in = (wd / B) < avail_units;
         st_w(DL_I + (uint32_t)row * 64u + (uint32_t)wd * 4u, in ? src[wd] : 0u);
       }
-      (void)words;
     }
 
     f32x16 acc[2][2];
@@ -415,7 +417,7 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
 #pragma unroll
       for (int b = 0; b < 2; ++b) zero16(acc[a][b]);
 
-    uint32_t ya[8], xb[8];
+    u32x4 ya[2], xb[2];
     load_step(0, j0, ya, xb);
     store_step(0, ya, xb);
     __syncthreads();
@@ -423,16 +425,14 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
       const uint32_t cur = k & 1u;
       const bool more = k + 1 < KS;
       if (more) load_step(k + 1, j0, ya, xb);
-      const uint32_t abase = DL_A + cur * (uint32_t)(DL_BM * DL_BK * 2);
-      const uint32_t bbase = DL_B + cur * (uint32_t)(DL_BN * DL_BK * 2);
+      const uint32_t yb = DL_Y + cur * DL_TILE, xbse = DL_X + cur * DL_TILE;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t ch = (uint32_t)(2 * ks) + khalf;
         u32x4 af[2], bf[2];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) af[a] = ld_q(abase + swz(arow + 32u * a, ch));
+        for (int a = 0; a < 2; ++a) af[a] = ld_frag_tr(yb + 16u * ks * DL_RS + (64u * wm + 32u * a) * 2u, DL_RS, lane);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) bf[b] = ld_q(bbase + swz(brow + 32u * b, ch));
+        for (int b = 0; b < 2; ++b) bf[b] = ld_frag_tr(xbse + 16u * ks * DL_RS + (64u * wn + 32u * b) * 2u, DL_RS, lane);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -444,21 +444,24 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
 
     // ---- scatter-add the finished dW tile into this wave's bins
     // D[i][j] of tile (a, b): i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4, j = 64 wn + 32 b + lane%32
+    // (fully unrolled so the accumulators stay in registers; the scheduling
+    // fences keep the compiler from hoisting all 64 index reads at once)
     const uint32_t binbase = DL_BINS + (uint32_t)wn * (128u * 16u * 4u);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const uint32_t j = (uint32_t)(64 * wn + 32 * b + (lane & 31));
-        const bool j_ok = j0 + (int64_t)j < jg0 + G;
+        const uint32_t j = 64u * wn + 32u * b + (lane & 31u);
+        const bool j_ok = j0 + (int64_t)j < jend;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const uint32_t i = (uint32_t)(64 * wm + 32 * a + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3));
+          const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (lane >> 5) + (e & 3);
           if (j_ok && i0 + (int64_t)i < n) {
             const uint32_t c = dl_field<B>(DL_I + i * 64u, j);
             __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * 16u + c) * 4u), acc[a][b][e],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
+          if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
   }
@@ -509,8 +512,13 @@ template <int B, typename TX>
 hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
                   hipStream_t s) {
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
-  hipLaunchKernelGGL((k_gemm_dlut<B, TX>), dim3((unsigned)(rb * p.gpr)), dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n,
-                     p.d, p.gpr, dLUT, accumulate);
+  const dim3 grid((unsigned)(rb * p.gpr));
+  if (p.n % 8 == 0)  // d is a multiple of 32 already
+    hipLaunchKernelGGL((k_gemm_dlut<B, TX, true>), grid, dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
+                       accumulate);
+  else
+    hipLaunchKernelGGL((k_gemm_dlut<B, TX, false>), grid, dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
+                       accumulate);
   return hipGetLastError();
 }
 

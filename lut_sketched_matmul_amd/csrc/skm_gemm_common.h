@@ -104,9 +104,45 @@ __device__ __forceinline__ u32x4 cvt_quad(u32x4 v) {
   }
 }
 
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane l receives 16-bit element l % 4 of the 8-byte pieces addressed
+// by lanes 4j + l/4 of its group, j = 0..3. If lane s of a group points at row
+// k0 + s/4, columns c0 + 4 (s % 4) .. +3 of a row-major tile T[k][c], then
+// lane l receives T[k0 + j][c0 + l] for j = 0..3: four consecutive k of one
+// column, i.e. an MFMA operand quarter from a K-major tile.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ld_tr(uint32_t a) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(uintptr_t)a);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// One 32x32x16 MFMA operand (8 consecutive k of one column per lane) from a
+// row-major K-major tile: `tile` is the LDS byte address of T[k0][c0] for the
+// fragment's first k row and first column, `rs` the tile's row stride.
+// Lane l covers column c0 + l % 32 and k rows k0 + 8 (l / 32) .. +7.
+__device__ __forceinline__ u32x4 ld_frag_tr(uint32_t tile, uint32_t rs, uint32_t lane) {
+  const uint32_t s = lane & 15u;
+  const uint32_t row = 8u * (lane >> 5) + (s >> 2);
+  const uint32_t col = 16u * ((lane >> 4) & 1u) + 4u * (s & 3u);
+  const uint32_t a = tile + row * rs + col * 2u;
+  const u32x2 lo = ld_tr(a), hi = ld_tr(a + 4u * rs);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
 __device__ __forceinline__ void zero16(f32x16& a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) a[e] = 0.0f;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Renumber them so that each XCD receives a contiguous range of logical block
+// ids (a bijection on [0, nblocks)): blocks that share operands are then
+// co-resident in one L2 instead of being spread over all eight.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
+  constexpr uint32_t NX = 8;
+  const uint32_t q = nblocks / NX, r = nblocks % NX;
+  const uint32_t x = b % NX, s = b / NX;
+  return x * q + (x < r ? x : r) + s;
 }
 
 // group index of unit u: multiply-high by the host's magic (0 = one unit/group)
