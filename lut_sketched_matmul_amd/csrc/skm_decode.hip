@@ -32,6 +32,8 @@
 // slots s = w, w + NW, ... (slot = 4 units = 128 columns), so the waves of a
 // block read adjacent pieces of each row. The NW partial 16x16 tiles are
 // summed in LDS in wave order (deterministic) and stored once.
+#include <stdlib.h>
+
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -40,12 +42,24 @@ namespace skm {
 namespace {
 
 constexpr int DEC_ROWS = 16;
-constexpr int DEC_NW = 8;     // waves per block
 constexpr int DEC_PF = 4;     // slots loaded per batch and wave
 constexpr int DEC_MAX_ENTRIES = 224;  // table entries per row kept in LDS (entry byte must fit in 8 bits)
+constexpr int DEC_LUT_CHUNKS = 2;     // 8-entry table chunks loaded per wave (16 * 2 * 8 >= 224)
+constexpr int64_t DEC_XL_MAX = 32768; // m * d elements staged in LDS (64 KB)
+constexpr int DEC_XL_CHUNKS = (int)(DEC_XL_MAX / 8 / (8 * 64));  // 16-byte chunks per thread (NW >= 8)
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// SKM_DECODE_WAVES=8|16 forces the waves per decode block (tuning aid)
+int decode_waves_override() {
+  static const int v = [] {
+    const char* e = getenv("SKM_DECODE_WAVES");
+    const int w = e ? atoi(e) : 0;
+    return (w == 8 || w == 16) ? w : 0;
+  }();
+  return v;
+}
 
 template <typename TC> struct mfma16;
 template <> struct mfma16<half_t> {
@@ -151,32 +165,55 @@ __device__ __forceinline__ u32x4 dequant_step(const uint32_t* w, int h, uint32_t
   return r;
 }
 
-// Write this lane's private table copies. Row j = lane%16 of the block; every
-// wave writes whole 64-lane entry rows, so each ds_write is conflict-free.
-template <int B, typename TL>
-__device__ __forceinline__ void fill_tables(uint32_t* tabs, const TL* __restrict__ lut, int64_t grow, bool row_ok,
-                                            int gpr, int lane, int wave) {
+// Private table copies. Row j = lane%16 of the block; every wave writes whole
+// 64-lane entry rows, so each ds_write is conflict-free. The loads are issued
+// before the first index loads and stored after them (vmcnt counts in order).
+template <int B> struct TabRegs { uint32_t v[2 * DEC_LUT_CHUNKS][4]; };
+
+template <int B, int NW, typename TL>
+__device__ __forceinline__ void tab_load(TabRegs<B>& R, const TL* __restrict__ lut, int64_t grow, int gpr, int wave) {
   constexpr int K = 1 << B;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(lut) + (row_ok ? grow : 0) * (int64_t)gpr * K;
-  if constexpr (B == 2) {
-    // one group per step: 4 entries -> 16 pairs (a + 4c) = (LUT[a], LUT[c])
-    for (int g = wave; g < gpr; g += DEC_NW) {
-      u32x2 v = row_ok ? *reinterpret_cast<const u32x2*>(src + g * 4) : u32x2{0u, 0u};
-      const uint32_t e[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * K;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) tabs[(g * 16 + a + 4 * c) * 64 + lane] = e[a] | (e[c] << 16);
+  for (int c = 0; c < DEC_LUT_CHUNKS * (16 / NW); ++c) {
+    const int ch = wave + NW * c;
+    if constexpr (B == 2) {
+      // chunk = one group's 4 entries
+      if (ch < gpr) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src + ch * 4);
+        R.v[c][0] = v.x;
+        R.v[c][1] = v.y;
+      }
+    } else {
+      if (ch * 8 < gpr * K) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + ch * 8);
+        R.v[c][0] = v.x; R.v[c][1] = v.y; R.v[c][2] = v.z; R.v[c][3] = v.w;
+      }
     }
-  } else {
-    // chunks of 8 entries (one 16-byte load; gpr*K is a multiple of 8)
-    const int E = gpr * K;
-    for (int c = wave; c * 8 < E; c += DEC_NW) {
-      u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(src + c * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int B, int NW>
+__device__ __forceinline__ void tab_store(const TabRegs<B>& R, uint32_t* tabs, int gpr, int lane, int wave) {
+  constexpr int K = 1 << B;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        tabs[(c * 8 + 2 * t) * 64 + lane] = v[t] & 0xFFFFu;
-        tabs[(c * 8 + 2 * t + 1) * 64 + lane] = v[t] >> 16;
+  for (int c = 0; c < DEC_LUT_CHUNKS * (16 / NW); ++c) {
+    const int ch = wave + NW * c;
+    if constexpr (B == 2) {
+      if (ch < gpr) {
+        const uint32_t e[4] = {R.v[c][0] & 0xFFFFu, R.v[c][0] >> 16, R.v[c][1] & 0xFFFFu, R.v[c][1] >> 16};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) tabs[(ch * 16 + a + 4 * cc) * 64 + lane] = e[a] | (e[cc] << 16);
+      }
+    } else {
+      if (ch * 8 < gpr * K) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          tabs[(ch * 8 + 2 * t) * 64 + lane] = R.v[c][t] & 0xFFFFu;
+          tabs[(ch * 8 + 2 * t + 1) * 64 + lane] = R.v[c][t] >> 16;
+        }
       }
     }
   }
@@ -187,6 +224,7 @@ struct SlotRegs {
   uint32_t w[DEC_PF][B];
   u32x4 x[DEC_PF][4];
   uint32_t gk[DEC_PF];
+  uint32_t u[DEC_PF];
   bool ok[DEC_PF];
 };
 
@@ -195,13 +233,13 @@ struct SlotRegs {
 // feeds outputs that are never stored, and a unit past the row end (RAGGED
 // only) is zeroed by the caller. g = u / UG is a multiply-high by the host's
 // magic constant (exact for u * UG < 2^32).
-template <int B, typename TX, bool RAGGED>
+template <int B, int NW, typename TX, bool RAGGED, bool XL>
 __device__ __forceinline__ void load_batch(SlotRegs<B, TX>& R, int64_t s0, int64_t S, uint32_t U, uint32_t ug_magic,
                                            int q, const uint8_t* rowp, const TX* xrow) {
   constexpr int T = tab_entries<B>::value;
 #pragma unroll
   for (int p = 0; p < DEC_PF; ++p) {
-    const int64_t s = s0 + (int64_t)p * DEC_NW;
+    const int64_t s = s0 + (int64_t)p * NW;
     if (s < S) {  // wave-uniform
       uint32_t u = 4u * (uint32_t)s + (uint32_t)q;
       if constexpr (RAGGED) {
@@ -209,20 +247,33 @@ __device__ __forceinline__ void load_batch(SlotRegs<B, TX>& R, int64_t s0, int64
         u = u < U ? u : U - 1u;
       }
       load_unit<B>(rowp, u, R.w[p]);
-      const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
+      R.u[p] = u;
+      if constexpr (!XL) {
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) R.x[p][h] = xp[h];
+        for (int h = 0; h < 4; ++h) R.x[p][h] = xp[h];
+      }
       R.gk[p] = (ug_magic ? __umulhi(u, ug_magic) : u) * T;  // magic 0: one unit per group
     }
   }
 }
 
-template <int B, typename TX, typename TL, bool RAGGED>
-__global__ void __launch_bounds__(DEC_NW * 64)
+template <typename T>
+__device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
+}
+
+// XL: the activations (m x d, converted to the compute dtype) are staged once
+// per block in LDS after the tables, and A fragments are read from there.
+// With XL the index words of the next batch of slots are loaded while the
+// current batch is being computed (two small register sets).
+template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
+__global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
          int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, TX* __restrict__ Y) {
   // Dynamic LDS only (this kernel has no static LDS, so it starts at address
-  // 0): [entries][64 lanes] table dwords, then the [NW][16][16] fp32 partials.
+  // 0): [entries][64 lanes] table dwords, [m][d] activations (XL), then the
+  // [NW][16][16] fp32 partials.
   extern __shared__ uint32_t smem[];
   constexpr int T = tab_entries<B>::value;
   typedef mfma16<TL> MF;
@@ -234,55 +285,98 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int q = lane >> 4;           // contraction quarter
   const int64_t grow = row0 + j;
   const bool row_ok = grow < n;
-  const int tok = lane & 15;         // A operand row = token
-  const bool tok_ok = tok < m;
-  (void)tok_ok;
+  const int tok = lane & 15;         // A operand row = token (clamped: rows >= m are never stored)
+  const int tokc = tok < m ? tok : m - 1;
 
   const uint32_t U = (uint32_t)(d / 32);         // units per row
   const int64_t S = (U + 3) / 4;                 // slots per row
   const uint8_t* rowp = idx_packed + (row_ok ? grow : n - 1) * (d * B / 8);
-  const TX* xrow = X + (int64_t)(tok_ok ? tok : m - 1) * d;
+  const TX* xrow = X + (int64_t)tokc * d;
   const uint32_t lane4 = (uint32_t)lane * 4u;
+  const uint32_t xl_base = (uint32_t)gpr * T * 256u;  // byte offset of the staged activations
+  const int64_t xl_elems = (int64_t)m * d;
+  constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
 
-  SlotRegs<B, TX> R;
+  // ---- prologue: table loads, activation loads (XL), first index loads, then
+  // the LDS stores of the first two (their loads complete first)
+  TabRegs<B> TR;
+  tab_load<B, NW, TL>(TR, lut, row_ok ? grow : n - 1, gpr, wave);
+  u32x4 xs[XCH];
+  if constexpr (XL) {
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
+    }
+  }
+  SlotRegs<B, TX> R0, R1;
   int64_t s0 = wave;
-  // first index loads go out before the tables are staged
-  load_batch<B, TX, RAGGED>(R, s0, S, U, ug_magic, q, rowp, xrow);
-  fill_tables<B, TL>(smem, lut, grow, row_ok, gpr, lane, wave);
+  load_batch<B, NW, TX, RAGGED, XL>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+  tab_store<B, NW>(TR, smem, gpr, lane, wave);
+  if constexpr (XL) {
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (e < xl_elems) {
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+      }
+    }
+  }
   __syncthreads();
   // the gathers address the tables with absolute LDS addresses (see gaddr)
   if ((uint32_t)(uintptr_t)smem != 0u) return;
+  const uint32_t xl_row = xl_base + (uint32_t)tokc * (uint32_t)d * 2u;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  while (true) {
+  auto compute = [&](const SlotRegs<B, TX>& Rc, int64_t sb) {
 #pragma unroll
     for (int p = 0; p < DEC_PF; ++p) {
-      if (s0 + (int64_t)p * DEC_NW >= S) break;  // wave-uniform
-      const uint32_t gk = R.gk[p];
+      if (sb + (int64_t)p * NW >= S) break;  // wave-uniform
+      const uint32_t gk = Rc.gk[p];
       const uint32_t gk4 = gk * 0x01010101u;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        u32x4 wb = dequant_step<B>(R.w[p], h, gk4, gk, lane4);
+        u32x4 wb = dequant_step<B>(Rc.w[p], h, gk4, gk, lane4);
         // a slot past the row end (only when d/32 is not a multiple of 4) has
         // X = 0; its weights are zeroed too so no table value can leak in
         if constexpr (RAGGED) {
-          if (!R.ok[p]) wb = u32x4{0u, 0u, 0u, 0u};
+          if (!Rc.ok[p]) wb = u32x4{0u, 0u, 0u, 0u};
         }
-        u32x4 xv = x_to_tc<TX, TL>(R.x[p][h]);
+        u32x4 xv;
+        if constexpr (XL) xv = lds_q16<TL>(xl_row + (Rc.u[p] * 32u + 8u * h) * 2u);
+        else xv = x_to_tc<TX, TL>(Rc.x[p][h]);
         if constexpr (RAGGED) {
-          if (!R.ok[p]) xv = u32x4{0u, 0u, 0u, 0u};
+          if (!Rc.ok[p]) xv = u32x4{0u, 0u, 0u, 0u};
         }
         acc = MF::run(__builtin_bit_cast(typename MF::vec, xv), __builtin_bit_cast(typename MF::vec, wb), acc);
       }
     }
-    s0 += (int64_t)DEC_NW * DEC_PF;
-    if (s0 >= S) break;
-    load_batch<B, TX, RAGGED>(R, s0, S, U, ug_magic, q, rowp, xrow);
+  };
+  constexpr int64_t STEP = (int64_t)NW * DEC_PF;
+  if constexpr (XL) {
+    while (true) {
+      const int64_t s1 = s0 + STEP;
+      if (s1 < S) load_batch<B, NW, TX, RAGGED, XL>(R1, s1, S, U, ug_magic, q, rowp, xrow);
+      compute(R0, s0);
+      if (s1 >= S) break;
+      const int64_t s2 = s1 + STEP;
+      if (s2 < S) load_batch<B, NW, TX, RAGGED, XL>(R0, s2, S, U, ug_magic, q, rowp, xrow);
+      compute(R1, s1);
+      if (s2 >= S) break;
+      s0 = s2;
+    }
+  } else {
+    while (true) {
+      compute(R0, s0);
+      s0 += STEP;
+      if (s0 >= S) break;
+      load_batch<B, NW, TX, RAGGED, XL>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+    }
   }
 
   // ---- sum the NW partial tiles in wave order, then store Y[token][row]
   // lane l holds D[token 4*(l/16)+r][row l%16]
-  float* red = reinterpret_cast<float*>(smem + gpr * T * 64);
+  float* red = reinterpret_cast<float*>(smem) + (xl_base + (XL ? (uint32_t)xl_elems * 2u : 0u)) / 4u;
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave * 256 + (4 * q + r) * 16 + j] = acc[r];
   __syncthreads();
@@ -292,31 +386,57 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     if (token < m && row0 + rr < n) {
       float sum = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < DEC_NW; ++wv) sum += red[wv * 256 + t];
+      for (int wv = 0; wv < NW; ++wv) sum += red[wv * 256 + t];
       Y[(int64_t)token * n + row0 + rr] = from_f32<TX>(sum);
     }
   }
 }
 
-template <int B>
-size_t decode_lds_bytes(int gpr) {
-  return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (size_t)DEC_NW * 256 * 4;
+template <int B, int NW>
+size_t decode_lds_bytes(int gpr, int64_t x_elems) {
+  // x_elems is rounded up to whole 16-byte chunks so the partials stay aligned
+  return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (size_t)((x_elems + 7) / 8) * 16 +
+         (size_t)NW * 256 * 4;
+}
+
+template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
+hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
+                         uint32_t magic) {
+  const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL>;
+  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? p.m * p.d : 0);
+  if (lds > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)kern,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+  }
+  const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y);
+  return hipGetLastError();
+}
+
+template <int B, int NW, typename TX, typename TL>
+hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
+                     uint32_t magic) {
+  const bool xl = p.m * p.d <= DEC_XL_MAX;
+  if (p.units() % 4 != 0)
+    return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic)
+              : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic);
+  return xl ? decode_launch<B, NW, TX, TL, false, true>(X, idx, lut, p, Y, s, magic)
+            : decode_launch<B, NW, TX, TL, false, false>(X, idx, lut, p, Y, s, magic);
 }
 
 template <int B, typename TX, typename TL>
 hipError_t decode_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
-  const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
-  const dim3 block(DEC_NW * 64);
-  const size_t lds = decode_lds_bytes<B>(p.gpr);
-  const int m = (int)p.m;
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   // u / ug == umulhi(u, magic) for u * ug < 2^32; ug == 1 is passed as 0
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
-  if (p.units() % 4 != 0)
-    hipLaunchKernelGGL((k_decode<B, TX, TL, true>), grid, block, lds, s, X, idx, lut, m, p.n, p.d, p.gpr, magic, Y);
-  else
-    hipLaunchKernelGGL((k_decode<B, TX, TL, false>), grid, block, lds, s, X, idx, lut, m, p.n, p.d, p.gpr, magic, Y);
-  return hipGetLastError();
+  // Few 16-row blocks (one per CU or less): 16 waves per block for more loads
+  // in flight. Many blocks: 8 waves so two or more blocks share a CU and one
+  // block's start-up latency hides behind another's work.
+  const int64_t blocks = (p.n + DEC_ROWS - 1) / DEC_ROWS;
+  const int nw = decode_waves_override() ? decode_waves_override() : (blocks <= 384 ? 16 : 8);
+  if (nw == 16) return decode_nw<B, 16>(X, idx, lut, p, Y, s, magic);
+  return decode_nw<B, 8>(X, idx, lut, p, Y, s, magic);
 }
 
 template <typename TX, typename TL>
