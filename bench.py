@@ -31,6 +31,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "LUT-GEMV GB/s (% HBM peak) at 7B shapes; LUT-GEMM + bwd TFLOP/s (% MFMA)"
 ROTATE_BYTES = 1 << 30
 SPIN_CYCLES_PER_LAUNCH = 100_000  # > host enqueue time of one launch at the GPU timer rate
+# rocprofv3 summary of the headline kernel (FETCH_SIZE / WRITE_SIZE counters)
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "k_decode_llama2_7b_attn_4096x4096_b4_m1.md")
 
 
 def parse():
@@ -249,6 +251,9 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(w, shape, 4, 1)
     value = dec["GBps"]
+    from lut_sketched_matmul_amd import profiling
+    # measured HBM bytes per launch (scaled counters); None once the kernel sources changed
+    traffic = profiling.measured_bytes(DECODE_PROFILE, "k_decode<4,")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -266,7 +271,7 @@ def main():
                    "m": 1, "x_dtype": "f16", "lut_dtype": "f16"},
         "roofline": {
             "bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
         },
         "cpu_baseline": cpu,
         "parts": parts,
