@@ -17,10 +17,11 @@
 // (up to 4 groups of the column tile, private copy per lane slot) are staged
 // every step, two steps ahead.
 //
-// k_gemm_dlut: one block owns 128 rows x one group. For each 128-column chunk
-// of the group it accumulates the dW = dY^T X tile over all tokens (K = 32
-// tokens per step, operands transposed into [row][token] / [column][token]
-// LDS tiles), then scatter-adds the tile into LDS bins [row][entry] using the
+// k_gemm_dlut: one block owns 128 rows x one group. For each chunk of up to
+// 512 columns of the group it accumulates the dW = dY^T X tile over all
+// tokens (K = 32 tokens per step; the operand tiles are stored as loaded,
+// [token][row] and [token][column], and read with gfx950's transposing LDS
+// reads), then scatter-adds the tile into LDS bins [row][entry] using the
 // chunk's indices staged in LDS. Waves own disjoint (row, bin copy) pairs, so
 // the bins need no cross-wave atomics and the sums are deterministic; the
 // block stores each gradient entry exactly once (no global atomics).
@@ -297,18 +298,25 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
 // ============================================================================
 // dLUT
 // ============================================================================
-// Operand tiles are stored as loaded: Yt[token][row] (dY) and Xt[token][col]
-// (X), 128 values per token row plus 64 bytes of padding (row stride 320 B =
-// 16 dwords mod 64 banks), so the 4 rows x 2 column halves read by one
-// 32-lane pass of ds_read_b64_tr_b16 fall in distinct banks.
-constexpr int DL_BM = 128, DL_BN = 128, DL_BK = 32;
-constexpr uint32_t DL_RS = 128u * 2u + 64u;                   // 320
-constexpr uint32_t DL_TILE = DL_BK * DL_RS;                   // 10240
-constexpr uint32_t DL_Y = 0;                                  // [2][32][RS] dY tiles
-constexpr uint32_t DL_X = 2u * DL_TILE;                       // 20480: [2][32][RS] X tiles
-constexpr uint32_t DL_I = DL_X + 2u * DL_TILE;                // 40960: packed indices [128 rows][64 B]
-constexpr uint32_t DL_BINS = DL_I + 128u * 64u;               // 49152: [2][128 rows][16] fp32
-constexpr uint32_t DL_LDS = DL_BINS + 2u * 128u * 16u * 4u;   // 65536
+// 8 waves in a 2 (rows) x 4 (columns) grid, 64 x 128 outputs per wave (2 x 4
+// tiles of v_mfma_f32_32x32x16, 16 MFMAs per step); one block per CU. In each
+// step waves 0-3 multiply first and then stage the next tiles, waves 4-7 the
+// other way round, so the two waves of a SIMD overlap. Operand tiles are
+// stored as loaded: Yt[token][row] (dY, 128 values) and Xt[token][col] (X, 512
+// values), each row padded by 64 bytes (row stride = 16 dwords mod 64 banks)
+// so the 4 rows x 2 column halves read by one 32-lane pass of
+// ds_read_b64_tr_b16 fall in distinct banks. The raw tiles of step k+2 are
+// loaded into registers during step k.
+constexpr int DL_BM = 128, DL_BN = 512, DL_BK = 32;
+constexpr uint32_t DL_RSA = 128u * 2u + 64u;                 // 320
+constexpr uint32_t DL_RSB = 512u * 2u + 64u;                 // 1088
+constexpr uint32_t DL_TA = DL_BK * DL_RSA;                   // 10240
+constexpr uint32_t DL_TB = DL_BK * DL_RSB;                   // 34816
+constexpr uint32_t DL_STAGE = DL_TA + DL_TB;                 // 45056: one buffer of both tiles
+constexpr uint32_t DL_BINS = 2u * DL_STAGE;                  // 90112: [4 copies][128 rows][16] fp32
+constexpr uint32_t DL_LDS = DL_BINS + 4u * 128u * 16u * 4u;  // 122880
+// during binning the chunk's packed indices, [128 rows][64 * B bytes], sit at 0
+constexpr uint32_t DL_IRS = 256u;                            // index row stride (b <= 4)
 
 // 8 consecutive 16-bit values p[e0 .. e0+7] (zero at or past `lim`).
 // VEC: rows are 16-byte aligned and `lim` is a multiple of 8, so a chunk is
@@ -347,8 +355,14 @@ __device__ __forceinline__ uint32_t dl_field(uint32_t row, uint32_t j) {
   return (w >> off) & ((1u << B) - 1u);
 }
 
+// raw operands of one step for one thread: one dY chunk, four X chunks
+struct DlStage {
+  u32x4 y;
+  u32x4 x[4];
+};
+
 template <int B, typename TX, bool VEC>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(512, 1)
 k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
             int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
   typedef mfma32<TX> MF;
@@ -364,115 +378,159 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
   const int g = (int)(lb % (uint32_t)gpr);
   const int64_t G = d / gpr;
-  const int64_t jg0 = (int64_t)g * G;              // first column of the group
+  const int64_t jg0 = (int64_t)g * G;  // first column of the group
   const int64_t jend = jg0 + G;
+  const int KS = (int)((m + DL_BK - 1) / DL_BK);
 
-  for (uint32_t q = (uint32_t)t; q < 2u * 128u * 16u; q += 256u) st_w(DL_BINS + q * 4u, 0u);
+  for (uint32_t q = (uint32_t)t; q < 4u * 128u * 16u; q += 512u) st_w(DL_BINS + q * 4u, 0u);
 
-  // staging role: 16-byte pieces c = t and t + 256 of a 32 x 128 tile
-  // (token c / 16, values 8 (c % 16) .. +7)
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t KS = (uint32_t)((m + DL_BK - 1) / DL_BK);
-
-  auto load_step = [&](uint32_t ks, int64_t j0, u32x4* ya, u32x4* xb) {
+  // ---- staging roles: dY chunk t (token t / 16, rows 8 (t % 16) ..), X
+  // chunks t + 512 h (token c / 64, columns 8 (c % 64) ..)
+  const int ytok = t >> 4;
+  const int64_t yrow = i0 + 8 * (t & 15);
+  const uint32_t y_st = (uint32_t)ytok * DL_RSA + (uint32_t)(t & 15) * 16u;
+  auto load_step = [&](DlStage& S, int k, int64_t j0) {
+    const int64_t tok = (int64_t)k * DL_BK + ytok;
+    const bool ok = tok < m;
+    S.y = dl_load8<VEC, TX>(dY + (ok ? tok : 0) * n, yrow, ok ? n : 0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = t + 256 * h;
-      const int64_t tok = (int64_t)ks * DL_BK + (c >> 4);
-      const bool ok = tok < m;
-      const int64_t tr = ok ? tok : 0;
-      ya[h] = dl_load8<VEC, TX>(dY + tr * n, i0 + 8 * (c & 15), ok ? n : 0);
-      xb[h] = dl_load8<VEC, TX>(X + tr * d, j0 + 8 * (c & 15), ok ? jend : 0);
+    for (int h = 0; h < 4; ++h) {
+      const int c = t + 512 * h;
+      const int64_t xt = (int64_t)k * DL_BK + (c >> 6);
+      const bool xok = xt < m;
+      // d and the group width are multiples of 32: a chunk is wholly in or out
+      S.x[h] = dl_load8<true, TX>(X + (xok ? xt : 0) * d, j0 + 8 * (c & 63), xok ? jend : 0);
     }
   };
-  auto store_step = [&](uint32_t buf, const u32x4* ya, const u32x4* xb) {
+  auto store_step = [&](const DlStage& S, int k) {
+    const uint32_t base = (uint32_t)(k & 1) * DL_STAGE;
+    st_q(base + y_st, S.y);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t c = (uint32_t)(t + 256 * h);
-      const uint32_t off = (c >> 4) * DL_RS + (c & 15u) * 16u;
-      st_q(DL_Y + buf * DL_TILE + off, ya[h]);
-      st_q(DL_X + buf * DL_TILE + off, xb[h]);
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t c = (uint32_t)(t + 512 * h);
+      st_q(base + DL_TA + (c >> 6) * DL_RSB + (c & 63u) * 16u, S.x[h]);
     }
+  };
+
+  // ---- matrix roles
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 acc[2][4];
+  auto mfma_step = [&](int k) {
+    const uint32_t base = (uint32_t)(k & 1) * DL_STAGE;
+    u32x4 af[2][2], bf[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[ks][a] = ld_frag_tr(base + 16u * ks * DL_RSA + (64u * wm + 32u * a) * 2u, DL_RSA, lane);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        bf[ks][b] = ld_frag_tr(base + DL_TA + 16u * ks * DL_RSB + (128u * wn + 32u * b) * 2u, DL_RSB, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = MF::run(af[ks][a], bf[ks][b], acc[a][b]);
+    // the first half's 12 reads, then its 8 MFMAs interleaved with the second
+    // half's reads, then the second half's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const bool mfma_first = wave < 4;  // the other wave of this SIMD stages first
+  DlStage S;
+  // step k: multiply tile k; store tile k+1 (in S) into the other buffer and
+  // load tile k+2 into S
+  auto step = [&](int k, int64_t j0) {
+    auto stage_part = [&]() {
+      if (k + 1 < KS) {
+        store_step(S, k + 1);
+        if (k + 2 < KS) load_step(S, k + 2, j0);
+      }
+    };
+    if (mfma_first) {
+      mfma_step(k);
+      stage_part();
+    } else {
+      stage_part();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(k);
+    }
+    __syncthreads();
   };
 
   for (int64_t j0 = jg0; j0 < jend; j0 += DL_BN) {
-    __syncthreads();  // the previous chunk's binning is done with the staged indices
-    {
-      // this chunk's packed indices: 128 rows x (16 * B) bytes, as dwords
-      const int row = t >> 1;
-      const int64_t grow = i0 + row < n ? i0 + row : n - 1;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
-      const int64_t avail_units = (jend - j0) / 32;
-#pragma unroll
-      for (int q = 0; q < 2 * B; ++q) {
-        const int wd = (t & 1) * 2 * B + q;
-        const bool in = (wd / B) < avail_units;
-        st_w(DL_I + (uint32_t)row * 64u + (uint32_t)wd * 4u, in ? src[wd] : 0u);
-      }
-    }
-
-    f32x16 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) zero16(acc[a][b]);
-
-    u32x4 ya[2], xb[2];
-    load_step(0, j0, ya, xb);
-    store_step(0, ya, xb);
+      for (int b = 0; b < 4; ++b) zero16(acc[a][b]);
+    __syncthreads();  // the previous chunk's binning is done with the staged indices
+    load_step(S, 0, j0);
+    store_step(S, 0);
+    if (KS > 1) load_step(S, 1, j0);
     __syncthreads();
-    for (uint32_t k = 0; k < KS; ++k) {
-      const uint32_t cur = k & 1u;
-      const bool more = k + 1 < KS;
-      if (more) load_step(k + 1, j0, ya, xb);
-      const uint32_t yb = DL_Y + cur * DL_TILE, xbse = DL_X + cur * DL_TILE;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 af[2], bf[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) af[a] = ld_frag_tr(yb + 16u * ks * DL_RS + (64u * wm + 32u * a) * 2u, DL_RS, lane);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) bf[b] = ld_frag_tr(xbse + 16u * ks * DL_RS + (64u * wn + 32u * b) * 2u, DL_RS, lane);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[a][b] = MF::run(af[a], bf[b], acc[a][b]);
+    for (int k = 0; k < KS; ++k) step(k, j0);
+
+    // ---- this chunk's packed indices: 128 rows x (16 * B) dwords
+    {
+      const int64_t units = (jend - j0) / 32 < DL_BN / 32 ? (jend - j0) / 32 : DL_BN / 32;
+      for (int q = t; q < 128 * 16 * B; q += 512) {
+        const int row = q / (16 * B), wd = q % (16 * B);
+        const int64_t grow = i0 + row < n ? i0 + row : n - 1;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
+        st_w((uint32_t)row * DL_IRS + (uint32_t)wd * 4u, (wd / B) < units ? src[wd] : 0u);
       }
-      if (more) store_step(cur ^ 1u, ya, xb);
-      __syncthreads();
     }
+    __syncthreads();
 
     // ---- scatter-add the finished dW tile into this wave's bins
-    // D[i][j] of tile (a, b): i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4, j = 64 wn + 32 b + lane%32
-    // (fully unrolled so the accumulators stay in registers; the scheduling
-    // fences keep the compiler from hoisting all 64 index reads at once)
+    // D[i][j] of tile (a, b): i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4,
+    // j = 128 wn + 32 b + lane%32 (fully unrolled so the accumulators stay in
+    // registers; the scheduling fences keep the index reads from being
+    // hoisted all at once)
+    // (an opaque copy of the lane id keeps the compiler from hoisting the 128
+    // bin addresses out of the chunk loop, where they would stay live across
+    // the K loop)
+    uint32_t bl = lane;
+    asm volatile("" : "+v"(bl));
     const uint32_t binbase = DL_BINS + (uint32_t)wn * (128u * 16u * 4u);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint32_t j = 64u * wn + 32u * b + (lane & 31u);
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t j = 128u * wn + 32u * b + (bl & 31u);
         const bool j_ok = j0 + (int64_t)j < jend;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (lane >> 5) + (e & 3);
-          if (j_ok && i0 + (int64_t)i < n) {
-            const uint32_t c = dl_field<B>(DL_I + i * 64u, j);
-            __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * 16u + c) * 4u), acc[a][b][e],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          }
+          // branch-free: an entry outside the matrix adds 0 to a bin that is
+          // never stored (rows past n) or to entry 0 (columns past the group,
+          // whose staged indices are 0)
+          const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (bl >> 5) + (e & 3);
+          const float v = (j_ok && i0 + (int64_t)i < n) ? acc[a][b][e] : 0.0f;
+          const uint32_t c = dl_field<B>(i * DL_IRS, j);
+          __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * 16u + c) * 4u), v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
           if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
   }
   __syncthreads();
 
-  // ---- one store per gradient entry
-  for (uint32_t q = (uint32_t)t; q < 128u * (uint32_t)K; q += 256u) {
+  // ---- one store per gradient entry (bin copies summed in a fixed order)
+  for (uint32_t q = (uint32_t)t; q < 128u * (uint32_t)K; q += 512u) {
     const uint32_t i = q / K, c = q % K;
     if (i0 + (int64_t)i >= n) continue;
-    const float s = *(const lds_f32*)(uintptr_t)(DL_BINS + (i * 16u + c) * 4u) +
-                    *(const lds_f32*)(uintptr_t)(DL_BINS + 128u * 16u * 4u + (i * 16u + c) * 4u);
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      s += *(const lds_f32*)(uintptr_t)(DL_BINS + (uint32_t)w * (128u * 16u * 4u) + (i * 16u + c) * 4u);
     float* dst = dLUT + ((i0 + i) * gpr + g) * K + c;
     *dst = accumulate ? *dst + s : s;
   }
@@ -508,18 +566,24 @@ hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& 
   }
 }
 
+template <int B, typename TX, bool VEC>
+hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
+                       hipStream_t s) {
+  const auto kern = k_gemm_dlut<B, TX, VEC>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DL_LDS);
+  if (attr != hipSuccess) return attr;
+  const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
+                     accumulate);
+  return hipGetLastError();
+}
+
 template <int B, typename TX>
 hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
                   hipStream_t s) {
-  const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
-  const dim3 grid((unsigned)(rb * p.gpr));
-  if (p.n % 8 == 0)  // d is a multiple of 32 already
-    hipLaunchKernelGGL((k_gemm_dlut<B, TX, true>), grid, dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
-                       accumulate);
-  else
-    hipLaunchKernelGGL((k_gemm_dlut<B, TX, false>), grid, dim3(256), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
-                       accumulate);
-  return hipGetLastError();
+  if (p.n % 8 == 0) return dlut_launch<B, TX, true>(dY, X, idx, p, dLUT, accumulate, s);
+  return dlut_launch<B, TX, false>(dY, X, idx, p, dLUT, accumulate, s);
 }
 
 template <typename TX>
