@@ -10,12 +10,13 @@
 // mapping is frozen ("SpaLLM", section 2.3), so there is no index gradient.
 // dX is the chain rule through Y = X W^T, needed to train lower layers.
 //
-// k_gemm_dx: M = tokens (256), N = columns of dX (128), K = weight rows (32
-// per step). The weight tile of 32 rows x 128 columns is dequantised once per
-// step and written transposed ([column][row]) so each MFMA B fragment is 8
-// consecutive rows of one column. Each step brings 32 new rows, so the tables
-// (up to 4 groups of the column tile, private copy per lane slot) are staged
-// every step, two steps ahead.
+// k_gemm_dx: M = tokens (256), N = columns of dX (256), K = weight rows (32
+// per step). The weight tile of 32 rows x 256 columns is dequantised once per
+// step into a row-major LDS tile and read with gfx950's transposing LDS reads
+// (each MFMA B fragment is 8 consecutive rows of one column). Each step brings
+// 32 new rows, so the tables (the groups of the column tile, private copy per
+// lane slot) are staged every step: loaded three steps ahead, stored two
+// steps ahead.
 //
 // k_gemm_dlut: one block owns 128 rows x one group. For each chunk of up to
 // 512 columns of the group it accumulates the dW = dY^T X tile over all
@@ -37,144 +38,113 @@ using namespace mm;
 // ============================================================================
 // dX
 // ============================================================================
-constexpr int DX_BM = 256, DX_BN = 128, DX_BK = 32, DX_NG = 4;
-constexpr uint32_t DX_A = 0;                                   // [2][256][32] dY (compute dtype)
-constexpr uint32_t DX_B = 2u * DX_BM * DX_BK * 2u;             // 32768: [2][128 cols][32 rows]
-constexpr uint32_t DX_T = DX_B + 2u * DX_BN * DX_BK * 2u;      // 49152: tables [2][NG][T][64] dwords
-constexpr uint32_t DX_LDS = DX_T + 2u * DX_NG * 16u * 64u * 4u;  // 81920
+// 8 waves in a 2 (tokens) x 4 (columns) grid, 128 x 64 outputs per wave (4 x 2
+// tiles of v_mfma_f32_32x32x16, 16 MFMAs per step); one block per CU; waves
+// 0-3 multiply first and stage second, waves 4-7 the other way round, so the
+// two waves of a SIMD overlap. LDS:
+//   tables [2][NG groups][T entries][64 lane slots] dwords            at 0
+//   A  [2][256 tokens][32 rows] dY in the compute dtype (mm::swz rows)
+//   Wt [2][32 rows][256 columns + 32 pad] dequantised weights; the row stride
+//      is 16 dwords mod 64 banks so the transposing reads are conflict-free
+// Staging roles: weight row r = t % 32 of the step, 16-column chunk t / 32
+// (16 weights); 16-byte chunk t % 4 of token rows t / 4 and t / 4 + 128 of dY.
+// Lane slot s holds the tables of step row s % 32.
+constexpr int DX_BM = 256, DX_BN = 256, DX_BK = 32;
+constexpr uint32_t DX_RSB = 256u * 2u + 64u;  // 576
+constexpr uint32_t DX_TA = DX_BM * DX_BK * 2u;  // 16384
+constexpr uint32_t DX_TB = DX_BK * DX_RSB;      // 18432
+template <int NG> struct DxLds {
+  static constexpr uint32_t T = 0;
+  static constexpr uint32_t A = 2u * NG * 16u * 64u * 4u;
+  static constexpr uint32_t B = A + 2u * DX_TA;
+  static constexpr uint32_t TOTAL = B + 2u * DX_TB;
+};
 
-template <int B> struct DxIdx { uint32_t w[B == 3 ? 3 : (B == 4 ? 2 : 1)]; };
-
-template <int B>
-__device__ __forceinline__ void dx_load_idx(DxIdx<B>& I, const uint8_t* rowp, uint32_t u, int hh) {
-  if constexpr (B == 4) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(rowp + u * 16u + hh * 8);
-    I.w[0] = v.x;
-    I.w[1] = v.y;
-  } else if constexpr (B == 2) {
-    I.w[0] = *reinterpret_cast<const uint32_t*>(rowp + u * 8u + hh * 4);
-  } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(rowp + u * 12u);
-    I.w[0] = p[0];
-    I.w[1] = p[1];
-    I.w[2] = p[2];
-  }
-}
+template <int B> struct DxStage {
+  u32x4 y[2];
+  uint32_t w[B == 3 ? 3 : (B == 4 ? 2 : 1)];
+};
 
 // 16 weights of half hh of a unit -> 8 words of packed consecutive columns
 template <int B>
-__device__ __forceinline__ void dx_dequant(const DxIdx<B>& I, int hh, uint32_t gk, uint32_t lane4, uint32_t* o) {
+__device__ __forceinline__ void dx_dequant(const uint32_t* w, int hh, uint32_t gk, uint32_t lane4, uint32_t* o) {
   const uint32_t gk4 = gk * 0x01010101u;
   if constexpr (B == 4) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t ev = (I.w[j] & 0x0F0F0F0Fu) | gk4;
-      const uint32_t od = ((I.w[j] >> 4) & 0x0F0F0F0Fu) | gk4;
+      const uint32_t ev = (w[j] & 0x0F0F0F0Fu) | gk4;
+      const uint32_t od = ((w[j] >> 4) & 0x0F0F0F0Fu) | gk4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        o[4 * j + t] = pack2(ld_h(gaddr(ev, lane4, t) + DX_T), ld_h(gaddr(od, lane4, t) + DX_T));
+      for (int t = 0; t < 4; ++t) o[4 * j + t] = pack2(ld_h(gaddr(ev, lane4, t)), ld_h(gaddr(od, lane4, t)));
     }
   } else if constexpr (B == 2) {
-    const uint32_t ev = (I.w[0] & 0x0F0F0F0Fu) | gk4;
-    const uint32_t od = ((I.w[0] >> 4) & 0x0F0F0F0Fu) | gk4;
+    const uint32_t ev = (w[0] & 0x0F0F0F0Fu) | gk4;
+    const uint32_t od = ((w[0] >> 4) & 0x0F0F0F0Fu) | gk4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      o[2 * t] = ld_w(gaddr(ev, lane4, t) + DX_T);
-      o[2 * t + 1] = ld_w(gaddr(od, lane4, t) + DX_T);
+      o[2 * t] = ld_w(gaddr(ev, lane4, t));
+      o[2 * t + 1] = ld_w(gaddr(od, lane4, t));
     }
   } else {
     if (hh) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint32_t e0 = unit_field<3>(I.w, 16 + 2 * t), e1 = unit_field<3>(I.w, 17 + 2 * t);
-        o[t] = pack2(ld_h((((gk + e0) << 8) | lane4) + DX_T), ld_h((((gk + e1) << 8) | lane4) + DX_T));
+        const uint32_t e0 = unit_field<3>(w, 16 + 2 * t), e1 = unit_field<3>(w, 17 + 2 * t);
+        o[t] = pack2(ld_h(((gk + e0) << 8) | lane4), ld_h(((gk + e1) << 8) | lane4));
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint32_t e0 = unit_field<3>(I.w, 2 * t), e1 = unit_field<3>(I.w, 1 + 2 * t);
-        o[t] = pack2(ld_h((((gk + e0) << 8) | lane4) + DX_T), ld_h((((gk + e1) << 8) | lane4) + DX_T));
+        const uint32_t e0 = unit_field<3>(w, 2 * t), e1 = unit_field<3>(w, 1 + 2 * t);
+        o[t] = pack2(ld_h(((gk + e0) << 8) | lane4), ld_h(((gk + e1) << 8) | lane4));
       }
     }
   }
 }
 
-// Tables of step rows k0..k0+31, groups glo..glo+ng-1, into buffer tb:
-// slot s (lane id) holds row k0 + s%32; wave w writes entries [w*T/4, (w+1)*T/4).
-template <int B> struct DxLut { uint32_t v[2]; };
+// Table words of one thread for one group: lane slot s = t % 64 (step row
+// s % 32), part p = t / 64 covers entries 2p, 2p+1 (b = 4 and the b = 2 pair
+// table) or, for p < 4, entries 2p, 2p+1 of the b = 3 table.
+template <int B> struct DxLutWord { uint32_t v[B == 2 ? 2 : 1]; };
 
 template <int B, typename TL>
-__device__ __forceinline__ void dx_load_lut(DxLut<B>& L, const TL* lut, int64_t row, bool row_ok, int gpr, uint32_t g,
-                                            int w) {
+__device__ __forceinline__ void dx_lut_load(DxLutWord<B>& L, const TL* lut, int64_t row, bool ok, int gpr, uint32_t g,
+                                            int part) {
   constexpr int K = 1 << B;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(lut) + ((int64_t)row * gpr + g) * K;
-  if (!row_ok) {
-    L.v[0] = L.v[1] = 0u;
-    return;
-  }
-  if constexpr (B == 4) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(src + 4 * w);
+  if constexpr (B == 2) {
+    const u32x2 v = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0u, 0u};
     L.v[0] = v.x;
     L.v[1] = v.y;
   } else if constexpr (B == 3) {
-    L.v[0] = *reinterpret_cast<const uint32_t*>(src + 2 * w);
-    L.v[1] = 0u;
+    L.v[0] = (ok && part < 4) ? *reinterpret_cast<const uint32_t*>(src + 2 * part) : 0u;
   } else {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-    L.v[0] = v.x;
-    L.v[1] = v.y;
+    L.v[0] = ok ? *reinterpret_cast<const uint32_t*>(src + 2 * part) : 0u;
   }
 }
 
 template <int B>
-__device__ __forceinline__ void dx_store_lut(const DxLut<B>& L, uint32_t tb, uint32_t gsel, int w, uint32_t lane4) {
-  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
-  const uint32_t base = (tb * DX_NG + gsel) * T;
-  if constexpr (B == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t v = (i & 1) ? (L.v[i >> 1] >> 16) : (L.v[i >> 1] & 0xFFFFu);
-      st_w(DX_T + ((base + 4u * w + i) << 8) + lane4, v);
-    }
-  } else if constexpr (B == 3) {
-    st_w(DX_T + ((base + 2u * w) << 8) + lane4, L.v[0] & 0xFFFFu);
-    st_w(DX_T + ((base + 2u * w + 1) << 8) + lane4, L.v[0] >> 16);
-  } else {
+__device__ __forceinline__ void dx_lut_store(const DxLutWord<B>& L, uint32_t ebase, int part, uint32_t lane4) {
+  if constexpr (B == 2) {
     const uint32_t e[4] = {L.v[0] & 0xFFFFu, L.v[0] >> 16, L.v[1] & 0xFFFFu, L.v[1] >> 16};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pe = 4 * w + i;
-      st_w(DX_T + ((base + pe) << 8) + lane4, e[pe & 3] | (e[pe >> 2] << 16));
+    for (int i = 0; i < 2; ++i) {
+      const int pe = 2 * part + i;  // pair entry a + 4c
+      st_w(((ebase + pe) << 8) | lane4, e[pe & 3] | (e[pe >> 2] << 16));
     }
-  }
-}
-
-// dY tile row (32 weight rows starting at k0) of one token -> compute dtype
-template <typename TX, typename TC>
-__device__ __forceinline__ void dx_load_a(u32x4* a, const TX* dyrow, int64_t k0, int64_t n, bool vec) {
-  if (vec && k0 + 32 <= n) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(dyrow + k0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a[c] = p[c];
   } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(dyrow);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t i0 = k0 + 8 * c + 2 * q;
-        const uint32_t lo = i0 < n ? p[i0] : 0u;
-        const uint32_t hi = i0 + 1 < n ? p[i0 + 1] : 0u;
-        a[c][q] = lo | (hi << 16);
-      }
+    if (B == 3 && part >= 4) return;
+    st_w(((ebase + 2u * part) << 8) | lane4, L.v[0] & 0xFFFFu);
+    st_w(((ebase + 2u * part + 1u) << 8) | lane4, L.v[0] >> 16);
   }
 }
 
-template <int B, typename TX, typename TL>
-__global__ void __launch_bounds__(256, 1)
+template <int B, int NG, typename TX, typename TL>
+__global__ void __launch_bounds__(512, 1)
 k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut, int64_t m,
           int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX) {
   typedef mfma32<TL> MF;
+  typedef DxLds<NG> LDS;
   constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
   extern __shared__ uint32_t smem[];
   (void)smem;
@@ -184,113 +154,199 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
   const int wave = t >> 6;
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
-  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;   // token / column tile origins
+  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;  // token / column tile origins
   const bool vec = (n % 8) == 0;
+  const int KS = (int)((n + DX_BK - 1) / DX_BK);   // K-steps over the weight rows
 
-  // dequant role: weight row r of the step, 16-column chunk c of the tile
+  // ---- dequant role: weight row r of the step, 16-column chunk cc
   const int r = t & 31;
-  const int c = t >> 5;
-  const int hh = c & 1;
-  const int64_t jc = n0 + 16 * c;                   // first column of the chunk
+  const int cc = t >> 5;
+  const int hh = cc & 1;
+  const int64_t jc = n0 + 16 * cc;  // first column of the chunk
   const bool col_ok = jc < d;
   const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
   const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
   const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
-  const uint32_t ng = ghi - glo + 1;                // groups touched by the column tile (<= 4)
+  const int ng = (int)(ghi - glo + 1);  // groups touched by the column tile (<= NG)
   const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
-  // activation role: token row t
-  const int64_t gtok = (m0 + t < m) ? m0 + t : m - 1;
-  const TX* dyrow = dY + gtok * n;
+  const int64_t rbytes = d * B / 8;
+  const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B) + (B == 3 ? 0 : hh * 2 * B);
+  const uint32_t b_st = (uint32_t)r * DX_RSB + 32u * (uint32_t)cc;
+  // ---- table role: lane slot `lane` (row lane % 32 of a step), part = wave
+  const int part = wave;
+  // ---- dY role: chunk t % 4 of token rows t / 4 + 128 c
+  const TX* yrow[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t tok = m0 + 128 * c + (t >> 2);
+    yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+  }
+  const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
+  const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
 
-  const int64_t rb = d * B / 8;
-  const uint32_t KS = (uint32_t)((n + DX_BK - 1) / DX_BK);  // K-steps
-
-  auto stage_tables = [&](uint32_t ks, uint32_t tb) {
-    const int64_t row = (int64_t)ks * DX_BK + (lane & 31);
-    const bool ok = row < n;
-    for (uint32_t gs = 0; gs < ng; ++gs) {
-      DxLut<B> L;
-      dx_load_lut<B, TL>(L, lut, ok ? row : 0, ok, gpr, glo + gs, wave);
-      dx_store_lut<B>(L, tb, gs, wave, lane4);
+  auto load_stage = [&](DxStage<B>& S, int j) {
+    const int64_t k0 = (int64_t)j * DX_BK;
+    const int64_t e0 = k0 + 8 * (t & 3);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (vec) {
+        const bool in = e0 < n;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
+        S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(yrow[c]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t i = e0 + 2 * q;
+          S.y[c][q] = (i < n ? p[i] : 0u) | ((i + 1 < n ? p[i + 1] : 0u) << 16);
+        }
+      }
+    }
+    const int64_t row = k0 + r;
+    const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
+    if constexpr (B == 4) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      S.w[0] = v.x;
+      S.w[1] = v.y;
+    } else if constexpr (B == 2) {
+      S.w[0] = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
+      S.w[0] = q[0];
+      S.w[1] = q[1];
+      S.w[2] = q[2];
     }
   };
-  auto dequant_step = [&](uint32_t ks, uint32_t buf) {
-    const int64_t row = (int64_t)ks * DX_BK + r;
-    const bool ok = row < n && col_ok;
+  // dequantise / convert tile j into buffer j & 1 (tables of tile j are in
+  // table buffer j & 1)
+  auto stage = [&](const DxStage<B>& S, int j) {
+    const uint32_t buf = (uint32_t)(j & 1);
+    const bool ok = (int64_t)j * DX_BK + r < n && col_ok;
     uint32_t o[8];
-    DxIdx<B> I;
-    dx_load_idx<B>(I, idx_packed + (ok ? row : 0) * rb, u, hh);
-    dx_dequant<B>(I, hh, ((ks & 1u) * DX_NG + gsel) * T, lane4, o);
-    const uint32_t bb = DX_B + buf * (uint32_t)(DX_BN * DX_BK * 2);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      const uint32_t v = ok ? ((f & 1) ? (o[f >> 1] >> 16) : (o[f >> 1] & 0xFFFFu)) : 0u;
-      st_h(bb + swz_elem((uint32_t)(16 * c + f), (uint32_t)r), v);
-    }
+    dx_dequant<B>(S.w, hh, (buf * NG + gsel) * T, lane4, o);
+    const uint32_t bb = LDS::B + buf * DX_TB + b_st;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st_q(bb, ok ? u32x4{o[0], o[1], o[2], o[3]} : z);
+    st_q(bb + 16u, ok ? u32x4{o[4], o[5], o[6], o[7]} : z);
+    const uint32_t ab = LDS::A + buf * DX_TA;
+    st_q(ab + a_st0, cvt_quad<TX, TL>(S.y[0]));
+    st_q(ab + a_st1, cvt_quad<TX, TL>(S.y[1]));
   };
-  auto store_a = [&](const u32x4* a, uint32_t buf) {
-    const uint32_t ab = DX_A + buf * (uint32_t)(DX_BM * DX_BK * 2);
+  DxLutWord<B> LW[NG];
+  auto lut_load = [&](int j) {
+    const int64_t row = (int64_t)j * DX_BK + (lane & 31);
+    const bool ok = row < n;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st_q(ab + swz((uint32_t)t, (uint32_t)q), cvt_quad<TX, TL>(a[q]));
+    for (int gs = 0; gs < NG; ++gs)
+      if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
+  };
+  auto lut_store = [&](int j) {
+    const uint32_t buf = (uint32_t)(j & 1);
+#pragma unroll
+    for (int gs = 0; gs < NG; ++gs)
+      if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
   };
 
-  // ---- prologue
-  u32x4 a[4];
-  stage_tables(0, 0);
-  if (KS > 1) stage_tables(1, 1);
-  dx_load_a<TX, TL>(a, dyrow, 0, n, vec);
-  __syncthreads();
-  dequant_step(0, 0);
-  store_a(a, 0);
-  __syncthreads();
-
+  // ---- matrix roles
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+  const uint32_t khalf = (uint32_t)(lane >> 5);
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) zero16(acc[i][j]);
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
-  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
-
-  for (uint32_t k = 0; k < KS; ++k) {
-    const uint32_t cur = k & 1u;
-    const bool more = k + 1 < KS;
-    if (more) dx_load_a<TX, TL>(a, dyrow, (int64_t)(k + 1) * DX_BK, n, vec);
-    const uint32_t abase = DX_A + cur * (uint32_t)(DX_BM * DX_BK * 2);
-    const uint32_t bbase = DX_B + cur * (uint32_t)(DX_BN * DX_BK * 2);
+    for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
+  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+    const uint32_t buf = (uint32_t)(k & 1);
+    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
-      u32x4 af[4], bf[2];
+    for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS::A + buf * DX_TA + swz(arow + 32u * i, ch));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = ld_q(abase + swz(arow + 32u * i, ch));
+    for (int jj = 0; jj < 2; ++jj)
+      fb[jj] = ld_frag_tr(LDS::B + buf * DX_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
+                          (uint32_t)lane);
+  };
+  auto mfma_step = [&](int k) {
+    u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+    load_frags(fa0, fb0, k, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = ld_q(bbase + swz(brow + 32u * j, ch));
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa0[i], fb0[jj], acc[i][jj]);
+    load_frags(fa1, fb1, k, 1);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(af[i], bf[j], acc[i][j]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa1[i], fb1[jj], acc[i][jj]);
+    // first half's 8 reads (4 A + 2 x 2 transposing B), then its MFMAs
+    // interleaved with the second half's reads, then the second half's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    if (more) {
-      dequant_step(k + 1, cur ^ 1u);
-      store_a(a, cur ^ 1u);
-      if (k + 2 < KS) stage_tables(k + 2, cur);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // staging work of step k: the tables of tile k+2 (loaded during step k-1)
+  // go to LDS and those of tile k+3 are loaded; tile k+1 goes from Sn into
+  // LDS and Sn is refilled with tile k+3
+  auto stage_step = [&](int k, DxStage<B>& Sn) {
+    if (k + 2 < KS) lut_store(k + 2);
+    if (k + 3 < KS) lut_load(k + 3);
+    if (k + 1 < KS) {
+      stage(Sn, k + 1);
+      if (k + 3 < KS) load_stage(Sn, k + 3);
+    }
+  };
+  const bool mfma_first = wave < 4;
+  DxStage<B> S0, S1;
+  auto step = [&](int k, DxStage<B>& Sn) {
+    if (mfma_first) {
+      mfma_step(k);
+      stage_step(k, Sn);
+    } else {
+      stage_step(k, Sn);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(k);
     }
     __syncthreads();
+  };
+
+  // ---- prologue: tables of tiles 0 and 1, tile 0 staged, tiles 1 and 2 in
+  // registers
+  lut_load(0);
+  load_stage(S0, 0);
+  if (KS > 1) load_stage(S1, 1);
+  lut_store(0);
+  if (KS > 1) {
+    lut_load(1);
+    lut_store(1);
   }
+  if (KS > 2) lut_load(2);
+  __syncthreads();
+  stage(S0, 0);
+  if (KS > 2) load_stage(S0, 2);
+  __syncthreads();
+
+  int k = 0;
+  for (; k + 1 < KS; k += 2) {
+    step(k, S1);
+    step(k + 1, S0);
+  }
+  if (k < KS) step(k, S1);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + 64 * wn + 32 * j + (lane & 31);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
       if (col >= d) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < m) dX[tok * d + col] = acc[i][j][e];
+        if (tok < m) dX[tok * d + col] = acc[i][jj][e];
       }
     }
 }
@@ -543,18 +599,26 @@ uint32_t ug_magic_of(const Problem& p) {
   return ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
 }
 
-template <int B, typename TX, typename TL>
-hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
-  const auto kern = k_gemm_dx<B, TX, TL>;
+template <int B, int NG, typename TX, typename TL>
+hipError_t dx_launch(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+  const auto kern = k_gemm_dx<B, NG, TX, TL>;
   // more than 64 KB of LDS per block must be requested once per kernel
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, DX_LDS);
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DxLds<NG>::TOTAL);
   if (attr != hipSuccess) return attr;
   const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
   const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(256), DX_LDS, s, dY, idx, lut, p.m, p.n, p.d, p.gpr,
-                     ug_magic_of(p), mb, dX);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), DxLds<NG>::TOTAL, s, dY, idx, lut, p.m, p.n, p.d,
+                     p.gpr, ug_magic_of(p), mb, dX);
   return hipGetLastError();
+}
+
+template <int B, typename TX, typename TL>
+hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+  // a 256-column tile touches at most 2 groups when groups are >= 256 columns
+  // wide, at most 8 (one per 32-column unit) otherwise
+  if (p.group_cols() >= 256) return dx_launch<B, 2>(dY, idx, lut, p, dX, s);
+  return dx_launch<B, 8>(dY, idx, lut, p, dX, s);
 }
 
 template <typename TX, typename TL>
