@@ -42,7 +42,8 @@ namespace skm {
 namespace {
 
 constexpr int DEC_ROWS = 16;
-constexpr int DEC_PF = 4;     // slots loaded per batch and wave
+// slots loaded per batch and wave: a batch of NW waves covers 32 slots
+template <int NW> struct dec_pf { static constexpr int value = 32 / NW; };
 constexpr int DEC_MAX_ENTRIES = 224;  // table entries per row kept in LDS (entry byte must fit in 8 bits)
 constexpr int DEC_LUT_CHUNKS = 2;     // 8-entry table chunks loaded per wave (16 * 2 * 8 >= 224)
 constexpr int64_t DEC_XL_MAX = 32768; // m * d elements staged in LDS (64 KB)
@@ -177,18 +178,18 @@ __device__ __forceinline__ void tab_load(TabRegs<B>& R, const TL* __restrict__ l
 #pragma unroll
   for (int c = 0; c < DEC_LUT_CHUNKS * (16 / NW); ++c) {
     const int ch = wave + NW * c;
+    // unconditional loads (a chunk past the row's tables re-reads chunk 0 and
+    // is not stored) so that the compiler can count them
     if constexpr (B == 2) {
       // chunk = one group's 4 entries
-      if (ch < gpr) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(src + ch * 4);
-        R.v[c][0] = v.x;
-        R.v[c][1] = v.y;
-      }
+      const int cc = ch < gpr ? ch : 0;
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src + cc * 4);
+      R.v[c][0] = v.x;
+      R.v[c][1] = v.y;
     } else {
-      if (ch * 8 < gpr * K) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + ch * 8);
-        R.v[c][0] = v.x; R.v[c][1] = v.y; R.v[c][2] = v.z; R.v[c][3] = v.w;
-      }
+      const int cc = ch * 8 < gpr * K ? ch : 0;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + cc * 8);
+      R.v[c][0] = v.x; R.v[c][1] = v.y; R.v[c][2] = v.z; R.v[c][3] = v.w;
     }
   }
 }
@@ -219,42 +220,44 @@ __device__ __forceinline__ void tab_store(const TabRegs<B>& R, uint32_t* tabs, i
   }
 }
 
-template <int B, typename TX>
+template <int B, typename TX, int PF>
 struct SlotRegs {
-  uint32_t w[DEC_PF][B];
-  u32x4 x[DEC_PF][4];
-  uint32_t gk[DEC_PF];
-  uint32_t u[DEC_PF];
-  bool ok[DEC_PF];
+  uint32_t w[PF][B];
+  u32x4 x[PF][4];
+  uint32_t gk[PF];
+  uint32_t u[PF];
+  bool ok[PF];
 };
 
-// Issue the index and activation loads of DEC_PF slots. Addresses are clamped
-// in range instead of masked: a token row >= m or a weight row >= n only
-// feeds outputs that are never stored, and a unit past the row end (RAGGED
-// only) is zeroed by the caller. g = u / UG is a multiply-high by the host's
-// magic constant (exact for u * UG < 2^32).
-template <int B, int NW, typename TX, bool RAGGED, bool XL>
-__device__ __forceinline__ void load_batch(SlotRegs<B, TX>& R, int64_t s0, int64_t S, uint32_t U, uint32_t ug_magic,
-                                           int q, const uint8_t* rowp, const TX* xrow) {
+// Issue the index and activation loads of PF slots. Addresses are clamped in
+// range instead of masked, and the loads are unconditional (so the compiler
+// can count them and wait for one batch while the next is in flight): a slot
+// past the last one re-reads the last slot and is skipped by the caller, a
+// token row >= m or a weight row >= n only feeds outputs that are never
+// stored, and a unit past the row end (RAGGED only) is zeroed by the caller.
+// g = u / UG is a multiply-high by the host's magic constant (exact for
+// u * UG < 2^32).
+template <int B, int NW, typename TX, bool RAGGED, bool XL, int PF>
+__device__ __forceinline__ void load_batch(SlotRegs<B, TX, PF>& R, int64_t s0, int64_t S, uint32_t U,
+                                           uint32_t ug_magic, int q, const uint8_t* rowp, const TX* xrow) {
   constexpr int T = tab_entries<B>::value;
 #pragma unroll
-  for (int p = 0; p < DEC_PF; ++p) {
-    const int64_t s = s0 + (int64_t)p * NW;
-    if (s < S) {  // wave-uniform
-      uint32_t u = 4u * (uint32_t)s + (uint32_t)q;
-      if constexpr (RAGGED) {
-        R.ok[p] = u < U;
-        u = u < U ? u : U - 1u;
-      }
-      load_unit<B>(rowp, u, R.w[p]);
-      R.u[p] = u;
-      if constexpr (!XL) {
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) R.x[p][h] = xp[h];
-      }
-      R.gk[p] = (ug_magic ? __umulhi(u, ug_magic) : u) * T;  // magic 0: one unit per group
+  for (int p = 0; p < PF; ++p) {
+    const int64_t sp = s0 + (int64_t)p * NW;
+    const int64_t s = sp < S ? sp : S - 1;
+    uint32_t u = 4u * (uint32_t)s + (uint32_t)q;
+    if constexpr (RAGGED) {
+      R.ok[p] = u < U;
+      u = u < U ? u : U - 1u;
     }
+    load_unit<B>(rowp, u, R.w[p]);
+    R.u[p] = u;
+    if constexpr (!XL) {
+      const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) R.x[p][h] = xp[h];
+    }
+    R.gk[p] = (ug_magic ? __umulhi(u, ug_magic) : u) * T;  // magic 0: one unit per group
   }
 }
 
@@ -309,9 +312,10 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
       if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
     }
   }
-  SlotRegs<B, TX> R0, R1;
+  constexpr int PF = dec_pf<NW>::value;
+  SlotRegs<B, TX, PF> R0, R1;
   int64_t s0 = wave;
-  load_batch<B, NW, TX, RAGGED, XL>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+  load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
   if constexpr (XL) {
 #pragma unroll
@@ -328,9 +332,9 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const uint32_t xl_row = xl_base + (uint32_t)tokc * (uint32_t)d * 2u;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const SlotRegs<B, TX>& Rc, int64_t sb) {
+  auto compute = [&](const SlotRegs<B, TX, PF>& Rc, int64_t sb) {
 #pragma unroll
-    for (int p = 0; p < DEC_PF; ++p) {
+    for (int p = 0; p < PF; ++p) {
       if (sb + (int64_t)p * NW >= S) break;  // wave-uniform
       const uint32_t gk = Rc.gk[p];
       const uint32_t gk4 = gk * 0x01010101u;
@@ -352,15 +356,15 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
       }
     }
   };
-  constexpr int64_t STEP = (int64_t)NW * DEC_PF;
+  constexpr int64_t STEP = (int64_t)NW * PF;
   if constexpr (XL) {
     while (true) {
       const int64_t s1 = s0 + STEP;
-      if (s1 < S) load_batch<B, NW, TX, RAGGED, XL>(R1, s1, S, U, ug_magic, q, rowp, xrow);
+      if (s1 < S) load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s1, S, U, ug_magic, q, rowp, xrow);
       compute(R0, s0);
       if (s1 >= S) break;
       const int64_t s2 = s1 + STEP;
-      if (s2 < S) load_batch<B, NW, TX, RAGGED, XL>(R0, s2, S, U, ug_magic, q, rowp, xrow);
+      if (s2 < S) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s2, S, U, ug_magic, q, rowp, xrow);
       compute(R1, s1);
       if (s2 >= S) break;
       s0 = s2;
@@ -370,7 +374,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
       compute(R0, s0);
       s0 += STEP;
       if (s0 >= S) break;
-      load_batch<B, NW, TX, RAGGED, XL>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+      load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
     }
   }
 
