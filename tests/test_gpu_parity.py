@@ -107,6 +107,34 @@ def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     assert oracle.rel_err(got, want) <= TOL16
 
 
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "bf16"), ("bf16", "f16")])
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 1, 8200, 1184, 3), (4, 4, 8200, 1152, 2), (3, 8, 9001, 2048, 1), (2, 8, 12000, 512, 16),
+    (4, 1, 16400, 96, 7), (4, 8, 8400, 4096, 1),
+])
+def test_fwd16_large_n_decode(x_dtype, lut_dtype, b, gpr, n, d, m):
+    """Decode with more 16-row blocks than the GPU holds at once (8-wave
+    blocks); ragged rows and ragged 128-column slots included. Every row is
+    checked."""
+    idx, lut, X, _ = make_case(f"stream/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
+                               x_dtype, lut_dtype)
+    got, want = _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_large_n_decode_selection_bit_exact(dt):
+    """One-hot activation rows through the decode at large n: exact weights."""
+    b, gpr, n, d, m = 4, 4, 9000, 1024, 5
+    idx, lut, _, _ = make_case(f"ssel/{dt}", n, d, b, gpr, 1, dt, dt)
+    cols = np.random.default_rng(5).choice(d, m, replace=False)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    Y = skm().sketch_matmul_fwd(to_dev(syn.to_storage(X, dt), dt), to_dev(idx, "u8"), to_dev(lut, dt), b, gpr)
+    W = oracle.dequantize(idx, syn.to_float64(lut, dt), d, b, gpr)
+    assert np.array_equal(to_f64(Y), W[:, cols].T)
+
+
 @pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 200, 4096, 300), (4, 1, 64, 512, 17), (2, 8, 130, 11008, 40), (3, 4, 257, 1536, 513),
