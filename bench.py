@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,prefill,finetune,copy (default all; decode always runs)")
+                    help="comma list of decode,fwd16,prefill,finetune,dense,copy (default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -157,6 +157,23 @@ def bench_finetune(torch, skm, steps, warmup):
     }
 
 
+def bench_dense_reference(torch, steps, warmup):
+    """The vendor dense GEMM (torch.matmul -> hipBLASLt) at the prefill shapes,
+    with an already dequantised 16-bit weight: context for the sketched GEMM,
+    which does the dequantisation inside the kernel."""
+    out = {}
+    for name, (m, n, d) in {"70b_up_m2048": (2048, 28672, 8192), "70b_down_m2048": (2048, 8192, 28672),
+                            "7b_gate_m8192": (8192, 11008, 4096)}.items():
+        a = torch.randn(m, d, device="cuda:0", dtype=torch.float16)
+        w = torch.randn(n, d, device="cuda:0", dtype=torch.float16)
+        c = torch.empty(m, n, device="cuda:0", dtype=torch.float16)
+        total = time_launches(torch, lambda: torch.matmul(a, w.t(), out=c), steps, warmup)
+        ms = total / steps
+        out[name] = {"ms": ms, "TFLOPs": 2.0 * m * n * d / (ms * 1e-3) / 1e12}
+        del a, w, c
+    return out
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -217,7 +234,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
-    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune", "copy"}
+    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune", "dense",
+                                                                   "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -244,6 +262,10 @@ def main():
         parts["finetune_7b_layer"] = ft
         log(f"fine-tune step 7B layer m=8192: {ft['ms_per_step']:.2f} ms, {ft['TFLOPs']:.0f} TFLOP/s")
 
+    if "dense" in want:
+        dr = bench_dense_reference(torch, big_steps, big_warm)
+        parts["dense_f16_gemm_reference"] = dr
+        log("dense f16 GEMM reference: " + ", ".join(f"{k} {v['TFLOPs']:.0f} TFLOP/s" for k, v in dr.items()))
     if "copy" in want:
         cp = bench_copy(torch, big_steps, big_warm)
         parts["copy_1GiB"] = cp
