@@ -26,6 +26,8 @@
 // chunk's indices staged in LDS. Waves own disjoint (row, bin copy) pairs, so
 // the bins need no cross-wave atomics and the sums are deterministic; the
 // block stores each gradient entry exactly once (no global atomics).
+#include <stdlib.h>
+
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -351,6 +353,234 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
     }
 }
 
+// dX with 64 weight rows per step, for groups of >= 256 columns (a 256-column
+// tile then touches at most 2 groups). Same roles as k_gemm_dx, but each
+// step's dY tile has 128-byte token rows (8 lanes read one row's full cache
+// line), each thread dequantises one whole 32-column unit of one weight row
+// (lane slot = row of the step, so the table copies are unchanged), every wave
+// issues 32 MFMAs per step, and one register stage suffices (the loads of
+// tile k+2 have a whole step to arrive). LDS: tables [2][2][T][64] at 0, A
+// [2][256 tokens][64 rows] (128-byte rows, mm::swz128), Wt [2][64 rows][256
+// columns + 32 pad].
+constexpr int D6_BK = 64;
+constexpr uint32_t D6_TA = 256u * 64u * 2u;               // 32768
+constexpr uint32_t D6_TB = 64u * DX_RSB;                  // 36864
+constexpr uint32_t D6_A = 2u * 2u * 16u * 64u * 4u;       // 16384
+constexpr uint32_t D6_B = D6_A + 2u * D6_TA;              // 81920
+constexpr uint32_t D6_LDS = D6_B + 2u * D6_TB;            // 155648
+
+template <int B> struct Dx6Stage {
+  u32x4 y[4];
+  uint32_t w[B == 3 ? 3 : (B == 4 ? 4 : 2)];
+};
+
+template <int B, typename TX, typename TL>
+__global__ void __launch_bounds__(512, 1)
+k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
+            int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX) {
+  typedef mfma32<TL> MF;
+  constexpr int NG = 2;
+  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
+  extern __shared__ uint32_t smem[];
+  (void)smem;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
+  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;
+  const bool vec = (n % 8) == 0;
+  const int KS = (int)((n + D6_BK - 1) / D6_BK);
+
+  // ---- dequant role: weight row r = lane of the step, unit uu = wave of the
+  // column tile (32 columns, 4 * B bytes)
+  const int r = lane;
+  const int uu = wave;
+  const int64_t jc = n0 + 32 * uu;
+  const bool col_ok = jc < d;
+  const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
+  const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
+  const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
+  const int ng = (int)(ghi - glo + 1);
+  const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
+  const int64_t rbytes = d * B / 8;
+  const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B);
+  const uint32_t b_st = (uint32_t)r * DX_RSB + 64u * (uint32_t)uu;
+  const int part = wave;
+  // ---- dY role: chunk t % 8 of token rows t / 8 + 64 c
+  const TX* yrow[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t tok = m0 + 64 * c + (t >> 3);
+    yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+  }
+
+  auto load_stage = [&](Dx6Stage<B>& S, int j) {
+    const int64_t k0 = (int64_t)j * D6_BK;
+    const int64_t e0 = k0 + 8 * (t & 7);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (vec) {
+        const bool in = e0 < n;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
+        S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const uint16_t* pp = reinterpret_cast<const uint16_t*>(yrow[c]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t i = e0 + 2 * q;
+          S.y[c][q] = (i < n ? pp[i] : 0u) | ((i + 1 < n ? pp[i + 1] : 0u) << 16);
+        }
+      }
+    }
+    const int64_t row = k0 + r;
+    const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
+    if constexpr (B == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+    } else if constexpr (B == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      S.w[0] = v.x; S.w[1] = v.y;
+    } else {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
+      S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
+    }
+  };
+  auto stage = [&](const Dx6Stage<B>& S, int j) {
+    const uint32_t buf = (uint32_t)(j & 1);
+    const bool ok = (int64_t)j * D6_BK + r < n && col_ok;
+    const uint32_t gk = (buf * NG + gsel) * T;
+    uint32_t o0[8], o1[8];
+    if constexpr (B == 3) {
+      dx_dequant<B>(S.w, 0, gk, lane4, o0);
+      dx_dequant<B>(S.w, 1, gk, lane4, o1);
+    } else {
+      dx_dequant<B>(S.w, 0, gk, lane4, o0);
+      dx_dequant<B>(S.w + (B == 4 ? 2 : 1), 1, gk, lane4, o1);
+    }
+    const uint32_t bb = D6_B + buf * D6_TB + b_st;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st_q(bb, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
+    st_q(bb + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
+    st_q(bb + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
+    st_q(bb + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
+    const uint32_t ab = D6_A + buf * D6_TA;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), cvt_quad<TX, TL>(S.y[c]));
+  };
+  DxLutWord<B> LW[NG];
+  auto lut_load = [&](int j) {
+    const int64_t row = (int64_t)j * D6_BK + lane;
+    const bool ok = row < n;
+#pragma unroll
+    for (int gs = 0; gs < NG; ++gs)
+      if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
+  };
+  auto lut_store = [&](int j) {
+    const uint32_t buf = (uint32_t)(j & 1);
+#pragma unroll
+    for (int gs = 0; gs < NG; ++gs)
+      if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
+  };
+
+  // ---- matrix roles
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+  const uint32_t khalf = (uint32_t)(lane >> 5);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
+  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+    const uint32_t buf = (uint32_t)(k & 1);
+    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = ld_q(D6_A + buf * D6_TA + swz128(arow + 32u * i, ch));
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      fb[jj] = ld_frag_tr(D6_B + buf * D6_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
+                          (uint32_t)lane);
+  };
+  // four 16-row quarters: each quarter's fragment reads are interleaved with
+  // the previous quarter's MFMAs
+  auto mfma_step = [&](int k) {
+    u32x4 fa[4][4], fb[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  Dx6Stage<B> S;
+  // staging work of step k: tables of tile k+2 to LDS, tables of tile k+3
+  // loaded; tile k+1 from S into LDS, S refilled with tile k+2
+  auto stage_step = [&](int k) {
+    if (k + 2 < KS) lut_store(k + 2);
+    if (k + 3 < KS) lut_load(k + 3);
+    if (k + 1 < KS) {
+      stage(S, k + 1);
+      if (k + 2 < KS) load_stage(S, k + 2);
+    }
+  };
+  const bool mfma_first = wave < 4;
+
+  // ---- prologue
+  lut_load(0);
+  load_stage(S, 0);
+  lut_store(0);
+  if (KS > 1) {
+    lut_load(1);
+    lut_store(1);
+  }
+  if (KS > 2) lut_load(2);
+  __syncthreads();
+  stage(S, 0);
+  if (KS > 1) load_stage(S, 1);
+  __syncthreads();
+
+  for (int k = 0; k < KS; ++k) {
+    if (mfma_first) {
+      mfma_step(k);
+      stage_step(k);
+    } else {
+      stage_step(k);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(k);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
+      if (col >= d) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (tok < m) dX[tok * d + col] = acc[i][jj][e];
+      }
+    }
+}
+
 // ============================================================================
 // dLUT
 // ============================================================================
@@ -594,6 +824,15 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
 
 // ---- launchers ---------------------------------------------------------------
 
+// SKM_DX64=0 selects the 32-row-step dX kernel for every shape (tuning aid)
+bool dx64_disabled() {
+  static const bool v = [] {
+    const char* e = getenv("SKM_DX64");
+    return e && e[0] == '0';
+  }();
+  return v;
+}
+
 uint32_t ug_magic_of(const Problem& p) {
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   return ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
@@ -617,6 +856,17 @@ template <int B, typename TX, typename TL>
 hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
   // a 256-column tile touches at most 2 groups when groups are >= 256 columns
   // wide, at most 8 (one per 32-column unit) otherwise
+  if (p.group_cols() >= 256 && !dx64_disabled()) {
+    const auto kern = k_gemm_dx64<B, TX, TL>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)D6_LDS);
+    if (attr != hipSuccess) return attr;
+    const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
+    const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), D6_LDS, s, dY, idx, lut, p.m, p.n, p.d, p.gpr,
+                       ug_magic_of(p), mb, dX);
+    return hipGetLastError();
+  }
   if (p.group_cols() >= 256) return dx_launch<B, 2>(dY, idx, lut, p, dX, s);
   return dx_launch<B, 8>(dY, idx, lut, p, dX, s);
 }

@@ -31,7 +31,15 @@ __device__ __forceinline__ void st_q(uint32_t a, u32x4 v) { *(lds_u32x4*)(uintpt
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3u)) << 4);
 }
-// byte offset of 16-bit element e (0..31) of row r in the same layout
+// 128-byte rows of eight 16-byte chunks: chunk c of row r is stored at
+// c ^ ((r >> 1) & 7). Even rows start on bank 0 and odd rows on bank 32, and
+// the 8 rows of each parity among 16 consecutive rows get 8 different chunks,
+// so one 16-lane ds_read_b128 pass over 16 rows at one chunk index touches all
+// 64 banks once.
+__device__ __forceinline__ uint32_t swz128(uint32_t row, uint32_t chunk) {
+  return row * 128u + ((chunk ^ ((row >> 1) & 7u)) << 4);
+}
+// byte offset of 16-bit element e (0..31) of row r in the 64-byte layout
 __device__ __forceinline__ uint32_t swz_elem(uint32_t row, uint32_t e) {
   return swz(row, e >> 3) + ((e & 7u) << 1);
 }
