@@ -33,6 +33,8 @@
 // registers during K-step k and staged in K-step k+2 (two register stages);
 // one barrier per K-step; tables are staged one group ahead into the other
 // table buffer.
+#include <stdlib.h>
+
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -41,6 +43,7 @@ namespace skm {
 namespace {
 
 using mm::swz;
+using mm::swz128;
 using mm::gaddr;
 using mm::pack2;
 using mm::tab_entries;
@@ -336,12 +339,228 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
     }
 }
 
+// ---- 64-column K-steps ------------------------------------------------------
+// When every group holds an even number of 32-column units, a K-step of two
+// units never straddles a group. Then: 128-byte activation rows per step (8
+// lanes read one token row's full cache line), each thread dequantises one
+// whole unit (32 weights) of its row, every wave issues 32 MFMAs per step,
+// and one register stage suffices (tile k+2 is loaded during step k). LDS
+// (160 KB): tables as above at 0, A [2][256 tokens][64 cols] and Bt [2][256
+// rows][64 cols] in 128-byte rows (mm::swz128).
+constexpr uint32_t A64_TILE = G_BM * 64u * 2u;            // 32768
+constexpr uint32_t B64_TILE = G_BN * 64u * 2u;            // 32768
+constexpr uint32_t LDS64_A = 2u * 4u * 16u * 64u * 4u;    // 32768
+constexpr uint32_t LDS64_B = LDS64_A + 2u * A64_TILE;     // 98304
+constexpr uint32_t LDS64_TOTAL = LDS64_B + 2u * B64_TILE; // 163840
+
+template <int B> struct Stage64 {
+  uint32_t w[B];  // one whole unit
+  u32x4 x[4];
+};
+
+template <int B, typename TX, typename TL>
+__global__ void __launch_bounds__(G_THREADS, 1)
+k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
+             int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y) {
+  typedef mm::mfma32<TL> MF;
+  extern __shared__ uint32_t smem[];
+  (void)smem;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  const int64_t bm = blockIdx.x % mblocks;
+  const int64_t bn = blockIdx.x / mblocks;
+  const int64_t m0 = bm * G_BM, n0 = bn * G_BN;
+  const int KS = (int)(d / 64);
+  // group of tile j (both of its units are in it)
+  auto group_of = [&](int j) -> uint32_t { return mm::group_of((uint32_t)(2 * j), ug_magic); };
+
+  // ---- staging state: weight row r, unit hh of the step; activation chunk
+  // t % 8 of token rows t / 8 + 64 c
+  const int r = t & 255;
+  const int hh = t >> 8;                     // wave-uniform
+  const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r
+  const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
+  const uint8_t* rowp = idx_packed + grow * (d * B / 8) + hh * (4 * B);
+  const TX* xrow[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t tok = m0 + 64 * c + (t >> 3);
+    xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 7);
+  }
+  auto load_stage = [&](Stage64<B>& S, int j) {
+    const uint8_t* p = rowp + (int64_t)j * (8 * B);
+    if constexpr (B == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+      S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+    } else if constexpr (B == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      S.w[0] = v.x; S.w[1] = v.y;
+    } else {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+      S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S.x[c] = *reinterpret_cast<const u32x4*>(xrow[c] + (int64_t)j * 64);
+  };
+  Stage64<B> S;
+  LutRegs<B> L;
+  auto stage = [&](const Stage64<B>& St, int j) {
+    const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
+    uint32_t o0[8], o1[8];
+    Stage<B> h0, h1;  // the two half units in the layout dequant16 expects
+    if constexpr (B == 4) {
+      h0.w[0] = St.w[0]; h0.w[1] = St.w[1];
+      h1.w[0] = St.w[2]; h1.w[1] = St.w[3];
+    } else if constexpr (B == 2) {
+      h0.w[0] = St.w[0];
+      h1.w[0] = St.w[1];
+    } else {
+      h0.w[0] = h1.w[0] = St.w[0];
+      h0.w[1] = h1.w[1] = St.w[1];
+      h0.w[2] = h1.w[2] = St.w[2];
+    }
+    dequant16<B, 0>(h0, tb, lane4, o0);
+    dequant16<B, 1>(h1, tb, lane4, o1);
+    const uint32_t buf = (uint32_t)(j & 1);
+    const uint32_t bb = LDS64_B + buf * B64_TILE;
+    st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
+    st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
+    st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
+    st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
+    const uint32_t ab = LDS64_A + buf * A64_TILE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad<TX, TL>(St.x[c]));
+  };
+  // staging work of step k: tile k+1 into the other buffer, S refilled with
+  // tile k+2, tables kept one group ahead
+  auto stage_step = [&](int k) {
+    if (k + 1 >= KS) return;
+    stage(S, k + 1);
+    if (k + 2 < KS) {
+      load_stage(S, k + 2);
+      const uint32_t g2 = group_of(k + 2);
+      if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
+      if (k + 3 < KS && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+    }
+  };
+
+  // ---- matrix state
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
+  const uint32_t khalf = (uint32_t)(lane >> 5);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
+  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+    const uint32_t buf = (uint32_t)(k & 1);
+    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS64_A + buf * A64_TILE + swz128(arow + 32u * i, ch));
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS64_B + buf * B64_TILE + swz128(brow + 32u * jj, ch));
+  };
+  auto mfma_step = [&](int k) {
+    u32x4 fa[4][4], fb[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
+    // each quarter's fragment reads interleaved with the previous quarter's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const bool mfma_first = wave < 4;
+
+  // ---- prologue: tables of tile 0's group (tile 1's in registers if new),
+  // tile 0 staged, tile 1 in registers, then tile 1's table staged and tile
+  // 2's loaded as in a step
+  load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
+  load_stage(S, 0);
+  store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
+  const bool new1 = KS > 1 && group_of(1) != group_of(0);
+  if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
+  __syncthreads();
+  stage(S, 0);
+  if (KS > 1) load_stage(S, 1);
+  if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
+  if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
+  __syncthreads();
+
+  for (int k = 0; k < KS; ++k) {
+    if (mfma_first) {
+      mfma_step(k);
+      stage_step(k);
+    } else {
+      stage_step(k);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(k);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
+      if (col >= n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (tok < m) Y[tok * n + col] = from_f32<TX>(acc[i][jj][e]);
+      }
+    }
+}
+
+// SKM_FWD64=0 selects the 32-column-step kernel for every shape (tuning aid)
+bool fwd64_disabled() {
+  static const bool v = [] {
+    const char* e = getenv("SKM_FWD64");
+    return e && e[0] == '0';
+  }();
+  return v;
+}
+
 template <int B, typename TX, typename TL>
 hipError_t gemm_fwd_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
   const int64_t mb = (p.m + G_BM - 1) / G_BM;
   const int64_t nb = (p.n + G_BN - 1) / G_BN;
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
+  if (ug % 2 == 0 && !fwd64_disabled()) {
+    const auto kern = k_gemm_fwd64<B, TX, TL>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS64_TOTAL);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(G_THREADS), LDS64_TOTAL, s, X, idx, lut, p.m, p.n,
+                       p.d, p.gpr, magic, mb, Y);
+    return hipGetLastError();
+  }
   const auto kern = k_gemm_fwd<B, TX, TL>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_TOTAL);
