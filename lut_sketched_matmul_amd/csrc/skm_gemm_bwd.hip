@@ -599,8 +599,13 @@ constexpr uint32_t DL_RSB = 512u * 2u + 64u;                 // 1088
 constexpr uint32_t DL_TA = DL_BK * DL_RSA;                   // 10240
 constexpr uint32_t DL_TB = DL_BK * DL_RSB;                   // 34816
 constexpr uint32_t DL_STAGE = DL_TA + DL_TB;                 // 45056: one buffer of both tiles
-constexpr uint32_t DL_BINS = 2u * DL_STAGE;                  // 90112: [4 copies][128 rows][16] fp32
-constexpr uint32_t DL_LDS = DL_BINS + 4u * 128u * 16u * 4u;  // 122880
+// bins: [4 copies][128 rows][24] fp32 (16 entries used). The row stride of 24
+// floats puts rows i and i+4 - the two halves of a wave's scatter - on
+// opposite halves of the 64 banks.
+constexpr uint32_t DL_BRS = 24;                                   // floats per bin row
+constexpr uint32_t DL_BCOPY = 128u * DL_BRS * 4u;                 // 12288 bytes per copy
+constexpr uint32_t DL_BINS = 2u * DL_STAGE;                       // 90112
+constexpr uint32_t DL_LDS = DL_BINS + 4u * DL_BCOPY;              // 139264
 // during binning the chunk's packed indices, [128 rows][64 * B bytes], sit at 0
 constexpr uint32_t DL_IRS = 256u;                            // index row stride (b <= 4)
 
@@ -668,21 +673,34 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int64_t jend = jg0 + G;
   const int KS = (int)((m + DL_BK - 1) / DL_BK);
 
-  for (uint32_t q = (uint32_t)t; q < 4u * 128u * 16u; q += 512u) st_w(DL_BINS + q * 4u, 0u);
+  for (uint32_t q = (uint32_t)t; q < 4u * DL_BCOPY / 4u; q += 512u) st_w(DL_BINS + q * 4u, 0u);
 
   // ---- staging roles: dY chunk t (token t / 16, rows 8 (t % 16) ..), X
   // chunks t + 512 h (token c / 64, columns 8 (c % 64) ..)
   const int ytok = t >> 4;
   const int64_t yrow = i0 + 8 * (t & 15);
   const uint32_t y_st = (uint32_t)ytok * DL_RSA + (uint32_t)(t & 15) * 16u;
+  // Full steps (all 32 tokens, all rows of the block and all columns of the
+  // chunk in range, 16-byte aligned rows) load through pointers that advance by
+  // a step's worth of rows; only the others take the clamped, masked path.
+  const bool rows_full = VEC && i0 + DL_BM <= n;
+  const TX* yfast = dY + (int64_t)ytok * n + yrow;
   auto load_step = [&](DlStage& S, int k, int64_t j0) {
-    const int64_t tok = (int64_t)k * DL_BK + ytok;
+    const int64_t t0 = (int64_t)k * DL_BK;
+    if (rows_full && j0 + DL_BN <= jend && t0 + DL_BK <= m) {  // wave-uniform
+      S.y = *reinterpret_cast<const u32x4*>(yfast + t0 * n);
+      const TX* xb = X + t0 * d + j0 + 8 * (t & 63);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) S.x[h] = *reinterpret_cast<const u32x4*>(xb + (int64_t)(8 * h + (t >> 6)) * d);
+      return;
+    }
+    const int64_t tok = t0 + ytok;
     const bool ok = tok < m;
     S.y = dl_load8<VEC, TX>(dY + (ok ? tok : 0) * n, yrow, ok ? n : 0);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int c = t + 512 * h;
-      const int64_t xt = (int64_t)k * DL_BK + (c >> 6);
+      const int64_t xt = t0 + (c >> 6);
       const bool xok = xt < m;
       // d and the group width are multiples of 32: a chunk is wholly in or out
       S.x[h] = dl_load8<true, TX>(X + (xok ? xt : 0) * d, j0 + 8 * (c & 63), xok ? jend : 0);
@@ -786,7 +804,7 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
     // the K loop)
     uint32_t bl = lane;
     asm volatile("" : "+v"(bl));
-    const uint32_t binbase = DL_BINS + (uint32_t)wn * (128u * 16u * 4u);
+    const uint32_t binbase = DL_BINS + (uint32_t)wn * DL_BCOPY;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -801,7 +819,7 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
           const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (bl >> 5) + (e & 3);
           const float v = (j_ok && i0 + (int64_t)i < n) ? acc[a][b][e] : 0.0f;
           const uint32_t c = dl_field<B>(i * DL_IRS, j);
-          __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * 16u + c) * 4u), v, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * DL_BRS + c) * 4u), v, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
           if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
@@ -816,7 +834,7 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      s += *(const lds_f32*)(uintptr_t)(DL_BINS + (uint32_t)w * (128u * 16u * 4u) + (i * 16u + c) * 4u);
+      s += *(const lds_f32*)(uintptr_t)(DL_BINS + (uint32_t)w * DL_BCOPY + (i * DL_BRS + c) * 4u);
     float* dst = dLUT + ((i0 + i) * gpr + g) * K + c;
     *dst = accumulate ? *dst + s : s;
   }
