@@ -416,9 +416,26 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     yrow[c] = dY + (tok < m ? tok : m - 1) * n;
   }
 
+  const uint8_t* urow = ucol + (int64_t)r * rbytes;  // row r of step 0
   auto load_stage = [&](Dx6Stage<B>& S, int j) {
     const int64_t k0 = (int64_t)j * D6_BK;
     const int64_t e0 = k0 + 8 * (t & 7);
+    if (vec && k0 + D6_BK <= n) {  // wave-uniform: every row of the step exists
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S.y[c] = *reinterpret_cast<const u32x4*>(yrow[c] + e0);
+      const uint8_t* src = urow + k0 * rbytes;
+      if constexpr (B == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+      } else if constexpr (B == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+        S.w[0] = v.x; S.w[1] = v.y;
+      } else {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
+        S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (vec) {
