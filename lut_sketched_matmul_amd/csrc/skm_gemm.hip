@@ -347,6 +347,12 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
 // and one register stage suffices (tile k+2 is loaded during step k). LDS
 // (160 KB): tables as above at 0, A [2][256 tokens][64 cols] and Bt [2][256
 // rows][64 cols] in 128-byte rows (mm::swz128).
+// For b = 4 the tables stay in registers (mm::dequant8_b4: byte-plane
+// lookups with v_perm_b32, about 3 vector instructions per weight, no LDS
+// gathers), loaded once per group, and the two threads of a row are adjacent
+// lanes, so one index load instruction covers 32 rows x 32 contiguous bytes
+// (32 cache lines instead of 64). Both MFMA operands are stored in the K
+// order of dequant8_b4 within each 8-column chunk.
 constexpr uint32_t A64_TILE = G_BM * 64u * 2u;            // 32768
 constexpr uint32_t B64_TILE = G_BN * 64u * 2u;            // 32768
 constexpr uint32_t LDS64_A = 2u * 4u * 16u * 64u * 4u;    // 32768
@@ -378,12 +384,15 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
   auto group_of = [&](int j) -> uint32_t { return mm::group_of((uint32_t)(2 * j), ug_magic); };
 
   // ---- staging state: weight row r, unit hh of the step; activation chunk
-  // t % 8 of token rows t / 8 + 64 c
-  const int r = t & 255;
-  const int hh = t >> 8;                     // wave-uniform
-  const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r
+  // t % 8 of token rows t / 8 + 64 c. b = 4 pairs adjacent lanes on one row
+  // (32 contiguous index bytes per row and step); the LDS tables of b = 2, 3
+  // need hh wave-uniform (threads t and t + 256 fill one lane's table copy).
+  const int r = B == 4 ? (t >> 1) : (t & 255);
+  const int hh = B == 4 ? (t & 1) : (t >> 8);
+  const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r (b = 2, 3)
   const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
   const uint8_t* rowp = idx_packed + grow * (d * B / 8) + hh * (4 * B);
+  const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
   const TX* xrow[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -406,34 +415,57 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     for (int c = 0; c < 4; ++c) S.x[c] = *reinterpret_cast<const u32x4*>(xrow[c] + (int64_t)j * 64);
   };
   Stage64<B> S;
+  // b = 4: the table of the group being staged, as byte planes (P), and the
+  // next group's table as loaded (Ln); the group changes every UG/2 steps
+  mm::Planes16 P;
+  uint32_t Ln[8];
+  uint32_t cur_g = 0xFFFFFFFFu;
+  auto load_tab = [&](uint32_t g) {
+    const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
+    const u32x4 a = tp[0], b = tp[1];
+    Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
+    Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
+  };
   LutRegs<B> L;
   auto stage = [&](const Stage64<B>& St, int j) {
-    const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
-    uint32_t o0[8], o1[8];
-    Stage<B> h0, h1;  // the two half units in the layout dequant16 expects
-    if constexpr (B == 4) {
-      h0.w[0] = St.w[0]; h0.w[1] = St.w[1];
-      h1.w[0] = St.w[2]; h1.w[1] = St.w[3];
-    } else if constexpr (B == 2) {
-      h0.w[0] = St.w[0];
-      h1.w[0] = St.w[1];
-    } else {
-      h0.w[0] = h1.w[0] = St.w[0];
-      h0.w[1] = h1.w[1] = St.w[1];
-      h0.w[2] = h1.w[2] = St.w[2];
-    }
-    dequant16<B, 0>(h0, tb, lane4, o0);
-    dequant16<B, 1>(h1, tb, lane4, o1);
     const uint32_t buf = (uint32_t)(j & 1);
     const uint32_t bb = LDS64_B + buf * B64_TILE;
-    st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
-    st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
-    st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
-    st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
     const uint32_t ab = LDS64_A + buf * A64_TILE;
+    if constexpr (B == 4) {
+      // tables in registers; both operands in the K order of dequant8_b4
+      const uint32_t g = group_of(j);
+      if (g != cur_g) {
+        mm::planes16(Ln, P);
+        cur_g = g;
+        load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
+      }
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad<TX, TL>(St.x[c]));
+      for (int q = 0; q < 4; ++q) st_q(bb + swz128((uint32_t)r, 4u * hh + q), mm::dequant8_b4(St.w[q], P));
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad_perm<TX, TL>(St.x[c]));
+    } else {
+      const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
+      uint32_t o0[8], o1[8];
+      Stage<B> h0, h1;  // the two half units in the layout dequant16 expects
+      if constexpr (B == 2) {
+        h0.w[0] = St.w[0];
+        h1.w[0] = St.w[1];
+      } else {
+        h0.w[0] = h1.w[0] = St.w[0];
+        h0.w[1] = h1.w[1] = St.w[1];
+        h0.w[2] = h1.w[2] = St.w[2];
+      }
+      dequant16<B, 0>(h0, tb, lane4, o0);
+      dequant16<B, 1>(h1, tb, lane4, o1);
+      st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
+      st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
+      st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
+      st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad<TX, TL>(St.x[c]));
+    }
   };
   // staging work of step k: tile k+1 into the other buffer, S refilled with
   // tile k+2, tables kept one group ahead
@@ -442,9 +474,11 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     stage(S, k + 1);
     if (k + 2 < KS) {
       load_stage(S, k + 2);
-      const uint32_t g2 = group_of(k + 2);
-      if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
-      if (k + 3 < KS && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+      if constexpr (B != 4) {
+        const uint32_t g2 = group_of(k + 2);
+        if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
+        if (k + 3 < KS && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+      }
     }
   };
 
@@ -499,16 +533,23 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
   // ---- prologue: tables of tile 0's group (tile 1's in registers if new),
   // tile 0 staged, tile 1 in registers, then tile 1's table staged and tile
   // 2's loaded as in a step
-  load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
-  load_stage(S, 0);
-  store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
-  const bool new1 = KS > 1 && group_of(1) != group_of(0);
-  if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
-  __syncthreads();
-  stage(S, 0);
-  if (KS > 1) load_stage(S, 1);
-  if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
-  if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
+  if constexpr (B == 4) {
+    load_tab(group_of(0));
+    load_stage(S, 0);
+    stage(S, 0);
+    if (KS > 1) load_stage(S, 1);
+  } else {
+    load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
+    load_stage(S, 0);
+    store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
+    const bool new1 = KS > 1 && group_of(1) != group_of(0);
+    if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
+    __syncthreads();
+    stage(S, 0);
+    if (KS > 1) load_stage(S, 1);
+    if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
+    if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
+  }
   __syncthreads();
 
   for (int k = 0; k < KS; ++k) {

@@ -112,6 +112,88 @@ __device__ __forceinline__ u32x4 cvt_quad(u32x4 v) {
   }
 }
 
+// ---- b = 4 table lookup in registers ------------------------------------
+// A 16-entry table of 16-bit values held as byte planes: lo[q] / hi[q] hold
+// the low / high bytes of entries 4q..4q+3. One v_perm_b32 picks four bytes
+// out of eight by 3-bit selectors, so a plane pair (entries 0-7 or 8-15)
+// answers four lookups at once and v_bfi_b32 chooses between the two halves
+// by bit 3 of each index.
+struct Planes16 { uint32_t lo[4], hi[4]; };
+
+// L[i] holds entries 2i (low half) and 2i+1 (high half)
+__device__ __forceinline__ void planes16(const uint32_t* L, Planes16& P) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    P.lo[q] = __builtin_amdgcn_perm(L[2 * q + 1], L[2 * q], 0x06040200u);
+    P.hi[q] = __builtin_amdgcn_perm(L[2 * q + 1], L[2 * q], 0x07050301u);
+  }
+}
+
+// bytes k of the result: plane byte selected by the low 3 bits of byte k of
+// `sel`, from entries 8..15 where byte k of `mask` is 0xFF, else 0..7
+__device__ __forceinline__ uint32_t plane_lookup(const uint32_t* pl, uint32_t sel, uint32_t mask) {
+  const uint32_t a = __builtin_amdgcn_perm(pl[1], pl[0], sel);
+  const uint32_t b = __builtin_amdgcn_perm(pl[3], pl[2], sel);
+  return (mask & b) | (~mask & a);
+}
+
+// The 8 weights of one index dword w (4-bit fields f0..f7 from the low end)
+// as four packed 16-bit pairs in the K order (f0,f2), (f4,f6), (f1,f3),
+// (f5,f7) (see cvt_quad_perm for the matching activation order). The masks
+// come from v_perm_b32's sign-replicating selectors 8..11 (top bits of bytes
+// 1 and 3 of either source), with bit 3 of each field shifted there.
+__device__ __forceinline__ u32x4 dequant8_b4(uint32_t w, const Planes16& P) {
+  const uint32_t se = w & 0x07070707u;
+  const uint32_t so = (w >> 4) & 0x07070707u;
+  const uint32_t me = __builtin_amdgcn_perm(w << 4, w << 12, 0x0B090A08u);
+  const uint32_t mo = __builtin_amdgcn_perm(w, w << 8, 0x0B090A08u);
+  const uint32_t le = plane_lookup(P.lo, se, me), he = plane_lookup(P.hi, se, me);
+  const uint32_t lo = plane_lookup(P.lo, so, mo), ho = plane_lookup(P.hi, so, mo);
+  return u32x4{__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(he, le, 0x07030602u),
+               __builtin_amdgcn_perm(ho, lo, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x07030602u)};
+}
+
+// Two values (fp32) rounded to the compute dtype TC and packed
+template <typename TC>
+__device__ __forceinline__ uint32_t pack_tc(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (__is_same(TC, half_t)) {
+    f16x2_t r;
+    r.x = (half_t)lo;
+    r.y = (half_t)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    bf16x2_t r;
+    r.x = (bf16_t)lo;
+    r.y = (bf16_t)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+}
+
+// 8 activations x0..x7 (16-bit storage TS, two per word) in the compute
+// dtype TC and the K order (x0,x2), (x4,x6), (x1,x3), (x5,x7)
+template <typename TS, typename TC>
+__device__ __forceinline__ u32x4 cvt_quad_perm(u32x4 v) {
+  if constexpr (__is_same(TS, TC)) {
+    return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                 __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+  } else {
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (__is_same(TS, bf16_t)) {
+        f[2 * q] = __builtin_bit_cast(float, v[q] << 16);
+        f[2 * q + 1] = __builtin_bit_cast(float, v[q] & 0xFFFF0000u);
+      } else {
+        f[2 * q] = (float)__builtin_bit_cast(half_t, (uint16_t)(v[q] & 0xFFFFu));
+        f[2 * q + 1] = (float)__builtin_bit_cast(half_t, (uint16_t)(v[q] >> 16));
+      }
+    }
+    return u32x4{pack_tc<TC>(f[0], f[2]), pack_tc<TC>(f[4], f[6]), pack_tc<TC>(f[1], f[3]), pack_tc<TC>(f[5], f[7])};
+  }
+}
+
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
 // lanes, lane l receives 16-bit element l % 4 of the 8-byte pieces addressed
 // by lanes 4j + l/4 of its group, j = 0..3. If lane s of a group points at row
