@@ -372,6 +372,7 @@ constexpr uint32_t D6_LDS = D6_B + 2u * D6_TB;            // 155648
 template <int B> struct Dx6Stage {
   u32x4 y[4];
   uint32_t w[B == 3 ? 3 : (B == 4 ? 4 : 2)];
+  uint32_t lut[B == 4 ? 8 : 1];  // b = 4: the row's table for the thread's group
 };
 
 template <int B, typename TX, typename TL>
@@ -394,9 +395,12 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   const int KS = (int)((n + D6_BK - 1) / D6_BK);
 
   // ---- dequant role: weight row r = lane of the step, unit uu = wave of the
-  // column tile (32 columns, 4 * B bytes)
-  const int r = lane;
-  const int uu = wave;
+  // column tile (32 columns, 4 * B bytes). b = 4 keeps the tables in
+  // registers instead (mm::dequant8_b4); then 4 adjacent lanes take 4
+  // adjacent units of one row (64 contiguous index bytes per row), 16 rows
+  // per wave.
+  const int r = B == 4 ? 16 * (wave & 3) + (lane >> 2) : lane;
+  const int uu = B == 4 ? 4 * (wave >> 2) + (lane & 3) : wave;
   const int64_t jc = n0 + 32 * uu;
   const bool col_ok = jc < d;
   const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
@@ -417,6 +421,17 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   }
 
   const uint8_t* urow = ucol + (int64_t)r * rbytes;  // row r of step 0
+  // b = 4: the table of (row, this thread's group), 16 entries
+  const uint32_t gabs = glo + gsel;
+  auto load_tab = [&](Dx6Stage<B>& S, int64_t row) {
+    if constexpr (B == 4) {
+      const u32x4* tp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lut) +
+                                                        (row * gpr + gabs) * 16);
+      const u32x4 a = tp[0], b = tp[1];
+      S.lut[0] = a.x; S.lut[1] = a.y; S.lut[2] = a.z; S.lut[3] = a.w;
+      S.lut[4] = b.x; S.lut[5] = b.y; S.lut[6] = b.z; S.lut[7] = b.w;
+    }
+  };
   auto load_stage = [&](Dx6Stage<B>& S, int j) {
     const int64_t k0 = (int64_t)j * D6_BK;
     const int64_t e0 = k0 + 8 * (t & 7);
@@ -427,6 +442,7 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
       if constexpr (B == 4) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src);
         S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+        load_tab(S, k0 + r);
       } else if constexpr (B == 2) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(src);
         S.w[0] = v.x; S.w[1] = v.y;
@@ -456,6 +472,7 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     if constexpr (B == 4) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(src);
       S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+      load_tab(S, row < n ? row : n - 1);
     } else if constexpr (B == 2) {
       const u32x2 v = *reinterpret_cast<const u32x2*>(src);
       S.w[0] = v.x; S.w[1] = v.y;
@@ -467,6 +484,16 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   auto stage = [&](const Dx6Stage<B>& S, int j) {
     const uint32_t buf = (uint32_t)(j & 1);
     const bool ok = (int64_t)j * D6_BK + r < n && col_ok;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (B == 4) {
+      // columns of each 8-column chunk in the order of mm::dequant8_b4 (undone
+      // when dX is stored)
+      mm::Planes16 P;
+      mm::planes16(S.lut, P);
+      const uint32_t bb = D6_B + buf * D6_TB + b_st;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st_q(bb + 16u * q, ok ? mm::dequant8_b4(S.w[q], P) : z);
+    } else {
     const uint32_t gk = (buf * NG + gsel) * T;
     uint32_t o0[8], o1[8];
     if constexpr (B == 3) {
@@ -477,11 +504,11 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
       dx_dequant<B>(S.w + (B == 4 ? 2 : 1), 1, gk, lane4, o1);
     }
     const uint32_t bb = D6_B + buf * D6_TB + b_st;
-    const u32x4 z = {0u, 0u, 0u, 0u};
     st_q(bb, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
     st_q(bb + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
     st_q(bb + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
     st_q(bb + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
+    }
     const uint32_t ab = D6_A + buf * D6_TA;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -549,8 +576,10 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   // staging work of step k: tables of tile k+2 to LDS, tables of tile k+3
   // loaded; tile k+1 from S into LDS, S refilled with tile k+2
   auto stage_step = [&](int k) {
-    if (k + 2 < KS) lut_store(k + 2);
-    if (k + 3 < KS) lut_load(k + 3);
+    if constexpr (B != 4) {
+      if (k + 2 < KS) lut_store(k + 2);
+      if (k + 3 < KS) lut_load(k + 3);
+    }
     if (k + 1 < KS) {
       stage(S, k + 1);
       if (k + 2 < KS) load_stage(S, k + 2);
@@ -559,15 +588,17 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   const bool mfma_first = wave < 4;
 
   // ---- prologue
-  lut_load(0);
+  if constexpr (B != 4) lut_load(0);
   load_stage(S, 0);
-  lut_store(0);
-  if (KS > 1) {
-    lut_load(1);
-    lut_store(1);
+  if constexpr (B != 4) {
+    lut_store(0);
+    if (KS > 1) {
+      lut_load(1);
+      lut_store(1);
+    }
+    if (KS > 2) lut_load(2);
+    __syncthreads();
   }
-  if (KS > 2) lut_load(2);
-  __syncthreads();
   stage(S, 0);
   if (KS > 1) load_stage(S, 1);
   __syncthreads();
@@ -588,7 +619,10 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
+      // b = 4: tile column p holds column (p & ~7) + (2 (p & 3) | (p & 7) >> 2)
+      const int p = 64 * wn + 32 * jj + (lane & 31);
+      const int pc = B == 4 ? (p & ~7) | ((p & 3) << 1) | ((p >> 2) & 1) : p;
+      const int64_t col = n0 + pc;
       if (col >= d) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
