@@ -195,12 +195,23 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
   const int U = (int)(d / 32);
   auto group_of = [&](int k) -> uint32_t { return mm::group_of((uint32_t)k, ug_magic); };
 
-  // ---- staging state
-  const int r = t & 255;
-  const int hh = t >> 8;                     // wave-uniform
-  const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r
+  // ---- staging state (b = 4: the two threads of a row are adjacent lanes and
+  // the tables stay in registers, as in k_gemm_fwd64)
+  const int r = B == 4 ? (t >> 1) : (t & 255);
+  const int hh = B == 4 ? (t & 1) : (t >> 8);  // wave-uniform for b = 2, 3
+  const uint32_t rq = (uint32_t)(wave & 3);    // row quarter of r (b = 2, 3)
   const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
   const uint8_t* rowp = idx_packed + grow * (d * B / 8);
+  const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
+  mm::Planes16 P;
+  uint32_t Ln[8];
+  uint32_t cur_g = 0xFFFFFFFFu;
+  auto load_tab = [&](uint32_t g) {
+    const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
+    const u32x4 a = tp[0], b = tp[1];
+    Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
+    Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
+  };
   const TX* xrow[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -215,17 +226,30 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
 
   // stage tile j (raw operands in S) into LDS buffer j & 1
   auto stage = [&](const Stage<B>& S, int j) {
-    uint32_t o[8];
-    const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
-    if (hh) dequant16<B, 1>(S, tb, lane4, o);
-    else dequant16<B, 0>(S, tb, lane4, o);
     const uint32_t buf = (uint32_t)(j & 1);
     const uint32_t bb = LDS_B + buf * B_TILE;
-    st_q(bb + b_st0, u32x4{o[0], o[1], o[2], o[3]});
-    st_q(bb + b_st1, u32x4{o[4], o[5], o[6], o[7]});
     const uint32_t ab = LDS_A + buf * A_TILE;
-    st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
-    st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
+    if constexpr (B == 4) {
+      const uint32_t g = group_of(j);
+      if (g != cur_g) {
+        mm::planes16(Ln, P);
+        cur_g = g;
+        load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
+      }
+      st_q(bb + b_st0, mm::dequant8_b4(S.w[0], P));
+      st_q(bb + b_st1, mm::dequant8_b4(S.w[1], P));
+      st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(S.x[0]));
+      st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(S.x[1]));
+    } else {
+      uint32_t o[8];
+      const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
+      if (hh) dequant16<B, 1>(S, tb, lane4, o);
+      else dequant16<B, 0>(S, tb, lane4, o);
+      st_q(bb + b_st0, u32x4{o[0], o[1], o[2], o[3]});
+      st_q(bb + b_st1, u32x4{o[4], o[5], o[6], o[7]});
+      st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
+      st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
+    }
   };
   // staging work of K-step k: tile k+1 from Sn into LDS, Sn refilled with
   // tile k+3, tables kept one group ahead (the table of tile k+2's group is
@@ -234,7 +258,7 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
     if (k + 1 >= U) return;
     stage(Sn, k + 1);
     if (k + 3 < U) load_stage<B, TX>(Sn, rowp, xrow, (uint32_t)(k + 3), hh);
-    if (k + 2 < U) {
+    if (B != 4 && k + 2 < U) {
       const uint32_t g2 = group_of(k + 2);
       if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
       if (k + 3 < U && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
@@ -301,17 +325,25 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
   // ---- prologue: tables of group 0 (group 1's in registers), tile 0 staged,
   // tiles 1 and 2 in registers, then the table of group 1 and of tile 2's
   // group staged / loaded as in a K-step
-  load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
-  load_stage<B, TX>(S0, rowp, xrow, 0, hh);
-  if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
-  store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
-  const bool new1 = U > 1 && group_of(1) != group_of(0);
-  if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
-  __syncthreads();
-  stage(S0, 0);
-  if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
-  if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
-  if (U > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
+  if constexpr (B == 4) {
+    load_tab(group_of(0));
+    load_stage<B, TX>(S0, rowp, xrow, 0, hh);
+    if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
+    stage(S0, 0);
+    if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
+  } else {
+    load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
+    load_stage<B, TX>(S0, rowp, xrow, 0, hh);
+    if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
+    store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
+    const bool new1 = U > 1 && group_of(1) != group_of(0);
+    if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
+    __syncthreads();
+    stage(S0, 0);
+    if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
+    if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
+    if (U > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
+  }
   __syncthreads();
 
   // ---- main loop: two K-steps per trip so each register stage keeps its

@@ -139,12 +139,13 @@ def test_large_n_decode_selection_bit_exact(dt):
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 200, 4096, 300), (4, 1, 64, 512, 17), (2, 8, 130, 11008, 40), (3, 4, 257, 1536, 513),
     (2, 2, 96, 1024, 256), (3, 8, 128, 11008, 33), (4, 4, 300, 8192, 260), (4, 1, 70, 64, 40),
-    (3, 1, 33, 128, 19), (2, 2, 300, 128, 300),
+    (3, 1, 33, 128, 19), (2, 2, 300, 128, 300), (4, 8, 150, 11008, 40), (4, 1, 96, 96, 33),
 ])
 def test_fwd16_gemm(x_dtype, lut_dtype, b, gpr, n, d, m):
     """m > 16 runs the tiled matrix-core GEMM: ragged token and row tiles; one-
     and two-step K loops; 32- and 64-column K-steps (odd / even units per
-    group)."""
+    group), for every bit width (b = 4 with 43 and 3 units per group takes the
+    32-column steps)."""
     idx, lut, X, _ = make_case(f"gemm16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
                                x_dtype, lut_dtype)
     got, want = _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype)
@@ -238,7 +239,7 @@ def _bwd16(idx, lut, X, dY, b, gpr, d, io, lut_dtype, accumulate=False, dlut_ini
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 200, 4096, 300), (2, 2, 130, 1024, 40), (3, 8, 96, 11008, 33), (4, 1, 257, 512, 17),
     (3, 4, 300, 1536, 260), (2, 32, 64, 1024, 64), (4, 4, 33, 8192, 5), (4, 1, 64, 256, 100),
-    (2, 2, 129, 512, 70),
+    (2, 2, 129, 512, 70), (4, 8, 70, 11008, 40),
 ])
 def test_bwd16(io, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, dY = make_case(f"bwd16/{io}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, lut_dtype)
