@@ -731,14 +731,16 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int ytok = t >> 4;
   const int64_t yrow = i0 + 8 * (t & 15);
   const uint32_t y_st = (uint32_t)ytok * DL_RSA + (uint32_t)(t & 15) * 16u;
-  // Full steps (all 32 tokens, all rows of the block and all columns of the
-  // chunk in range, 16-byte aligned rows) load through pointers that advance by
-  // a step's worth of rows; only the others take the clamped, masked path.
+  // Full steps (all 32 tokens and all rows of the block in range, the chunk's
+  // 512 columns inside the row, 16-byte aligned rows) load through pointers
+  // that advance by a step's worth of rows; only the others take the clamped,
+  // masked path.
   const bool rows_full = VEC && i0 + DL_BM <= n;
   const TX* yfast = dY + (int64_t)ytok * n + yrow;
   auto load_step = [&](DlStage& S, int k, int64_t j0) {
     const int64_t t0 = (int64_t)k * DL_BK;
-    if (rows_full && j0 + DL_BN <= jend && t0 + DL_BK <= m) {  // wave-uniform
+    // (columns past the group but inside the row are read too: binning leaves them out)
+    if (rows_full && j0 + DL_BN <= d && t0 + DL_BK <= m) {  // wave-uniform
       S.y = *reinterpret_cast<const u32x4*>(yfast + t0 * n);
       const TX* xb = X + t0 * d + j0 + 8 * (t & 63);
 #pragma unroll

@@ -239,7 +239,7 @@ def _bwd16(idx, lut, X, dY, b, gpr, d, io, lut_dtype, accumulate=False, dlut_ini
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 200, 4096, 300), (2, 2, 130, 1024, 40), (3, 8, 96, 11008, 33), (4, 1, 257, 512, 17),
     (3, 4, 300, 1536, 260), (2, 32, 64, 1024, 64), (4, 4, 33, 8192, 5), (4, 1, 64, 256, 100),
-    (2, 2, 129, 512, 70), (4, 8, 70, 11008, 40),
+    (2, 2, 129, 512, 70), (4, 8, 70, 11008, 40), (4, 8, 256, 11008, 64),
 ])
 def test_bwd16(io, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, dY = make_case(f"bwd16/{io}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, lut_dtype)
