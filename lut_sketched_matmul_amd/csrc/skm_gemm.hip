@@ -22,17 +22,21 @@
 //   Bt [2][256 rows][32 cols]   dequantised weights                  at 64 KB
 // Rows of A and Bt are 64 bytes with XOR-swizzled 16-byte chunks (mm::swz).
 //
-// Staging roles: thread t owns weight row r = t % 256 with column half
-// hh = t / 256 (16 weights per K-step), and 16-byte chunk t % 4 of token rows
-// t / 4 and t / 4 + 128 (16 activations; the 4 lanes that share a row read
-// its 64 bytes together). Its table copy sits at lane slot t % 64 of row
+// Staging roles (b = 2, 3): thread t owns weight row r = t % 256 with column
+// half hh = t / 256 (16 weights per K-step), and 16-byte chunk t % 4 of token
+// rows t / 4 and t / 4 + 128 (16 activations; the 4 lanes that share a row
+// read its 64 bytes together). Its table copy sits at lane slot t % 64 of row
 // quarter (t / 64) % 4, entry-major, so the gathers of one wave (64 distinct
 // rows) are conflict-free; the gather address is one v_perm_b32.
+// b = 4 looks its weights up in registers instead (mm::dequant8_b4, tables
+// loaded once per group) and pairs the two threads of a row on adjacent lanes
+// (r = t / 2, hh = t % 2); both operands are then staged in that lookup's K
+// order within each 8-column chunk.
 //
 // Pipeline: the raw index words and activations of tile k+3 are loaded into
 // registers during K-step k and staged in K-step k+2 (two register stages);
-// one barrier per K-step; tables are staged one group ahead into the other
-// table buffer.
+// one barrier per K-step; LDS tables (b = 2, 3) are staged one group ahead
+// into the other table buffer.
 #include <stdlib.h>
 
 #include "skm_gemm_common.h"

@@ -16,7 +16,9 @@
 // (each MFMA B fragment is 8 consecutive rows of one column). Each step brings
 // 32 new rows, so the tables (the groups of the column tile, private copy per
 // lane slot) are staged every step: loaded three steps ahead, stored two
-// steps ahead.
+// steps ahead. k_gemm_dx64 takes 64 rows per step for groups of >= 256
+// columns; with b = 4 it looks its weights up in registers (mm::dequant8_b4)
+// from a table loaded with each step's index words.
 //
 // k_gemm_dlut: one block owns 128 rows x one group. For each chunk of up to
 // 512 columns of the group it accumulates the dW = dY^T X tile over all

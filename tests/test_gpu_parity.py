@@ -98,7 +98,7 @@ def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
 @pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 4096, 4096, 1), (4, 1, 100, 160, 3), (2, 2, 257, 1024, 16), (3, 4, 77, 1536, 5),
-    (2, 8, 300, 11008, 4), (3, 8, 48, 11008, 16), (4, 4, 64, 8192, 2),
+    (2, 8, 300, 11008, 4), (3, 8, 48, 11008, 16), (4, 4, 64, 8192, 2), (4, 32, 70, 2048, 3),
 ])
 def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
