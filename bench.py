@@ -8,8 +8,9 @@ HBM peak. Every timed launch reads a different copy of the indices and tables
 (>= 1 GiB in rotation) so the 256 MB last-level cache cannot serve repeats.
 
 The same JSON line carries the other measured parts of the hot path (16-token
-forward, 70B-shaped prefill GEMM, 7B decoder-layer fine-tuning step) and the
-CPU oracle timed on this host as a baseline.
+forward, the 7B MLP at 2 and 3 bits, 70B-shaped decode and prefill GEMM, the
+7B decoder-layer fine-tuning step) and the CPU oracle timed on this host as a
+baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -41,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,prefill,finetune,dense,copy (default all; decode always runs)")
+                    help="comma list of decode,fwd16,lowbit,decode70b,prefill,finetune,dense,copy "
+                         "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -234,8 +236,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
-    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "prefill", "finetune", "dense",
-                                                                   "copy"}
+    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "decode70b",
+                                                                   "prefill", "finetune", "dense", "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -248,6 +250,26 @@ def main():
         f16 = bench_fwd(torch, skm, w, shape, 4, 16, args.steps, args.warmup)
         parts["fwd_m16"] = f16
         log(f"forward 4096x4096 b=4 m=16: {f16['ms_per_launch'] * 1e3:.2f} us/launch, {f16['GBps']:.0f} GB/s")
+    if "lowbit" in want:
+        # the 7B MLP at 2- and 3-bit indices, 1 / 4 / 16 tokens (decode kernel)
+        wlb = wl.LLAMA2_7B_MLP_LOWBIT
+        lb = {}
+        for s_, b_, m_ in wl.runs(wlb):
+            r = bench_fwd(torch, skm, wlb, s_, b_, m_, args.steps, args.warmup)
+            r["frac_hbm_peak"] = r["GBps"] / HBM_PEAK_GBS
+            lb[f"{s_.name}_b{b_}_m{m_}"] = r
+        parts["decode_lowbit_7b_mlp"] = lb
+        log("7B MLP b=2/3 decode: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in lb.items()))
+    if "decode70b" in want:
+        w7 = wl.LLAMA3_70B_MLP
+        d7 = {}
+        for s_ in w7.shapes:
+            r = bench_fwd(torch, skm, w7, s_, 4, 1, max(20, args.steps // 4), max(2, args.warmup // 4))
+            r["frac_hbm_peak"] = r["GBps"] / HBM_PEAK_GBS
+            d7[s_.name] = r
+        parts["decode_70b_mlp_m1"] = d7
+        log("70B MLP decode m=1: " + ", ".join(f"{k} {v['ms_per_launch'] * 1e3:.1f} us {v['GBps']:.0f} GB/s"
+                                                for k, v in d7.items()))
     big_steps = max(2, min(args.steps, 10))
     big_warm = max(1, min(args.warmup, 2))
     if "prefill" in want:
