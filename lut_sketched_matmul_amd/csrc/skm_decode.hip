@@ -76,6 +76,8 @@ template <> struct mfma16<bf16_t> {
   }
 };
 
+template <bool V> struct btag { static constexpr bool value = V; };
+
 // table entries per group for bit width B (b = 2 stores pairs)
 template <int B> struct tab_entries { static constexpr int value = (B == 2) ? 16 : (1 << B); };
 
@@ -261,15 +263,25 @@ __device__ __forceinline__ void load_batch(SlotRegs<B, TX, PF>& R, int64_t s0, i
   }
 }
 
+// s_waitcnt that bounds only the vector-memory counter (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <typename T>
 __device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
   return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
 }
 
 // XL: the activations (m x d, converted to the compute dtype) are staged once
-// per block in LDS after the tables, and A fragments are read from there.
-// With XL the index words of the next batch of slots are loaded while the
-// current batch is being computed (two small register sets).
+// per block in LDS after the tables, and A fragments are read from there;
+// otherwise each slot's A fragments are loaded from global memory with its
+// index words. The next batch of slots is loaded while the current one is
+// being computed (two register sets), except for activations in registers at
+// 4 slots per batch.
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
@@ -282,7 +294,9 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   typedef mfma16<TL> MF;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar, so that the slot loop's branches are scalar
+  // branches and every path through it is a real path
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = (int64_t)blockIdx.x * DEC_ROWS;
   const int j = lane & 15;           // weight row within the block (B operand column)
   const int q = lane >> 4;           // contraction quarter
@@ -326,18 +340,27 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
       }
     }
   }
+  // Every table and activation load has been consumed by now on the paths
+  // that store it; the ones past the row's tables (or past m*d) were issued
+  // but not consumed. Waiting for all but the first batch's index loads here
+  // (at most 3 loads per slot) settles them on every path, so the compiler's
+  // load counting below starts from the first batch alone.
+  wait_vmcnt<PF * ((B == 3 ? 3 : 1) + (XL ? 0 : 4))>();
   __syncthreads();
   // the gathers address the tables with absolute LDS addresses (see gaddr)
   if ((uint32_t)(uintptr_t)smem != 0u) return;
   const uint32_t xl_row = xl_base + (uint32_t)tokc * (uint32_t)d * 2u;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const SlotRegs<B, TX, PF>& Rc, int64_t sb) {
+  // compute(R, first slot, tail): a batch can be partial only when it is a
+  // wave's last one (tail = true); full batches carry no early exits, so every
+  // path through them consumes all of their loads.
+  auto compute = [&](const SlotRegs<B, TX, PF>& Rc, int64_t sb, auto tail) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      if (sb + (int64_t)p * NW >= S) break;  // wave-uniform
+      if (decltype(tail)::value && sb + (int64_t)p * NW >= S) break;  // wave-uniform
       const uint32_t gk = Rc.gk[p];
-      const uint32_t gk4 = gk * 0x01010101u;
+      const uint32_t gk4 = __builtin_amdgcn_perm(0u, gk, 0u);  // gk < 256 in all four bytes
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         u32x4 wb = dequant_step<B>(Rc.w[p], h, gk4, gk, lane4);
@@ -357,25 +380,41 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     }
   };
   constexpr int64_t STEP = (int64_t)NW * PF;
-  if constexpr (XL) {
-    while (true) {
-      const int64_t s1 = s0 + STEP;
-      if (s1 < S) load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s1, S, U, ug_magic, q, rowp, xrow);
-      compute(R0, s0);
-      if (s1 >= S) break;
-      const int64_t s2 = s1 + STEP;
-      if (s2 < S) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s2, S, U, ug_magic, q, rowp, xrow);
-      compute(R1, s1);
-      if (s2 >= S) break;
-      s0 = s2;
+  // batches of PF slots this wave computes (at least one, which may be empty
+  // when the row has fewer slots than the block has waves)
+  const int64_t nb_raw = (S - s0 + STEP - 1) / STEP;
+  const int64_t nb = nb_raw > 1 ? nb_raw : 1;
+  if constexpr (XL || PF <= 2) {
+    // Two register sets: the next batch is loaded while the current one is
+    // computed. The loop has one exit and issues its loads unconditionally,
+    // so the compiler knows exactly how many loads are younger than the batch
+    // it waits for (a load under a condition, or a batch with early exits,
+    // makes it wait as if fewer were in flight: every batch would then stall
+    // on the next one's first load); the last one or two batches run after it.
+    int64_t b = 0;
+    for (; b + 2 < nb; b += 2) {
+      load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow);
+      compute(R0, s0, btag<false>{});
+      load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0 + 2 * STEP, S, U, ug_magic, q, rowp, xrow);
+      compute(R1, s0 + STEP, btag<false>{});
+      s0 += 2 * STEP;
+    }
+    if (nb - b == 2) {
+      load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow);
+      compute(R0, s0, btag<false>{});
+      compute(R1, s0 + STEP, btag<true>{});
+    } else {
+      compute(R0, s0, btag<true>{});
     }
   } else {
-    while (true) {
-      compute(R0, s0);
+    // activations in registers for 4 slots per batch: one register set (two
+    // would halve the waves a SIMD holds)
+    for (int64_t b = 0; b + 1 < nb; ++b) {
+      compute(R0, s0, btag<false>{});
       s0 += STEP;
-      if (s0 >= S) break;
       load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
     }
+    compute(R0, s0, btag<true>{});
   }
 
   // ---- sum the NW partial tiles in wave order, then store Y[token][row]

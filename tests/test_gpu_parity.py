@@ -99,6 +99,9 @@ def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 4096, 4096, 1), (4, 1, 100, 160, 3), (2, 2, 257, 1024, 16), (3, 4, 77, 1536, 5),
     (2, 8, 300, 11008, 4), (3, 8, 48, 11008, 16), (4, 4, 64, 8192, 2), (4, 32, 70, 2048, 3),
+    # decode rows of 48 and 80 128-column slots (several slot batches per
+    # wave, the last one partial), and rows of one and of two slots
+    (4, 4, 40, 6144, 2), (2, 2, 33, 10240, 1), (3, 2, 40, 10240, 16), (4, 1, 21, 128, 3), (2, 1, 18, 256, 5),
 ])
 def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
