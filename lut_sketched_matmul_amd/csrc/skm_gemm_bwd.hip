@@ -28,6 +28,9 @@
 // chunk's indices staged in LDS. Waves own disjoint (row, bin copy) pairs, so
 // the bins need no cross-wave atomics and the sums are deterministic; the
 // block stores each gradient entry exactly once (no global atomics).
+// k_gemm_dlut_dma (whole 32-token steps, the common case) copies the operand
+// tiles from global memory into a three-stage LDS ring with global_load_lds
+// instead of staging them through registers.
 #include <stdlib.h>
 
 #include "skm_gemm_common.h"
@@ -699,6 +702,71 @@ __device__ __forceinline__ uint32_t dl_field(uint32_t row, uint32_t j) {
   return (w >> off) & ((1u << B) - 1u);
 }
 
+// Stage this chunk's packed indices (128 rows x 16*B dwords, columns past the
+// group read as 0) at LDS 0, row stride DL_IRS.
+template <int B>
+__device__ __forceinline__ void dl_stage_indices(const uint8_t* __restrict__ idx_packed, int64_t i0, int64_t n,
+                                                 int64_t d, int64_t j0, int64_t jend, int t) {
+  const int64_t units = (jend - j0) / 32 < DL_BN / 32 ? (jend - j0) / 32 : DL_BN / 32;
+  for (int q = t; q < 128 * 16 * B; q += 512) {
+    const int row = q / (16 * B), wd = q % (16 * B);
+    const int64_t grow = i0 + row < n ? i0 + row : n - 1;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
+    st_w((uint32_t)row * DL_IRS + (uint32_t)wd * 4u, (wd / B) < units ? src[wd] : 0u);
+  }
+}
+
+// Scatter-add a wave's finished 64 x 128 dW tile (acc[a][b]: D[i][j] with
+// i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4, j = 128 wn + 32 b + lane%32)
+// into its bin copy at `binbase` ([128 rows][brs] fp32), using the indices
+// staged by dl_stage_indices. Branch-free: an entry outside the matrix adds 0
+// to a bin that is never stored (rows past n) or to entry 0 (columns past the
+// group, whose staged indices are 0). Fully unrolled so that the accumulators
+// stay in registers; the scheduling fences keep the index reads from being
+// hoisted all at once, and an opaque copy of the lane id keeps the compiler
+// from hoisting the 128 bin addresses out of the chunk loop (where they would
+// stay live across the K loop).
+template <int B>
+__device__ __forceinline__ void dl_scatter(const f32x16 (&acc)[2][4], uint32_t lane, int wm, int wn, int64_t i0,
+                                           int64_t n, int64_t j0, int64_t jend, uint32_t binbase, uint32_t brs) {
+  uint32_t bl = lane;
+  asm volatile("" : "+v"(bl));
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t j = 128u * wn + 32u * b + (bl & 31u);
+      const bool j_ok = j0 + (int64_t)j < jend;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (bl >> 5) + (e & 3);
+        const float v = (j_ok && i0 + (int64_t)i < n) ? acc[a][b][e] : 0.0f;
+        const uint32_t c = dl_field<B>(i * DL_IRS, j);
+        __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * brs + c) * 4u), v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+}
+
+// One store per gradient entry of the block's rows and group: the four bin
+// copies at `bins` (stride `bcopy` bytes, rows of `brs` floats) summed in a
+// fixed order.
+template <int B>
+__device__ __forceinline__ void dl_store_bins(float* __restrict__ dLUT, int64_t i0, int64_t n, int gpr, int g,
+                                              uint32_t bins, uint32_t bcopy, uint32_t brs, int accumulate, int t) {
+  constexpr int K = 1 << B;
+  for (uint32_t q = (uint32_t)t; q < 128u * (uint32_t)K; q += 512u) {
+    const uint32_t i = q / K, c = q % K;
+    if (i0 + (int64_t)i >= n) continue;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += *(const lds_f32*)(uintptr_t)(bins + (uint32_t)w * bcopy + (i * brs + c) * 4u);
+    float* dst = dLUT + ((i0 + i) * gpr + g) * K + c;
+    *dst = accumulate ? *dst + s : s;
+  }
+}
+
 // raw operands of one step for one thread: one dY chunk, four X chunks
 struct DlStage {
   u32x4 y;
@@ -710,7 +778,6 @@ __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
             int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
   typedef mfma32<TX> MF;
-  constexpr int K = 1 << B;
   extern __shared__ uint32_t smem[];
   (void)smem;
 
@@ -837,62 +904,194 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
     __syncthreads();
     for (int k = 0; k < KS; ++k) step(k, j0);
 
-    // ---- this chunk's packed indices: 128 rows x (16 * B) dwords
-    {
-      const int64_t units = (jend - j0) / 32 < DL_BN / 32 ? (jend - j0) / 32 : DL_BN / 32;
-      for (int q = t; q < 128 * 16 * B; q += 512) {
-        const int row = q / (16 * B), wd = q % (16 * B);
-        const int64_t grow = i0 + row < n ? i0 + row : n - 1;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(idx_packed + grow * (d * B / 8) + j0 * B / 8);
-        st_w((uint32_t)row * DL_IRS + (uint32_t)wd * 4u, (wd / B) < units ? src[wd] : 0u);
+    // ---- this chunk's packed indices, then the scatter into this wave's bins
+    dl_stage_indices<B>(idx_packed, i0, n, d, j0, jend, t);
+    __syncthreads();
+    dl_scatter<B>(acc, lane, wm, wn, i0, n, j0, jend, DL_BINS + (uint32_t)wn * DL_BCOPY, DL_BRS);
+  }
+  __syncthreads();
+  dl_store_bins<B>(dLUT, i0, n, gpr, g, DL_BINS, DL_BCOPY, DL_BRS, accumulate, t);
+}
+
+// ---------------------------------------------------------------------------
+// k_gemm_dlut_dma: k_gemm_dlut's blocks, wave grid and binning, with the
+// operand tiles copied from global memory straight into LDS (16-byte
+// global_load_lds, two steps ahead into a ring of three stages), so that no
+// registers and no LDS store instructions carry them and the waves only
+// multiply. A DMA'd tile cannot be padded (a wave's 64 lanes write 1 KB
+// contiguously), so its 16-byte chunks are XOR-swizzled instead: chunk c of
+// token row r sits at c ^ 4 (r % 4), which puts the 4 rows x 4 chunks of one
+// 32-lane pass of ds_read_b64_tr_b16 on 64 distinct banks; each lane of a DMA
+// fetches the global chunk that belongs at its slot. The copies are issued
+// from asm: given the builtin, the compiler cannot tell the transposing reads
+// apart from the copies still in flight and drains every copy before each
+// read. Ordering is explicit instead: a wave waits for its own copies of step
+// k+1 (vmcnt) before the barrier that ends step k, so after that barrier the
+// whole tile of step k+1 is in LDS, and the compiler, which does not count
+// the copies, schedules the reads with exact LDS waits between the MFMAs. No
+// other global load is in flight while copies are (the counts would be off).
+// (Steps of 64 tokens in two stages, half the barriers, were slower: the
+// copies then have one step instead of two to land. Reads written as asm
+// blocks that wait for all 12 of a half step were 3-4 % slower.)
+// Requires m % 32 == 0 (there is no zero fill for tokens) and n % 8 == 0
+// (16-byte aligned dY rows). Rows past n and columns past the row are read
+// from clamped addresses; they only feed outputs that are not binned.
+constexpr uint32_t DD_TA = DL_BK * 256u;              // 8192: dY tile [32 tokens][128 rows]
+constexpr uint32_t DD_TB = DL_BK * 1024u;             // 32768: X tile [32 tokens][512 columns]
+constexpr uint32_t DD_STAGE = DD_TA + DD_TB;          // 40960
+constexpr uint32_t DD_BRS = 16;                       // floats per bin row (b <= 4)
+constexpr uint32_t DD_BCOPY = 128u * DD_BRS * 4u;     // 8192
+constexpr uint32_t DD_BINS = 3u * DD_STAGE;           // 122880
+constexpr uint32_t DD_LDS = DD_BINS + 4u * DD_BCOPY;  // 155648
+
+
+// 16 bytes per lane from `src` into LDS at `lds` + 16 * lane (lds wave-uniform;
+// M0 takes one wait state before the copy reads it)
+__device__ __forceinline__ void dd_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// raw barrier, with compiler-only fences so that no LDS access moves across it
+__device__ __forceinline__ void dd_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt bounding only the vector-memory counter (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean "no wait")
+template <int N>
+__device__ __forceinline__ void dd_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int B, typename TX>
+__global__ void __launch_bounds__(512, 1)
+k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed,
+                int64_t m, int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
+  typedef mfma32<TX> MF;
+  extern __shared__ uint32_t smem[];
+
+  const int t = threadIdx.x;
+  const uint32_t lane = (uint32_t)(t & 63);
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t lb = xcd_block(blockIdx.x, gridDim.x);
+  const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
+  const int g = (int)(lb % (uint32_t)gpr);
+  const int64_t G = d / gpr;
+  const int64_t jg0 = (int64_t)g * G;
+  const int64_t jend = jg0 + G;
+  const int KS = (int)(m / DL_BK);
+
+  for (uint32_t q = (uint32_t)t; q < 4u * DD_BCOPY / 4u; q += 512u) st_w(DD_BINS + q * 4u, 0u);
+  // the absolute LDS addresses below assume the dynamic LDS starts at 0
+  if ((uint32_t)(uintptr_t)smem != 0u) return;
+
+  // ---- DMA roles: this wave's token rows 4 wave .. +3. dY: one 1 KB
+  // instruction (lane = row (lane / 16) x slot (lane % 16)); X: one
+  // instruction per row (lane = slot).
+  const uint32_t ycg = (lane & 15u) ^ (((lane >> 4) & 3u) << 2);
+  const int64_t yrow = i0 + 8 * (int64_t)ycg <= n - 8 ? i0 + 8 * (int64_t)ycg : n - 8;
+  const TX* ysrc = dY + (int64_t)(4u * (uint32_t)wave + (lane >> 4)) * n + yrow;
+  const uint32_t ydst = 1024u * (uint32_t)wave;
+  const int64_t ystep = (int64_t)DL_BK * n;
+  const int64_t xstep = (int64_t)DL_BK * d;
+  const TX* xsrc[4];
+  auto dma = [&](int k, uint32_t stage) {
+    dd_dma16(ysrc + (int64_t)k * ystep, stage + ydst);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) dd_dma16(xsrc[h] + (int64_t)k * xstep, stage + DD_TA + 1024u * (4u * (uint32_t)wave + h));
+  };
+
+  // ---- matrix roles: fragment addresses relative to a stage (the half step's
+  // 16-token offset and the +4-row read go into the instruction offsets)
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t fs = lane & 15u;
+  const uint32_t frow = 8u * (lane >> 5) + (fs >> 2);
+  const uint32_t fx = (fs >> 2) << 2;  // swizzle of the fragment's rows (frow % 4 == fs / 4)
+  const uint32_t fin = 2u * ((lane >> 4) & 1u) + ((fs & 3u) >> 1);
+  const uint32_t fw = 8u * (fs & 1u);
+  uint32_t fa[2], fb[4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) fa[a] = frow * 256u + (((8u * wm + 4u * a + fin) ^ fx) << 4) + fw;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) fb[b] = DD_TA + frow * 1024u + (((16u * wn + 4u * b + fin) ^ fx) << 4) + fw;
+
+  f32x16 acc[2][4];
+  auto mfma_step = [&](uint32_t stage) {
+    u32x4 af[2][2], bf[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const uint32_t p = stage + fa[a] + 16u * 256u * ks;
+        const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 256u);
+        af[ks][a] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t p = stage + fb[b] + 16u * 1024u * ks;
+        const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 1024u);
+        bf[ks][b] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = MF::run(af[ks][a], bf[ks][b], acc[a][b]);
+    // the first half's 12 reads, then its 8 MFMAs interleaved with the second
+    // half's reads, then the second half's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // ---- scatter-add the finished dW tile into this wave's bins
-    // D[i][j] of tile (a, b): i = 64 wm + 32 a + 8 (e/4) + 4 (lane/32) + e%4,
-    // j = 128 wn + 32 b + lane%32 (fully unrolled so the accumulators stay in
-    // registers; the scheduling fences keep the index reads from being
-    // hoisted all at once)
-    // (an opaque copy of the lane id keeps the compiler from hoisting the 128
-    // bin addresses out of the chunk loop, where they would stay live across
-    // the K loop)
-    uint32_t bl = lane;
-    asm volatile("" : "+v"(bl));
-    const uint32_t binbase = DL_BINS + (uint32_t)wn * DL_BCOPY;
+  for (int64_t j0 = jg0; j0 < jend; j0 += DL_BN) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int64_t col = j0 + 8 * (int64_t)(lane ^ ((uint32_t)h << 2));
+      xsrc[h] = X + (int64_t)(4u * (uint32_t)wave + h) * d + (col <= d - 8 ? col : d - 8);
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t j = 128u * wn + 32u * b + (bl & 31u);
-        const bool j_ok = j0 + (int64_t)j < jend;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          // branch-free: an entry outside the matrix adds 0 to a bin that is
-          // never stored (rows past n) or to entry 0 (columns past the group,
-          // whose staged indices are 0)
-          const uint32_t i = 64u * wm + 32u * a + 8u * (e >> 2) + 4u * (bl >> 5) + (e & 3);
-          const float v = (j_ok && i0 + (int64_t)i < n) ? acc[a][b][e] : 0.0f;
-          const uint32_t c = dl_field<B>(i * DL_IRS, j);
-          __hip_atomic_fetch_add((lds_f32*)(uintptr_t)(binbase + (i * DL_BRS + c) * 4u), v, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-          if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int b = 0; b < 4; ++b) zero16(acc[a][b]);
+    __syncthreads();  // the previous chunk's binning is done with the staged indices
+    dma(0, 0u);
+    if (KS > 1) {
+      dma(1, DD_STAGE);
+      dd_wait_vmcnt<5>();
+    } else {
+      dd_wait_vmcnt<0>();
+    }
+    dd_barrier();
+    uint32_t st = 0u;  // stage of step k
+    for (int k = 0; k < KS; ++k) {
+      const uint32_t st2 = st >= DD_STAGE ? st - DD_STAGE : st + 2u * DD_STAGE;  // stage of step k+2
+      if (k + 2 < KS) dma(k + 2, st2);
+      mfma_step(st);
+      // this wave's DMA of step k+1 has landed (the one of step k+2 may not)
+      if (k + 2 < KS) dd_wait_vmcnt<5>();
+      else dd_wait_vmcnt<0>();
+      dd_barrier();
+      st = st + DD_STAGE == 3u * DD_STAGE ? 0u : st + DD_STAGE;
+    }
+    dd_wait_vmcnt<0>();  // (no copy is in flight here; the compiler does not count them)
+
+    dl_stage_indices<B>(idx_packed, i0, n, d, j0, jend, t);
+    __syncthreads();
+    dl_scatter<B>(acc, lane, wm, wn, i0, n, j0, jend, DD_BINS + (uint32_t)wn * DD_BCOPY, DD_BRS);
   }
   __syncthreads();
-
-  // ---- one store per gradient entry (bin copies summed in a fixed order)
-  for (uint32_t q = (uint32_t)t; q < 128u * (uint32_t)K; q += 512u) {
-    const uint32_t i = q / K, c = q % K;
-    if (i0 + (int64_t)i >= n) continue;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      s += *(const lds_f32*)(uintptr_t)(DL_BINS + (uint32_t)w * DL_BCOPY + (i * DL_BRS + c) * 4u);
-    float* dst = dLUT + ((i0 + i) * gpr + g) * K + c;
-    *dst = accumulate ? *dst + s : s;
-  }
+  dl_store_bins<B>(dLUT, i0, n, gpr, g, DD_BINS, DD_BCOPY, DD_BRS, accumulate, t);
 }
 
 // ---- launchers ---------------------------------------------------------------
@@ -966,9 +1165,34 @@ hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Prob
   return hipGetLastError();
 }
 
+// SKM_DLUT_DMA=0 selects the register-staged dLUT kernel for every shape (tuning aid)
+bool dlut_dma_disabled() {
+  static const bool v = [] {
+    const char* e = getenv("SKM_DLUT_DMA");
+    return e && e[0] == '0';
+  }();
+  return v;
+}
+
+template <int B, typename TX>
+hipError_t dlut_dma_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT,
+                           int accumulate, hipStream_t s) {
+  const auto kern = k_gemm_dlut_dma<B, TX>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DD_LDS);
+  if (attr != hipSuccess) return attr;
+  const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr,
+                     dLUT, accumulate);
+  return hipGetLastError();
+}
+
 template <int B, typename TX>
 hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
                   hipStream_t s) {
+  // DMA staging: whole 32-token steps and 16-byte aligned dY rows
+  if (p.m % DL_BK == 0 && p.n % 8 == 0 && !dlut_dma_disabled())
+    return dlut_dma_launch<B, TX>(dY, X, idx, p, dLUT, accumulate, s);
   if (p.n % 8 == 0) return dlut_launch<B, TX, true>(dY, X, idx, p, dLUT, accumulate, s);
   return dlut_launch<B, TX, false>(dY, X, idx, p, dLUT, accumulate, s);
 }

@@ -243,6 +243,11 @@ def _bwd16(idx, lut, X, dY, b, gpr, d, io, lut_dtype, accumulate=False, dlut_ini
     (4, 8, 200, 4096, 300), (2, 2, 130, 1024, 40), (3, 8, 96, 11008, 33), (4, 1, 257, 512, 17),
     (3, 4, 300, 1536, 260), (2, 32, 64, 1024, 64), (4, 4, 33, 8192, 5), (4, 1, 64, 256, 100),
     (2, 2, 129, 512, 70), (4, 8, 70, 11008, 40), (4, 8, 256, 11008, 64),
+    # whole 32-token steps and rows a multiple of 8 (tiles copied into LDS by
+    # DMA): one, two and several steps, partial row blocks, groups of 3 and 4
+    # column chunks, columns clamped at the row end
+    (2, 2, 64, 1024, 32), (4, 1, 128, 512, 64), (4, 8, 200, 4096, 96), (3, 4, 136, 1536, 64),
+    (3, 8, 72, 11008, 96), (4, 4, 40, 8192, 160),
 ])
 def test_bwd16(io, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, dY = make_case(f"bwd16/{io}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, lut_dtype)
@@ -267,9 +272,10 @@ def test_dlut_bins_exact(b):
     assert np.array_equal(gdl, want)
 
 
-def test_bwd_accumulate_and_deterministic():
-    b, gpr, n, d, m = 4, 8, 160, 4096, 80
-    idx, lut, X, dY = make_case("bwdacc", n, d, b, gpr, m, "bf16", "f16")
+@pytest.mark.parametrize("m", [80, 96])
+def test_bwd_accumulate_and_deterministic(m):
+    b, gpr, n, d = 4, 8, 160, 4096
+    idx, lut, X, dY = make_case(f"bwdacc/{m}", n, d, b, gpr, m, "bf16", "f16")
     a1 = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
     a2 = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
     assert np.array_equal(a1[0], a2[0]) and np.array_equal(a1[1], a2[1])
