@@ -930,9 +930,9 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
 // whole tile of step k+1 is in LDS, and the compiler, which does not count
 // the copies, schedules the reads with exact LDS waits between the MFMAs. No
 // other global load is in flight while copies are (the counts would be off).
-// (Steps of 64 tokens in two stages, half the barriers, were slower: the
-// copies then have one step instead of two to land. Reads written as asm
-// blocks that wait for all 12 of a half step were 3-4 % slower.)
+// (Steps of 64 tokens in two stages, half the barriers, were 1-4 % slower;
+// reads written as asm blocks that wait for all 12 of a half step were 3-4 %
+// slower.)
 // Requires m % 32 == 0 (there is no zero fill for tokens) and n % 8 == 0
 // (16-byte aligned dY rows). Rows past n and columns past the row are read
 // from clamped addresses; they only feed outputs that are not binned.
@@ -969,16 +969,21 @@ __device__ __forceinline__ void dd_wait_vmcnt() {
 template <int B, typename TX>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed,
-                int64_t m, int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
+                int64_t m, int64_t n, int64_t d, int gpr, int gband, float* __restrict__ dLUT, int accumulate) {
   typedef mfma32<TX> MF;
   extern __shared__ uint32_t smem[];
 
   const int t = threadIdx.x;
   const uint32_t lane = (uint32_t)(t & 63);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // Consecutive logical blocks (one XCD's share, see xcd_block) take `gband`
+  // groups of consecutive row blocks: an XCD's co-resident blocks then share
+  // dY strips (same row block) and X slabs (same group) in its L2.
   const uint32_t lb = xcd_block(blockIdx.x, gridDim.x);
-  const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
-  const int g = (int)(lb % (uint32_t)gpr);
+  const uint32_t rblocks = gridDim.x / (uint32_t)gpr;
+  const uint32_t gi = lb % (uint32_t)gband, rest = lb / (uint32_t)gband;
+  const int64_t i0 = (int64_t)(rest % rblocks) * DL_BM;
+  const int g = (int)((rest / rblocks) * (uint32_t)gband + gi);
   const int64_t G = d / gpr;
   const int64_t jg0 = (int64_t)g * G;
   const int64_t jend = jg0 + G;
@@ -1165,7 +1170,9 @@ hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Prob
   return hipGetLastError();
 }
 
-// SKM_DLUT_DMA=0 selects the register-staged dLUT kernel for every shape (tuning aid)
+// SKM_DLUT_DMA=0 selects the register-staged dLUT kernel for every shape, and
+// SKM_DLUT_GBAND=g sets the groups per band of k_gemm_dlut_dma's block order
+// (tuning aids)
 bool dlut_dma_disabled() {
   static const bool v = [] {
     const char* e = getenv("SKM_DLUT_DMA");
@@ -1182,8 +1189,13 @@ hipError_t dlut_dma_launch(const TX* dY, const TX* X, const uint8_t* idx, const 
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DD_LDS);
   if (attr != hipSuccess) return attr;
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
+  static const int gb_env = [] {
+    const char* e = getenv("SKM_DLUT_GBAND");
+    return e ? atoi(e) : 0;
+  }();
+  int gband = gb_env > 0 && p.gpr % gb_env == 0 ? gb_env : (p.gpr % 4 == 0 ? 4 : (p.gpr % 2 == 0 ? 2 : 1));
   hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr,
-                     dLUT, accumulate);
+                     gband, dLUT, accumulate);
   return hipGetLastError();
 }
 
