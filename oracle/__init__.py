@@ -5,6 +5,7 @@ from .sketch_oracle import (  # noqa: F401
     backward_dx,
     dequantize,
     forward,
+    forward_multi,
     group_of_column,
     pack_indices,
     rel_err,

@@ -31,6 +31,11 @@ Efficient LLM Adaptation" (called *Sketch to Adapt* below).
   frozen (SpaLLM, section 2.3), so there is no gradient for the indices.
 * Gradient of the input: the chain rule through ``Y = X W^T`` gives
   ``dX = dY W``; the pages use it implicitly to train lower layers.
+* Several adapters over one mapping (SpaLLM, section 2.3, the paragraph on
+  dynamic maintenance of multiple adapters): each task owns its own set of
+  tables in the same format while the mapping Pi is shared, so a batch can mix
+  tasks; token t then uses table set s(t): ``Y[t, i] = sum_j X[t, j]
+  W_{s(t)}[i, j]``.
 
 Readings where the pages leave a step open (listed with the design notes):
 the packed bit order is little-endian (field j at bits b*j .. b*j+b-1 of the
@@ -110,6 +115,20 @@ def forward(X: np.ndarray, idx_packed: np.ndarray, lut: np.ndarray, b: int, gpr:
     X = np.asarray(X, dtype=np.float64)
     W = dequantize(idx_packed, lut, X.shape[1], b, gpr)
     return X @ W.T
+
+
+def forward_multi(X: np.ndarray, idx_packed: np.ndarray, luts: np.ndarray, lut_set, b: int,
+                  gpr: int) -> np.ndarray:
+    """Y[t, i] = sum_j X[t, j] W_{s(t)}[i, j], with W_s dequantised from table
+    set luts[s] over the shared indices and s(t) = lut_set[t]  (float64)."""
+    X = np.asarray(X, dtype=np.float64)
+    luts = np.asarray(luts)
+    m, d = X.shape
+    Y = np.zeros((m, idx_packed.shape[0]), dtype=np.float64)
+    for t in range(m):
+        W = dequantize(idx_packed, luts[int(lut_set[t])], d, b, gpr)
+        Y[t] = W @ X[t]
+    return Y
 
 
 def backward_dx(dY: np.ndarray, idx_packed: np.ndarray, lut: np.ndarray, d: int, b: int, gpr: int) -> np.ndarray:

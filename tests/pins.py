@@ -17,7 +17,11 @@ module, or a copy with a planted mistake) and raises ``AssertionError`` when
   since Y is linear in X and in LUT);
 * invariants: bins partition a group (sum over c of dLUT equals the group's sum
   of dW), adjointness <dY, X W^T> = <dY W, X>, entry-permutation invariance;
-* exact integer histograms for selection inputs.
+* exact integer histograms for selection inputs;
+* several table sets over one mapping (SpaLLM section 2.3, multiple
+  adapters): the identity mapping with per-set values 1, 2, -1 scales each
+  token by its set's value; per-set dense cases give the textbook product with
+  the token's own matrix; a token's output ignores the sets it does not use.
 """
 from __future__ import annotations
 
@@ -285,10 +289,62 @@ def pin_loop_vs_bincount(o):
                        o.backward_dlut(dY, X, packed, b, gpr), rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------------------
+# several table sets over one mapping
+# ---------------------------------------------------------------------------
+
+def pin_multi_identity_sets(o):
+    """Identity mapping, set 0 = {0, 1}, set 1 = {0, 2}, set 2 = {0, -1}: token
+    t's output is X[t] times its set's value."""
+    for b, gpr, n in ((2, 1, 32), (4, 2, 64)):
+        k = 1 << b
+        luts = np.full((3, n, gpr, k), 5.5)
+        luts[:, :, :, 0] = 0.0
+        luts[0, :, :, 1], luts[1, :, :, 1], luts[2, :, :, 1] = 1.0, 2.0, -1.0
+        packed = o.pack_indices(np.eye(n, dtype=np.int64), b)
+        X = _rng(11).normal(size=(6, n))
+        sets = [0, 2, 1, 1, 0, 2]
+        scale = np.array([1.0, -1.0, 2.0, 2.0, 1.0, -1.0])[:, None]
+        assert np.array_equal(o.forward_multi(X, packed, luts, sets, b, gpr), X * scale)
+
+
+def pin_multi_dense(o):
+    """Per-set dense special case: Y[t] = W_{s(t)} X[t]."""
+    r = _rng(12)
+    for b in (2, 3, 4):
+        k = 1 << b
+        n, gpr, m = 5, 3, 6
+        d = gpr * k
+        Ws = r.normal(size=(3, n, d))
+        luts = Ws.reshape(3, n, gpr, k).copy()
+        packed = o.pack_indices(np.tile(np.arange(d) % k, (n, 1)), b)
+        X = r.normal(size=(m, d))
+        sets = [2, 0, 1, 2, 0, 1]
+        Y = o.forward_multi(X, packed, luts, sets, b, gpr)
+        for t in range(m):
+            assert np.allclose(Y[t], Ws[sets[t]] @ X[t], rtol=1e-12, atol=1e-12), (b, t)
+
+
+def pin_multi_unused_sets(o):
+    """A token's output does not depend on table sets it does not use."""
+    b, gpr, n, d, m = 4, 2, 9, 64, 3
+    idx, lut, X, _ = _random_case(13, n, d, b, gpr, m)
+    packed = o.pack_indices(idx, b)
+    luts = np.stack([lut, lut[::-1], lut * 3.0])
+    sets = [0, 0, 2]
+    Y = o.forward_multi(X, packed, luts, sets, b, gpr)
+    luts2 = luts.copy()
+    luts2[1] = _rng(14).normal(size=lut.shape)
+    assert np.array_equal(o.forward_multi(X, packed, luts2, sets, b, gpr), Y)
+    luts2[2] = -luts2[2]
+    Y2 = o.forward_multi(X, packed, luts2, sets, b, gpr)
+    assert np.array_equal(Y2[:2], Y[:2]) and not np.allclose(Y2[2], Y[2])
+
+
 ALL_PINS = [
     pin_bitstream_golden, pin_unpack_bigint, pin_unpack_exhaustive_b3,
     pin_identity, pin_dense_special_case, pin_dequant_elementwise,
     pin_forward_binned, pin_permutation_invariance,
     pin_finite_difference, pin_bins_partition_group, pin_adjoint, pin_histogram,
-    pin_loop_vs_bincount,
+    pin_loop_vs_bincount, pin_multi_identity_sets, pin_multi_dense, pin_multi_unused_sets,
 ]

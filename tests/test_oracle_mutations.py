@@ -30,6 +30,10 @@ MUTATIONS = {
     "dx_transposed": ("return dY @ W", "return dY @ W.T"),
     "dw_transposed": ("return np.asarray(dY, dtype=np.float64).T @ np.asarray(X, dtype=np.float64)",
                       "return (np.asarray(X, dtype=np.float64).T @ np.asarray(dY, dtype=np.float64)).T[:, ::-1]"),
+    "multi_set_ignored": ("W = dequantize(idx_packed, luts[int(lut_set[t])], d, b, gpr)",
+                          "W = dequantize(idx_packed, luts[0], d, b, gpr)"),
+    "multi_set_of_next_token": ("W = dequantize(idx_packed, luts[int(lut_set[t])], d, b, gpr)",
+                                "W = dequantize(idx_packed, luts[int(lut_set[(t + 1) % m])], d, b, gpr)"),
     "dlut_overwrite": ("out[i, g[j], idx[i, j]] += dW[i, j]", "out[i, g[j], idx[i, j]] = dW[i, j]"),
     "dlut_average": (
         "out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)",
