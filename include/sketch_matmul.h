@@ -93,6 +93,29 @@ int sketch_matmul_fwd(const void* X, int x_dtype,
                       void* Y, hipStream_t stream);
 
 /*
+ * Forward pass with one table set per token, over one shared index stream
+ * (SpaLLM section 2.3, multiple adapters: each adapter is a set of tables in
+ * the same format over the frozen mapping, so requests of different tasks can
+ * share a batch):
+ *   luts     [n_sets][n][gpr][2^b] lut_dtype   (set s at luts + s*n*gpr*2^b)
+ *   lut_set  [m] int32 (device): token t uses set lut_set[t]; values outside
+ *            [0, n_sets) are clamped to that range
+ *   Y[t][i] = sum_j X[t][j] * luts[lut_set[t]][i][j/G][idx[i][j]]
+ * Decode-sized batches (1 <= m <= 16, tables of a 16-row block within the
+ * decode limit) with a 16-bit dtype pair; other sizes and the fp32 pair return
+ * SKM_EUNSUPPORTED. The index stream is read from memory once; each set that
+ * some token uses adds its tables and one round of table lookups. lut_set must
+ * be 4-byte aligned, the other pointers 16-byte aligned; Y must not overlap
+ * any input. m == 0 returns OK.
+ */
+int sketch_matmul_fwd_multi(const void* X, int x_dtype,
+                            const uint8_t* idx_packed,
+                            const void* luts, int lut_dtype,
+                            const int32_t* lut_set, int n_sets,
+                            int64_t m, int64_t n, int64_t d, int b, int gpr,
+                            void* Y, hipStream_t stream);
+
+/*
  * Backward pass (the mapping is frozen, SpaLLM section 2.3, so there is no
  * index gradient):
  *   dX   = dY * W                      [m][d] fp32, NULL = skip

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     sketch_dequant,
     sketch_matmul_bwd,
     sketch_matmul_fwd,
+    sketch_matmul_fwd_multi,
     sketch_unpack_indices,
 )
 

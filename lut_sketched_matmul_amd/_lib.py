@@ -41,6 +41,8 @@ _c_size = ctypes.c_size_t
 _SIGNATURES = {
     "sketch_matmul_fwd": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_vp, _c_vp]),
+    "sketch_matmul_fwd_multi": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_vp, _c_int, _c_i64, _c_i64, _c_i64,
+                                         _c_int, _c_int, _c_vp, _c_vp]),
     "sketch_matmul_bwd": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_vp, _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
     "sketch_matmul_bwd_workspace": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int]),
@@ -130,6 +132,27 @@ def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=Non
                                  dtype_code(lut), m, n, d, b, gpr, out.data_ptr() if out.numel() else None,
                                  _stream_ptr(stream))
     _check("sketch_matmul_fwd", st)
+    return out
+
+
+def sketch_matmul_fwd_multi(X, idx_packed, luts, lut_set, b: int, gpr: int, out=None, stream=None):
+    """Y[t] = X[t] W_{lut_set[t]}^T: one table set per token over shared indices.
+
+    X [m, d] (f16/bf16, m <= 16), idx_packed [n, d*b/8] uint8, luts [n_sets, n,
+    gpr, 2^b], lut_set [m] int32 (device). Returns Y [m, n] in X's dtype.
+    """
+    torch = _torch()
+    _require_device(X, idx_packed, luts, lut_set, out)
+    m, d = X.shape
+    n = idx_packed.shape[0]
+    if lut_set.dtype != torch.int32 or lut_set.numel() != m:
+        raise ValueError("lut_set must be an int32 tensor with one entry per token")
+    if out is None:
+        out = torch.empty((m, n), dtype=X.dtype, device=X.device)
+    st = lib().sketch_matmul_fwd_multi(X.data_ptr(), dtype_code(X), idx_packed.data_ptr(), luts.data_ptr(),
+                                       dtype_code(luts), lut_set.data_ptr() if m else None, luts.shape[0], m, n, d,
+                                       b, gpr, out.data_ptr() if out.numel() else None, _stream_ptr(stream))
+    _check("sketch_matmul_fwd_multi", st)
     return out
 
 

@@ -117,6 +117,28 @@ int sketch_matmul_fwd(const void* X, int x_dtype, const uint8_t* idx_packed, con
   return SKM_EUNSUPPORTED;
 }
 
+int sketch_matmul_fwd_multi(const void* X, int x_dtype, const uint8_t* idx_packed, const void* luts, int lut_dtype,
+                            const int32_t* lut_set, int n_sets, int64_t m, int64_t n, int64_t d, int b, int gpr,
+                            void* Y, hipStream_t stream) {
+  int st = check_shape(m, n, d, b, gpr);
+  if (st != SKM_OK) return st;
+  if (!supported_pair(x_dtype, lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!idx_packed || !luts || n_sets < 1) return SKM_EINVAL;
+  if (m > 0 && (!X || !Y || !lut_set)) return SKM_EINVAL;
+  if (!aligned16(idx_packed) || !aligned16(luts) || (X && !aligned16(X)) || (Y && !aligned16(Y)) ||
+      ((uintptr_t)lut_set & 3u) != 0)
+    return SKM_EALIGN;
+  const int xs = elem_bytes(x_dtype), ls = elem_bytes(lut_dtype);
+  const Range out{Y, m * n * xs};
+  if (overlap(out, {X, m * d * xs}) || overlap(out, {idx_packed, n * d * b / 8}) ||
+      overlap(out, {luts, (int64_t)n_sets * n * gpr * (int64_t(1) << b) * ls}) || overlap(out, {lut_set, m * 4}))
+    return SKM_EALIAS;
+  if (m == 0) return SKM_OK;
+  const Problem p{m, n, d, b, gpr};
+  if (x_dtype == SKM_F32 || !skm::decode_supported(p)) return SKM_EUNSUPPORTED;
+  return status_of(skm::launch_decode_multi(X, x_dtype, idx_packed, luts, lut_dtype, lut_set, n_sets, p, Y, stream));
+}
+
 size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr, int io_dtype, int lut_dtype) {
   (void)m; (void)n; (void)d; (void)b; (void)gpr; (void)io_dtype; (void)lut_dtype;
   return 0;

@@ -282,10 +282,20 @@ __device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
 // index words. The next batch of slots is loaded while the current one is
 // being computed (two register sets), except for activations in registers at
 // 4 slots per batch.
-template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
+// MULTI: several table sets over the one index stream ("SpaLLM", section 2.3:
+// every adapter is a set of tables in the same format over the frozen
+// mapping), token t using set lut_set[t] (clamped into [0, n_sets)). The block
+// takes one pass per set that some token uses, in the order of first use:
+// stage that set's tables, run the slot loop over all the block's weights
+// (after the first pass the index words come from the L2), and keep for each
+// output element the result of its token's set. The activations are staged
+// once. Each pass costs the set's tables and one round of table lookups; the
+// index stream is read from memory once.
+template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool MULTI>
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
-         int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, TX* __restrict__ Y) {
+         int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, TX* __restrict__ Y,
+         const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride) {
   // Dynamic LDS only (this kernel has no static LDS, so it starts at address
   // 0): [entries][64 lanes] table dwords, [m][d] activations (XL), then the
   // [NW][16][16] fp32 partials.
@@ -314,29 +324,56 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int64_t xl_elems = (int64_t)m * d;
   constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
 
+  // MULTI: the set of token t (wave-uniform), and the sets of the four tokens
+  // whose outputs this lane holds (lane l: tokens 4 (l / 16) + r)
+  auto set_of = [&](int tt) -> int {
+    const int v = __builtin_amdgcn_readfirstlane(lut_set[tt]);
+    return v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v);
+  };
+  int lset[4] = {0, 0, 0, 0};
+  int tfirst = 0;  // first token of the set being processed
+  int cur = 0;     // that set
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 4 * q + r < m ? 4 * q + r : m - 1;
+      const int v = lut_set[tt];
+      lset[r] = v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v);
+    }
+    cur = set_of(0);
+  }
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  bool first = true;
+  constexpr int PF = dec_pf<NW>::value;
+  SlotRegs<B, TX, PF> R0, R1;
+  int64_t s0;
+  while (true) {
+  const TL* lutp = MULTI ? lut + (int64_t)cur * set_stride : lut;
   // ---- prologue: table loads, activation loads (XL), first index loads, then
   // the LDS stores of the first two (their loads complete first)
   TabRegs<B> TR;
-  tab_load<B, NW, TL>(TR, lut, row_ok ? grow : n - 1, gpr, wave);
+  tab_load<B, NW, TL>(TR, lutp, row_ok ? grow : n - 1, gpr, wave);
   u32x4 xs[XCH];
   if constexpr (XL) {
+    if (first) {
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-      if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
+      for (int c = 0; c < XCH; ++c) {
+        const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+        if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
+      }
     }
   }
-  constexpr int PF = dec_pf<NW>::value;
-  SlotRegs<B, TX, PF> R0, R1;
-  int64_t s0 = wave;
+  s0 = wave;
   load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
   if constexpr (XL) {
+    if (first) {
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-      if (e < xl_elems) {
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+      for (int c = 0; c < XCH; ++c) {
+        const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+        if (e < xl_elems) {
+          *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+        }
       }
     }
   }
@@ -417,11 +454,33 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     compute(R0, s0, btag<true>{});
   }
 
+  if constexpr (!MULTI) {
+    out = acc;
+    break;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = lset[r] == cur ? acc[r] : out[r];
+    // the next set in order of first use (sets of earlier tokens are done)
+    int nxt = -1;
+    for (int tt = tfirst + 1; tt < m && nxt < 0; ++tt) {
+      const int st = set_of(tt);
+      bool seen = false;
+      for (int u = 0; u < tt && !seen; ++u) seen = set_of(u) == st;
+      if (!seen) nxt = tt;
+    }
+    if (nxt < 0) break;
+    tfirst = nxt;
+    cur = set_of(nxt);
+    first = false;
+    __syncthreads();  // every wave is done with this set's tables
+  }
+  }  // per-set passes
+
   // ---- sum the NW partial tiles in wave order, then store Y[token][row]
   // lane l holds D[token 4*(l/16)+r][row l%16]
   float* red = reinterpret_cast<float*>(smem) + (xl_base + (XL ? (uint32_t)xl_elems * 2u : 0u)) / 4u;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave * 256 + (4 * q + r) * 16 + j] = acc[r];
+  for (int r = 0; r < 4; ++r) red[wave * 256 + (4 * q + r) * 16 + j] = out[r];
   __syncthreads();
   const int t = threadIdx.x;
   if (t < 256) {
@@ -442,34 +501,55 @@ size_t decode_lds_bytes(int gpr, int64_t x_elems) {
          (size_t)NW * 256 * 4;
 }
 
+// Table sets for the MULTI kernel (a single set: lut_set == nullptr)
+struct SetArgs {
+  const int32_t* lut_set = nullptr;
+  int n_sets = 1;
+  int64_t set_stride = 0;  // table elements per set
+};
+
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
 hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
-                         uint32_t magic) {
-  const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL>;
+                         uint32_t magic, const SetArgs& sa) {
   const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? p.m * p.d : 0);
+  const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
+  // (the LDS limit is raised once per kernel, the first time one needs it)
+  if (sa.lut_set) {
+    const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
+    if (lds > 65536) {
+      static const hipError_t attr = hipFuncSetAttribute((const void*)kern,
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (attr != hipSuccess) return attr;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
+                       sa.lut_set, sa.n_sets, sa.set_stride);
+    return hipGetLastError();
+  }
+  const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false>;
   if (lds > 65536) {
     static const hipError_t attr = hipFuncSetAttribute((const void*)kern,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
   }
-  const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
+                     sa.lut_set, sa.n_sets, sa.set_stride);
   return hipGetLastError();
 }
 
 template <int B, int NW, typename TX, typename TL>
 hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
-                     uint32_t magic) {
+                     uint32_t magic, const SetArgs& sa) {
   const bool xl = p.m * p.d <= DEC_XL_MAX;
   if (p.units() % 4 != 0)
-    return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic)
-              : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic);
-  return xl ? decode_launch<B, NW, TX, TL, false, true>(X, idx, lut, p, Y, s, magic)
-            : decode_launch<B, NW, TX, TL, false, false>(X, idx, lut, p, Y, s, magic);
+    return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic, sa)
+              : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic, sa);
+  return xl ? decode_launch<B, NW, TX, TL, false, true>(X, idx, lut, p, Y, s, magic, sa)
+            : decode_launch<B, NW, TX, TL, false, false>(X, idx, lut, p, Y, s, magic, sa);
 }
 
 template <int B, typename TX, typename TL>
-hipError_t decode_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
+hipError_t decode_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
+                    const SetArgs& sa) {
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   // u / ug == umulhi(u, magic) for u * ug < 2^32; ug == 1 is passed as 0
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
@@ -478,17 +558,29 @@ hipError_t decode_b(const TX* X, const uint8_t* idx, const TL* lut, const Proble
   // block's start-up latency hides behind another's work.
   const int64_t blocks = (p.n + DEC_ROWS - 1) / DEC_ROWS;
   const int nw = decode_waves_override() ? decode_waves_override() : (blocks <= 384 ? 16 : 8);
-  if (nw == 16) return decode_nw<B, 16>(X, idx, lut, p, Y, s, magic);
-  return decode_nw<B, 8>(X, idx, lut, p, Y, s, magic);
+  if (nw == 16) return decode_nw<B, 16>(X, idx, lut, p, Y, s, magic, sa);
+  return decode_nw<B, 8>(X, idx, lut, p, Y, s, magic, sa);
 }
 
 template <typename TX, typename TL>
-hipError_t decode_t(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
+hipError_t decode_t(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
+                    const SetArgs& sa) {
   switch (p.b) {
-    case 2: return decode_b<2>(X, idx, lut, p, Y, s);
-    case 3: return decode_b<3>(X, idx, lut, p, Y, s);
-    default: return decode_b<4>(X, idx, lut, p, Y, s);
+    case 2: return decode_b<2>(X, idx, lut, p, Y, s, sa);
+    case 3: return decode_b<3>(X, idx, lut, p, Y, s, sa);
+    default: return decode_b<4>(X, idx, lut, p, Y, s, sa);
   }
+}
+
+hipError_t decode_dispatch(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
+                           const Problem& p, void* Y, hipStream_t s, const SetArgs& sa) {
+  if (x_dtype == DT_F16 && lut_dtype == DT_F16)
+    return decode_t((const half_t*)X, idx, (const half_t*)lut, p, (half_t*)Y, s, sa);
+  if (x_dtype == DT_BF16 && lut_dtype == DT_F16)
+    return decode_t((const bf16_t*)X, idx, (const half_t*)lut, p, (bf16_t*)Y, s, sa);
+  if (x_dtype == DT_F16 && lut_dtype == DT_BF16)
+    return decode_t((const half_t*)X, idx, (const bf16_t*)lut, p, (half_t*)Y, s, sa);
+  return decode_t((const bf16_t*)X, idx, (const bf16_t*)lut, p, (bf16_t*)Y, s, sa);
 }
 
 }  // namespace
@@ -503,13 +595,16 @@ bool decode_supported(const Problem& p) {
 
 hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
                          const Problem& p, void* Y, hipStream_t s) {
-  if (x_dtype == DT_F16 && lut_dtype == DT_F16)
-    return decode_t((const half_t*)X, idx, (const half_t*)lut, p, (half_t*)Y, s);
-  if (x_dtype == DT_BF16 && lut_dtype == DT_F16)
-    return decode_t((const bf16_t*)X, idx, (const half_t*)lut, p, (bf16_t*)Y, s);
-  if (x_dtype == DT_F16 && lut_dtype == DT_BF16)
-    return decode_t((const half_t*)X, idx, (const bf16_t*)lut, p, (half_t*)Y, s);
-  return decode_t((const bf16_t*)X, idx, (const bf16_t*)lut, p, (bf16_t*)Y, s);
+  return decode_dispatch(X, x_dtype, idx, lut, lut_dtype, p, Y, s, SetArgs{});
+}
+
+hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
+                               const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s) {
+  SetArgs sa;
+  sa.lut_set = lut_set;
+  sa.n_sets = n_sets;
+  sa.set_stride = p.n * p.gpr * p.k();
+  return decode_dispatch(X, x_dtype, idx, luts, lut_dtype, p, Y, s, sa);
 }
 
 }  // namespace skm

@@ -945,10 +945,21 @@ constexpr uint32_t DD_BINS = 3u * DD_STAGE;           // 122880
 constexpr uint32_t DD_LDS = DD_BINS + 4u * DD_BCOPY;  // 155648
 
 
-// 16 bytes per lane from `src` into LDS at `lds` + 16 * lane (lds wave-uniform;
-// M0 takes one wait state before the copy reads it)
+// 16 bytes per lane from `src` into LDS at `lds` + 16 * lane (lds wave-uniform).
+// The copy takes its LDS address from M0 (one wait state after writing it);
+// M0 is saved and restored around it, since the compiler may keep a value
+// there.
 __device__ __forceinline__ void dd_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 // raw barrier, with compiler-only fences so that no LDS access moves across it

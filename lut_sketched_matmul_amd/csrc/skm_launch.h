@@ -42,6 +42,9 @@ int decode_max_m();
 bool decode_supported(const Problem& p);
 hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
                          const Problem& p, void* Y, hipStream_t s);
+// decode with one table set per token: luts [n_sets][n][gpr][2^b], lut_set [m]
+hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
+                               const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s);
 
 // prefill / training forward: m > 16, tiled matrix-core GEMM
 bool gemm_fwd_supported(const Problem& p);

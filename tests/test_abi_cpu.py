@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert {"sketch_matmul_fwd", "sketch_matmul_bwd", "sketch_matmul_bwd_workspace", "sketch_dequant",
+    assert {"sketch_matmul_fwd", "sketch_matmul_fwd_multi", "sketch_matmul_bwd", "sketch_matmul_bwd_workspace", "sketch_dequant",
             "sketch_unpack_indices", "sketch_status_str", "sketch_version"} <= set(names)
     for nme in names:
         assert hasattr(lib, nme), nme
@@ -65,6 +65,22 @@ def test_fwd_rejects_bad_pointers_and_dtypes(lib):
 
 def test_fwd_empty_is_noop(lib):
     assert fwd(lib, m=0, X=0, Y=0) == 0
+
+
+def fwd_multi(lib, X=A, xdt=1, idx=B_, luts=C, ldt=1, sets=0x50000000, ns=2, m=4, n=64, d=512, b=4, gpr=1, Y=Dp):
+    return lib.sketch_matmul_fwd_multi(X, xdt, idx, luts, ldt, sets, ns, m, n, d, b, gpr, Y, None)
+
+
+def test_fwd_multi_rejects_bad_arguments(lib):
+    assert fwd_multi(lib, ns=0) == EINVAL
+    assert fwd_multi(lib, sets=0) == EINVAL
+    assert fwd_multi(lib, b=5) == EINVAL
+    assert fwd_multi(lib, sets=0x50000002) == EALIGN
+    assert fwd_multi(lib, m=17) == EUNSUP               # decode-sized batches only
+    assert fwd_multi(lib, xdt=0, ldt=0) == EUNSUP       # no fp32 path
+    assert fwd_multi(lib, Y=0x50000000) == EALIAS       # output over the set array
+    assert fwd_multi(lib, Y=C + 2048) == EALIAS         # output over the second table set
+    assert fwd_multi(lib, m=0, X=0, Y=0, sets=0) == 0
 
 
 def bwd(lib, dY=A, X=Dp, dt=1, idx=B_, lut=C, ldt=1, m=4, n=64, d=512, b=4, gpr=1, dX=0x70000000,

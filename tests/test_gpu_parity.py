@@ -204,6 +204,73 @@ def test_fwd_selection_bit_exact(dt, m):
     assert np.array_equal(to_f64(Y), W[:, cols].T)
 
 
+# ---------------------------------------------------------------------------
+# several table sets over one mapping, one set per token (SpaLLM section 2.3)
+# ---------------------------------------------------------------------------
+
+def _multi_case(tag, n, d, b, gpr, m, n_sets, x_dtype, lut_dtype):
+    idx, _, X, _ = make_case(tag, n, d, b, gpr, m, x_dtype, lut_dtype)
+    luts = np.stack([syn.random_lut(f"{tag}/lut{s}", n, gpr, b, 0.02, lut_dtype) for s in range(n_sets)])
+    return idx, luts, X
+
+
+def _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype):
+    return skm().sketch_matmul_fwd_multi(to_dev(X, x_dtype), to_dev(idx, "u8"), to_dev(luts, lut_dtype),
+                                         to_dev(np.asarray(sets, dtype=np.int32), "i32"), b, gpr)
+
+
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("b,gpr,n,d,sets,n_sets", [
+    (4, 8, 64, 4096, [0, 1, 2, 3], 4),
+    (4, 8, 70, 4096, [2, 0, 1, 1, 0, 2, 2, 2, 0, 1, 0, 2, 1, 1, 0, 0], 3),
+    (2, 8, 40, 11008, [1, 1, 0], 2),       # 11008 columns: ragged 128-column slots
+    (3, 4, 33, 1536, [4, 3, 2, 1, 0], 5),
+    (4, 1, 20, 512, [1], 2),               # one token, using set 1 only
+    (4, 4, 8200, 1152, [0, 1], 2),         # more blocks than the GPU holds at once
+])
+def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
+    idx, luts, X = _multi_case(f"multi/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}", n, d, b, gpr, len(sets),
+                               n_sets, x_dtype, lut_dtype)
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype))
+    want = oracle.forward_multi(syn.to_float64(X, x_dtype), idx, syn.to_float64(luts, lut_dtype), sets, b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fwd_multi_one_set_is_fwd(dt):
+    """All tokens on one set: the same numbers as the single-set forward."""
+    b, gpr, n, d, m = 4, 8, 80, 4096, 5
+    idx, luts, X = _multi_case(f"multi1/{dt}", n, d, b, gpr, m, 3, dt, dt)
+    got = _fwd_multi(idx, luts, X, [1] * m, b, gpr, dt, dt)
+    ref = skm().sketch_matmul_fwd(to_dev(X, dt), to_dev(idx, "u8"), to_dev(luts[1], dt), b, gpr)
+    assert bool((got == ref).all())
+
+
+def test_fwd_multi_clamps_set_indices():
+    b, gpr, n, d = 4, 4, 48, 1024
+    sets, clamped = [-3, 0, 7, 1], [0, 0, 1, 1]
+    idx, luts, X = _multi_case("multiclamp", n, d, b, gpr, len(sets), 2, "f16", "f16")
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, "f16", "f16"))
+    want = oracle.forward_multi(syn.to_float64(X, "f16"), idx, syn.to_float64(luts, "f16"), clamped, b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_fwd_multi_selection_bit_exact(b):
+    """One-hot activation rows: token t reads W_{s(t)}[i, j_t] exactly."""
+    gpr, n, d, m, n_sets = 4, 96, 2048, 6, 3
+    idx, luts, _ = _multi_case(f"multisel/{b}", n, d, b, gpr, 1, n_sets, "f16", "f16")
+    cols = np.random.default_rng(b).choice(d, m, replace=False)
+    sets = [2, 0, 1, 1, 2, 0]
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    got = to_f64(_fwd_multi(idx, luts, syn.to_storage(X, "f16"), sets, b, gpr, "f16", "f16"))
+    L = syn.to_float64(luts, "f16")
+    for t in range(m):
+        W = oracle.dequantize(idx, L[sets[t]], d, b, gpr)
+        assert np.array_equal(got[t], W[:, cols[t]]), t
+
+
 @pytest.mark.parametrize("b", [2, 3, 4])
 def test_fwd_identity_exact(b):
     """SpaLLM section 2.4: the identity sketched with the two values 0 and 1."""
