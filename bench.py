@@ -8,9 +8,9 @@ HBM peak. Every timed launch reads a different copy of the indices and tables
 (>= 1 GiB in rotation) so the 256 MB last-level cache cannot serve repeats.
 
 The same JSON line carries the other measured parts of the hot path (16-token
-forward, the 7B MLP at 2 and 3 bits, 70B-shaped decode and prefill GEMM, the
-7B decoder-layer fine-tuning step) and the CPU oracle timed on this host as a
-baseline.
+forward, the 7B MLP at 2 and 3 bits, decode with one table set per token over
+one index stream, 70B-shaped decode and prefill GEMM, the 7B decoder-layer
+fine-tuning step) and the CPU oracle timed on this host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,lowbit,decode70b,prefill,finetune,dense,copy "
+                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,dense,copy "
                          "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
@@ -116,6 +116,51 @@ def bench_fwd(torch, skm, w, shape, b, m, steps, warmup, rotate=True):
         "GBps": nbytes / (ms * 1e-3) / 1e9, "TFLOPs": flops / (ms * 1e-3) / 1e12,
         "rotation_copies": rot.count if rot else 1,
     }
+
+
+def bench_multi(torch, skm, steps, warmup):
+    """Decode with one table set per token over one shared index stream (the
+    7B attention projection, b=4): one multi-set launch against one
+    single-set launch per set on that set's tokens."""
+    from lut_sketched_matmul_amd import synthetic as syn
+    from lut_sketched_matmul_amd import workloads as wl
+    w = wl.LLAMA2_7B_ATTN
+    shape = w.shapes[0]
+    b = 4
+    out = {}
+    for m, n_sets in ((4, 4), (16, 4), (16, 16)):
+        t = w.make(shape, b, m)
+        X = dev(torch, t["X"], w.x_dtype)
+        idx = dev(torch, t["idx_packed"], "u8")
+        luts = dev(torch, np.stack([syn.random_lut(f"bench-multi/{m}/{n_sets}/{s}", shape.n, w.gpr, b,
+                                                   w.lut_sigma, w.lut_dtype) for s in range(n_sets)]), w.lut_dtype)
+        sets = [tt % n_sets for tt in range(m)]
+        lut_set = torch.tensor(sets, dtype=torch.int32, device="cuda:0")
+        Y = torch.empty((m, shape.n), dtype=X.dtype, device="cuda:0")
+        rot = Rotation(torch, idx, luts)
+        total = time_launches(torch, lambda: skm.sketch_matmul_fwd_multi(X, *rot.next(), lut_set, b, w.gpr, out=Y),
+                              steps, warmup)
+        # one single-set launch per set, on that set's tokens
+        Xs = [X[[tt for tt in range(m) if sets[tt] == s]].contiguous() for s in range(n_sets)]
+        Ys = [torch.empty((x.shape[0], shape.n), dtype=X.dtype, device="cuda:0") for x in Xs]
+
+        def per_set():
+            i, l = rot.next()
+            for s in range(n_sets):
+                skm.sketch_matmul_fwd(Xs[s], i, l[s], b, w.gpr, out=Ys[s])
+
+        total_sep = time_launches(torch, per_set, steps, warmup)
+        nbytes = (shape.n * shape.d * b // 8 + n_sets * shape.n * w.gpr * (1 << b) * 2 + m * shape.d * 2
+                  + m * shape.n * 2)
+        ms, ms_sep = total / steps, total_sep / steps
+        out[f"m{m}_sets{n_sets}"] = {
+            "shape": f"{shape.name} {shape.n}x{shape.d}", "b": b, "m": m, "n_sets": n_sets,
+            "ms_per_launch": ms, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_one_launch_per_set": ms_sep, "speedup_vs_one_launch_per_set": ms_sep / ms,
+            "rotation_copies": rot.count,
+        }
+    return out
 
 
 def bench_finetune(torch, skm, steps, warmup):
@@ -236,8 +281,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
-    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "decode70b",
-                                                                   "prefill", "finetune", "dense", "copy"}
+    want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "multilut",
+                                                                   "decode70b", "prefill", "finetune", "dense",
+                                                                   "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -260,6 +306,12 @@ def main():
             lb[f"{s_.name}_b{b_}_m{m_}"] = r
         parts["decode_lowbit_7b_mlp"] = lb
         log("7B MLP b=2/3 decode: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in lb.items()))
+    if "multilut" in want:
+        ml = bench_multi(torch, skm, args.steps, args.warmup)
+        parts["decode_multi_lut_7b_attn"] = ml
+        log("multi-LUT decode 4096x4096: " + ", ".join(
+            f"{k} {v['ms_per_launch'] * 1e3:.2f} us ({v['speedup_vs_one_launch_per_set']:.2f}x vs one launch per set)"
+            for k, v in ml.items()))
     if "decode70b" in want:
         w7 = wl.LLAMA3_70B_MLP
         d7 = {}

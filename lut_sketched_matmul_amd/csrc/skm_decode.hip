@@ -342,17 +342,28 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     }
     cur = set_of(0);
   }
+  // MULTI: the next set after `cur` in order of first use (-1: none)
+  auto next_set_token = [&](int from) -> int {
+    for (int tt = from + 1; tt < m; ++tt) {
+      const int st = set_of(tt);
+      bool seen = false;
+      for (int u = 0; u < tt && !seen; ++u) seen = set_of(u) == st;
+      if (!seen) return tt;
+    }
+    return -1;
+  };
   f32x4 out = {0.f, 0.f, 0.f, 0.f};
   bool first = true;
   constexpr int PF = dec_pf<NW>::value;
   SlotRegs<B, TX, PF> R0, R1;
-  int64_t s0;
+  int64_t s0 = wave;
+  TabRegs<B> TR;  // MULTI: after the first pass, loaded during the previous pass
   while (true) {
-  const TL* lutp = MULTI ? lut + (int64_t)cur * set_stride : lut;
+  const int tnext = MULTI ? next_set_token(tfirst) : -1;
   // ---- prologue: table loads, activation loads (XL), first index loads, then
-  // the LDS stores of the first two (their loads complete first)
-  TabRegs<B> TR;
-  tab_load<B, NW, TL>(TR, lutp, row_ok ? grow : n - 1, gpr, wave);
+  // the LDS stores of the first two (their loads complete first). Later passes
+  // of MULTI find their tables and first index batch already loaded.
+  if (first) tab_load<B, NW, TL>(TR, MULTI ? lut + (int64_t)cur * set_stride : lut, row_ok ? grow : n - 1, gpr, wave);
   u32x4 xs[XCH];
   if constexpr (XL) {
     if (first) {
@@ -364,7 +375,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     }
   }
   s0 = wave;
-  load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+  if (first) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
   if constexpr (XL) {
     if (first) {
@@ -387,6 +398,12 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // the gathers address the tables with absolute LDS addresses (see gaddr)
   if ((uint32_t)(uintptr_t)smem != 0u) return;
   const uint32_t xl_row = xl_base + (uint32_t)tokc * (uint32_t)d * 2u;
+  if constexpr (MULTI) {
+    // the next set's tables (this set's again when none is left: the loads
+    // stay unconditional), in flight while this set is computed
+    const int sn = tnext >= 0 ? set_of(tnext) : cur;
+    tab_load<B, NW, TL>(TR, lut + (int64_t)sn * set_stride, row_ok ? grow : n - 1, gpr, wave);
+  }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   // compute(R, first slot, tail): a batch can be partial only when it is a
@@ -460,19 +477,14 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[r] = lset[r] == cur ? acc[r] : out[r];
-    // the next set in order of first use (sets of earlier tokens are done)
-    int nxt = -1;
-    for (int tt = tfirst + 1; tt < m && nxt < 0; ++tt) {
-      const int st = set_of(tt);
-      bool seen = false;
-      for (int u = 0; u < tt && !seen; ++u) seen = set_of(u) == st;
-      if (!seen) nxt = tt;
-    }
-    if (nxt < 0) break;
-    tfirst = nxt;
-    cur = set_of(nxt);
+    if (tnext < 0) break;
+    tfirst = tnext;
+    cur = set_of(tnext);
     first = false;
-    __syncthreads();  // every wave is done with this set's tables
+    // the next pass's first index batch (from the L2), then every wave is done
+    // with this set's tables
+    load_batch<B, NW, TX, RAGGED, XL, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow);
+    __syncthreads();
   }
   }  // per-set passes
 
