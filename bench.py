@@ -10,7 +10,8 @@ HBM peak. Every timed launch reads a different copy of the indices and tables
 The same JSON line carries the other measured parts of the hot path (16-token
 forward, the 7B MLP at 2 and 3 bits, decode with one table set per token over
 one index stream, 70B-shaped decode and prefill GEMM, the 7B decoder-layer
-fine-tuning step) and the CPU oracle timed on this host as a baseline.
+fine-tuning step, the fused table optimizer steps and a grouped q/k/v decode)
+and the CPU oracle timed on this host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -42,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,dense,copy "
+                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,dense,copy "
                          "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
@@ -160,6 +161,68 @@ def bench_multi(torch, skm, steps, warmup):
             "ms_one_launch_per_set": ms_sep, "speedup_vs_one_launch_per_set": ms_sep / ms,
             "rotation_copies": rot.count,
         }
+    return out
+
+
+def bench_glue(torch, skm, steps, warmup):
+    """Fine-tuning glue: the fused table optimizer steps over a 7B decoder layer's tables, and the
+    q/k/v decode as one grouped launch against three launches."""
+    from lut_sketched_matmul_amd import synthetic as syn
+    from lut_sketched_matmul_amd import workloads as wl
+    out = {}
+    wf = wl.LLAMA2_7B_FINETUNE
+    count = sum(s.n for s in wf.shapes) * wf.gpr * 16
+    per_set = count * (4 * 4 + 2)
+    sets = max(2, -(-ROTATE_BYTES // per_set))
+    g0 = torch.from_numpy(syn.random_normal("bench-glue/grad", (count,), 1e-3, "f32")).to("cuda:0")
+    p0 = torch.from_numpy(syn.random_normal("bench-glue/master", (count,), 0.02, "f32")).to("cuda:0")
+    bufs = [dict(p=p0.clone(), g=g0.clone(), m=torch.zeros_like(p0), v=torch.zeros_like(p0),
+                 c=torch.empty(count, dtype=torch.float16, device="cuda:0")) for _ in range(sets)]
+    it = [0]
+
+    def adam():
+        b_ = bufs[it[0] % sets]
+        it[0] += 1
+        skm.sketch_lut_adam_step(b_["p"], b_["g"], b_["m"], b_["v"], 1 + it[0] // sets, 1e-5, lut=b_["c"])
+
+    def sgd():
+        b_ = bufs[it[0] % sets]
+        it[0] += 1
+        skm.sketch_lut_sgd_step(b_["p"], b_["g"], 1e-5, lut=b_["c"])
+
+    for name, fn, bpe in (("adam", adam, 30), ("sgd", sgd, 14)):
+        ms = time_launches(torch, fn, steps, warmup) / steps
+        gbs = count * bpe / (ms * 1e-3) / 1e9
+        out[f"optimizer_{name}_7b_layer_tables"] = {
+            "entries": count, "bytes_per_entry": bpe, "ms_per_step": ms, "GBps": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "rotation_copies": sets}
+    del bufs
+    # q, k, v of the 7B attention at m = 1: three launches against one over the 12288 stacked rows
+    w = wl.LLAMA2_7B_ATTN
+    shape = w.shapes[0]
+    t = w.make(shape, 4, 1)
+    X = dev(torch, t["X"], w.x_dtype)
+    idx = dev(torch, t["idx_packed"], "u8")
+    lut = dev(torch, t["lut"], w.lut_dtype)
+    idx3, lut3 = torch.cat([idx] * 3, 0), torch.cat([lut] * 3, 0)
+    rot1, rot3 = Rotation(torch, idx, lut), Rotation(torch, idx3, lut3)
+    Y1 = torch.empty((1, shape.n), dtype=X.dtype, device="cuda:0")
+    Y3 = torch.empty((1, 3 * shape.n), dtype=X.dtype, device="cuda:0")
+
+    def three():
+        for _ in range(3):
+            i, l = rot1.next()
+            skm.sketch_matmul_fwd(X, i, l, 4, w.gpr, out=Y1)
+
+    def grouped():
+        i, l = rot3.next()
+        skm.sketch_matmul_fwd(X, i, l, 4, w.gpr, out=Y3)
+
+    ms3 = time_launches(torch, three, steps, warmup) / steps
+    msg = time_launches(torch, grouped, steps, warmup) / steps
+    nbytes = 3 * wl.algorithmic_bytes_fwd(shape.n, shape.d, 4, w.gpr, 1, 2, 2)
+    out["decode_qkv_7b_m1"] = {"ms_three_launches": ms3, "ms_grouped": msg, "speedup": ms3 / msg,
+                               "GBps_grouped": nbytes / (msg * 1e-3) / 1e9, "bytes": nbytes}
     return out
 
 
@@ -282,8 +345,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     skm.lib()
     want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "multilut",
-                                                                   "decode70b", "prefill", "finetune", "dense",
-                                                                   "copy"}
+                                                                   "decode70b", "prefill", "finetune", "glue",
+                                                                   "dense", "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -335,6 +398,14 @@ def main():
         ft = bench_finetune(torch, skm, big_steps, big_warm)
         parts["finetune_7b_layer"] = ft
         log(f"fine-tune step 7B layer m=8192: {ft['ms_per_step']:.2f} ms, {ft['TFLOPs']:.0f} TFLOP/s")
+    if "glue" in want:
+        gl = bench_glue(torch, skm, args.steps, args.warmup)
+        parts["finetune_glue"] = gl
+        q = gl["decode_qkv_7b_m1"]
+        log("optimizer steps over a 7B layer's tables: " + ", ".join(
+            f"{k} {v['ms_per_step'] * 1e3:.1f} us {v['GBps']:.0f} GB/s" for k, v in gl.items() if "optimizer" in k)
+            + f"; q/k/v decode m=1: three launches {q['ms_three_launches'] * 1e3:.2f} us, grouped "
+              f"{q['ms_grouped'] * 1e3:.2f} us")
 
     if "dense" in want:
         dr = bench_dense_reference(torch, big_steps, big_warm)

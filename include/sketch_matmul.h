@@ -157,6 +157,56 @@ int sketch_dequant(const uint8_t* idx_packed, const void* lut, int lut_dtype,
 int sketch_unpack_indices(const uint8_t* idx_packed, int64_t n, int64_t d, int b,
                           uint8_t* idx, hipStream_t stream);
 
+/*
+ * Fused optimizer steps for the trainable tables (SpaLLM section 2.3: only the
+ * table values are fine-tuned; the mapping stays frozen). The pages give the
+ * learning rates searched (SpaLLM appendix B.1, Table 7) but no optimizer;
+ * these are the textbook rules. One pass over `count` table entries (count =
+ * n * gpr * 2^b for one layer; any count >= 0 is accepted, 0 is a no-op):
+ *   master     [count] fp32, updated in place (the trained values)
+ *   grad       [count] fp32, read only (e.g. dLUT of sketch_matmul_bwd), used
+ *              as grad * grad_scale
+ *   lut        [count] compute copy in lut_dtype (SKM_F16 or SKM_BF16),
+ *              written as the new master rounded to nearest even; NULL = none
+ *              (lut_dtype is then ignored)
+ * Adam with decoupled weight decay (Kingma & Ba, Algorithm 1; Loshchilov &
+ * Hutter), step = 1, 2, ... counts this call among the steps taken so far:
+ *   g = grad * grad_scale
+ *   master *= 1 - lr * weight_decay
+ *   exp_avg    = beta1 * exp_avg    + (1 - beta1) * g
+ *   exp_avg_sq = beta2 * exp_avg_sq + (1 - beta2) * g * g
+ *   master -= lr / (1 - beta1^step) * exp_avg
+ *             / (sqrt(exp_avg_sq) / sqrt(1 - beta2^step) + eps)
+ * exp_avg and exp_avg_sq [count] fp32 start as zeros before step 1.
+ * Requires lr, eps, weight_decay >= 0, 0 <= beta1, beta2 < 1, all finite.
+ * All pointers 16-byte aligned; the written buffers must not overlap each
+ * other or grad (SKM_EALIAS). Computed in fp32.
+ */
+int sketch_lut_adam_step(float* master, void* lut, int lut_dtype,
+                         const float* grad, float* exp_avg, float* exp_avg_sq,
+                         int64_t count, int64_t step,
+                         float lr, float beta1, float beta2, float eps,
+                         float weight_decay, float grad_scale,
+                         hipStream_t stream);
+
+/*
+ * SGD with heavy-ball momentum and coupled weight decay, over the same
+ * buffers as above:
+ *   g = grad * grad_scale + weight_decay * master
+ *   momentum_buf = momentum * momentum_buf + g;  g = momentum_buf
+ *                                               (only when momentum != 0)
+ *   master -= lr * g
+ * momentum_buf [count] fp32 starts as zeros (then step 1 stores g, as
+ * torch.optim.SGD does); it may be NULL when momentum == 0. Requires lr,
+ * momentum, weight_decay >= 0 and finite. Alignment and overlap rules as for
+ * sketch_lut_adam_step.
+ */
+int sketch_lut_sgd_step(float* master, void* lut, int lut_dtype,
+                        const float* grad, float* momentum_buf,
+                        int64_t count,
+                        float lr, float momentum, float weight_decay, float grad_scale,
+                        hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* sketch_status_str(int status);
 

@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     sketch_dequant,
+    sketch_lut_adam_step,
+    sketch_lut_sgd_step,
     sketch_matmul_bwd,
     sketch_matmul_fwd,
     sketch_matmul_fwd_multi,

@@ -37,6 +37,7 @@ _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
 _c_vp = ctypes.c_void_p
 _c_size = ctypes.c_size_t
+_c_f32 = ctypes.c_float
 
 _SIGNATURES = {
     "sketch_matmul_fwd": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
@@ -48,6 +49,10 @@ _SIGNATURES = {
     "sketch_matmul_bwd_workspace": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int]),
     "sketch_dequant": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp]),
     "sketch_unpack_indices": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "sketch_lut_adam_step": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_f32, _c_f32,
+                                      _c_f32, _c_f32, _c_f32, _c_f32, _c_vp]),
+    "sketch_lut_sgd_step": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_f32, _c_f32, _c_f32, _c_f32,
+                                     _c_vp]),
     "sketch_status_str": (ctypes.c_char_p, [_c_int]),
     "sketch_version": (_c_int, []),
 }
@@ -204,3 +209,50 @@ def sketch_unpack_indices(idx_packed, d: int, b: int, stream=None):
     st = lib().sketch_unpack_indices(idx_packed.data_ptr(), n, d, b, out.data_ptr(), _stream_ptr(stream))
     _check("sketch_unpack_indices", st)
     return out
+
+
+def _copy_args(lut):
+    """(pointer, dtype code) of an optional 16-bit compute copy."""
+    if lut is None:
+        return None, SKM_F16
+    return lut.data_ptr(), dtype_code(lut)
+
+
+def _check_f32(*ts):
+    torch = _torch()
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("master tables, gradients and optimizer state are fp32")
+
+
+def sketch_lut_adam_step(master, grad, exp_avg, exp_avg_sq, step: int, lr: float, beta1: float = 0.9,
+                         beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+                         grad_scale: float = 1.0, lut=None, stream=None) -> None:
+    """One fused Adam(W) step on fp32 master tables; writes the 16-bit copy `lut` if given."""
+    _require_device(master, grad, exp_avg, exp_avg_sq, lut)
+    _check_f32(master, grad, exp_avg, exp_avg_sq)
+    count = master.numel()
+    for t in (grad, exp_avg, exp_avg_sq, lut):
+        if t is not None and t.numel() != count:
+            raise ValueError("all buffers must have the master's number of entries")
+    lp, ldt = _copy_args(lut)
+    st = lib().sketch_lut_adam_step(master.data_ptr(), lp, ldt, grad.data_ptr(), exp_avg.data_ptr(),
+                                    exp_avg_sq.data_ptr(), count, step, lr, beta1, beta2, eps, weight_decay,
+                                    grad_scale, _stream_ptr(stream))
+    _check("sketch_lut_adam_step", st)
+
+
+def sketch_lut_sgd_step(master, grad, lr: float, momentum: float = 0.0, weight_decay: float = 0.0,
+                        grad_scale: float = 1.0, momentum_buf=None, lut=None, stream=None) -> None:
+    """One fused SGD step on fp32 master tables; writes the 16-bit copy `lut` if given."""
+    _require_device(master, grad, momentum_buf, lut)
+    _check_f32(master, grad, momentum_buf)
+    count = master.numel()
+    for t in (grad, momentum_buf, lut):
+        if t is not None and t.numel() != count:
+            raise ValueError("all buffers must have the master's number of entries")
+    lp, ldt = _copy_args(lut)
+    st = lib().sketch_lut_sgd_step(master.data_ptr(), lp, ldt, grad.data_ptr(),
+                                   momentum_buf.data_ptr() if momentum_buf is not None else None, count, lr,
+                                   momentum, weight_decay, grad_scale, _stream_ptr(stream))
+    _check("sketch_lut_sgd_step", st)

@@ -2,6 +2,8 @@
 // The formulas, layouts and error rules are documented in sketch_matmul.h.
 #include "sketch_matmul.h"
 
+#include <cmath>
+
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -47,6 +49,9 @@ bool overlap(Range a, Range b) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? SKM_OK : SKM_EHIP; }
+
+// finite and at least lo
+bool finite_in(float v, float lo) { return std::isfinite(v) && v >= lo; }
 
 }  // namespace
 
@@ -189,6 +194,65 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
   }
   if (dLUT) return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, stream));
   return SKM_OK;
+}
+
+int sketch_lut_adam_step(float* master, void* lut, int lut_dtype, const float* grad, float* exp_avg,
+                         float* exp_avg_sq, int64_t count, int64_t step, float lr, float beta1, float beta2,
+                         float eps, float weight_decay, float grad_scale, hipStream_t stream) {
+  if (count < 0 || step < 1) return SKM_EINVAL;
+  if (!finite_in(lr, 0.f) || !finite_in(eps, 0.f) || !finite_in(weight_decay, 0.f) || !std::isfinite(grad_scale))
+    return SKM_EINVAL;
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f)) return SKM_EINVAL;
+  if (lut && lut_dtype != SKM_F16 && lut_dtype != SKM_BF16) return SKM_EUNSUPPORTED;
+  if (count == 0) return SKM_OK;
+  if (!master || !grad || !exp_avg || !exp_avg_sq) return SKM_EINVAL;
+  if (!aligned16(master) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      (lut && !aligned16(lut)))
+    return SKM_EALIGN;
+  const Range w[4] = {{master, count * 4}, {exp_avg, count * 4}, {exp_avg_sq, count * 4}, {lut, count * 2}};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(w[i], {grad, count * 4})) return SKM_EALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(w[i], w[j])) return SKM_EALIAS;
+  }
+  // bias corrections in double on the host, handed to the kernel in fp32
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0)) return SKM_EINVAL;
+  skm::AdamArgs a;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.one_minus_beta1 = (float)(1.0 - (double)beta1);
+  a.one_minus_beta2 = (float)(1.0 - (double)beta2);
+  a.eps = eps;
+  a.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  a.step_size = (float)((double)lr / bc1);
+  a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  a.grad_scale = grad_scale;
+  return status_of(skm::launch_lut_adam(master, lut, lut_dtype, grad, exp_avg, exp_avg_sq, count, a, stream));
+}
+
+int sketch_lut_sgd_step(float* master, void* lut, int lut_dtype, const float* grad, float* momentum_buf,
+                        int64_t count, float lr, float momentum, float weight_decay, float grad_scale,
+                        hipStream_t stream) {
+  if (count < 0) return SKM_EINVAL;
+  if (!finite_in(lr, 0.f) || !finite_in(momentum, 0.f) || !finite_in(weight_decay, 0.f) ||
+      !std::isfinite(grad_scale))
+    return SKM_EINVAL;
+  if (lut && lut_dtype != SKM_F16 && lut_dtype != SKM_BF16) return SKM_EUNSUPPORTED;
+  if (count == 0) return SKM_OK;
+  if (!master || !grad || (momentum != 0.f && !momentum_buf)) return SKM_EINVAL;
+  float* buf = momentum != 0.f ? momentum_buf : nullptr;
+  if (!aligned16(master) || !aligned16(grad) || (buf && !aligned16(buf)) || (lut && !aligned16(lut)))
+    return SKM_EALIGN;
+  const Range w[3] = {{master, count * 4}, {buf, count * 4}, {lut, count * 2}};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(w[i], {grad, count * 4})) return SKM_EALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(w[i], w[j])) return SKM_EALIAS;
+  }
+  const skm::SgdArgs a{lr, momentum, weight_decay, grad_scale};
+  return status_of(skm::launch_lut_sgd(master, lut, lut_dtype, grad, buf, count, a, stream));
 }
 
 }  // extern "C"

@@ -58,4 +58,22 @@ hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, cons
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
                             float* dLUT, int accumulate, hipStream_t s);
 
+// fused table optimizer steps (fp32 master, optional 16-bit compute copy;
+// lut == nullptr skips the copy)
+struct AdamArgs {
+  float beta1, beta2, one_minus_beta1, one_minus_beta2;
+  float eps;
+  float decay;         // 1 - lr * weight_decay (decoupled decay)
+  float step_size;     // lr / (1 - beta1^step)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^step)
+  float grad_scale;
+};
+struct SgdArgs {
+  float lr, momentum, weight_decay, grad_scale;
+};
+hipError_t launch_lut_adam(float* master, void* lut, int lut_dtype, const float* grad, float* exp_avg,
+                           float* exp_avg_sq, int64_t count, const AdamArgs& a, hipStream_t s);
+hipError_t launch_lut_sgd(float* master, void* lut, int lut_dtype, const float* grad, float* buf, int64_t count,
+                          const SgdArgs& a, hipStream_t s);
+
 }  // namespace skm

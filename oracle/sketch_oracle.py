@@ -37,6 +37,14 @@ Efficient LLM Adaptation" (called *Sketch to Adapt* below).
   tasks; token t then uses table set s(t): ``Y[t, i] = sum_j X[t, j]
   W_{s(t)}[i, j]``.
 
+* Fine-tuning updates only the tables (SpaLLM, section 2.3); the pages list
+  the learning rates tried (SpaLLM, appendix B.1, Table 7) but name no
+  optimizer. ``adam_step`` follows Adam as Kingma & Ba state it (their
+  Algorithm 1: moment estimates, bias correction, step) with the decoupled
+  weight decay of Loshchilov & Hutter (AdamW); ``sgd_step`` is gradient descent
+  with heavy-ball momentum and an L2 term added to the gradient. Both work on
+  fp32 master tables in the library; here they are carried in float64.
+
 Readings where the pages leave a step open (listed with the design notes):
 the packed bit order is little-endian (field j at bits b*j .. b*j+b-1 of the
 row's byte stream, LSB first); gradients of shared entries are summed, as the
@@ -176,6 +184,47 @@ def backward_dlut(dY: np.ndarray, X: np.ndarray, idx_packed: np.ndarray, b: int,
 # ---------------------------------------------------------------------------
 # scoring
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# optimizer steps on the tables (textbook rules; the pages name none)
+# ---------------------------------------------------------------------------
+
+def adam_step(master: np.ndarray, grad: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray, step: int,
+              lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+              grad_scale: float = 1.0):
+    """One Adam step with decoupled weight decay; returns (master, exp_avg, exp_avg_sq) as new float64 arrays.
+
+    Kingma & Ba, Algorithm 1: m <- beta1 m + (1 - beta1) g; v <- beta2 v + (1 - beta2) g^2;
+    m_hat = m / (1 - beta1^t); v_hat = v / (1 - beta2^t); theta <- theta - lr m_hat / (sqrt(v_hat) + eps).
+    The decay shrinks theta by (1 - lr * weight_decay) before the step (Loshchilov & Hutter).
+    """
+    p = np.asarray(master, dtype=np.float64)
+    g = np.asarray(grad, dtype=np.float64) * grad_scale
+    m = beta1 * np.asarray(exp_avg, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(exp_avg_sq, dtype=np.float64) + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** step)
+    v_hat = v / (1.0 - beta2 ** step)
+    p = p * (1.0 - lr * weight_decay)
+    p = p - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return p, m, v
+
+
+def sgd_step(master: np.ndarray, grad: np.ndarray, lr: float, momentum: float = 0.0, weight_decay: float = 0.0,
+             grad_scale: float = 1.0, momentum_buf=None):
+    """One SGD step; returns (master, momentum_buf) as new float64 arrays (buf None without momentum).
+
+    g = grad * grad_scale + weight_decay * theta; with momentum, buf <- momentum * buf + g and the step
+    uses buf (a zero buffer before the first step makes the first step use g itself); theta <- theta - lr g.
+    """
+    p = np.asarray(master, dtype=np.float64)
+    g = np.asarray(grad, dtype=np.float64) * grad_scale + weight_decay * p
+    buf = None
+    if momentum != 0.0:
+        prev = np.zeros_like(p) if momentum_buf is None else np.asarray(momentum_buf, dtype=np.float64)
+        buf = momentum * prev + g
+        g = buf
+    return p - lr * g, buf
+
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """max |got - ref| / max |ref| (0 when both are all zero)."""

@@ -21,7 +21,12 @@ module, or a copy with a planted mistake) and raises ``AssertionError`` when
 * several table sets over one mapping (SpaLLM section 2.3, multiple
   adapters): the identity mapping with per-set values 1, 2, -1 scales each
   token by its set's value; per-set dense cases give the textbook product with
-  the token's own matrix; a token's output ignores the sets it does not use.
+  the token's own matrix; a token's output ignores the sets it does not use;
+* the table optimizer steps: torch.optim.AdamW and torch.optim.SGD (float64
+  on the CPU, an independent implementation of the same textbook rules) over
+  several steps; Adam's closed form under a constant gradient (bias correction
+  makes every step move by lr * g / (|g| + eps)); Adam's invariance when the
+  gradient and eps are scaled together.
 """
 from __future__ import annotations
 
@@ -341,10 +346,74 @@ def pin_multi_unused_sets(o):
     assert np.array_equal(Y2[:2], Y[:2]) and not np.allclose(Y2[2], Y[2])
 
 
+def _opt_inputs(seed, count=257):
+    rng = np.random.default_rng(seed)
+    p0 = rng.normal(0.0, 0.02, count)
+    grads = [rng.normal(0.0, 1.0, count) * 10.0 ** rng.uniform(-3, 1, count) for _ in range(6)]
+    return p0, grads
+
+
+def pin_adam_vs_torch(o):
+    import torch
+    for wd, scale in ((0.0, 1.0), (0.05, 1.0), (0.01, 0.125)):
+        p0, grads = _opt_inputs(11)
+        prm = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float64))
+        opt = torch.optim.AdamW([prm], lr=3e-3, betas=(0.8, 0.95), eps=1e-6, weight_decay=wd, foreach=False)
+        p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+        for t, g in enumerate(grads, start=1):
+            prm.grad = torch.tensor(g * scale, dtype=torch.float64)
+            opt.step()
+            p, m, v = o.adam_step(p, g, m, v, t, 3e-3, 0.8, 0.95, 1e-6, wd, scale)
+            ref = prm.detach().numpy()
+            assert np.allclose(p, ref, rtol=1e-12, atol=1e-15), (wd, scale, t)
+            st = opt.state[prm]
+            assert np.allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=0)
+            assert np.allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=0)
+
+
+def pin_adam_constant_gradient(o):
+    # with zero initial moments and a constant gradient the bias-corrected
+    # moments are exactly g and g^2, so every step is lr * g / (|g| + eps)
+    g = np.array([3.0, -0.5, 1e-3, 0.0, -2e2])
+    lr, eps = 1e-2, 1e-4
+    p, m, v = np.zeros_like(g), np.zeros_like(g), np.zeros_like(g)
+    for t in range(1, 8):
+        p, m, v = o.adam_step(p, g, m, v, t, lr, 0.9, 0.999, eps)
+        assert np.allclose(p, -t * lr * g / (np.abs(g) + eps), rtol=1e-9, atol=1e-15), t
+
+
+def pin_adam_scale_invariance(o):
+    # scaling the gradient and eps by s scales both moments' square roots by s
+    # and leaves the step unchanged
+    p0, grads = _opt_inputs(12, 64)
+    s = 1024.0
+    a = (p0.copy(), np.zeros_like(p0), np.zeros_like(p0))
+    b = (p0.copy(), np.zeros_like(p0), np.zeros_like(p0))
+    for t, g in enumerate(grads, start=1):
+        a = o.adam_step(*a[:1], g, a[1], a[2], t, 1e-3, 0.9, 0.99, 1e-3)
+        b = o.adam_step(*b[:1], g * s, b[1], b[2], t, 1e-3, 0.9, 0.99, 1e-3 * s)
+        assert np.allclose(a[0], b[0], rtol=1e-10, atol=1e-15), t
+
+
+def pin_sgd_vs_torch(o):
+    import torch
+    for mom, wd, scale in ((0.0, 0.0, 1.0), (0.9, 0.0, 1.0), (0.9, 0.01, 0.5), (0.0, 0.02, 2.0)):
+        p0, grads = _opt_inputs(13)
+        prm = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float64))
+        opt = torch.optim.SGD([prm], lr=0.05, momentum=mom, weight_decay=wd, foreach=False)
+        p, buf = p0.copy(), None
+        for g in grads:
+            prm.grad = torch.tensor(g * scale, dtype=torch.float64)
+            opt.step()
+            p, buf = o.sgd_step(p, g, 0.05, mom, wd, scale, buf)
+            assert np.allclose(p, prm.detach().numpy(), rtol=1e-12, atol=1e-15), (mom, wd)
+
+
 ALL_PINS = [
     pin_bitstream_golden, pin_unpack_bigint, pin_unpack_exhaustive_b3,
     pin_identity, pin_dense_special_case, pin_dequant_elementwise,
     pin_forward_binned, pin_permutation_invariance,
     pin_finite_difference, pin_bins_partition_group, pin_adjoint, pin_histogram,
     pin_loop_vs_bincount, pin_multi_identity_sets, pin_multi_dense, pin_multi_unused_sets,
+    pin_adam_vs_torch, pin_adam_constant_gradient, pin_adam_scale_invariance, pin_sgd_vs_torch,
 ]

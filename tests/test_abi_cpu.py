@@ -23,7 +23,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert {"sketch_matmul_fwd", "sketch_matmul_fwd_multi", "sketch_matmul_bwd", "sketch_matmul_bwd_workspace", "sketch_dequant",
-            "sketch_unpack_indices", "sketch_status_str", "sketch_version"} <= set(names)
+            "sketch_unpack_indices", "sketch_status_str", "sketch_version", "sketch_lut_adam_step",
+            "sketch_lut_sgd_step"} <= set(names)
     for nme in names:
         assert hasattr(lib, nme), nme
 
@@ -97,6 +98,47 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, dt=0) == EUNSUP
     assert bwd(lib, dX=A) == EALIAS
     assert bwd(lib, dL=0x70000000) == EALIAS          # dX and dLUT overlap
+
+
+def adam(lib, p=A, lut=B_, ldt=1, g=C, m1=Dp, m2=0x70000000, count=1000, step=1, lr=1e-3, b1=0.9, b2=0.999,
+         eps=1e-8, wd=0.0, gs=1.0):
+    return lib.sketch_lut_adam_step(p, lut, ldt, g, m1, m2, count, step, lr, b1, b2, eps, wd, gs, None)
+
+
+def sgd(lib, p=A, lut=B_, ldt=1, g=C, buf=Dp, count=1000, lr=1e-2, mom=0.9, wd=0.0, gs=1.0):
+    return lib.sketch_lut_sgd_step(p, lut, ldt, g, buf, count, lr, mom, wd, gs, None)
+
+
+def test_adam_step_rejects_bad_arguments(lib):
+    assert adam(lib, count=-1) == EINVAL
+    assert adam(lib, step=0) == EINVAL
+    assert adam(lib, lr=-1.0) == EINVAL
+    assert adam(lib, lr=float("nan")) == EINVAL
+    assert adam(lib, b1=1.0) == EINVAL
+    assert adam(lib, b2=-0.1) == EINVAL
+    assert adam(lib, eps=float("inf")) == EINVAL
+    assert adam(lib, gs=float("nan")) == EINVAL
+    assert adam(lib, ldt=0) == EUNSUP                  # the compute copy is 16-bit
+    assert adam(lib, m1=0) == EINVAL
+    assert adam(lib, g=0) == EINVAL
+    assert adam(lib, m2=0x70000008) == EALIGN
+    assert adam(lib, lut=B_ + 2) == EALIGN
+    assert adam(lib, m1=A + 3984) == EALIAS            # first moment over the master's last entries
+    assert adam(lib, lut=C) == EALIAS                  # copy over the gradient
+    assert adam(lib, count=0, p=0, g=0, m1=0, m2=0) == 0
+    assert adam(lib, b1=0.0, b2=0.0, count=0) == 0
+
+
+def test_sgd_step_rejects_bad_arguments(lib):
+    assert sgd(lib, count=-1) == EINVAL
+    assert sgd(lib, mom=-0.5) == EINVAL
+    assert sgd(lib, wd=float("nan")) == EINVAL
+    assert sgd(lib, buf=0) == EINVAL                   # momentum needs its buffer
+    assert sgd(lib, ldt=2, lut=B_ + 8) == EALIGN
+    assert sgd(lib, ldt=7) == EUNSUP
+    assert sgd(lib, buf=A) == EALIAS
+    assert sgd(lib, g=A + 16) == EALIAS
+    assert sgd(lib, count=0, p=0, g=0) == 0
 
 
 def test_dequant_and_unpack_reject(lib):

@@ -34,6 +34,16 @@ MUTATIONS = {
                           "W = dequantize(idx_packed, luts[0], d, b, gpr)"),
     "multi_set_of_next_token": ("W = dequantize(idx_packed, luts[int(lut_set[t])], d, b, gpr)",
                                 "W = dequantize(idx_packed, luts[int(lut_set[(t + 1) % m])], d, b, gpr)"),
+    "adam_no_bias_correction": ("m_hat = m / (1.0 - beta1 ** step)", "m_hat = m"),
+    "adam_bias_correction_power": ("v_hat = v / (1.0 - beta2 ** step)", "v_hat = v / (1.0 - beta2 ** (step + 1))"),
+    "adam_swapped_betas": ("m = beta1 * np.asarray(exp_avg, dtype=np.float64) + (1.0 - beta1) * g",
+                           "m = beta2 * np.asarray(exp_avg, dtype=np.float64) + (1.0 - beta2) * g"),
+    "adam_eps_inside_sqrt": ("p = p - lr * m_hat / (np.sqrt(v_hat) + eps)", "p = p - lr * m_hat / np.sqrt(v_hat + eps)"),
+    "adam_coupled_decay": ("p = p * (1.0 - lr * weight_decay)", "g = g + weight_decay * p"),
+    "adam_grad_scale_ignored": ("g = np.asarray(grad, dtype=np.float64) * grad_scale\n    m =",
+                                "g = np.asarray(grad, dtype=np.float64)\n    m ="),
+    "sgd_dampened_momentum": ("buf = momentum * prev + g", "buf = momentum * prev + (1.0 - momentum) * g"),
+    "sgd_decay_sign": ("* grad_scale + weight_decay * p", "* grad_scale - weight_decay * p"),
     "dlut_overwrite": ("out[i, g[j], idx[i, j]] += dW[i, j]", "out[i, g[j], idx[i, j]] = dW[i, j]"),
     "dlut_average": (
         "out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)",
