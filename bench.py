@@ -10,7 +10,8 @@ HBM peak. Every timed launch reads a different copy of the indices and tables
 The same JSON line carries the other measured parts of the hot path (16-token
 forward, the 7B MLP at 2 and 3 bits, decode with one table set per token over
 one index stream, 70B-shaped decode and prefill GEMM, the 7B decoder-layer
-fine-tuning step, the fused table optimizer steps and a grouped q/k/v decode)
+fine-tuning step, the fused table optimizer steps and a grouped q/k/v decode,
+LLaMA-2-13B decode at one group per row, the backward at 2 and 3 bits)
 and the CPU oracle timed on this host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,dense,copy "
+                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,13b,bwdlowbit,dense,copy "
                          "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
@@ -71,7 +72,7 @@ class Rotation:
         return self.idx[k], self.lut[k]
 
 
-def time_launches(torch, launch, steps, warmup):
+def time_launches(torch, launch, steps, warmup, launches_per_step=1):
     """GPU time (ms) of `steps` back-to-back launches, from HIP events on the launch stream.
 
     The stream is held by a spin kernel while the host enqueues every timed
@@ -83,7 +84,7 @@ def time_launches(torch, launch, steps, warmup):
         launch()
     torch.cuda.synchronize()
     first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(SPIN_CYCLES_PER_LAUNCH * steps))
+    torch.cuda._sleep(int(SPIN_CYCLES_PER_LAUNCH * steps * launches_per_step))
     first.record(stream)
     for _ in range(steps):
         launch()
@@ -150,7 +151,7 @@ def bench_multi(torch, skm, steps, warmup):
             for s in range(n_sets):
                 skm.sketch_matmul_fwd(Xs[s], i, l[s], b, w.gpr, out=Ys[s])
 
-        total_sep = time_launches(torch, per_set, steps, warmup)
+        total_sep = time_launches(torch, per_set, steps, warmup, launches_per_step=n_sets)
         nbytes = (shape.n * shape.d * b // 8 + n_sets * shape.n * w.gpr * (1 << b) * 2 + m * shape.d * 2
                   + m * shape.n * 2)
         ms, ms_sep = total / steps, total_sep / steps
@@ -218,7 +219,7 @@ def bench_glue(torch, skm, steps, warmup):
         i, l = rot3.next()
         skm.sketch_matmul_fwd(X, i, l, 4, w.gpr, out=Y3)
 
-    ms3 = time_launches(torch, three, steps, warmup) / steps
+    ms3 = time_launches(torch, three, steps, warmup, launches_per_step=3) / steps
     msg = time_launches(torch, grouped, steps, warmup) / steps
     nbytes = 3 * wl.algorithmic_bytes_fwd(shape.n, shape.d, 4, w.gpr, 1, 2, 2)
     out["decode_qkv_7b_m1"] = {"ms_three_launches": ms3, "ms_grouped": msg, "speedup": ms3 / msg,
@@ -246,7 +247,7 @@ def bench_finetune(torch, skm, steps, warmup):
             skm.sketch_matmul_fwd(p["X"], p["idx"], p["lut"], 4, w.gpr, out=p["Y"])
             skm.sketch_matmul_bwd(p["dY"], p["X"], p["idx"], p["lut"], 4, w.gpr, dlut_out=p["dL"])
 
-    total = time_launches(torch, step, steps, warmup)
+    total = time_launches(torch, step, steps, warmup, launches_per_step=2 * len(projs))
     flops = sum(3 * wl.flops_pass(p["s"].n, p["s"].d, m) for p in projs)
     ms = total / steps
     # per-pass split, timed the same way on the largest projection (gate)
@@ -265,6 +266,77 @@ def bench_finetune(torch, skm, steps, warmup):
                             "dlut_TFLOPs": fg / (t_dl * 1e-3) / 1e12, "fwd_ms": t_fwd, "dx_ms": t_dx,
                             "dlut_ms": t_dl},
     }
+
+
+def bench_13b(torch, skm, steps, warmup):
+    """LLaMA-2-13B decode at 4-bit indices and one group per row (the decode-efficiency comparison's second
+    model): each projection shape at m = 1, and one token through the sketched projections of all 40
+    layers (distinct weights per layer; q/k/v and gate/up as grouped launches)."""
+    from lut_sketched_matmul_amd import workloads as wl
+    w = wl.LLAMA2_13B_DECODE
+    out = {}
+    for s_ in w.shapes:
+        r = bench_fwd(torch, skm, w, s_, 4, 1, steps, warmup)
+        r["frac_hbm_peak"] = r["GBps"] / HBM_PEAK_GBS
+        out[f"{s_.name}_m1"] = r
+    layers = 40
+    sh = {s_.name: s_ for s_ in w.shapes}
+    t_attn, t_up, t_down = (w.make(sh[k], 4, 1) for k in ("qkvo", "gate_up", "down"))
+    X = dev(torch, t_attn["X"], w.x_dtype)
+    Xm = torch.empty((1, sh["gate_up"].n), dtype=X.dtype, device="cuda:0")   # input of the down projection
+    Xm.copy_(dev(torch, t_down["X"], w.x_dtype))
+    base = {
+        "qkv": (dev(torch, t_attn["idx_packed"], "u8").repeat(3, 1), dev(torch, t_attn["lut"], w.lut_dtype).repeat(3, 1, 1)),
+        "o": (dev(torch, t_attn["idx_packed"], "u8"), dev(torch, t_attn["lut"], w.lut_dtype)),
+        "gate_up": (dev(torch, t_up["idx_packed"], "u8").repeat(2, 1), dev(torch, t_up["lut"], w.lut_dtype).repeat(2, 1, 1)),
+        "down": (dev(torch, t_down["idx_packed"], "u8"), dev(torch, t_down["lut"], w.lut_dtype)),
+    }
+    mats = [{k: (i.clone(), l.clone()) for k, (i, l) in base.items()} for _ in range(layers)]
+    outs = {k: torch.empty((1, i.shape[0]), dtype=X.dtype, device="cuda:0") for k, (i, _) in base.items()}
+    ins = {"qkv": X, "o": X, "gate_up": X, "down": Xm}
+
+    def token():
+        for L in mats:
+            for k, (i, l) in L.items():
+                skm.sketch_matmul_fwd(ins[k], i, l, 4, w.gpr, out=outs[k])
+
+    tok_steps = max(3, steps // 20)
+    ms = time_launches(torch, token, tok_steps, max(1, warmup // 10), launches_per_step=4 * layers) / tok_steps
+    nbytes = sum(wl.algorithmic_bytes_fwd(i.shape[0], ins[k].shape[1], 4, w.gpr, 1, 2, 2)
+                 for k, (i, _) in base.items()) * layers
+    out["token_all_40_layers"] = {"launches": 4 * layers, "ms_per_token": ms, "bytes": nbytes,
+                                  "GBps": nbytes / (ms * 1e-3) / 1e9,
+                                  "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del mats
+    return out
+
+
+def bench_bwd_lowbit(torch, skm, steps, warmup):
+    """Forward, dX and dLUT at 2- and 3-bit indices on the 7B gate and down projections (m = 8192)."""
+    from lut_sketched_matmul_amd import workloads as wl
+    w = wl.LLAMA2_7B_FINETUNE_LOWBIT
+    m = w.tokens[0]
+    out = {}
+    for s_ in w.shapes:
+        for b in w.bits:
+            t = w.make(s_, b, m)
+            X, dY = dev(torch, t["X"], w.x_dtype), dev(torch, t["dY"], w.x_dtype)
+            idx, lut = dev(torch, t["idx_packed"], "u8"), dev(torch, t["lut"], w.lut_dtype)
+            Y = torch.empty((m, s_.n), dtype=X.dtype, device="cuda:0")
+            dL = torch.empty((s_.n, w.gpr, 1 << b), dtype=torch.float32, device="cuda:0")
+            del t
+            t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(X, idx, lut, b, w.gpr, out=Y),
+                                  steps, warmup) / steps
+            t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, need_dlut=False),
+                                 steps, warmup) / steps
+            t_dl = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, need_dx=False,
+                                                                       dlut_out=dL), steps, warmup) / steps
+            f = wl.flops_pass(s_.n, s_.d, m)
+            out[f"{s_.name}_{s_.n}x{s_.d}_b{b}"] = {
+                "fwd_ms": t_fwd, "dx_ms": t_dx, "dlut_ms": t_dl,
+                "fwd_TFLOPs": f / (t_fwd * 1e-3) / 1e12, "dx_TFLOPs": f / (t_dx * 1e-3) / 1e12,
+                "dlut_TFLOPs": f / (t_dl * 1e-3) / 1e12}
+    return out
 
 
 def bench_dense_reference(torch, steps, warmup):
@@ -346,7 +418,7 @@ def main():
     skm.lib()
     want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "multilut",
                                                                    "decode70b", "prefill", "finetune", "glue",
-                                                                   "dense", "copy"}
+                                                                   "13b", "bwdlowbit", "dense", "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -398,6 +470,18 @@ def main():
         ft = bench_finetune(torch, skm, big_steps, big_warm)
         parts["finetune_7b_layer"] = ft
         log(f"fine-tune step 7B layer m=8192: {ft['ms_per_step']:.2f} ms, {ft['TFLOPs']:.0f} TFLOP/s")
+    if "13b" in want:
+        r13 = bench_13b(torch, skm, args.steps, args.warmup)
+        parts["decode_13b_gpr1"] = r13
+        tk = r13["token_all_40_layers"]
+        log("13B decode gpr=1 m=1: " + ", ".join(f"{k} {v['ms_per_launch'] * 1e3:.1f} us {v['GBps']:.0f} GB/s"
+                                                 for k, v in r13.items() if k != "token_all_40_layers")
+            + f"; one token through 40 layers: {tk['ms_per_token']:.3f} ms, {tk['GBps']:.0f} GB/s")
+    if "bwdlowbit" in want:
+        rb = bench_bwd_lowbit(torch, skm, big_steps, big_warm)
+        parts["finetune_lowbit_7b_m8192"] = rb
+        log("7B b=2/3 m=8192 fwd/dX/dLUT TFLOP/s: " + ", ".join(
+            f"{k} {v['fwd_TFLOPs']:.0f}/{v['dx_TFLOPs']:.0f}/{v['dlut_TFLOPs']:.0f}" for k, v in rb.items()))
     if "glue" in want:
         gl = bench_glue(torch, skm, args.steps, args.warmup)
         parts["finetune_glue"] = gl

@@ -3,8 +3,8 @@
 Each workload is a list of weight shapes (n rows = output features, d columns =
 input features) sketched with b-bit indices and ``gpr`` groups per row, the
 token counts m it runs at, the storage dtypes and the normal distributions its
-tensors are drawn from. Shapes follow the public LLaMA-2-7B / LLaMA-3-70B model
-configs; every tensor is drawn by :mod:`lut_sketched_matmul_amd.synthetic`
+tensors are drawn from. Shapes follow the public LLaMA-2-7B / 13B / LLaMA-3-70B
+model configs (LLaMA-2-13B: hidden 5120, MLP 13824); every tensor is drawn by :mod:`lut_sketched_matmul_amd.synthetic`
 under a name ``"<workload>/<shape>/<tensor>"``.
 """
 from __future__ import annotations
@@ -101,7 +101,24 @@ LLAMA2_7B_FINETUNE = Workload(
     notes="one decoder layer's seven projections: forward + dX + dLUT, fp32 gradients",
 )
 
-ALL: List[Workload] = [TINY, LLAMA2_7B_ATTN, LLAMA2_7B_MLP_LOWBIT, LLAMA3_70B_MLP, LLAMA2_7B_FINETUNE]
+LLAMA2_13B_DECODE = Workload(
+    name="llama2-13b-decode-gpr1",
+    shapes=(Shape("qkvo", 5120, 5120), Shape("gate_up", 13824, 5120), Shape("down", 5120, 13824)),
+    bits=(4,), gpr=1, lut_dtype="f16", lut_sigma=0.02, x_dtype="f16",
+    tokens=(1, 16), backward=False,
+    notes="the second model of the decode-efficiency comparison: 4-bit indices, one group per row",
+)
+
+LLAMA2_7B_FINETUNE_LOWBIT = Workload(
+    name="llama2-7b-finetune-lowbit",
+    shapes=(Shape("gate", 11008, 4096), Shape("down", 4096, 11008)),
+    bits=(2, 3), gpr=8, lut_dtype="f16", lut_sigma=0.02, x_dtype="bf16",
+    tokens=(8192,), backward=True, dy_sigma=1e-2,
+    notes="forward, dX and dLUT at 2- and 3-bit indices (m = 8192)",
+)
+
+ALL: List[Workload] = [TINY, LLAMA2_7B_ATTN, LLAMA2_7B_MLP_LOWBIT, LLAMA3_70B_MLP, LLAMA2_7B_FINETUNE,
+                       LLAMA2_13B_DECODE, LLAMA2_7B_FINETUNE_LOWBIT]
 BY_NAME = {w.name: w for w in ALL}
 
 

@@ -174,7 +174,8 @@ def _workload_rows(n, seed):
     return np.unique(rows)
 
 
-@pytest.mark.parametrize("wname", [wl.LLAMA2_7B_ATTN.name, wl.LLAMA2_7B_MLP_LOWBIT.name, wl.LLAMA3_70B_MLP.name])
+@pytest.mark.parametrize("wname", [wl.LLAMA2_7B_ATTN.name, wl.LLAMA2_7B_MLP_LOWBIT.name, wl.LLAMA3_70B_MLP.name,
+                                   wl.LLAMA2_13B_DECODE.name])
 def test_fwd_workloads(wname):
     """Every (shape, b, m) of the forward workloads at full size; sampled rows."""
     w = wl.BY_NAME[wname]
@@ -351,26 +352,29 @@ def test_bwd_accumulate_and_deterministic(m):
     assert np.allclose(acc, base.astype(np.float64) + a1[1], rtol=0, atol=1e-6 * max(1.0, np.abs(a1[1]).max()))
 
 
-def test_finetune_workload_sampled():
+@pytest.mark.parametrize("wname,b", [(wl.LLAMA2_7B_FINETUNE.name, 4), (wl.LLAMA2_7B_FINETUNE_LOWBIT.name, 2),
+                                     (wl.LLAMA2_7B_FINETUNE_LOWBIT.name, 3)])
+def test_finetune_workload_sampled(wname, b):
     """The 7B decoder layer's projections at full size (m = 8192): sampled outputs."""
-    w = wl.LLAMA2_7B_FINETUNE
-    r = np.random.default_rng(11)
-    for s in (w.shapes[0], w.shapes[4], w.shapes[6]):   # q, gate, down
-        t = w.make(s, 4, 8192)
+    w = wl.BY_NAME[wname]
+    r = np.random.default_rng(11 + b)
+    shapes = (w.shapes[0], w.shapes[4], w.shapes[6]) if b == 4 else w.shapes   # q, gate, down
+    for s in shapes:
+        t = w.make(s, b, 8192)
         X64 = syn.to_float64(t["X"], w.x_dtype)
         dY64 = syn.to_float64(t["dY"], w.x_dtype)
         L64 = syn.to_float64(t["lut"], w.lut_dtype)
         gi, gl = to_dev(t["idx_packed"], "u8"), to_dev(t["lut"], w.lut_dtype)
         gx, gdy = to_dev(t["X"], w.x_dtype), to_dev(t["dY"], w.x_dtype)
-        Y = to_f64(skm().sketch_matmul_fwd(gx, gi, gl, 4, w.gpr))
-        dX, dL = skm().sketch_matmul_bwd(gdy, gx, gi, gl, 4, w.gpr)
+        Y = to_f64(skm().sketch_matmul_fwd(gx, gi, gl, b, w.gpr))
+        dX, dL = skm().sketch_matmul_bwd(gdy, gx, gi, gl, b, w.gpr)
         dX, dL = to_f64(dX), to_f64(dL)
         rows = np.unique(np.concatenate([[0, s.n - 1], r.choice(s.n, 256, replace=False)]))
         cols = np.unique(np.concatenate([[0, s.d - 1], r.choice(s.d, 256, replace=False)]))
         toks = np.unique(np.concatenate([[0, 8191], r.choice(8192, 512, replace=False)]))
-        want_y = oracle.forward(X64[toks], t["idx_packed"][rows], L64[rows], 4, w.gpr)
+        want_y = oracle.forward(X64[toks], t["idx_packed"][rows], L64[rows], b, w.gpr)
         assert oracle.rel_err(Y[np.ix_(toks, rows)], want_y) <= w.tol, s.name
-        W = oracle.dequantize(t["idx_packed"], L64, s.d, 4, w.gpr)
+        W = oracle.dequantize(t["idx_packed"], L64, s.d, b, w.gpr)
         assert oracle.rel_err(dX[np.ix_(toks, cols)], dY64[toks] @ W[:, cols]) <= w.tol, s.name
-        want_dl = oracle.backward_dlut(dY64[:, rows], X64, t["idx_packed"][rows], 4, w.gpr)
+        want_dl = oracle.backward_dlut(dY64[:, rows], X64, t["idx_packed"][rows], b, w.gpr)
         assert oracle.rel_err(dL[rows], want_dl) <= w.tol, s.name
