@@ -45,6 +45,18 @@ Efficient LLM Adaptation" (called *Sketch to Adapt* below).
   with heavy-ball momentum and an L2 term added to the gradient. Both work on
   fp32 master tables in the library; here they are carried in float64.
 
+* Sketch construction (SpaLLM, section 2.2, "Weighted Lloyd's algorithm ..."
+  and "Learning the sketching matrix"; Sketch to Adapt, reply to Concern 1):
+  with H = X^T X from sample inputs X of the layer, the table of each (row,
+  group) holds the k centroids of Lloyd's algorithm over the group's weights,
+  each weight counted with weight 1 / [H^-1]_jj of its column; then the
+  columns of the row are mapped one at a time, in order, to the nearest table
+  entry, and the error of each mapped weight is spread over the columns not
+  yet mapped by the update of Frantar et al. (GPTQ): with H^-1 = U^T U (U upper
+  triangular), err = (w_j - q_j) / U_jj and w_{j'} -= err * U_{j j'} for
+  j' > j. ``hessian_factor``, ``column_weights``, ``weighted_lloyd`` and
+  ``map_error_compensated`` follow these steps.
+
 Readings where the pages leave a step open (listed with the design notes):
 the packed bit order is little-endian (field j at bits b*j .. b*j+b-1 of the
 row's byte stream, LSB first); gradients of shared entries are summed, as the
@@ -184,6 +196,89 @@ def backward_dlut(dY: np.ndarray, X: np.ndarray, idx_packed: np.ndarray, b: int,
 # ---------------------------------------------------------------------------
 # scoring
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# sketch construction (the step before the path)
+# ---------------------------------------------------------------------------
+
+def hessian_factor(Xs: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """Upper-triangular U with U^T U = (X^T X + damp * mean(diag) * I)^-1, float64 ``[d][d]``.
+
+    X^T X of the sample inputs ``Xs`` ``[s][d]``; the damping term keeps it invertible (the pages do not
+    say; 1 % of the mean diagonal is GPTQ's choice).
+    """
+    X = np.asarray(Xs, dtype=np.float64)
+    H = X.T @ X
+    H = H + damp * np.mean(np.diag(H)) * np.eye(H.shape[0])
+    Hinv = np.linalg.inv(H)
+    L = np.linalg.cholesky(Hinv)      # Hinv = L L^T
+    return L.T
+
+
+def column_weights(U: np.ndarray) -> np.ndarray:
+    """1 / [H^-1]_jj for every column, from the factor U (H^-1 = U^T U, so [H^-1]_jj = sum_k U_kj^2)."""
+    U = np.asarray(U, dtype=np.float64)
+    return 1.0 / np.sum(U * U, axis=0)
+
+
+def lloyd_init(x: np.ndarray, k: int) -> np.ndarray:
+    """k starting centroids spread evenly over [min x, max x] (cell midpoints)."""
+    lo, hi = float(np.min(x)), float(np.max(x))
+    return lo + (np.arange(k, dtype=np.float64) + 0.5) * ((hi - lo) / k)
+
+
+def lloyd_group(x: np.ndarray, wt: np.ndarray, k: int, iters: int):
+    """Weighted Lloyd's algorithm on one group: (centroids, iterations run).
+
+    Each iteration assigns every value to its nearest centroid (ties to the lower index) and moves every
+    centroid to the weighted mean of its values; a centroid with no values stays. Stops after ``iters``
+    iterations or when the centroids no longer change.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    wt = np.asarray(wt, dtype=np.float64)
+    c = lloyd_init(x, k)
+    for it in range(iters):
+        a = np.argmin(np.abs(x[:, None] - c[None, :]), axis=1)
+        sw = np.bincount(a, weights=wt, minlength=k)
+        swx = np.bincount(a, weights=wt * x, minlength=k)
+        new = np.where(sw > 0, swx / np.where(sw > 0, sw, 1.0), c)
+        if np.array_equal(new, c):
+            return c, it
+        c = new
+    return c, iters
+
+
+def weighted_lloyd(W: np.ndarray, h: np.ndarray, gpr: int, k: int, iters: int) -> np.ndarray:
+    """Tables ``[n][gpr][k]``: weighted Lloyd centroids of every (row, group); column j weighs h[j]."""
+    W = np.asarray(W, dtype=np.float64)
+    n, d = W.shape
+    G = d // gpr
+    out = np.empty((n, gpr, k), dtype=np.float64)
+    for i in range(n):
+        for g in range(gpr):
+            out[i, g], _ = lloyd_group(W[i, g * G:(g + 1) * G], h[g * G:(g + 1) * G], k, iters)
+    return out
+
+
+def map_error_compensated(W: np.ndarray, U: np.ndarray, lut: np.ndarray, gpr: int) -> np.ndarray:
+    """Indices ``[n][d]``: columns in order, each weight to its nearest table entry (ties to the lower
+    index) after the errors of the columns before it were spread by the update err = (w_j - q_j) / U_jj,
+    w_{j'} -= err * U_{j j'} (j' > j)."""
+    w = np.array(W, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    lut = np.asarray(lut, dtype=np.float64)
+    n, d = w.shape
+    G = d // gpr
+    rows = np.arange(n)
+    idx = np.empty((n, d), dtype=np.int64)
+    for j in range(d):
+        t = lut[:, j // G, :]
+        a = np.argmin(np.abs(w[:, j:j + 1] - t), axis=1)
+        idx[:, j] = a
+        err = (w[:, j] - t[rows, a]) / U[j, j]
+        w[:, j + 1:] -= err[:, None] * U[j, j + 1:][None, :]
+    return idx
+
 
 # ---------------------------------------------------------------------------
 # optimizer steps on the tables (textbook rules; the pages name none)

@@ -26,7 +26,16 @@ module, or a copy with a planted mistake) and raises ``AssertionError`` when
   on the CPU, an independent implementation of the same textbook rules) over
   several steps; Adam's closed form under a constant gradient (bias correction
   makes every step move by lr * g / (|g| + eps)); Adam's invariance when the
-  gradient and eps are scaled together.
+  gradient and eps are scaled together;
+* sketch construction: scikit-learn's KMeans (Lloyd, with sample weights and
+  the same starting centroids) for the weighted Lloyd step; hand-worked
+  groups (the starting centroids, a weighted two-cluster case, an empty
+  cluster); the objective never increasing; the factor of the damped inverse
+  Hessian checked by multiplication; the column weights against the
+  diagonal of an explicitly inverted Hessian; the mapping with U = I (plain
+  nearest rounding), with tables that hold every weight exactly, and against
+  the closed-form optimal compensation (the free weights that minimise the
+  quadratic loss given the columns already mapped, solved from H directly).
 """
 from __future__ import annotations
 
@@ -409,6 +418,117 @@ def pin_sgd_vs_torch(o):
             assert np.allclose(p, prm.detach().numpy(), rtol=1e-12, atol=1e-15), (mom, wd)
 
 
+def _own_init(x, k):
+    # written here independently of the oracle: cell midpoints of k equal cells over [min, max]
+    lo, hi = float(np.min(x)), float(np.max(x))
+    step = (hi - lo) / k
+    return np.array([lo + step * (r + 0.5) for r in range(k)])
+
+
+def pin_lloyd_worked(o):
+    # starting centroids: [0, 8] in 4 cells -> 1, 3, 5, 7
+    assert np.allclose(o.lloyd_init(np.array([8.0, 0.0, 3.0]), 4), [1.0, 3.0, 5.0, 7.0], rtol=0, atol=1e-12)
+    # weighted two clusters: start 3, 9 -> {0, 1} and {10, 12}; weighted means 0.75 and 11
+    x4, w4 = np.array([0.0, 1.0, 10.0, 12.0]), np.array([1.0, 3.0, 1.0, 1.0])
+    for iters, want in ((0, [3.0, 9.0]), (1, [0.75, 11.0]), (20, [0.75, 11.0])):
+        c, _ = o.lloyd_group(x4, w4, 2, iters)
+        assert np.allclose(c, want, rtol=0, atol=1e-12), (iters, c)
+    # an empty cluster keeps its centroid: start 5/3, 5, 25/3; the middle one gets no value
+    c, _ = o.lloyd_group(np.array([0.0, 0.1, 9.9, 10.0]), np.ones(4), 3, 20)
+    assert np.allclose(c, [0.05, 5.0, 9.95], rtol=0, atol=1e-12), c
+
+
+def pin_lloyd_vs_sklearn(o):
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(21)
+    for k, G in ((4, 64), (8, 256), (16, 512)):
+        for trial in range(3):
+            x = rng.standard_normal(G) * 0.02
+            wt = np.exp(rng.uniform(-3, 3, G))
+            init = _own_init(x, k)
+            km = KMeans(n_clusters=k, init=init.reshape(-1, 1), n_init=1, max_iter=300, tol=0.0,
+                        algorithm="lloyd").fit(x.reshape(-1, 1), sample_weight=wt)
+            if len(np.unique(km.labels_)) < k:
+                continue          # scikit-learn moves empty clusters; the pin uses inputs without any
+            c, _ = o.lloyd_group(x, wt, k, 300)
+            assert np.allclose(np.sort(c), np.sort(km.cluster_centers_.ravel()), rtol=1e-9, atol=1e-12), (k, trial)
+            for it in (1, 2, 3):       # the same number of iterations
+                km = KMeans(n_clusters=k, init=init.reshape(-1, 1), n_init=1, max_iter=it, tol=0.0,
+                            algorithm="lloyd").fit(x.reshape(-1, 1), sample_weight=wt)
+                c, _ = o.lloyd_group(x, wt, k, it)
+                assert np.allclose(c, km.cluster_centers_.ravel(), rtol=1e-9, atol=1e-12), (k, trial, it)
+
+
+def pin_lloyd_monotone(o):
+    rng = np.random.default_rng(22)
+    x, wt = rng.standard_normal(300), np.exp(rng.uniform(-2, 2, 300))
+    prev = np.inf
+    for it in range(12):
+        c, _ = o.lloyd_group(x, wt, 8, it)
+        obj = float(np.sum(wt * np.min((x[:, None] - c[None, :]) ** 2, axis=1)))
+        assert obj <= prev * (1 + 1e-12), (it, obj, prev)
+        prev = obj
+
+
+def _calib(seed, s, d):
+    rng = np.random.default_rng(seed)
+    mix = rng.standard_normal((d, d)) / np.sqrt(d) + np.eye(d)
+    return rng.standard_normal((s, d)) @ mix          # correlated columns
+
+
+def pin_hessian_factor(o):
+    Xs = _calib(23, 64, 24)
+    U = o.hessian_factor(Xs, 0.01)
+    H = Xs.T @ Xs
+    H = H + 0.01 * np.mean(np.diag(H)) * np.eye(24)
+    assert np.allclose(np.tril(U, -1), 0.0)
+    assert np.allclose(U.T @ U @ H, np.eye(24), atol=1e-9)
+    assert np.allclose(o.column_weights(U), 1.0 / np.diag(np.linalg.inv(H)), rtol=1e-9)
+
+
+def pin_map_identity_factor(o):
+    rng = np.random.default_rng(24)
+    n, d, gpr, k = 6, 64, 2, 8
+    W = rng.standard_normal((n, d))
+    lut = np.sort(rng.standard_normal((n, gpr, k)), axis=2)
+    idx = o.map_error_compensated(W, np.eye(d), lut, gpr)
+    G = d // gpr
+    for i in range(n):
+        for j in range(d):
+            t = lut[i, j // G]
+            assert idx[i, j] == int(np.argmin(np.abs(W[i, j] - t)))
+
+
+def pin_map_exact_tables(o):
+    rng = np.random.default_rng(25)
+    n, d, gpr, k = 5, 48, 3, 4
+    lut = rng.standard_normal((n, gpr, k))
+    want = rng.integers(0, k, (n, d))
+    W = lut[np.arange(n)[:, None], (np.arange(d) // (d // gpr))[None, :], want]
+    U = o.hessian_factor(_calib(26, 80, d), 0.01)
+    assert np.array_equal(o.map_error_compensated(W, U, lut, gpr), want)
+
+
+def pin_map_closed_form(o):
+    """After columns 0..j-1 are fixed at their table values, the compensated weights are the minimisers of
+    (w - w0)^T H (w - w0) over the free columns; column j's entry must be the one nearest that optimum."""
+    rng = np.random.default_rng(27)
+    n, d, gpr, k = 4, 8, 2, 4
+    Xs = _calib(28, 40, d)
+    U = o.hessian_factor(Xs, 0.01)
+    H = np.linalg.inv(U.T @ U)
+    W = rng.standard_normal((n, d))
+    lut = rng.standard_normal((n, gpr, k))
+    idx = o.map_error_compensated(W, U, lut, gpr)
+    G = d // gpr
+    for i in range(n):
+        q = lut[i, np.arange(d) // G, idx[i]]
+        for j in range(d):
+            Q, F = np.arange(j), np.arange(j, d)
+            wf = W[i, F] - np.linalg.solve(H[np.ix_(F, F)], H[np.ix_(F, Q)] @ (q[Q] - W[i, Q]))
+            assert idx[i, j] == int(np.argmin(np.abs(wf[0] - lut[i, j // G]))), (i, j)
+
+
 ALL_PINS = [
     pin_bitstream_golden, pin_unpack_bigint, pin_unpack_exhaustive_b3,
     pin_identity, pin_dense_special_case, pin_dequant_elementwise,
@@ -416,4 +536,6 @@ ALL_PINS = [
     pin_finite_difference, pin_bins_partition_group, pin_adjoint, pin_histogram,
     pin_loop_vs_bincount, pin_multi_identity_sets, pin_multi_dense, pin_multi_unused_sets,
     pin_adam_vs_torch, pin_adam_constant_gradient, pin_adam_scale_invariance, pin_sgd_vs_torch,
+    pin_lloyd_worked, pin_lloyd_vs_sklearn, pin_lloyd_monotone, pin_hessian_factor, pin_map_identity_factor,
+    pin_map_exact_tables, pin_map_closed_form,
 ]

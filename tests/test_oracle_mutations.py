@@ -44,6 +44,20 @@ MUTATIONS = {
                                 "g = np.asarray(grad, dtype=np.float64)\n    m ="),
     "sgd_dampened_momentum": ("buf = momentum * prev + g", "buf = momentum * prev + (1.0 - momentum) * g"),
     "sgd_decay_sign": ("* grad_scale + weight_decay * p", "* grad_scale - weight_decay * p"),
+    "lloyd_unweighted_mean": ("swx = np.bincount(a, weights=wt * x, minlength=k)",
+                              "swx = np.bincount(a, weights=x, minlength=k) * (sw / np.maximum(np.bincount(a, minlength=k), 1))"),
+    "lloyd_init_edges": ("(np.arange(k, dtype=np.float64) + 0.5)", "(np.arange(k, dtype=np.float64) + 1.0)"),
+    "lloyd_empty_to_zero": ("new = np.where(sw > 0, swx / np.where(sw > 0, sw, 1.0), c)",
+                            "new = np.where(sw > 0, swx / np.where(sw > 0, sw, 1.0), 0.0)"),
+    "lloyd_one_step_short": ("    for it in range(iters):\n        a = np.argmin",
+                             "    for it in range(max(iters - 1, 0)):\n        a = np.argmin"),
+    "map_no_division": ("err = (w[:, j] - t[rows, a]) / U[j, j]", "err = (w[:, j] - t[rows, a])"),
+    "map_sign": ("w[:, j + 1:] -= err[:, None] * U[j, j + 1:][None, :]",
+                 "w[:, j + 1:] += err[:, None] * U[j, j + 1:][None, :]"),
+    "map_transposed_factor": ("w[:, j + 1:] -= err[:, None] * U[j, j + 1:][None, :]",
+                              "w[:, j + 1:] -= err[:, None] * U[j + 1:, j][None, :]"),
+    "column_weights_rows": ("return 1.0 / np.sum(U * U, axis=0)", "return 1.0 / np.sum(U * U, axis=1)"),
+    "hessian_not_inverted": ("Hinv = np.linalg.inv(H)", "Hinv = H"),
     "dlut_overwrite": ("out[i, g[j], idx[i, j]] += dW[i, j]", "out[i, g[j], idx[i, j]] = dW[i, j]"),
     "dlut_average": (
         "out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)",
