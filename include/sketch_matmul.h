@@ -158,6 +158,49 @@ int sketch_unpack_indices(const uint8_t* idx_packed, int64_t n, int64_t d, int b
                           uint8_t* idx, hipStream_t stream);
 
 /*
+ * Sketch construction, the step before the matmul (SpaLLM section 2.2,
+ * "Weighted Lloyd's algorithm for learning sketched parameters" and
+ * "Learning the sketching matrix"; Sketch to Adapt, reply to Concern 1).
+ * From a layer's dense weights W [n][d] fp32 and sample inputs X_s [s][d] of
+ * the layer, with H = X_s^T X_s (damped so that it is invertible; the caller
+ * chooses the damping) and the upper-triangular factor U of its inverse,
+ * H^-1 = U^T U ([d][d] fp32, row-major; entries below the diagonal are not
+ * read):
+ *   1. sketch_column_weights: h[j] = 1 / [H^-1]_jj = 1 / sum_{k<=j} U[k][j]^2
+ *   2. sketch_lloyd: the table of each (row i, group g) holds the 2^b
+ *      centroids of weighted Lloyd's algorithm over W[i][j], j in g, weight
+ *      h[j]. Start: centroid r at lo + (r + 1/2) (hi - lo) / 2^b, lo and hi
+ *      the group's smallest and largest weight. Each iteration assigns every
+ *      weight to its nearest centroid (ties to the lower index) and moves
+ *      each centroid to the weighted mean of its weights (a centroid with no
+ *      weights stays); at most `iters` iterations, fewer when the centroids
+ *      stop changing. Written to lut [n][gpr][2^b] in lut_dtype (F32, F16 or
+ *      BF16, rounded to nearest even).
+ *   3. sketch_map: columns j = 0 .. d-1 in order; weight j of every row goes
+ *      to the nearest entry q of its group's table (ties to the lower index,
+ *      the table as stored in lut_dtype) and its error is spread over the
+ *      later columns: err = (w_j - q) / U[j][j], w_j' -= err * U[j][j'] for
+ *      j' > j (the update of Frantar et al., GPTQ). Writes idx_packed in the
+ *      layout above. W is overwritten with the compensated weights (it is the
+ *      working buffer). workspace: sketch_map_workspace(n) bytes.
+ * All arithmetic is fp32. Shapes as for the matmul (b in {2,3,4}, d % gpr ==
+ * 0, (d / gpr) % 32 == 0); d <= 2^20, and n <= 2^22 for sketch_map. Pointers
+ * 16-byte aligned; outputs must
+ * not overlap inputs (SKM_EALIAS).
+ */
+int sketch_column_weights(const float* U, int64_t d, float* h, hipStream_t stream);
+
+int sketch_lloyd(const float* W, const float* h, int64_t n, int64_t d, int b, int gpr, int iters,
+                 void* lut, int lut_dtype, hipStream_t stream);
+
+size_t sketch_map_workspace(int64_t n);
+
+int sketch_map(float* W, const float* U, const void* lut, int lut_dtype,
+               int64_t n, int64_t d, int b, int gpr,
+               uint8_t* idx_packed, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/*
  * Fused optimizer steps for the trainable tables (SpaLLM section 2.3: only the
  * table values are fine-tuned; the mapping stays frozen). The pages give the
  * learning rates searched (SpaLLM appendix B.1, Table 7) but no optimizer;

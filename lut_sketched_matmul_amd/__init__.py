@@ -11,9 +11,12 @@ from ._lib import (  # noqa: F401
     SketchError,
     header_functions,
     lib,
+    sketch_column_weights,
     sketch_dequant,
+    sketch_lloyd,
     sketch_lut_adam_step,
     sketch_lut_sgd_step,
+    sketch_map,
     sketch_matmul_bwd,
     sketch_matmul_fwd,
     sketch_matmul_fwd_multi,

@@ -53,6 +53,11 @@ _SIGNATURES = {
                                       _c_f32, _c_f32, _c_f32, _c_f32, _c_vp]),
     "sketch_lut_sgd_step": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_f32, _c_f32, _c_f32, _c_f32,
                                      _c_vp]),
+    "sketch_column_weights": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp]),
+    "sketch_lloyd": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_int, _c_vp]),
+    "sketch_map_workspace": (_c_size, [_c_i64]),
+    "sketch_map": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_size,
+                            _c_vp]),
     "sketch_status_str": (ctypes.c_char_p, [_c_int]),
     "sketch_version": (_c_int, []),
 }
@@ -256,3 +261,46 @@ def sketch_lut_sgd_step(master, grad, lr: float, momentum: float = 0.0, weight_d
                                    momentum_buf.data_ptr() if momentum_buf is not None else None, count, lr,
                                    momentum, weight_decay, grad_scale, _stream_ptr(stream))
     _check("sketch_lut_sgd_step", st)
+
+
+def sketch_column_weights(U, stream=None):
+    """h[j] = 1 / [H^-1]_jj from the upper factor U (H^-1 = U^T U), fp32 [d]."""
+    torch = _torch()
+    _require_device(U)
+    _check_f32(U)
+    d = U.shape[0]
+    h = torch.empty(d, dtype=torch.float32, device=U.device)
+    _check("sketch_column_weights", lib().sketch_column_weights(U.data_ptr(), d, h.data_ptr(), _stream_ptr(stream)))
+    return h
+
+
+def sketch_lloyd(W, h, b: int, gpr: int, iters: int, lut_dtype=None, out=None, stream=None):
+    """Weighted Lloyd tables [n, gpr, 2^b] (fp32 unless lut_dtype / out say otherwise)."""
+    torch = _torch()
+    _require_device(W, h, out)
+    _check_f32(W, h)
+    n, d = W.shape
+    if out is None:
+        out = torch.empty((n, gpr, 1 << b), dtype=lut_dtype or torch.float32, device=W.device)
+    st = lib().sketch_lloyd(W.data_ptr(), h.data_ptr(), n, d, b, gpr, iters, out.data_ptr(), dtype_code(out),
+                            _stream_ptr(stream))
+    _check("sketch_lloyd", st)
+    return out
+
+
+def sketch_map(W_work, U, lut, b: int, gpr: int, out=None, workspace=None, stream=None):
+    """Error-compensated mapping -> idx_packed [n, d*b/8] uint8. W_work (fp32 [n, d]) is overwritten."""
+    torch = _torch()
+    _require_device(W_work, U, lut, out, workspace)
+    _check_f32(W_work, U)
+    n, d = W_work.shape
+    if out is None:
+        out = torch.empty((n, d * b // 8), dtype=torch.uint8, device=W_work.device)
+    ws = lib().sketch_map_workspace(n)
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=W_work.device)
+    st = lib().sketch_map(W_work.data_ptr(), U.data_ptr(), lut.data_ptr(), dtype_code(lut), n, d, b, gpr,
+                          out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_ptr(stream))
+    _check("sketch_map", st)
+    return out

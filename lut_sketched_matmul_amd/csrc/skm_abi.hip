@@ -196,6 +196,53 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
   return SKM_OK;
 }
 
+int sketch_column_weights(const float* U, int64_t d, float* h, hipStream_t stream) {
+  if (d < 1 || d > (int64_t(1) << 20)) return SKM_EINVAL;
+  if (!U || !h) return SKM_EINVAL;
+  if (!aligned16(U) || !aligned16(h)) return SKM_EALIGN;
+  if (overlap({h, d * 4}, {U, d * d * 4})) return SKM_EALIAS;
+  return status_of(skm::launch_col_weights(U, d, h, stream));
+}
+
+int sketch_lloyd(const float* W, const float* h, int64_t n, int64_t d, int b, int gpr, int iters, void* lut,
+                 int lut_dtype, hipStream_t stream) {
+  int st = check_shape(0, n, d, b, gpr);
+  if (st) return st;
+  if (iters < 0) return SKM_EINVAL;
+  if (!valid_dtype(lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!W || !h || !lut) return SKM_EINVAL;
+  if (!aligned16(W) || !aligned16(h) || !aligned16(lut)) return SKM_EALIGN;
+  const Range o{lut, n * gpr * (int64_t(1) << b) * elem_bytes(lut_dtype)};
+  if (overlap(o, {W, n * d * 4}) || overlap(o, {h, d * 4})) return SKM_EALIAS;
+  const Problem p{0, n, d, b, gpr};
+  return status_of(skm::launch_lloyd(W, h, p, iters, lut, lut_dtype, stream));
+}
+
+size_t sketch_map_workspace(int64_t n) { return n > 0 ? skm::map_workspace_bytes(n) : 0; }
+
+int sketch_map(float* W, const float* U, const void* lut, int lut_dtype, int64_t n, int64_t d, int b, int gpr,
+               uint8_t* idx_packed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(0, n, d, b, gpr);
+  if (st) return st;
+  // the trailing update's grid has ceil(n / 64) rows of blocks
+  if (d > (int64_t(1) << 20) || n > (int64_t(1) << 22)) return SKM_EINVAL;
+  if (!valid_dtype(lut_dtype)) return SKM_EUNSUPPORTED;
+  if (!W || !U || !lut || !idx_packed || !workspace) return SKM_EINVAL;
+  if (!aligned16(W) || !aligned16(U) || !aligned16(lut) || !aligned16(idx_packed) || !aligned16(workspace))
+    return SKM_EALIGN;
+  if (workspace_bytes < skm::map_workspace_bytes(n)) return SKM_EWORKSPACE;
+  const Range w[3] = {{W, n * d * 4}, {idx_packed, n * d * b / 8}, {workspace, (int64_t)skm::map_workspace_bytes(n)}};
+  const Range r[2] = {{U, d * d * 4}, {lut, n * gpr * (int64_t(1) << b) * elem_bytes(lut_dtype)}};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(w[i], r[j])) return SKM_EALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(w[i], w[j])) return SKM_EALIAS;
+  }
+  const Problem p{0, n, d, b, gpr};
+  return status_of(skm::launch_map(W, U, lut, lut_dtype, p, idx_packed, (float*)workspace, stream));
+}
+
 int sketch_lut_adam_step(float* master, void* lut, int lut_dtype, const float* grad, float* exp_avg,
                          float* exp_avg_sq, int64_t count, int64_t step, float lr, float beta1, float beta2,
                          float eps, float weight_decay, float grad_scale, hipStream_t stream) {

@@ -58,6 +58,16 @@ hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, cons
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
                             float* dLUT, int accumulate, hipStream_t s);
 
+// sketch construction: column weights 1 / [H^-1]_jj from the factor U, the
+// weighted Lloyd tables, and the error-compensated mapping (Wc is overwritten;
+// E holds map_workspace_bytes(n))
+hipError_t launch_col_weights(const float* U, int64_t d, float* h, hipStream_t s);
+hipError_t launch_lloyd(const float* W, const float* h, const Problem& p, int iters, void* lut, int lut_dtype,
+                        hipStream_t s);
+size_t map_workspace_bytes(int64_t n);
+hipError_t launch_map(float* Wc, const float* U, const void* lut, int lut_dtype, const Problem& p, uint8_t* idx,
+                      float* E, hipStream_t s);
+
 // fused table optimizer steps (fp32 master, optional 16-bit compute copy;
 // lut == nullptr skips the copy)
 struct AdamArgs {

@@ -1,0 +1,298 @@
+// Sketch construction: the tables and the index stream of a layer from its
+// dense weights and the factor of its damped inverse Hessian.
+//
+// SpaLLM section 2.2 ("Weighted Lloyd's algorithm ...", "Learning the
+// sketching matrix") and the Sketch to Adapt reply to Concern 1:
+//   h_j = 1 / [H^-1]_jj, H^-1 = U^T U (U upper triangular, from the caller)
+//   tables: weighted Lloyd's algorithm over the weights of each (row, group),
+//           weight j counted with h_j, starting from k centroids spread evenly
+//           over [min, max] of the group
+//   indices: columns in order, each weight to its nearest table entry, its
+//           error err = (w_j - q_j) / U_jj spread over the later columns as
+//           w_j' -= err * U_jj' (the update of Frantar et al.)
+//
+// Kernels: k_col_weights (one thread per column); k_lloyd (one wave per
+// (row, group), everything in registers and wave reductions); the mapping in
+// blocks of 64 columns: k_map_block runs the sequential sweep of one block
+// (one thread per row, the block's 64 x 64 part of U in LDS) and writes the
+// packed indices and the block's errors, then k_map_trail applies the block's
+// errors to every later column at once (an fp32 rank-64 update,
+// W[:, j1:] -= E * U[block, j1:]). The sum each weight receives is the
+// sequential one, in another order.
+#include "skm_common.h"
+#include "skm_launch.h"
+
+namespace skm {
+
+namespace {
+
+constexpr int MAP_COLS = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// [H^-1]_jj = sum_{k <= j} U_kj^2 (U is upper triangular)
+__global__ void __launch_bounds__(256) k_col_weights(const float* __restrict__ U, int64_t d, float* __restrict__ h) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  float s = 0.f;
+  for (int64_t k = 0; k <= j; ++k) {
+    const float u = U[k * d + j];
+    s += u * u;
+  }
+  h[j] = 1.f / s;
+}
+
+// one wave per (row, group); K = 2^b centroids
+template <int K, typename TL>
+__global__ void __launch_bounds__(256) k_lloyd(const float* __restrict__ W, const float* __restrict__ h, int64_t n,
+                                                int64_t d, int gpr, int iters, TL* __restrict__ lut) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wg >= n * gpr) return;  // whole waves; no block barriers below
+  const int64_t i = wg / gpr;
+  const int g = (int)(wg % gpr);
+  const int64_t G = d / gpr;
+  const float* x = W + i * d + g * G;
+  const float* hw = h + g * G;
+
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int64_t j = lane; j < G; j += 64) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  float c[K];
+  const float step = (hi - lo) / (float)K;
+#pragma unroll
+  for (int r = 0; r < K; ++r) c[r] = lo + step * ((float)r + 0.5f);
+
+  for (int it = 0; it < iters; ++it) {
+    float sw[K], swx[K];
+#pragma unroll
+    for (int r = 0; r < K; ++r) sw[r] = swx[r] = 0.f;
+    for (int64_t j = lane; j < G; j += 64) {
+      const float v = x[j], wt = hw[j];
+      // nearest centroid, ties to the lower index
+      float best = fabsf(v - c[0]);
+      int a = 0;
+#pragma unroll
+      for (int r = 1; r < K; ++r) {
+        const float dr = fabsf(v - c[r]);
+        if (dr < best) {
+          best = dr;
+          a = r;
+        }
+      }
+      const float wx = wt * v;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        sw[r] += a == r ? wt : 0.f;
+        swx[r] += a == r ? wx : 0.f;
+      }
+    }
+    bool same = true;
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const float s = wave_sum(sw[r]), sx = wave_sum(swx[r]);
+      const float nc = s > 0.f ? sx / s : c[r];  // an empty cluster keeps its centroid
+      same = same && nc == c[r];
+      c[r] = nc;
+    }
+    if (same) break;  // wave-uniform: every lane holds the same sums
+  }
+  if (lane < K) {
+    float v = c[0];
+#pragma unroll
+    for (int r = 1; r < K; ++r) v = lane == r ? c[r] : v;
+    lut[wg * K + lane] = from_f32<TL>(v);
+  }
+}
+
+// One 64-column block of the mapping sweep; one thread per row. Reads the
+// compensated weights Wc[:, j0 : j0 + cols] (all earlier blocks' errors
+// applied), writes the block's packed indices and its errors E [64][n].
+template <int B, typename TL>
+__global__ void __launch_bounds__(64) k_map_block(float* __restrict__ Wc, const float* __restrict__ U,
+                                                   const TL* __restrict__ lut, int64_t n, int64_t d, int gpr,
+                                                   int64_t j0, int cols, uint8_t* __restrict__ idx_packed,
+                                                   float* __restrict__ E) {
+  constexpr int K = 1 << B;
+  __shared__ float ub[MAP_COLS][MAP_COLS + 1];
+  // the block's part of U (zero beyond the last column)
+  for (int e = threadIdx.x; e < MAP_COLS * MAP_COLS; e += 64) {
+    const int r = e / MAP_COLS, cc = e % MAP_COLS;
+    ub[r][cc] = (r < cols && cc < cols) ? U[(j0 + r) * d + j0 + cc] : 0.f;
+  }
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t G = d / gpr;
+  float w[MAP_COLS];
+#pragma unroll
+  for (int c = 0; c < MAP_COLS; ++c) w[c] = c < cols ? Wc[i * d + j0 + c] : 0.f;
+  // the block spans at most two groups, split at a multiple of 32 columns
+  float t0[K], t1[K];
+  const int64_t g0 = j0 / G, g1 = (j0 + 32) / G;
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    t0[r] = to_f32(lut[(i * gpr + g0) * K + r]);
+    t1[r] = to_f32(lut[(i * gpr + (g1 < gpr ? g1 : g0)) * K + r]);
+  }
+  constexpr int WORDS = MAP_COLS * B / 32;
+  uint32_t pk[WORDS];
+#pragma unroll
+  for (int q = 0; q < WORDS; ++q) pk[q] = 0u;
+#pragma unroll
+  for (int c = 0; c < MAP_COLS; ++c) {
+    if (c < cols) {  // uniform
+      float t[K];  // (c is a compile-time index: the select keeps both tables in registers)
+#pragma unroll
+      for (int r = 0; r < K; ++r) t[r] = c < 32 ? t0[r] : t1[r];
+      float best = fabsf(w[c] - t[0]);
+      int a = 0;
+#pragma unroll
+      for (int r = 1; r < K; ++r) {
+        const float dr = fabsf(w[c] - t[r]);
+        if (dr < best) {
+          best = dr;
+          a = r;
+        }
+      }
+      float q = t[0];
+#pragma unroll
+      for (int r = 1; r < K; ++r) q = a == r ? t[r] : q;
+      const float err = (w[c] - q) / ub[c][c];
+      E[c * n + i] = err;
+#pragma unroll
+      for (int c2 = c + 1; c2 < MAP_COLS; ++c2) w[c2] -= err * ub[c][c2];
+      const int p = B * c;
+      pk[p >> 5] |= (uint32_t)a << (p & 31);
+      if ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)a >> (32 - (p & 31));
+    } else {
+      E[c * n + i] = 0.f;
+    }
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(idx_packed + i * (d * B / 8) + j0 * B / 8);
+  const int words = cols * B / 32;
+#pragma unroll
+  for (int q = 0; q < WORDS; ++q)
+    if (q < words) dst[q] = pk[q];
+}
+
+// Wc[:, j1:] -= E^T * U[j0 : j0 + 64, j1:] (E is [64][n]); 64 x 64 output tiles,
+// 4 x 4 outputs per thread
+__global__ void __launch_bounds__(256) k_map_trail(float* __restrict__ Wc, const float* __restrict__ U,
+                                                    const float* __restrict__ E, int64_t n, int64_t d, int64_t j0,
+                                                    int64_t j1) {
+  __shared__ float es[MAP_COLS][MAP_COLS + 4];  // [k][row]
+  __shared__ float us[MAP_COLS][MAP_COLS + 4];  // [k][col]
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = j1 + (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int k = e / 64, a = e % 64;  // error of column j0 + k for row r0 + a (coalesced along a)
+    es[k][a] = r0 + a < n ? E[k * n + r0 + a] : 0.f;
+    const int kk = e / 64, cc = e % 64;  // U row j0 + kk, column c0 + cc
+    us[kk][cc] = c0 + cc < d ? U[(j0 + kk) * d + c0 + cc] : 0.f;
+  }
+  __syncthreads();
+  const int tr = tid / 16, tc = tid % 16;  // rows tr + 16 a, columns 4 tc + b
+  float acc[4][4] = {};
+#pragma unroll 8
+  for (int k = 0; k < MAP_COLS; ++k) {
+    float ev[4], uv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ev[a] = es[k][tr + 16 * a];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) uv[b] = us[k][4 * tc + b];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] += ev[a] * uv[b];
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t r = r0 + tr + 16 * a;
+    if (r >= n) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t c = c0 + 4 * tc + b;
+      if (c < d) Wc[r * d + c] -= acc[a][b];
+    }
+  }
+}
+
+template <int B, typename TL>
+hipError_t map_run(float* Wc, const float* U, const TL* lut, const Problem& p, uint8_t* idx, float* E, hipStream_t s) {
+  for (int64_t j0 = 0; j0 < p.d; j0 += MAP_COLS) {
+    const int cols = (int)(p.d - j0 < MAP_COLS ? p.d - j0 : MAP_COLS);
+    hipLaunchKernelGGL((k_map_block<B, TL>), dim3((unsigned)((p.n + 63) / 64)), dim3(64), 0, s, Wc, U, lut, p.n, p.d,
+                       p.gpr, j0, cols, idx, E);
+    const int64_t j1 = j0 + cols;
+    if (j1 < p.d) {
+      const dim3 grid((unsigned)((p.d - j1 + 63) / 64), (unsigned)((p.n + 63) / 64));
+      hipLaunchKernelGGL(k_map_trail, grid, dim3(256), 0, s, Wc, U, E, p.n, p.d, j0, j1);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename TL>
+hipError_t lloyd_run(const float* W, const float* h, const Problem& p, int iters, TL* lut, hipStream_t s) {
+  const dim3 grid((unsigned)((p.n * p.gpr + 3) / 4));
+  switch (p.b) {
+    case 2: hipLaunchKernelGGL((k_lloyd<4, TL>), grid, dim3(256), 0, s, W, h, p.n, p.d, p.gpr, iters, lut); break;
+    case 3: hipLaunchKernelGGL((k_lloyd<8, TL>), grid, dim3(256), 0, s, W, h, p.n, p.d, p.gpr, iters, lut); break;
+    default: hipLaunchKernelGGL((k_lloyd<16, TL>), grid, dim3(256), 0, s, W, h, p.n, p.d, p.gpr, iters, lut); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_col_weights(const float* U, int64_t d, float* h, hipStream_t s) {
+  hipLaunchKernelGGL(k_col_weights, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, U, d, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_lloyd(const float* W, const float* h, const Problem& p, int iters, void* lut, int lut_dtype,
+                        hipStream_t s) {
+  if (lut_dtype == DT_F32) return lloyd_run<float>(W, h, p, iters, (float*)lut, s);
+  if (lut_dtype == DT_F16) return lloyd_run<half_t>(W, h, p, iters, (half_t*)lut, s);
+  return lloyd_run<bf16_t>(W, h, p, iters, (bf16_t*)lut, s);
+}
+
+size_t map_workspace_bytes(int64_t n) { return (size_t)n * MAP_COLS * sizeof(float); }
+
+template <typename TL>
+hipError_t map_dispatch(float* Wc, const float* U, const TL* lut, const Problem& p, uint8_t* idx, float* E,
+                        hipStream_t s) {
+  switch (p.b) {
+    case 2: return map_run<2, TL>(Wc, U, lut, p, idx, E, s);
+    case 3: return map_run<3, TL>(Wc, U, lut, p, idx, E, s);
+    default: return map_run<4, TL>(Wc, U, lut, p, idx, E, s);
+  }
+}
+
+hipError_t launch_map(float* Wc, const float* U, const void* lut, int lut_dtype, const Problem& p, uint8_t* idx,
+                      float* E, hipStream_t s) {
+  if (lut_dtype == DT_F32) return map_dispatch<float>(Wc, U, (const float*)lut, p, idx, E, s);
+  if (lut_dtype == DT_F16) return map_dispatch<half_t>(Wc, U, (const half_t*)lut, p, idx, E, s);
+  return map_dispatch<bf16_t>(Wc, U, (const bf16_t*)lut, p, idx, E, s);
+}
+
+}  // namespace skm

@@ -24,7 +24,8 @@ def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert {"sketch_matmul_fwd", "sketch_matmul_fwd_multi", "sketch_matmul_bwd", "sketch_matmul_bwd_workspace", "sketch_dequant",
             "sketch_unpack_indices", "sketch_status_str", "sketch_version", "sketch_lut_adam_step",
-            "sketch_lut_sgd_step"} <= set(names)
+            "sketch_lut_sgd_step", "sketch_column_weights", "sketch_lloyd", "sketch_map",
+            "sketch_map_workspace"} <= set(names)
     for nme in names:
         assert hasattr(lib, nme), nme
 
@@ -139,6 +140,33 @@ def test_sgd_step_rejects_bad_arguments(lib):
     assert sgd(lib, buf=A) == EALIAS
     assert sgd(lib, g=A + 16) == EALIAS
     assert sgd(lib, count=0, p=0, g=0) == 0
+
+
+def test_construction_rejects_bad_arguments(lib):
+    assert lib.sketch_column_weights(A, 0, B_, None) == EINVAL
+    assert lib.sketch_column_weights(0, 64, B_, None) == EINVAL
+    assert lib.sketch_column_weights(A, 64, A + 4096, None) == EALIAS      # h inside U (64 x 64 floats)
+    assert lib.sketch_column_weights(A, 64, B_ + 4, None) == EALIGN
+    lloyd = lambda W=A, h=B_, n=64, d=512, b=4, gpr=4, it=10, lut=C, ldt=1: lib.sketch_lloyd(
+        W, h, n, d, b, gpr, it, lut, ldt, None)
+    assert lloyd(b=5) == EINVAL
+    assert lloyd(gpr=3) == EINVAL
+    assert lloyd(it=-1) == EINVAL
+    assert lloyd(ldt=9) == EUNSUP
+    assert lloyd(lut=0) == EINVAL
+    assert lloyd(h=B_ + 8) == EALIGN
+    assert lloyd(lut=A + 1024) == EALIAS
+    ws = lib.sketch_map_workspace(64)
+    assert ws >= 64 * 64 * 4 and lib.sketch_map_workspace(0) == 0
+    mp = lambda W=A, U=B_, lut=C, ldt=1, n=64, d=512, b=4, gpr=4, idx=Dp, w=0x70000000, wsb=ws: lib.sketch_map(
+        W, U, lut, ldt, n, d, b, gpr, idx, w, wsb, None)
+    assert mp(d=48) == EINVAL
+    assert mp(w=0) == EINVAL
+    assert mp(wsb=ws - 1) == EWS
+    assert mp(idx=Dp + 2) == EALIGN
+    assert mp(idx=A + 16) == EALIAS                     # indices over the weights
+    assert mp(w=B_) == EALIAS                           # workspace over U
+    assert mp(ldt=5) == EUNSUP
 
 
 def test_dequant_and_unpack_reject(lib):
