@@ -11,7 +11,8 @@ The same JSON line carries the other measured parts of the hot path (16-token
 forward, the 7B MLP at 2 and 3 bits, decode with one table set per token over
 one index stream, 70B-shaped decode and prefill GEMM, the 7B decoder-layer
 fine-tuning step, the fused table optimizer steps and a grouped q/k/v decode,
-LLaMA-2-13B decode at one group per row, the backward at 2 and 3 bits)
+LLaMA-2-13B decode at one group per row, the backward at 2 and 3 bits, sketch
+construction of a 4096 x 4096 layer)
 and the CPU oracle timed on this host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,13b,bwdlowbit,dense,copy "
+                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,13b,bwdlowbit,construct,"
+                         "dense,copy "
                          "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
@@ -339,6 +341,46 @@ def bench_bwd_lowbit(torch, skm, steps, warmup):
     return out
 
 
+def bench_construct(torch, skm):
+    """Sketching one 4096 x 4096 layer at 4-bit indices and 4 groups per row (the configuration whose
+    sketching time the pages report): factor of the damped inverse Hessian from 2048 sample inputs
+    (torch.linalg), column weights, 30 weighted Lloyd iterations, the mapping sweep."""
+    from lut_sketched_matmul_amd import construct
+    from lut_sketched_matmul_amd import synthetic as syn
+    n = d = 4096
+    b, gpr, iters = 4, 4, 30
+    W = torch.from_numpy(syn.random_normal("bench-construct/W", (n, d), 0.02, "f32")).to("cuda:0")
+    Xs = torch.from_numpy(syn.random_normal("bench-construct/X", (2048, d), 1.0, "f32")).to("cuda:0")
+    Wk = torch.empty_like(W)
+    out = {}
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            r = fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps, r
+
+    out["factor_ms"], U = timed(lambda: construct.hessian_factor(Xs))
+    out["column_weights_ms"], h = timed(lambda: skm.sketch_column_weights(U))
+    out["lloyd_ms"], lut = timed(lambda: skm.sketch_lloyd(W, h, b, gpr, iters, lut_dtype=torch.float16))
+
+    def mapping():
+        Wk.copy_(W)
+        return skm.sketch_map(Wk, U, lut, b, gpr)
+
+    out["map_ms"], _ = timed(mapping)
+    out["total_ms"] = out["factor_ms"] + out["column_weights_ms"] + out["lloyd_ms"] + out["map_ms"]
+    # the mapping's arithmetic: n d^2 multiply-adds of the error spreading (fp32)
+    out["map_TFLOPs"] = 2.0 * n * d * d / 2 / (out["map_ms"] * 1e-3) / 1e12
+    out.update({"n": n, "d": d, "b": b, "gpr": gpr, "lloyd_iters": iters, "samples": 2048})
+    return out
+
+
 def bench_dense_reference(torch, steps, warmup):
     """The vendor dense GEMM (torch.matmul -> hipBLASLt) at the prefill shapes,
     with an already dequantised 16-bit weight: context for the sketched GEMM,
@@ -418,7 +460,7 @@ def main():
     skm.lib()
     want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "multilut",
                                                                    "decode70b", "prefill", "finetune", "glue",
-                                                                   "13b", "bwdlowbit", "dense", "copy"}
+                                                                   "13b", "bwdlowbit", "construct", "dense", "copy"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
@@ -482,6 +524,12 @@ def main():
         parts["finetune_lowbit_7b_m8192"] = rb
         log("7B b=2/3 m=8192 fwd/dX/dLUT TFLOP/s: " + ", ".join(
             f"{k} {v['fwd_TFLOPs']:.0f}/{v['dx_TFLOPs']:.0f}/{v['dlut_TFLOPs']:.0f}" for k, v in rb.items()))
+    if "construct" in want:
+        cs = bench_construct(torch, skm)
+        parts["sketch_construction_4096x4096_b4_gpr4"] = cs
+        log(f"sketch construction 4096x4096 b=4 gpr=4: factor {cs['factor_ms']:.1f} ms, column weights "
+            f"{cs['column_weights_ms']:.2f} ms, Lloyd {cs['lloyd_ms']:.2f} ms, mapping {cs['map_ms']:.2f} ms, "
+            f"total {cs['total_ms']:.1f} ms")
     if "glue" in want:
         gl = bench_glue(torch, skm, args.steps, args.warmup)
         parts["finetune_glue"] = gl

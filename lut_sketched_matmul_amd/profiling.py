@@ -35,6 +35,12 @@ KERNEL_SOURCES = {
              "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
              "lut_sketched_matmul_amd/csrc/skm_gemm_common.h", "lut_sketched_matmul_amd/csrc/skm_gemm.hip",
              "lut_sketched_matmul_amd/csrc/skm_gemm_bwd.hip"],
+    "optim": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
+              "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
+              "lut_sketched_matmul_amd/csrc/skm_optim.hip"],
+    "sketch": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
+               "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
+               "lut_sketched_matmul_amd/csrc/skm_sketch.hip"],
 }
 
 # torch.add(src, 1.0, out=dst) on fp32: reads and writes this many bytes per launch
