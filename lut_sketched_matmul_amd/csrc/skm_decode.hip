@@ -286,11 +286,14 @@ __device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
 // every adapter is a set of tables in the same format over the frozen
 // mapping), token t using set lut_set[t] (clamped into [0, n_sets)). The block
 // takes one pass per set that some token uses, in the order of first use:
-// stage that set's tables, run the slot loop over all the block's weights
+// stage that set's tables (and, with XL, the activations of that set's tokens
+// only, so that a pass stages at most 32768 / d tokens and a set with more
+// takes several passes), run the slot loop over all the block's weights
 // (after the first pass the index words come from the L2), and keep for each
-// output element the result of its token's set. The activations are staged
-// once. Each pass costs the set's tables and one round of table lookups; the
-// index stream is read from memory once.
+// output element the result of its token's pass. Each pass costs the set's
+// tables and one round of table lookups; the index stream is read from memory
+// once. A pass's tables, activations and first index batch are loaded during
+// the pass before it.
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool MULTI>
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
@@ -321,70 +324,138 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const TX* xrow = X + (int64_t)tokc * d;
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const uint32_t xl_base = (uint32_t)gpr * T * 256u;  // byte offset of the staged activations
-  const int64_t xl_elems = (int64_t)m * d;
+  // activation elements staged (MULTI + XL: one pass's tokens)
+  const int64_t xl_elems =
+      (int64_t)((MULTI && XL) ? (m < (int)(DEC_XL_MAX / d) ? m : (int)(DEC_XL_MAX / d)) : m) * d;
   constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
 
-  // MULTI: the set of token t (wave-uniform), and the sets of the four tokens
-  // whose outputs this lane holds (lane l: tokens 4 (l / 16) + r)
-  auto set_of = [&](int tt) -> int {
-    const int v = __builtin_amdgcn_readfirstlane(lut_set[tt]);
-    return v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v);
-  };
-  int lset[4] = {0, 0, 0, 0};
-  int tfirst = 0;  // first token of the set being processed
-  int cur = 0;     // that set
+  // MULTI: the block's passes, worked out once in lanes. A pass covers the
+  // tokens of one set, at most `cap` of them (with XL the pass stages only its
+  // own tokens' activations: cap = min(m, activation elements that fit / d));
+  // sets go in order of first use and a set with more than cap tokens takes
+  // several passes (chunks of cap tokens in token order). Lane t (< m) holds
+  // token t's set and its position in the pass-ordered token list (tokens of
+  // earlier sets first, then by rank within the set); lane p holds pass p's
+  // set, chunk, first list position and token count; lane i holds the token
+  // at list position i.
+  const int cap = (MULTI && XL) ? (m < (int)(DEC_XL_MAX / d) ? m : (int)(DEC_XL_MAX / d)) : m;
+  int tpos = 0, ps_set = 0, ps_start = 0, ps_cnt = 0, sorted_tok = 0, npass = 1;
+  if constexpr (MULTI) {
+    const int tl = lane < m ? lane : m - 1;
+    const int v = lut_set[tl];
+    const int setv = v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v);
+    int rank = 0, ftok = tl;  // rank of token tl in its set; the set's first token
+    for (int u = 0; u < m; ++u) {
+      const int su = __builtin_amdgcn_readlane(setv, u);
+      if (su == setv) {
+        rank += u < tl ? 1 : 0;
+        ftok = u < ftok ? u : ftok;
+      }
+    }
+    int before = 0, count = 0;  // tokens of sets used earlier; tokens of this set
+    for (int u = 0; u < m; ++u) {
+      const int fu = __builtin_amdgcn_readlane(ftok, u);
+      before += fu < ftok ? 1 : 0;
+      count += fu == ftok ? 1 : 0;
+    }
+    tpos = before + rank;
+    const int nch = (lane < m && rank == 0) ? (count + cap - 1) / cap : 0;  // passes of a set, at its first token
+    int pbase = 0;
+    npass = 0;
+    for (int u = 0; u < m; ++u) {
+      const int nu = __builtin_amdgcn_readlane(nch, u);
+      pbase += u < lane ? nu : 0;
+      npass += nu;
+    }
+    for (int u = 0; u < m; ++u) {
+      const int nu = __builtin_amdgcn_readlane(nch, u), bu = __builtin_amdgcn_readlane(pbase, u);
+      if (nu > 0 && lane >= bu && lane < bu + nu) {
+        ps_set = __builtin_amdgcn_readlane(setv, u);
+        const int kc = lane - bu;  // chunk of the set
+        ps_start = __builtin_amdgcn_readlane(before, u) + kc * cap;
+        const int left = __builtin_amdgcn_readlane(count, u) - kc * cap;
+        ps_cnt = left < cap ? left : cap;
+      }
+    }
+    // lane tpos(t) receives t (lanes >= m repeat token m - 1's position and value)
+    sorted_tok = __builtin_amdgcn_ds_permute(tpos * 4, tl);
+  }
+  // the four tokens whose outputs this lane holds (lane l: tokens 4 (l / 16) + r)
+  int lpos[4] = {0, 0, 0, 0};
+  int apos = 0;  // the token of this lane's A row
   if constexpr (MULTI) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = 4 * q + r < m ? 4 * q + r : m - 1;
-      const int v = lut_set[tt];
-      lset[r] = v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v);
-    }
-    cur = set_of(0);
+    for (int r = 0; r < 4; ++r) lpos[r] = __shfl(tpos, 4 * q + r < m ? 4 * q + r : m - 1, 64);
+    apos = __shfl(tpos, tokc, 64);
   }
-  // MULTI: the next set after `cur` in order of first use (-1: none)
-  auto next_set_token = [&](int from) -> int {
-    for (int tt = from + 1; tt < m; ++tt) {
-      const int st = set_of(tt);
-      bool seen = false;
-      for (int u = 0; u < tt && !seen; ++u) seen = set_of(u) == st;
-      if (!seen) return tt;
-    }
-    return -1;
+  int pass = 0;
+  int cur = 0, pstart = 0, pcnt = m;  // this pass: set, first list position, tokens
+  auto load_pass = [&](int pp) {
+    cur = __builtin_amdgcn_readlane(ps_set, pp);
+    pstart = __builtin_amdgcn_readlane(ps_start, pp);
+    pcnt = __builtin_amdgcn_readlane(ps_cnt, pp);
+  };
+  if constexpr (MULTI) load_pass(0);
+  // MULTI + XL: one pass's activation loads into registers, unconditional (a
+  // chunk with no token of the pass re-reads X[0] and is not stored), so the
+  // compiler's load counts stay exact
+  auto stage_src = [&](int c, int st, int cnt, bool& ok) -> const TX* {
+    const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+    const int slot = (int)((uint32_t)e / (uint32_t)d);
+    const int col = (int)(e - (int64_t)slot * d);
+    ok = slot < cnt;
+    const int t = __shfl(sorted_tok, ok ? st + slot : 0, 64);
+    return ok ? X + (int64_t)t * d + col : X;
   };
   f32x4 out = {0.f, 0.f, 0.f, 0.f};
-  bool first = true;
   constexpr int PF = dec_pf<NW>::value;
   SlotRegs<B, TX, PF> R0, R1;
   int64_t s0 = wave;
   TabRegs<B> TR;  // MULTI: after the first pass, loaded during the previous pass
-  while (true) {
-  const int tnext = MULTI ? next_set_token(tfirst) : -1;
-  // ---- prologue: table loads, activation loads (XL), first index loads, then
-  // the LDS stores of the first two (their loads complete first). Later passes
-  // of MULTI find their tables and first index batch already loaded.
-  if (first) tab_load<B, NW, TL>(TR, MULTI ? lut + (int64_t)cur * set_stride : lut, row_ok ? grow : n - 1, gpr, wave);
-  u32x4 xs[XCH];
-  if constexpr (XL) {
-    if (first) {
+  u32x4 xs[XCH];   // MULTI + XL: likewise the pass's activations
+  bool xok[XCH];
+  if constexpr (MULTI) {
+    // the first pass's loads, issued before the loop so that every pass starts
+    // with the same loads in flight, in the same order (tables, activations,
+    // first index batch)
+    tab_load<B, NW, TL>(TR, lut + (int64_t)cur * set_stride, row_ok ? grow : n - 1, gpr, wave);
+    if constexpr (XL) {
 #pragma unroll
-      for (int c = 0; c < XCH; ++c) {
-        const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-        if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
-      }
+      for (int c = 0; c < XCH; ++c) xs[c] = *reinterpret_cast<const u32x4*>(stage_src(c, pstart, pcnt, xok[c]));
+    }
+    load_batch<B, NW, TX, RAGGED, XL, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow);
+  }
+  while (true) {
+  const bool has_next = MULTI && pass + 1 < npass;
+  // ---- prologue: table loads, activation loads (XL), first index loads, then
+  // the LDS stores of the first two (their loads complete first). MULTI passes
+  // find their tables, activations and first index batch loaded.
+  if constexpr (!MULTI) tab_load<B, NW, TL>(TR, lut, row_ok ? grow : n - 1, gpr, wave);
+  if constexpr (XL && !MULTI) {
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
     }
   }
   s0 = wave;
-  if (first) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+  if constexpr (!MULTI) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
-  if constexpr (XL) {
-    if (first) {
+  if constexpr (XL && !MULTI) {
 #pragma unroll
-      for (int c = 0; c < XCH; ++c) {
-        const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-        if (e < xl_elems) {
-          *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
-        }
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (e < xl_elems) {
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+      }
+    }
+  }
+  if constexpr (XL && MULTI) {
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (xok[c]) {
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
       }
     }
   }
@@ -397,12 +468,25 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   __syncthreads();
   // the gathers address the tables with absolute LDS addresses (see gaddr)
   if ((uint32_t)(uintptr_t)smem != 0u) return;
-  const uint32_t xl_row = xl_base + (uint32_t)tokc * (uint32_t)d * 2u;
+  // this lane's A row: its token's staged row (MULTI + XL: the token's slot in
+  // the pass, or slot 0 for a token outside the pass, whose results are not kept)
+  int aslot = tokc;
+  if constexpr (MULTI && XL) {
+    const bool in = apos >= pstart && apos < pstart + pcnt;
+    aslot = in ? apos - pstart : 0;
+  }
+  const uint32_t xl_row = xl_base + (uint32_t)aslot * (uint32_t)d * 2u;
   if constexpr (MULTI) {
-    // the next set's tables (this set's again when none is left: the loads
-    // stay unconditional), in flight while this set is computed
-    const int sn = tnext >= 0 ? set_of(tnext) : cur;
+    // the next pass's tables and activations (this pass's again when none is
+    // left: the loads stay unconditional), in flight while this pass computes
+    const int pn = has_next ? pass + 1 : pass;
+    const int sn = __builtin_amdgcn_readlane(ps_set, pn);
     tab_load<B, NW, TL>(TR, lut + (int64_t)sn * set_stride, row_ok ? grow : n - 1, gpr, wave);
+    if constexpr (XL) {
+      const int stn = __builtin_amdgcn_readlane(ps_start, pn), cnn = __builtin_amdgcn_readlane(ps_cnt, pn);
+#pragma unroll
+      for (int c = 0; c < XCH; ++c) xs[c] = *reinterpret_cast<const u32x4*>(stage_src(c, stn, cnn, xok[c]));
+    }
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -476,14 +560,17 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     break;
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = lset[r] == cur ? acc[r] : out[r];
-    if (tnext < 0) break;
-    tfirst = tnext;
-    cur = set_of(tnext);
-    first = false;
-    // the next pass's first index batch (from the L2), then every wave is done
-    // with this set's tables
+    for (int r = 0; r < 4; ++r) {
+      const bool in = lpos[r] >= pstart && lpos[r] < pstart + pcnt;
+      out[r] = in ? acc[r] : out[r];
+    }
+    // the next pass's first index batch (from the L2), issued before the exit
+    // test so that every path into the next pass has it in flight (after the
+    // last pass it re-reads batch 0, unused); then every wave is done with
+    // this pass's tables
     load_batch<B, NW, TX, RAGGED, XL, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow);
+    if (!has_next) break;
+    load_pass(++pass);
     __syncthreads();
   }
   }  // per-set passes
@@ -523,7 +610,9 @@ struct SetArgs {
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
 hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
                          uint32_t magic, const SetArgs& sa) {
-  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? p.m * p.d : 0);
+  // MULTI + XL stages one pass's tokens: at most min(m, DEC_XL_MAX / d) of them
+  const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
+  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
   // (the LDS limit is raised once per kernel, the first time one needs it)
   if (sa.lut_set) {
@@ -551,7 +640,10 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
 template <int B, int NW, typename TX, typename TL>
 hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
                      uint32_t magic, const SetArgs& sa) {
-  const bool xl = p.m * p.d <= DEC_XL_MAX;
+  // one table set: stage the activations when all m rows fit. Several sets:
+  // each pass stages its own tokens, so it suffices that one row fits (with a
+  // single set in use, the m rows then take several passes)
+  const bool xl = p.m * p.d <= DEC_XL_MAX || (sa.lut_set && sa.n_sets > 1 && p.d <= DEC_XL_MAX);
   if (p.units() % 4 != 0)
     return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic, sa)
               : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic, sa);

@@ -228,6 +228,12 @@ def _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype):
     (3, 4, 33, 1536, [4, 3, 2, 1, 0], 5),
     (4, 1, 20, 512, [1], 2),               # one token, using set 1 only
     (4, 4, 8200, 1152, [0, 1], 2),         # more blocks than the GPU holds at once
+    # more tokens of one set than one pass stages (32768 // d of them): the set
+    # takes several passes
+    (4, 8, 64, 4096, [0] * 12 + [1] * 4, 2),
+    (2, 8, 40, 11008, [0, 0, 0, 1, 0], 2),
+    (4, 4, 33, 16384, [1, 0, 1, 1, 0, 0, 1], 2),
+    (4, 8, 16, 32768, [0, 0, 1], 2),       # one token per pass
 ])
 def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     idx, luts, X = _multi_case(f"multi/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}", n, d, b, gpr, len(sets),
@@ -238,10 +244,12 @@ def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_fwd_multi_one_set_is_fwd(dt):
-    """All tokens on one set: the same numbers as the single-set forward."""
-    b, gpr, n, d, m = 4, 8, 80, 4096, 5
-    idx, luts, X = _multi_case(f"multi1/{dt}", n, d, b, gpr, m, 3, dt, dt)
+@pytest.mark.parametrize("m", [5, 16])
+def test_fwd_multi_one_set_is_fwd(dt, m):
+    """All tokens on one set: the same numbers as the single-set forward (m = 16: the set takes two
+    passes of 8 staged tokens, the single-set kernel reads all 16 from memory)."""
+    b, gpr, n, d = 4, 8, 80, 4096
+    idx, luts, X = _multi_case(f"multi1/{dt}/{m}", n, d, b, gpr, m, 3, dt, dt)
     got = _fwd_multi(idx, luts, X, [1] * m, b, gpr, dt, dt)
     ref = skm().sketch_matmul_fwd(to_dev(X, dt), to_dev(idx, "u8"), to_dev(luts[1], dt), b, gpr)
     assert bool((got == ref).all())
