@@ -85,12 +85,21 @@ def short_name(name: str) -> str:
     m = re.search(r"::(k_[a-z0-9_]+)<([^,>]*)", name)  # already demangled by the profiler
     if m:
         return f"{m.group(1)}<{m.group(2)},...>"
+    m = re.search(r"::(k_[a-z0-9_]+)\(", name)  # demangled, not a template
+    if m:
+        return m.group(1)
     if COPY_KERNEL in name:
         return "torch add (copy reference)"
     return name[:60]
 
 
+# kernels whose launches are reported together whatever their grid size
+MERGE_GRIDS = None
+
+
 def _key(name: str, grid: int, wg: int):
+    if MERGE_GRIDS and re.search(MERGE_GRIDS, short_name(name)):
+        return (name, -1)
     return (name, grid // max(wg, 1))
 
 
@@ -142,7 +151,7 @@ def summarize(stats_dir, pmc_dirs, kernel_regex, family, title, commands, copy_b
     pat = re.compile(kernel_regex)
     mine = sorted((k for k in st if pat.search(k[0])), key=lambda k: (short_name(k[0]), k[1]))
     copy = [k for k in st if COPY_KERNEL in k[0]]
-    label = lambda k: f"{short_name(k[0])} [{k[1]} blocks]"
+    label = lambda k: f"{short_name(k[0])} [{k[1]} blocks]" if k[1] >= 0 else f"{short_name(k[0])} [all grids]"
 
     lines = [f"# {title}", "", "Commands (from the repository root; OUT is any output folder):", "", "```"]
     lines += commands
@@ -250,8 +259,11 @@ def main():
     ap.add_argument("--command", action="append", default=[], help="command line to record (repeatable)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--algorithmic-bytes", type=int, default=None)
+    ap.add_argument("--merge-grids", default=None, help="regex: report these kernels' launches together")
     ap.add_argument("-o", "--out", required=True)
     a = ap.parse_args()
+    global MERGE_GRIDS
+    MERGE_GRIDS = a.merge_grids
     text = summarize(a.stats, a.pmc, a.kernels, a.family, a.title, a.command, a.copy_bytes, a.algorithmic_bytes)
     with open(a.out, "w") as f:
         f.write(text)
