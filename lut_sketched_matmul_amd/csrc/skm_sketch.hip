@@ -44,16 +44,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// [H^-1]_jj = sum_{k <= j} U_kj^2 (U is upper triangular)
+// [H^-1]_jj = sum_{k <= j} U_kj^2 (U is upper triangular). A block takes 64
+// columns; its 4 waves take every 4th row (each lane one column, so a wave
+// reads 256 contiguous bytes per row) and the 4 partial sums meet in LDS.
 __global__ void __launch_bounds__(256) k_col_weights(const float* __restrict__ U, int64_t d, float* __restrict__ h) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= d) return;
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int64_t k = 0; k <= j; ++k) {
-    const float u = U[k * d + j];
-    s += u * u;
-  }
-  h[j] = 1.f / s;
+  if (j < d)
+    for (int64_t k = w; k <= j; k += 4) {
+      const float u = U[k * d + j];
+      s += u * u;
+    }
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && j < d) h[j] = 1.f / (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]);
 }
 
 // one wave per (row, group); K = 2^b centroids
@@ -265,7 +271,7 @@ hipError_t lloyd_run(const float* W, const float* h, const Problem& p, int iters
 }  // namespace
 
 hipError_t launch_col_weights(const float* U, int64_t d, float* h, hipStream_t s) {
-  hipLaunchKernelGGL(k_col_weights, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, U, d, h);
+  hipLaunchKernelGGL(k_col_weights, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, U, d, h);
   return hipGetLastError();
 }
 

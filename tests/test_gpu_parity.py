@@ -234,6 +234,8 @@ def _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype):
     (2, 8, 40, 11008, [0, 0, 0, 1, 0], 2),
     (4, 4, 33, 16384, [1, 0, 1, 1, 0, 0, 1], 2),
     (4, 8, 16, 32768, [0, 0, 1], 2),       # one token per pass
+    (4, 8, 32, 36864, [1, 0, 1], 2),       # no activation staging (one row exceeds it)
+    (3, 4, 24, 4096, [0] * 16, 1),         # one set: all 16 rows read from memory, one pass
 ])
 def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     idx, luts, X = _multi_case(f"multi/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}", n, d, b, gpr, len(sets),
