@@ -102,6 +102,9 @@ def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
     # decode rows of 48 and 80 128-column slots (several slot batches per
     # wave, the last one partial), and rows of one and of two slots
     (4, 4, 40, 6144, 2), (2, 2, 33, 10240, 1), (3, 2, 40, 10240, 16), (4, 1, 21, 128, 3), (2, 1, 18, 256, 5),
+    # just over the activation staging limit (m * d > 32768: activations read
+    # per slot), and a ragged row
+    (4, 8, 40, 4096, 16), (2, 8, 50, 3072, 16), (3, 2, 17, 4096, 12), (4, 8, 70, 4096, 9), (4, 1, 24, 2080, 16),
 ])
 def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
