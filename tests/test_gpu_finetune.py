@@ -249,3 +249,41 @@ def test_training_steps_lockstep(opt):
         moved = float(np.max(np.abs(to_f64(layer.lut_master) - start)))
     assert moved > 0.0
     assert t.equal(layer.idx_packed.cpu(), t.from_numpy(idx))      # the mapping stays frozen
+
+
+def test_training_recovers_tables():
+    """Fine-tuning end to end: the target layer uses the same frozen mapping with other tables, so the
+    tables can be recovered exactly; SGD through the autograd function and the fused optimizer step must
+    bring the loss on fresh random batches down by three orders of magnitude (60 steps, f16)."""
+    t = torch()
+    n, d, b, gpr, m = 128, 512, 4, 4, 32
+    idx = syn.random_packed_indices("recover/idx", n, d, b)
+    target = syn.random_lut("recover/target", n, gpr, b, 0.02, "f16")
+    noise = syn.random_normal("recover/noise", (n, gpr, 1 << b), 0.01, "f32").astype(np.float64)
+    start = syn.to_storage(syn.to_float64(target, "f16") + noise, "f16")
+    gi = to_dev(idx, "u8")
+    layer = ft().SketchedLinear(gi, to_dev(start, "f16"), d, b, gpr)
+    goal = to_dev(target, "f16")
+    opt = ft().LutSGD([layer.lut_master], lr=2.0, grad_scale=1.0 / (m * n))
+    losses = []
+    for step in range(60):
+        X = to_dev(syn.random_normal(f"recover/X{step}", (m, d), 1.0, "f16"), "f16")
+        with t.no_grad():
+            Ystar = skm().sketch_matmul_fwd(X, gi, goal, b, gpr).float()
+        opt.zero_grad()
+        loss = ((layer(X).float() - Ystar) ** 2).sum()
+        loss.backward()
+        opt.step()
+        losses.append(float(loss.detach()))
+    assert losses[-1] < 1e-3 * losses[0], (losses[0], losses[-1])
+    # entries that some columns map to approach the target; an entry no column
+    # maps to gets a zero gradient and keeps its starting value exactly
+    u = oracle.unpack_indices(idx, d, b)
+    uses = np.zeros((n, gpr, 1 << b), dtype=np.int64)
+    np.add.at(uses, (np.arange(n)[:, None], (np.arange(d) // (d // gpr))[None, :], u), 1)
+    got, tgt, st = to_f64(layer.lut_master), syn.to_float64(target, "f16"), syn.to_float64(start, "f16")
+    well = uses >= 4
+    err0 = np.abs(st - tgt)[well].max()
+    err = np.abs(got - tgt)[well].max()
+    assert err < 0.05 * err0, (err0, err)
+    assert np.array_equal(got[uses == 0], st[uses == 0])
