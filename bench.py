@@ -230,7 +230,8 @@ def bench_glue(torch, skm, steps, warmup):
 
 
 def bench_finetune(torch, skm, steps, warmup):
-    """One fine-tuning step of a 7B decoder layer: forward, dX and dLUT of all seven projections."""
+    """One fine-tuning step of a 7B decoder layer: forward, dX and dLUT of all seven projections, then the
+    fused Adam step on their fp32 master tables (which also writes the f16 copies the kernels read)."""
     from lut_sketched_matmul_amd import workloads as wl
     w = wl.LLAMA2_7B_FINETUNE
     m = w.tokens[0]
@@ -242,14 +243,23 @@ def bench_finetune(torch, skm, steps, warmup):
             idx=dev(torch, t["idx_packed"], "u8"), lut=dev(torch, t["lut"], w.lut_dtype),
             Y=torch.empty((m, s.n), dtype=torch.bfloat16, device="cuda:0"),
             dL=torch.empty((s.n, w.gpr, 16), dtype=torch.float32, device="cuda:0")))
+        p = projs[-1]
+        # fp32 master tables and Adam moments; the step refreshes the f16 copy the kernels read
+        p["master"] = p["lut"].float()
+        p["m1"], p["m2"] = torch.zeros_like(p["master"]), torch.zeros_like(p["master"])
         del t
+    it = [0]
 
     def step():
+        it[0] += 1
         for p in projs:
             skm.sketch_matmul_fwd(p["X"], p["idx"], p["lut"], 4, w.gpr, out=p["Y"])
             skm.sketch_matmul_bwd(p["dY"], p["X"], p["idx"], p["lut"], 4, w.gpr, dlut_out=p["dL"])
+        for p in projs:
+            skm.sketch_lut_adam_step(p["master"], p["dL"], p["m1"], p["m2"], it[0], 1e-5, grad_scale=1.0 / m,
+                                     lut=p["lut"])
 
-    total = time_launches(torch, step, steps, warmup, launches_per_step=2 * len(projs))
+    total = time_launches(torch, step, steps, warmup, launches_per_step=3 * len(projs))
     flops = sum(3 * wl.flops_pass(p["s"].n, p["s"].d, m) for p in projs)
     ms = total / steps
     # per-pass split, timed the same way on the largest projection (gate)
