@@ -14,11 +14,12 @@
 // Kernels: k_col_weights (one thread per column); k_lloyd (one wave per
 // (row, group), everything in registers and wave reductions); the mapping in
 // blocks of 64 columns: k_map_block runs the sequential sweep of one block
-// (one thread per row, the block's 64 x 64 part of U in LDS) and writes the
-// packed indices and the block's errors, then k_map_trail applies the block's
-// errors to every later column at once (an fp32 rank-64 update,
-// W[:, j1:] -= E * U[block, j1:]). The sum each weight receives is the
-// sequential one, in another order.
+// (four lanes per row, the block's 64 x 64 part of U in LDS) and writes the
+// packed indices and the block's errors; k_map_trail applies errors to later
+// columns as fp32 rank-k updates (W[:, cols] -= E^T U[rows, cols]), in two
+// levels: each 64-column block's errors to the rest of its 512-column outer
+// block, each outer block's 512 errors to every column after it. The sum each
+// weight receives is the sequential one, in another order.
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -129,106 +130,144 @@ __global__ void __launch_bounds__(256) k_lloyd(const float* __restrict__ W, cons
   }
 }
 
-// One 64-column block of the mapping sweep; one thread per row. Reads the
-// compensated weights Wc[:, j0 : j0 + cols] (all earlier blocks' errors
-// applied), writes the block's packed indices and its errors E [64][n].
+// One 64-column block of the mapping sweep. Four lanes per row (16 rows per
+// wave): lane `sub` of a row holds the row's columns 4 t + sub (t < 16) of the
+// block, so the updates of each step split over the four lanes. Column c is
+// owned by lane c % 4: every lane finds the nearest entry to its own
+// column-(4 (c / 4) + sub) weight, and a quad broadcast (DPP) hands the
+// owner's entry and error to the other three. The error is (w - q) times
+// 1 / U[c][c] (the reciprocals are taken once per block). Reads the compensated weights
+// Wc[:, j0 : j0 + cols] (all earlier blocks' errors applied), writes the
+// block's packed indices and its errors E [64][n]. The block's part of U sits
+// in LDS as [c][sub][t] so a lane's 16 coefficients of a step are contiguous.
+template <int OWN>
+__device__ __forceinline__ float quad_bcast(float v) {
+  constexpr int ctrl = OWN | (OWN << 2) | (OWN << 4) | (OWN << 6);  // quad_perm [OWN, OWN, OWN, OWN]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+template <int OWN>
+__device__ __forceinline__ int quad_bcast_i(int v) {
+  constexpr int ctrl = OWN | (OWN << 2) | (OWN << 4) | (OWN << 6);
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+
+template <int C, int B, int K>
+__device__ __forceinline__ void map_step(float (&w)[16], const float (&t0)[K], const float (&t1)[K],
+                                         const float (*ub)[MAP_COLS], const float* rdiag, int sub, int cols,
+                                         bool row_ok, int64_t n,
+                                         int64_t i, float* __restrict__ E, uint32_t (&pk)[MAP_COLS * B / 32]) {
+  if constexpr (C < MAP_COLS) {
+    constexpr int T = C / 4, OWN = C % 4;
+    if (C < cols) {  // uniform
+      float tv[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) tv[r] = C < 32 ? t0[r] : t1[r];
+      // nearest entry to this lane's weight of column 4 T + sub (ties to the lower index)
+      float best = fabsf(w[T] - tv[0]), q = tv[0];
+      int a = 0;
+#pragma unroll
+      for (int r = 1; r < K; ++r) {
+        const float dr = fabsf(w[T] - tv[r]);
+        const bool lt = dr < best;
+        best = lt ? dr : best;
+        q = lt ? tv[r] : q;
+        a = lt ? r : a;
+      }
+      const float err_l = (w[T] - q) * rdiag[C];
+      const float err = quad_bcast<OWN>(err_l);
+      const int ai = quad_bcast_i<OWN>(a);
+      if (sub == OWN && row_ok) E[C * n + i] = err;
+      const float* u = ub[C] + sub * 16;
+#pragma unroll
+      for (int t2 = T + 1; t2 < 16; ++t2) w[t2] -= err * u[t2];
+      if (sub > OWN) w[T] -= err * u[T];
+      constexpr int p = B * C;
+      pk[p >> 5] |= (uint32_t)ai << (p & 31);
+      if constexpr ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)ai >> (32 - (p & 31));
+    }
+    map_step<C + 1, B, K>(w, t0, t1, ub, rdiag, sub, cols, row_ok, n, i, E, pk);
+  }
+}
+
 template <int B, typename TL>
 __global__ void __launch_bounds__(64) k_map_block(float* __restrict__ Wc, const float* __restrict__ U,
                                                    const TL* __restrict__ lut, int64_t n, int64_t d, int gpr,
                                                    int64_t j0, int cols, uint8_t* __restrict__ idx_packed,
                                                    float* __restrict__ E) {
   constexpr int K = 1 << B;
-  __shared__ float ub[MAP_COLS][MAP_COLS + 1];
-  // the block's part of U (zero beyond the last column)
+  __shared__ float ub[MAP_COLS][MAP_COLS];  // [c][sub * 16 + t] = U[j0 + c][j0 + 4 t + sub]
+  __shared__ float rdiag[MAP_COLS];         // 1 / U[j0 + c][j0 + c] (the steps multiply)
   for (int e = threadIdx.x; e < MAP_COLS * MAP_COLS; e += 64) {
     const int r = e / MAP_COLS, cc = e % MAP_COLS;
-    ub[r][cc] = (r < cols && cc < cols) ? U[(j0 + r) * d + j0 + cc] : 0.f;
+    ub[r][(cc & 3) * 16 + (cc >> 2)] = (r < cols && cc < cols) ? U[(j0 + r) * d + j0 + cc] : 0.f;
   }
+  rdiag[threadIdx.x] = threadIdx.x < cols ? 1.f / U[(j0 + threadIdx.x) * d + j0 + threadIdx.x] : 0.f;
   __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (i >= n) return;
+  const int sub = threadIdx.x & 3;
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 2);
+  const bool row_ok = i < n;  // no early exit: the quad broadcasts need every lane
+  const int64_t ic = row_ok ? i : n - 1;
   const int64_t G = d / gpr;
-  float w[MAP_COLS];
+  float w[16];
 #pragma unroll
-  for (int c = 0; c < MAP_COLS; ++c) w[c] = c < cols ? Wc[i * d + j0 + c] : 0.f;
+  for (int t = 0; t < 16; ++t) {
+    const int col = 4 * t + sub;
+    w[t] = col < cols ? Wc[ic * d + j0 + col] : 0.f;
+  }
   // the block spans at most two groups, split at a multiple of 32 columns
   float t0[K], t1[K];
   const int64_t g0 = j0 / G, g1 = (j0 + 32) / G;
 #pragma unroll
   for (int r = 0; r < K; ++r) {
-    t0[r] = to_f32(lut[(i * gpr + g0) * K + r]);
-    t1[r] = to_f32(lut[(i * gpr + (g1 < gpr ? g1 : g0)) * K + r]);
+    t0[r] = to_f32(lut[(ic * gpr + g0) * K + r]);
+    t1[r] = to_f32(lut[(ic * gpr + (g1 < gpr ? g1 : g0)) * K + r]);
   }
   constexpr int WORDS = MAP_COLS * B / 32;
   uint32_t pk[WORDS];
 #pragma unroll
   for (int q = 0; q < WORDS; ++q) pk[q] = 0u;
+  map_step<0, B, K>(w, t0, t1, ub, rdiag, sub, cols, row_ok, n, i, E, pk);
+  if (sub == 0 && row_ok) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(idx_packed + i * (d * B / 8) + j0 * B / 8);
+    const int words = cols * B / 32;
 #pragma unroll
-  for (int c = 0; c < MAP_COLS; ++c) {
-    if (c < cols) {  // uniform
-      float t[K];  // (c is a compile-time index: the select keeps both tables in registers)
-#pragma unroll
-      for (int r = 0; r < K; ++r) t[r] = c < 32 ? t0[r] : t1[r];
-      float best = fabsf(w[c] - t[0]);
-      int a = 0;
-#pragma unroll
-      for (int r = 1; r < K; ++r) {
-        const float dr = fabsf(w[c] - t[r]);
-        if (dr < best) {
-          best = dr;
-          a = r;
-        }
-      }
-      float q = t[0];
-#pragma unroll
-      for (int r = 1; r < K; ++r) q = a == r ? t[r] : q;
-      const float err = (w[c] - q) / ub[c][c];
-      E[c * n + i] = err;
-#pragma unroll
-      for (int c2 = c + 1; c2 < MAP_COLS; ++c2) w[c2] -= err * ub[c][c2];
-      const int p = B * c;
-      pk[p >> 5] |= (uint32_t)a << (p & 31);
-      if ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)a >> (32 - (p & 31));
-    } else {
-      E[c * n + i] = 0.f;
-    }
+    for (int q = 0; q < WORDS; ++q)
+      if (q < words) dst[q] = pk[q];
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(idx_packed + i * (d * B / 8) + j0 * B / 8);
-  const int words = cols * B / 32;
-#pragma unroll
-  for (int q = 0; q < WORDS; ++q)
-    if (q < words) dst[q] = pk[q];
 }
 
-// Wc[:, j1:] -= E^T * U[j0 : j0 + 64, j1:] (E is [64][n]); 64 x 64 output tiles,
-// 4 x 4 outputs per thread
+// Wc[:, c0 : c1] -= E[e0 : e0 + k]^T * U[u0 : u0 + k, c0 : c1] (E is [rows][n],
+// k a multiple of 64); 64 x 64 output tiles, 4 x 4 outputs per thread, the
+// k rows taken 64 at a time through LDS
 __global__ void __launch_bounds__(256) k_map_trail(float* __restrict__ Wc, const float* __restrict__ U,
-                                                    const float* __restrict__ E, int64_t n, int64_t d, int64_t j0,
-                                                    int64_t j1) {
+                                                    const float* __restrict__ E, int64_t n, int64_t d, int64_t u0,
+                                                    int k, int64_t cbeg, int64_t cend) {
   __shared__ float es[MAP_COLS][MAP_COLS + 4];  // [k][row]
   __shared__ float us[MAP_COLS][MAP_COLS + 4];  // [k][col]
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = j1 + (int64_t)blockIdx.x * 64;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = cbeg + (int64_t)blockIdx.x * 64;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int k = e / 64, a = e % 64;  // error of column j0 + k for row r0 + a (coalesced along a)
-    es[k][a] = r0 + a < n ? E[k * n + r0 + a] : 0.f;
-    const int kk = e / 64, cc = e % 64;  // U row j0 + kk, column c0 + cc
-    us[kk][cc] = c0 + cc < d ? U[(j0 + kk) * d + c0 + cc] : 0.f;
-  }
-  __syncthreads();
   const int tr = tid / 16, tc = tid % 16;  // rows tr + 16 a, columns 4 tc + b
   float acc[4][4] = {};
+  for (int kb = 0; kb < k; kb += MAP_COLS) {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int kk = e / 64, x = e % 64;  // error kb + kk of row r0 + x; U row u0 + kb + kk, column c0 + x
+      es[kk][x] = r0 + x < n ? E[(int64_t)(kb + kk) * n + r0 + x] : 0.f;
+      us[kk][x] = c0 + x < cend ? U[(u0 + kb + kk) * d + c0 + x] : 0.f;
+    }
+    __syncthreads();
 #pragma unroll 8
-  for (int k = 0; k < MAP_COLS; ++k) {
-    float ev[4], uv[4];
+    for (int kk = 0; kk < MAP_COLS; ++kk) {
+      float ev[4], uv[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) ev[a] = es[k][tr + 16 * a];
+      for (int a = 0; a < 4; ++a) ev[a] = es[kk][tr + 16 * a];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) uv[b] = us[k][4 * tc + b];
+      for (int b = 0; b < 4; ++b) uv[b] = us[kk][4 * tc + b];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] += ev[a] * uv[b];
+        for (int b = 0; b < 4; ++b) acc[a][b] += ev[a] * uv[b];
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -237,21 +276,43 @@ __global__ void __launch_bounds__(256) k_map_trail(float* __restrict__ Wc, const
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int64_t c = c0 + 4 * tc + b;
-      if (c < d) Wc[r * d + c] -= acc[a][b];
+      if (c < cend) Wc[r * d + c] -= acc[a][b];
     }
   }
 }
 
+hipError_t map_trail(float* Wc, const float* U, const float* E, const Problem& p, int64_t u0, int k, int64_t cbeg,
+                     int64_t cend, hipStream_t s) {
+  const dim3 grid((unsigned)((cend - cbeg + 63) / 64), (unsigned)((p.n + 63) / 64));
+  hipLaunchKernelGGL(k_map_trail, grid, dim3(256), 0, s, Wc, U, E, p.n, p.d, u0, k, cbeg, cend);
+  return hipGetLastError();
+}
+
+// The errors of MAP_OUTER columns are kept (E is [MAP_OUTER][n]): inside an
+// outer block each 64-column block updates only the rest of the outer block;
+// after it, one rank-MAP_OUTER update brings every later column up to date
+// (GPTQ's lazy batches, two levels). The later columns are then read and
+// written once per outer block instead of once per 64 columns.
+constexpr int MAP_OUTER = 512;
+
 template <int B, typename TL>
 hipError_t map_run(float* Wc, const float* U, const TL* lut, const Problem& p, uint8_t* idx, float* E, hipStream_t s) {
-  for (int64_t j0 = 0; j0 < p.d; j0 += MAP_COLS) {
-    const int cols = (int)(p.d - j0 < MAP_COLS ? p.d - j0 : MAP_COLS);
-    hipLaunchKernelGGL((k_map_block<B, TL>), dim3((unsigned)((p.n + 63) / 64)), dim3(64), 0, s, Wc, U, lut, p.n, p.d,
-                       p.gpr, j0, cols, idx, E);
-    const int64_t j1 = j0 + cols;
-    if (j1 < p.d) {
-      const dim3 grid((unsigned)((p.d - j1 + 63) / 64), (unsigned)((p.n + 63) / 64));
-      hipLaunchKernelGGL(k_map_trail, grid, dim3(256), 0, s, Wc, U, E, p.n, p.d, j0, j1);
+  for (int64_t ob = 0; ob < p.d; ob += MAP_OUTER) {
+    const int64_t oend = p.d - ob < MAP_OUTER ? p.d : ob + MAP_OUTER;
+    for (int64_t j0 = ob; j0 < oend; j0 += MAP_COLS) {
+      const int cols = (int)(p.d - j0 < MAP_COLS ? p.d - j0 : MAP_COLS);
+      float* Eb = E + (j0 - ob) * p.n;
+      hipLaunchKernelGGL((k_map_block<B, TL>), dim3((unsigned)((p.n + 15) / 16)), dim3(64), 0, s, Wc, U, lut, p.n,
+                         p.d, p.gpr, j0, cols, idx, Eb);
+      const int64_t j1 = j0 + cols;
+      if (j1 < oend) {
+        const hipError_t e = map_trail(Wc, U, Eb, p, j0, MAP_COLS, j1, oend, s);
+        if (e != hipSuccess) return e;
+      }
+    }
+    if (oend < p.d) {
+      const hipError_t e = map_trail(Wc, U, E, p, ob, (int)(oend - ob), oend, p.d, s);
+      if (e != hipSuccess) return e;
     }
   }
   return hipGetLastError();
@@ -282,7 +343,7 @@ hipError_t launch_lloyd(const float* W, const float* h, const Problem& p, int it
   return lloyd_run<bf16_t>(W, h, p, iters, (bf16_t*)lut, s);
 }
 
-size_t map_workspace_bytes(int64_t n) { return (size_t)n * MAP_COLS * sizeof(float); }
+size_t map_workspace_bytes(int64_t n) { return (size_t)n * MAP_OUTER * sizeof(float); }
 
 template <typename TL>
 hipError_t map_dispatch(float* Wc, const float* U, const TL* lut, const Problem& p, uint8_t* idx, float* E,

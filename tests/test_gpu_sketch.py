@@ -91,6 +91,8 @@ def _map_case(tag, n, d, b, gpr, lut_dtype):
     (4, 3, 9, 288),      # 96-column groups: a group boundary in the middle of a 64-column block
     (3, 7, 12, 224),     # 32-column groups, and a last block of 32 columns
     (4, 1, 70, 96),      # a last block of 32 columns
+    (4, 2, 20, 1088),    # past one 512-column batch of errors: two batches and a 64-column rest
+    (3, 3, 9, 1056),     # the same with a last block of 32 columns
 ])
 def test_map_small(b, gpr, n, d, lut_dtype):
     U, W, lut = _map_case(f"map/{b}/{gpr}/{n}/{d}/{lut_dtype}", n, d, b, gpr, lut_dtype)
