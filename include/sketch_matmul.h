@@ -104,7 +104,8 @@ int sketch_matmul_fwd(const void* X, int x_dtype,
  * Decode-sized batches (1 <= m <= 16, tables of a 16-row block within the
  * decode limit) with a 16-bit dtype pair; other sizes and the fp32 pair return
  * SKM_EUNSUPPORTED. The index stream is read from memory once; each set that
- * some token uses adds its tables and one round of table lookups. lut_set must
+ * some token uses adds its tables and one round of table lookups (one per
+ * 32768 / d of its tokens when more of them than that share the set). lut_set must
  * be 4-byte aligned, the other pointers 16-byte aligned; Y must not overlap
  * any input. m == 0 returns OK.
  */
@@ -182,7 +183,8 @@ int sketch_unpack_indices(const uint8_t* idx_packed, int64_t n, int64_t d, int b
  *      later columns: err = (w_j - q) / U[j][j], w_j' -= err * U[j][j'] for
  *      j' > j (the update of Frantar et al., GPTQ). Writes idx_packed in the
  *      layout above. W is overwritten with the compensated weights (it is the
- *      working buffer). workspace: sketch_map_workspace(n) bytes.
+ *      working buffer). workspace: sketch_map_workspace(n) bytes. U must
+ *      have a positive diagonal (a Cholesky factor does).
  * All arithmetic is fp32. Shapes as for the matmul (b in {2,3,4}, d % gpr ==
  * 0, (d / gpr) % 32 == 0); d <= 2^20, and n <= 2^22 for sketch_map. Pointers
  * 16-byte aligned; outputs must
