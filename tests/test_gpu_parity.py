@@ -248,6 +248,25 @@ def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     assert oracle.rel_err(got, want) <= TOL16
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_fwd_multi_random_patterns(seed):
+    """Seeded random batches: token count, set count, set indices (some out of range, clamped), bit width,
+    groups and column count (staging capacities of 32768 / d = 32, 8, 2 or 1 tokens per pass)."""
+    r = np.random.default_rng(1000 + seed)
+    b = int(r.choice([2, 3, 4]))
+    d, gpr = [(1024, 4), (4096, 8), (11008, 8), (16384, 4), (32768, 8)][seed % 5]
+    m = int(r.integers(1, 17))
+    n_sets = int(r.integers(1, 7))
+    sets = r.integers(-1, n_sets + 1, m).tolist()
+    clamped = [min(max(v, 0), n_sets - 1) for v in sets]
+    n = 24
+    xdt, ldt = [("f16", "f16"), ("bf16", "f16"), ("bf16", "bf16")][seed % 3]
+    idx, luts, X = _multi_case(f"multirand/{seed}", n, d, b, gpr, m, n_sets, xdt, ldt)
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, xdt, ldt))
+    want = oracle.forward_multi(syn.to_float64(X, xdt), idx, syn.to_float64(luts, ldt), clamped, b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16, (b, d, gpr, m, n_sets, sets)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("m", [5, 16])
 def test_fwd_multi_one_set_is_fwd(dt, m):
