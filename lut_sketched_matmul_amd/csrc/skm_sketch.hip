@@ -133,10 +133,11 @@ __global__ void __launch_bounds__(256) k_lloyd(const float* __restrict__ W, cons
 // One 64-column block of the mapping sweep. Four lanes per row (16 rows per
 // wave): lane `sub` of a row holds the row's columns 4 t + sub (t < 16) of the
 // block, so the updates of each step split over the four lanes. Column c is
-// owned by lane c % 4: every lane finds the nearest entry to its own
-// column-(4 (c / 4) + sub) weight, and a quad broadcast (DPP) hands the
-// owner's entry and error to the other three. The error is (w - q) times
-// 1 / U[c][c] (the reciprocals are taken once per block). Reads the compensated weights
+// owned by lane c % 4: a quad broadcast (DPP) hands the owner's weight to the
+// other three, each lane scans a quarter of the table and two DPP butterfly
+// steps leave the nearest entry (ties to the lower index) in all four. The
+// error is (w - q) times 1 / U[c][c] (the reciprocals are taken once per
+// block). Reads the compensated weights
 // Wc[:, j0 : j0 + cols] (all earlier blocks' errors applied), writes the
 // block's packed indices and its errors E [64][n]. The block's part of U sits
 // in LDS as [c][sub][t] so a lane's 16 coefficients of a step are contiguous.
@@ -145,45 +146,59 @@ __device__ __forceinline__ float quad_bcast(float v) {
   constexpr int ctrl = OWN | (OWN << 2) | (OWN << 4) | (OWN << 6);  // quad_perm [OWN, OWN, OWN, OWN]
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
 }
-template <int OWN>
-__device__ __forceinline__ int quad_bcast_i(int v) {
-  constexpr int ctrl = OWN | (OWN << 2) | (OWN << 4) | (OWN << 6);
-  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int quad_perm_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// merge with the quad partner given by CTRL: the partner's entry wins when it
+// is nearer, or as near with a lower index
+template <int CTRL>
+__device__ __forceinline__ void quad_min(float& best, float& q, int& a) {
+  const float pb = quad_perm_f<CTRL>(best), pq = quad_perm_f<CTRL>(q);
+  const int pa = quad_perm_i<CTRL>(a);
+  const bool take = pb < best || (pb == best && pa < a);
+  best = take ? pb : best;
+  q = take ? pq : q;
+  a = take ? pa : a;
 }
 
 template <int C, int B, int K>
-__device__ __forceinline__ void map_step(float (&w)[16], const float (&t0)[K], const float (&t1)[K],
+__device__ __forceinline__ void map_step(float (&w)[16], const float (&t0)[K / 4], const float (&t1)[K / 4],
                                          const float (*ub)[MAP_COLS], const float* rdiag, int sub, int cols,
-                                         bool row_ok, int64_t n,
-                                         int64_t i, float* __restrict__ E, uint32_t (&pk)[MAP_COLS * B / 32]) {
+                                         bool row_ok, int64_t n, int64_t i, float* __restrict__ E,
+                                         uint32_t (&pk)[MAP_COLS * B / 32]) {
   if constexpr (C < MAP_COLS) {
     constexpr int T = C / 4, OWN = C % 4;
     if (C < cols) {  // uniform
-      float tv[K];
+      // the owner's weight; each lane scans its quarter of the table (entries
+      // sub K/4 .. sub K/4 + K/4 - 1), then two butterfly steps over the quad
+      const float wv = quad_bcast<OWN>(w[T]);
+      float best = fabsf(wv - (C < 32 ? t0[0] : t1[0])), q = C < 32 ? t0[0] : t1[0];
+      int a = sub * (K / 4);
 #pragma unroll
-      for (int r = 0; r < K; ++r) tv[r] = C < 32 ? t0[r] : t1[r];
-      // nearest entry to this lane's weight of column 4 T + sub (ties to the lower index)
-      float best = fabsf(w[T] - tv[0]), q = tv[0];
-      int a = 0;
-#pragma unroll
-      for (int r = 1; r < K; ++r) {
-        const float dr = fabsf(w[T] - tv[r]);
+      for (int e = 1; e < K / 4; ++e) {
+        const float tvv = C < 32 ? t0[e] : t1[e];
+        const float dr = fabsf(wv - tvv);
         const bool lt = dr < best;
         best = lt ? dr : best;
-        q = lt ? tv[r] : q;
-        a = lt ? r : a;
+        q = lt ? tvv : q;
+        a = lt ? sub * (K / 4) + e : a;
       }
-      const float err_l = (w[T] - q) * rdiag[C];
-      const float err = quad_bcast<OWN>(err_l);
-      const int ai = quad_bcast_i<OWN>(a);
+      quad_min<0xB1>(best, q, a);  // quad_perm [1, 0, 3, 2]
+      quad_min<0x4E>(best, q, a);  // quad_perm [2, 3, 0, 1]
+      const float err = (wv - q) * rdiag[C];  // the same on all four lanes
       if (sub == OWN && row_ok) E[C * n + i] = err;
       const float* u = ub[C] + sub * 16;
 #pragma unroll
       for (int t2 = T + 1; t2 < 16; ++t2) w[t2] -= err * u[t2];
       if (sub > OWN) w[T] -= err * u[T];
       constexpr int p = B * C;
-      pk[p >> 5] |= (uint32_t)ai << (p & 31);
-      if constexpr ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)ai >> (32 - (p & 31));
+      pk[p >> 5] |= (uint32_t)a << (p & 31);
+      if constexpr ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)a >> (32 - (p & 31));
     }
     map_step<C + 1, B, K>(w, t0, t1, ub, rdiag, sub, cols, row_ok, n, i, E, pk);
   }
@@ -214,13 +229,14 @@ __global__ void __launch_bounds__(64) k_map_block(float* __restrict__ Wc, const 
     const int col = 4 * t + sub;
     w[t] = col < cols ? Wc[ic * d + j0 + col] : 0.f;
   }
-  // the block spans at most two groups, split at a multiple of 32 columns
-  float t0[K], t1[K];
+  // the block spans at most two groups, split at a multiple of 32 columns;
+  // each lane keeps its quarter of both tables
+  float t0[K / 4], t1[K / 4];
   const int64_t g0 = j0 / G, g1 = (j0 + 32) / G;
 #pragma unroll
-  for (int r = 0; r < K; ++r) {
-    t0[r] = to_f32(lut[(ic * gpr + g0) * K + r]);
-    t1[r] = to_f32(lut[(ic * gpr + (g1 < gpr ? g1 : g0)) * K + r]);
+  for (int e = 0; e < K / 4; ++e) {
+    t0[e] = to_f32(lut[(ic * gpr + g0) * K + sub * (K / 4) + e]);
+    t1[e] = to_f32(lut[(ic * gpr + (g1 < gpr ? g1 : g0)) * K + sub * (K / 4) + e]);
   }
   constexpr int WORDS = MAP_COLS * B / 32;
   uint32_t pk[WORDS];
