@@ -322,7 +322,15 @@ def sgd_step(master: np.ndarray, grad: np.ndarray, lr: float, momentum: float = 
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
-    """max |got - ref| / max |ref| (0 when both are all zero)."""
+    """max |got - ref| / max |ref| (0 when both are all zero).
+
+    The parity score of every comparison with this oracle: the largest
+    absolute error over the largest absolute reference value, both taken over
+    the whole output tensor. The pages print no tolerance rule; this is the
+    acceptance measure stated for the path (5e-3 for 16-bit inputs, 1e-5 for
+    fp32). Shapes must match exactly (no broadcasting); an all-zero reference
+    scores 0 against an exact result and infinity against anything else.
+    """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if got.shape != ref.shape:

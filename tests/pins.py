@@ -35,7 +35,13 @@ module, or a copy with a planted mistake) and raises ``AssertionError`` when
   diagonal of an explicitly inverted Hessian; the mapping with U = I (plain
   nearest rounding), with tables that hold every weight exactly, and against
   the closed-form optimal compensation (the free weights that minimise the
-  quadratic loss given the columns already mapped, solved from H directly).
+  quadratic loss given the columns already mapped, solved from H directly);
+* the parity score, max |got - ref| / max |ref| (the stated acceptance
+  measure: largest absolute error over the largest absolute reference value):
+  hand-worked arrays whose largest error is negative and whose largest
+  reference value is negative, the vector infinity norm of numpy.linalg as a
+  second definition, scale invariance, an all-zero reference, empty arrays
+  and a shape mismatch.
 """
 from __future__ import annotations
 
@@ -529,6 +535,50 @@ def pin_map_closed_form(o):
             assert idx[i, j] == int(np.argmin(np.abs(wf[0] - lut[i, j // G]))), (i, j)
 
 
+def pin_rel_err_worked(o):
+    # errors 0, -0.5, -1, 0.009 -> largest |error| 1, from a negative error;
+    # largest |reference| 4, from a negative reference value; 1 / 4 = 0.25.
+    # (The small entry's own relative error is 9: a per-element score differs.)
+    got = np.array([[1.0, 2.0], [-5.0, 0.01]])
+    ref = np.array([[1.0, 2.5], [-4.0, 0.001]])
+    assert o.rel_err(got, ref) == 0.25
+    # the score is not symmetric: the reference alone sets the scale (max |got| = 5)
+    assert o.rel_err(ref, got) == 1.0 / 5.0
+    # an exact result scores 0; a result of all zeros scores 1
+    assert o.rel_err(ref.copy(), ref) == 0.0
+    assert o.rel_err(np.zeros_like(ref), ref) == 1.0
+
+
+def pin_rel_err_inf_norm(o):
+    rng = _rng(4242)
+    for shape in ((7,), (5, 9), (3, 4, 6)):
+        ref = rng.standard_normal(shape) * 10.0 ** rng.integers(-3, 3, size=shape)
+        got = ref + rng.standard_normal(shape) * 1e-3
+        want = np.linalg.norm((got - ref).ravel(), np.inf) / np.linalg.norm(ref.ravel(), np.inf)
+        assert abs(o.rel_err(got, ref) - want) <= 1e-15 * want
+        # invariant under a common scale of both arguments (powers of two: exact)
+        assert o.rel_err(got * 2.0 ** -20, ref * 2.0 ** -20) == o.rel_err(got, ref)
+
+
+def pin_rel_err_degenerate(o):
+    z = np.zeros((3, 2))
+    assert o.rel_err(z, z) == 0.0
+    assert o.rel_err(z + 1e-30, z) == float("inf")
+    assert o.rel_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    try:
+        o.rel_err(np.zeros((2, 3)), np.zeros((3, 2)))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("shape mismatch accepted")
+    try:
+        o.rel_err(np.zeros((1, 3)), np.zeros((3,)))  # broadcastable, still a mismatch
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("broadcastable shape mismatch accepted")
+
+
 ALL_PINS = [
     pin_bitstream_golden, pin_unpack_bigint, pin_unpack_exhaustive_b3,
     pin_identity, pin_dense_special_case, pin_dequant_elementwise,
@@ -537,5 +587,5 @@ ALL_PINS = [
     pin_loop_vs_bincount, pin_multi_identity_sets, pin_multi_dense, pin_multi_unused_sets,
     pin_adam_vs_torch, pin_adam_constant_gradient, pin_adam_scale_invariance, pin_sgd_vs_torch,
     pin_lloyd_worked, pin_lloyd_vs_sklearn, pin_lloyd_monotone, pin_hessian_factor, pin_map_identity_factor,
-    pin_map_exact_tables, pin_map_closed_form,
+    pin_map_exact_tables, pin_map_closed_form, pin_rel_err_worked, pin_rel_err_inf_norm, pin_rel_err_degenerate,
 ]

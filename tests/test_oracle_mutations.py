@@ -63,6 +63,16 @@ MUTATIONS = {
         "out[i] = np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k).reshape(gpr, k)",
         "out[i] = (np.bincount(g * k + idx[i], weights=dW[i], minlength=gpr * k)"
         " / np.maximum(1, np.bincount(g * k + idx[i], minlength=gpr * k))).reshape(gpr, k)"),
+    "rel_err_mean_error": ("num = float(np.max(np.abs(got - ref)))", "num = float(np.mean(np.abs(got - ref)))"),
+    "rel_err_sum_reference": ("den = float(np.max(np.abs(ref)))", "den = float(np.sum(np.abs(ref)))"),
+    "rel_err_error_abs_dropped": ("num = float(np.max(np.abs(got - ref)))", "num = float(np.max(got - ref))"),
+    "rel_err_reference_abs_dropped": ("den = float(np.max(np.abs(ref)))", "den = float(np.max(ref))"),
+    "rel_err_swapped": ("    return num / den", "    return den / num"),
+    "rel_err_scale_from_got": ("den = float(np.max(np.abs(ref)))", "den = float(np.max(np.abs(got)))"),
+    "rel_err_elementwise": ("    return num / den",
+                            "    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)))"),
+    "rel_err_zero_reference_passes": ('return 0.0 if num == 0.0 else float("inf")', "return 0.0"),
+    "rel_err_no_shape_check": ("if got.shape != ref.shape:", "if got.ndim != ref.ndim and False:"),
 }
 
 
