@@ -126,6 +126,54 @@ def _require_device(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+# The C ABI takes raw pointers and sizes, so it cannot see a tensor's extent:
+# every tensor's shape (or element count) and dtype is checked against the
+# sizes passed with it before the call, so that a wrong buffer is an exception
+# here and never an out-of-bounds access on the device.
+
+_FLOAT_DTYPES = ("float32", "float16", "bfloat16")
+
+
+def _dtype_name(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _expect(t, name: str, shape=None, numel=None, dtypes=None):
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if dtypes is not None and _dtype_name(t) not in dtypes:
+        raise TypeError(f"{name} has dtype {_dtype_name(t)}, expected one of {dtypes}")
+
+
+def _check_bits(b: int, d: int):
+    if b not in (2, 3, 4):
+        raise ValueError(f"bit width b = {b}: supported are 2, 3 and 4")
+    if d < 0 or (d * b) % 8:
+        raise ValueError(f"d = {d} columns of {b} bits do not fill whole bytes")
+
+
+def _check_sketch(idx_packed, lut, n: int, d: int, b: int, gpr: int, n_sets=None, lut_name="lut"):
+    """idx_packed [n, d*b/8] uint8 and tables of n (x n_sets) rows of gpr groups of 2^b entries."""
+    _check_bits(b, d)
+    if gpr < 1:
+        raise ValueError(f"gpr = {gpr} must be at least 1")
+    _expect(idx_packed, "idx_packed", shape=(n, d * b // 8), dtypes=("uint8",))
+    count = n * gpr * (1 << b) * (1 if n_sets is None else n_sets)
+    _expect(lut, lut_name, numel=count, dtypes=_FLOAT_DTYPES)
+    if n_sets is not None and (lut.dim() < 1 or lut.shape[0] != n_sets):
+        raise ValueError(f"{lut_name} must have the table sets as its first dimension")
+
+
+def _matrix(t, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a matrix, got {t.dim()} dimensions")
+    return t.shape
+
+
 def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=None):
     """Y = X W^T with W[i, j] = lut[i, j // (d/gpr), idx[i, j]].
 
@@ -133,9 +181,12 @@ def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=Non
     Returns Y [m, n] in X's dtype.
     """
     torch = _torch()
-    _require_device(X, idx_packed, lut, out)
-    m, d = X.shape
+    m, d = _matrix(X, "X")
     n = idx_packed.shape[0]
+    _expect(X, "X", dtypes=_FLOAT_DTYPES)
+    _check_sketch(idx_packed, lut, n, d, b, gpr)
+    _expect(out, "out", shape=(m, n), dtypes=(_dtype_name(X),))
+    _require_device(X, idx_packed, lut, out)
     if out is None:
         out = torch.empty((m, n), dtype=X.dtype, device=X.device)
     st = lib().sketch_matmul_fwd(X.data_ptr(), dtype_code(X), idx_packed.data_ptr(), lut.data_ptr(),
@@ -152,11 +203,16 @@ def sketch_matmul_fwd_multi(X, idx_packed, luts, lut_set, b: int, gpr: int, out=
     gpr, 2^b], lut_set [m] int32 (device). Returns Y [m, n] in X's dtype.
     """
     torch = _torch()
-    _require_device(X, idx_packed, luts, lut_set, out)
-    m, d = X.shape
+    m, d = _matrix(X, "X")
     n = idx_packed.shape[0]
+    _expect(X, "X", dtypes=_FLOAT_DTYPES)
+    if luts.dim() < 1:
+        raise ValueError("luts must have the table sets as its first dimension")
+    _check_sketch(idx_packed, luts, n, d, b, gpr, n_sets=luts.shape[0], lut_name="luts")
     if lut_set.dtype != torch.int32 or lut_set.numel() != m:
         raise ValueError("lut_set must be an int32 tensor with one entry per token")
+    _expect(out, "out", shape=(m, n), dtypes=(_dtype_name(X),))
+    _require_device(X, idx_packed, luts, lut_set, out)
     if out is None:
         out = torch.empty((m, n), dtype=X.dtype, device=X.device)
     st = lib().sketch_matmul_fwd_multi(X.data_ptr(), dtype_code(X), idx_packed.data_ptr(), luts.data_ptr(),
@@ -166,16 +222,40 @@ def sketch_matmul_fwd_multi(X, idx_packed, luts, lut_set, b: int, gpr: int, out=
     return out
 
 
+def sketch_matmul_bwd_workspace(m: int, n: int, d: int, b: int, gpr: int, io_dtype: int, lut_dtype: int) -> int:
+    """Bytes of device workspace sketch_matmul_bwd needs for these sizes and dtypes."""
+    return int(lib().sketch_matmul_bwd_workspace(m, n, d, b, gpr, io_dtype, lut_dtype))
+
+
 def sketch_matmul_bwd(dY, X, idx_packed, lut, b: int, gpr: int, d: Optional[int] = None,
                       need_dx: bool = True, need_dlut: bool = True, dlut_out=None, accumulate: bool = False,
                       workspace=None, stream=None) -> Tuple[object, object]:
-    """(dX, dLUT) of the sketched matmul; both fp32. dLUT sums shared entries."""
+    """(dX, dLUT) of the sketched matmul; both fp32. dLUT sums shared entries.
+
+    dY [m, n], X [m, d] in the same dtype (X may be None when need_dlut is
+    False; then d must be given), idx_packed [n, d*b/8] uint8, lut [n, gpr,
+    2^b]. dlut_out: optional fp32 [n, gpr, 2^b] to write (accumulate=True adds
+    to it). workspace: optional uint8 device buffer of at least
+    sketch_matmul_bwd_workspace(...) bytes (allocated here when omitted).
+    """
     torch = _torch()
-    _require_device(dY, X, idx_packed, lut, dlut_out)
-    m, n = dY.shape
+    m, n = _matrix(dY, "dY")
+    _expect(dY, "dY", dtypes=_FLOAT_DTYPES)
+    if X is not None:
+        mx, dx_cols = _matrix(X, "X")
+        if d is not None and d != dx_cols:
+            raise ValueError(f"d = {d} does not match X's {dx_cols} columns")
+        d = dx_cols
+        _expect(X, "X", shape=(m, d), dtypes=(_dtype_name(dY),))
+    elif need_dlut:
+        raise ValueError("the table gradient needs X")
     if d is None:
-        d = X.shape[1]
+        raise ValueError("d must be given when X is None")
     K = 1 << b
+    _check_sketch(idx_packed, lut, n, d, b, gpr)
+    _expect(dlut_out, "dlut_out", shape=(n, gpr, K), dtypes=("float32",))
+    _expect(workspace, "workspace", dtypes=("uint8",))
+    _require_device(dY, X, idx_packed, lut, dlut_out, workspace)
     dX = torch.empty((m, d), dtype=torch.float32, device=dY.device) if need_dx else None
     dL = None
     if need_dlut:
@@ -196,8 +276,9 @@ def sketch_matmul_bwd(dY, X, idx_packed, lut, b: int, gpr: int, d: Optional[int]
 def sketch_dequant(idx_packed, lut, d: int, b: int, gpr: int, stream=None):
     """Dense W [n, d] in the table dtype (a checking aid)."""
     torch = _torch()
-    _require_device(idx_packed, lut)
     n = idx_packed.shape[0]
+    _check_sketch(idx_packed, lut, n, d, b, gpr)
+    _require_device(idx_packed, lut)
     W = torch.empty((n, d), dtype=lut.dtype, device=lut.device)
     st = lib().sketch_dequant(idx_packed.data_ptr(), lut.data_ptr(), dtype_code(lut), n, d, b, gpr, W.data_ptr(),
                               _stream_ptr(stream))
@@ -208,8 +289,10 @@ def sketch_dequant(idx_packed, lut, d: int, b: int, gpr: int, stream=None):
 def sketch_unpack_indices(idx_packed, d: int, b: int, stream=None):
     """One uint8 per weight: idx [n, d] (a checking aid)."""
     torch = _torch()
-    _require_device(idx_packed)
     n = idx_packed.shape[0]
+    _check_bits(b, d)
+    _expect(idx_packed, "idx_packed", shape=(n, d * b // 8), dtypes=("uint8",))
+    _require_device(idx_packed)
     out = torch.empty((n, d), dtype=torch.uint8, device=idx_packed.device)
     st = lib().sketch_unpack_indices(idx_packed.data_ptr(), n, d, b, out.data_ptr(), _stream_ptr(stream))
     _check("sketch_unpack_indices", st)
@@ -266,9 +349,10 @@ def sketch_lut_sgd_step(master, grad, lr: float, momentum: float = 0.0, weight_d
 def sketch_column_weights(U, stream=None):
     """h[j] = 1 / [H^-1]_jj from the upper factor U (H^-1 = U^T U), fp32 [d]."""
     torch = _torch()
-    _require_device(U)
-    _check_f32(U)
     d = U.shape[0]
+    _expect(U, "U", shape=(d, d))
+    _check_f32(U)
+    _require_device(U)
     h = torch.empty(d, dtype=torch.float32, device=U.device)
     _check("sketch_column_weights", lib().sketch_column_weights(U.data_ptr(), d, h.data_ptr(), _stream_ptr(stream)))
     return h
@@ -277,9 +361,12 @@ def sketch_column_weights(U, stream=None):
 def sketch_lloyd(W, h, b: int, gpr: int, iters: int, lut_dtype=None, out=None, stream=None):
     """Weighted Lloyd tables [n, gpr, 2^b] (fp32 unless lut_dtype / out say otherwise)."""
     torch = _torch()
-    _require_device(W, h, out)
+    n, d = _matrix(W, "W")
     _check_f32(W, h)
-    n, d = W.shape
+    _check_bits(b, d)
+    _expect(h, "h", numel=d)
+    _expect(out, "out", numel=n * gpr * (1 << b), dtypes=_FLOAT_DTYPES)
+    _require_device(W, h, out)
     if out is None:
         out = torch.empty((n, gpr, 1 << b), dtype=lut_dtype or torch.float32, device=W.device)
     st = lib().sketch_lloyd(W.data_ptr(), h.data_ptr(), n, d, b, gpr, iters, out.data_ptr(), dtype_code(out),
@@ -291,9 +378,11 @@ def sketch_lloyd(W, h, b: int, gpr: int, iters: int, lut_dtype=None, out=None, s
 def sketch_map(W_work, U, lut, b: int, gpr: int, out=None, workspace=None, stream=None):
     """Error-compensated mapping -> idx_packed [n, d*b/8] uint8. W_work (fp32 [n, d]) is overwritten."""
     torch = _torch()
-    _require_device(W_work, U, lut, out, workspace)
+    n, d = _matrix(W_work, "W_work")
     _check_f32(W_work, U)
-    n, d = W_work.shape
+    _expect(U, "U", shape=(d, d))
+    _check_sketch(out, lut, n, d, b, gpr)
+    _require_device(W_work, U, lut, out, workspace)
     if out is None:
         out = torch.empty((n, d * b // 8), dtype=torch.uint8, device=W_work.device)
     ws = lib().sketch_map_workspace(n)
