@@ -32,8 +32,6 @@
 // slots s = w, w + NW, ... (slot = 4 units = 128 columns), so the waves of a
 // block read adjacent pieces of each row. The NW partial 16x16 tiles are
 // summed in LDS in wave order (deterministic) and stored once.
-#include <stdlib.h>
-
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -51,16 +49,6 @@ constexpr int DEC_XL_CHUNKS = (int)(DEC_XL_MAX / 8 / (8 * 64));  // 16-byte chun
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-// SKM_DECODE_WAVES=8|16 forces the waves per decode block (tuning aid)
-int decode_waves_override() {
-  static const int v = [] {
-    const char* e = getenv("SKM_DECODE_WAVES");
-    const int w = e ? atoi(e) : 0;
-    return (w == 8 || w == 16) ? w : 0;
-  }();
-  return v;
-}
 
 template <typename TC> struct mfma16;
 template <> struct mfma16<half_t> {
@@ -466,8 +454,6 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // load counting below starts from the first batch alone.
   wait_vmcnt<PF * ((B == 3 ? 3 : 1) + (XL ? 0 : 4))>();
   __syncthreads();
-  // the gathers address the tables with absolute LDS addresses (see gaddr)
-  if ((uint32_t)(uintptr_t)smem != 0u) return;
   // this lane's A row: its token's staged row (MULTI + XL: the token's slot in
   // the pass, or slot 0 for a token outside the pass, whose results are not kept)
   int aslot = tokc;
@@ -614,24 +600,19 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
   const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
-  // (the LDS limit is raised once per kernel, the first time one needs it)
+  // (the gathers address the tables with absolute LDS addresses, see gaddr:
+  // checked once per kernel, which also raises its LDS limit to 160 KB)
   if (sa.lut_set) {
     const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
-    if (lds > 65536) {
-      static const hipError_t attr = hipFuncSetAttribute((const void*)kern,
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (attr != hipSuccess) return attr;
-    }
+    static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
+    if (prep != hipSuccess) return prep;
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
                        sa.lut_set, sa.n_sets, sa.set_stride);
     return hipGetLastError();
   }
   const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false>;
-  if (lds > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)kern,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-  }
+  static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
+  if (prep != hipSuccess) return prep;
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
                      sa.lut_set, sa.n_sets, sa.set_stride);
   return hipGetLastError();
@@ -661,7 +642,7 @@ hipError_t decode_b(const TX* X, const uint8_t* idx, const TL* lut, const Proble
   // in flight. Many blocks: 8 waves so two or more blocks share a CU and one
   // block's start-up latency hides behind another's work.
   const int64_t blocks = (p.n + DEC_ROWS - 1) / DEC_ROWS;
-  const int nw = decode_waves_override() ? decode_waves_override() : (blocks <= 384 ? 16 : 8);
+  const int nw = blocks <= 384 ? 16 : 8;
   if (nw == 16) return decode_nw<B, 16>(X, idx, lut, p, Y, s, magic, sa);
   return decode_nw<B, 8>(X, idx, lut, p, Y, s, magic, sa);
 }

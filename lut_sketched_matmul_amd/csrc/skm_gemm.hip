@@ -37,8 +37,6 @@
 // registers during K-step k and staged in K-step k+2 (two register stages);
 // one barrier per K-step; LDS tables (b = 2, 3) are staged one group ahead
 // into the other table buffer.
-#include <stdlib.h>
-
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -614,34 +612,23 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     }
 }
 
-// SKM_FWD64=0 selects the 32-column-step kernel for every shape (tuning aid)
-bool fwd64_disabled() {
-  static const bool v = [] {
-    const char* e = getenv("SKM_FWD64");
-    return e && e[0] == '0';
-  }();
-  return v;
-}
-
 template <int B, typename TX, typename TL>
 hipError_t gemm_fwd_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
   const int64_t mb = (p.m + G_BM - 1) / G_BM;
   const int64_t nb = (p.n + G_BN - 1) / G_BN;
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
-  if (ug % 2 == 0 && !fwd64_disabled()) {
+  if (ug % 2 == 0) {
     const auto kern = k_gemm_fwd64<B, TX, TL>;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS64_TOTAL);
-    if (attr != hipSuccess) return attr;
+    static const hipError_t prep = prepare_kernel((const void*)kern, LDS64_TOTAL);
+    if (prep != hipSuccess) return prep;
     hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(G_THREADS), LDS64_TOTAL, s, X, idx, lut, p.m, p.n,
                        p.d, p.gpr, magic, mb, Y);
     return hipGetLastError();
   }
   const auto kern = k_gemm_fwd<B, TX, TL>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_TOTAL);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t prep = prepare_kernel((const void*)kern, LDS_TOTAL);
+  if (prep != hipSuccess) return prep;
   hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(G_THREADS), LDS_TOTAL, s, X, idx, lut, p.m, p.n, p.d,
                      p.gpr, magic, mb, Y);
   return hipGetLastError();

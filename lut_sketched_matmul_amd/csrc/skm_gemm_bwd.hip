@@ -31,8 +31,6 @@
 // k_gemm_dlut_dma (whole 32-token steps, the common case) copies the operand
 // tiles from global memory into a three-stage LDS ring with global_load_lds
 // instead of staging them through registers.
-#include <stdlib.h>
-
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -982,7 +980,8 @@ __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed,
                 int64_t m, int64_t n, int64_t d, int gpr, int gband, float* __restrict__ dLUT, int accumulate) {
   typedef mfma32<TX> MF;
-  extern __shared__ uint32_t smem[];
+  extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
+  (void)smem;
 
   const int t = threadIdx.x;
   const uint32_t lane = (uint32_t)(t & 63);
@@ -1001,8 +1000,6 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
   const int KS = (int)(m / DL_BK);
 
   for (uint32_t q = (uint32_t)t; q < 4u * DD_BCOPY / 4u; q += 512u) st_w(DD_BINS + q * 4u, 0u);
-  // the absolute LDS addresses below assume the dynamic LDS starts at 0
-  if ((uint32_t)(uintptr_t)smem != 0u) return;
 
   // ---- DMA roles: this wave's token rows 4 wave .. +3. dY: one 1 KB
   // instruction (lane = row (lane / 16) x slot (lane % 16)); X: one
@@ -1112,15 +1109,6 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
 
 // ---- launchers ---------------------------------------------------------------
 
-// SKM_DX64=0 selects the 32-row-step dX kernel for every shape (tuning aid)
-bool dx64_disabled() {
-  static const bool v = [] {
-    const char* e = getenv("SKM_DX64");
-    return e && e[0] == '0';
-  }();
-  return v;
-}
-
 uint32_t ug_magic_of(const Problem& p) {
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   return ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
@@ -1129,10 +1117,8 @@ uint32_t ug_magic_of(const Problem& p) {
 template <int B, int NG, typename TX, typename TL>
 hipError_t dx_launch(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
   const auto kern = k_gemm_dx<B, NG, TX, TL>;
-  // more than 64 KB of LDS per block must be requested once per kernel
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DxLds<NG>::TOTAL);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t prep = prepare_kernel((const void*)kern, DxLds<NG>::TOTAL);
+  if (prep != hipSuccess) return prep;
   const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
   const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
   hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), DxLds<NG>::TOTAL, s, dY, idx, lut, p.m, p.n, p.d,
@@ -1144,18 +1130,16 @@ template <int B, typename TX, typename TL>
 hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
   // a 256-column tile touches at most 2 groups when groups are >= 256 columns
   // wide, at most 8 (one per 32-column unit) otherwise
-  if (p.group_cols() >= 256 && !dx64_disabled()) {
+  if (p.group_cols() >= 256) {
     const auto kern = k_gemm_dx64<B, TX, TL>;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)D6_LDS);
-    if (attr != hipSuccess) return attr;
+    static const hipError_t prep = prepare_kernel((const void*)kern, D6_LDS);
+    if (prep != hipSuccess) return prep;
     const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
     const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
     hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), D6_LDS, s, dY, idx, lut, p.m, p.n, p.d, p.gpr,
                        ug_magic_of(p), mb, dX);
     return hipGetLastError();
   }
-  if (p.group_cols() >= 256) return dx_launch<B, 2>(dY, idx, lut, p, dX, s);
   return dx_launch<B, 8>(dY, idx, lut, p, dX, s);
 }
 
@@ -1172,39 +1156,23 @@ template <int B, typename TX, bool VEC>
 hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
                        hipStream_t s) {
   const auto kern = k_gemm_dlut<B, TX, VEC>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DL_LDS);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t prep = prepare_kernel((const void*)kern, DL_LDS);
+  if (prep != hipSuccess) return prep;
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
                      accumulate);
   return hipGetLastError();
 }
 
-// SKM_DLUT_DMA=0 selects the register-staged dLUT kernel for every shape, and
-// SKM_DLUT_GBAND=g sets the groups per band of k_gemm_dlut_dma's block order
-// (tuning aids)
-bool dlut_dma_disabled() {
-  static const bool v = [] {
-    const char* e = getenv("SKM_DLUT_DMA");
-    return e && e[0] == '0';
-  }();
-  return v;
-}
-
 template <int B, typename TX>
 hipError_t dlut_dma_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT,
                            int accumulate, hipStream_t s) {
   const auto kern = k_gemm_dlut_dma<B, TX>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DD_LDS);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t prep = prepare_kernel((const void*)kern, DD_LDS);
+  if (prep != hipSuccess) return prep;
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
-  static const int gb_env = [] {
-    const char* e = getenv("SKM_DLUT_GBAND");
-    return e ? atoi(e) : 0;
-  }();
-  int gband = gb_env > 0 && p.gpr % gb_env == 0 ? gb_env : (p.gpr % 4 == 0 ? 4 : (p.gpr % 2 == 0 ? 2 : 1));
+  // bands of 4 groups (or 2, or 1) in the XCD-local block order
+  const int gband = p.gpr % 4 == 0 ? 4 : (p.gpr % 2 == 0 ? 2 : 1);
   hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr,
                      gband, dLUT, accumulate);
   return hipGetLastError();
@@ -1214,7 +1182,7 @@ template <int B, typename TX>
 hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
                   hipStream_t s) {
   // DMA staging: whole 32-token steps and 16-byte aligned dY rows
-  if (p.m % DL_BK == 0 && p.n % 8 == 0 && !dlut_dma_disabled())
+  if (p.m % DL_BK == 0 && p.n % 8 == 0)
     return dlut_dma_launch<B, TX>(dY, X, idx, p, dLUT, accumulate, s);
   if (p.n % 8 == 0) return dlut_launch<B, TX, true>(dY, X, idx, p, dLUT, accumulate, s);
   return dlut_launch<B, TX, false>(dY, X, idx, p, dLUT, accumulate, s);

@@ -10,6 +10,21 @@
 
 namespace skm {
 
+// The tiled kernels allocate only dynamic LDS and address it with absolute
+// byte offsets, which holds only when the dynamic LDS starts at address 0,
+// i.e. when the kernel has no static LDS. prepare_kernel checks that on the
+// host (hipFuncGetAttributes) and raises the kernel's dynamic LDS limit when
+// it needs more than 64 KB; callers run it once per kernel and return its
+// error instead of launching.
+inline hipError_t prepare_kernel(const void* kern, size_t dyn_lds) {
+  hipFuncAttributes a;
+  hipError_t e = hipFuncGetAttributes(&a, kern);
+  if (e != hipSuccess) return e;
+  if (a.sharedSizeBytes != 0) return hipErrorInvalidConfiguration;
+  if (dyn_lds > 65536) e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_lds);
+  return e;
+}
+
 struct Problem {
   int64_t m, n, d;
   int b, gpr;
