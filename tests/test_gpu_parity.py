@@ -158,17 +158,22 @@ def test_fwd16_gemm(x_dtype, lut_dtype, b, gpr, n, d, m):
     assert oracle.rel_err(got, want) <= TOL16
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_gemm_selection_bit_exact(dt):
-    """m > 16 one-hot rows through the GEMM: Y[t, i] = W[i, j_t] exactly."""
-    b, gpr, n, d, m = 4, 8, 150, 4096, 70
-    idx, lut, _, _ = make_case(f"gsel/{dt}", n, d, b, gpr, 1, dt, dt)
-    cols = np.random.default_rng(7).choice(d, m, replace=False)
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "f16")])
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("gpr,d", [(8, 4096), (8, 11008)])
+def test_gemm_selection_bit_exact(x_dtype, lut_dtype, b, gpr, d):
+    """m > 16 one-hot rows through the GEMM: Y[t, i] = W[i, j_t] exactly. Groups of 16 units take the
+    64-column K-steps, groups of 43 units (11008 / 8 columns) the 32-column K-steps."""
+    n, m = 150, 70
+    idx, lut, _, _ = make_case(f"gsel/{x_dtype}/{lut_dtype}/{b}/{d}", n, d, b, gpr, 1, x_dtype, lut_dtype)
+    cols = np.random.default_rng(7 + b).choice(d, m, replace=False)
     X = np.zeros((m, d), dtype=np.float32)
     X[np.arange(m), cols] = 1.0
-    Y = skm().sketch_matmul_fwd(to_dev(syn.to_storage(X, dt), dt), to_dev(idx, "u8"), to_dev(lut, dt), b, gpr)
-    W = oracle.dequantize(idx, syn.to_float64(lut, dt), d, b, gpr)
-    assert np.array_equal(to_f64(Y), W[:, cols].T)
+    Y = skm().sketch_matmul_fwd(to_dev(syn.to_storage(X, x_dtype), x_dtype), to_dev(idx, "u8"),
+                                to_dev(lut, lut_dtype), b, gpr)
+    W = oracle.dequantize(idx, syn.to_float64(lut, lut_dtype), d, b, gpr)
+    want = round_to(W[:, cols].T, x_dtype)  # Y is stored in X's dtype
+    assert np.array_equal(to_f64(Y), want)
 
 
 def _workload_rows(n, seed):
@@ -370,6 +375,37 @@ def test_dlut_bins_exact(b):
     _, gdl = _bwd16(idx, lut, Xs, dY, b, gpr, d, "bf16", "bf16")
     want = oracle.backward_dlut(syn.to_float64(dY, "bf16"), X.astype(np.float64), idx, b, gpr)
     assert np.array_equal(gdl, want)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_dlut_bins_exact_dma(b):
+    """As above with whole 32-token steps and rows a multiple of 8, which take the kernel that copies its
+    operand tiles into LDS (swizzled chunks): exact integer bin sums."""
+    n, gpr, d, m = 128, 4, 2048, 96
+    idx, lut, _, _ = make_case(f"binsdma/{b}", n, d, b, gpr, 1, "bf16", "bf16")
+    cols = np.random.default_rng(20 + b).choice(d, m, replace=False)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    dY = syn.random_int_valued(f"binsdma/{b}/dY", (m, n), -3, 3, "bf16")
+    _, gdl = _bwd16(idx, lut, syn.to_storage(X, "bf16"), dY, b, gpr, d, "bf16", "bf16")
+    want = oracle.backward_dlut(syn.to_float64(dY, "bf16"), X.astype(np.float64), idx, b, gpr)
+    assert np.array_equal(gdl, want)
+
+
+@pytest.mark.parametrize("io,lut_dtype", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "f16")])
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("gpr,d", [(8, 4096), (32, 4096)])
+def test_dx_selection_bit_exact(io, lut_dtype, b, gpr, d):
+    """One-hot dY rows: dX[t, :] = W[i_t, :] exactly (one non-zero product per output). Groups of 512
+    columns take the 64-row dX steps, groups of 128 columns the 32-row steps."""
+    n, m = 200, 40
+    idx, lut, X, _ = make_case(f"dxsel/{io}/{lut_dtype}/{b}/{gpr}", n, d, b, gpr, m, io, lut_dtype)
+    rows = np.random.default_rng(30 + b).choice(n, m, replace=False)
+    dY = np.zeros((m, n), dtype=np.float32)
+    dY[np.arange(m), rows] = 1.0
+    gdx, _ = _bwd16(idx, lut, X, syn.to_storage(dY, io), b, gpr, d, io, lut_dtype)
+    W = oracle.dequantize(idx, syn.to_float64(lut, lut_dtype), d, b, gpr)
+    assert np.array_equal(gdx, W[rows])
 
 
 @pytest.mark.parametrize("m", [80, 96])
