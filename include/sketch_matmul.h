@@ -38,6 +38,17 @@
  * fp32 accumulation. The table gradient's dY^T X product always uses the
  * activations' own dtype.
  *
+ * Range of the (BF16, F16) pair: f16 holds a far narrower range than bf16,
+ * so before the conversion every token row of X (forward) or dY (dX) is
+ * multiplied by a power of two 2^-e chosen from the row's largest magnitude
+ * (which lands in [2^14, 2^15)), and the fp32 results of that row are
+ * multiplied by 2^e afterwards. Both steps are exact, and every bf16 value at
+ * most 2^31 below its row's largest converts exactly (smaller ones to f16
+ * subnormals, an absolute error below 2^-38 of that largest), for any finite
+ * bf16 input; infinities and NaNs propagate. The exponents are computed by a
+ * pre-pass into the workspace (forward GEMM, dX, and the decode when m * d >
+ * 32768) or inside the decode kernel.
+ *
  * Alignment: every pointer must be 16-byte aligned.
  *
  * Ownership and threading: the caller allocates and owns every buffer; the
@@ -83,6 +94,11 @@ typedef enum {
  * matrix multiplication per layer; W is never materialised).
  *   X          [m][d] x_dtype     idx_packed [n][d*b/8]   lut [n][gpr][2^b]
  *   Y          [m][n] x_dtype (written, must not overlap any input)
+ * workspace/workspace_bytes: device scratch of at least
+ * sketch_matmul_fwd_workspace(...) bytes, 16-byte aligned, not overlapping
+ * any other buffer; may be NULL when that size is 0 (every dtype pair except
+ * (BF16, F16), and that pair's decode-sized calls with m * d <= 32768). It
+ * holds the row exponents of X (see "Range" above) during the call only.
  * Decode-sized m streams the indices once; larger m runs a tiled matrix-core
  * GEMM. Returns SKM_OK or an error status (see above).
  */
@@ -90,7 +106,13 @@ int sketch_matmul_fwd(const void* X, int x_dtype,
                       const uint8_t* idx_packed,
                       const void* lut, int lut_dtype,
                       int64_t m, int64_t n, int64_t d, int b, int gpr,
-                      void* Y, hipStream_t stream);
+                      void* Y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Bytes of device workspace sketch_matmul_fwd needs for these sizes (0 for
+ * invalid arguments, which the call itself then rejects). */
+size_t sketch_matmul_fwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr,
+                                   int x_dtype, int lut_dtype);
 
 /*
  * Forward pass with one table set per token, over one shared index stream
@@ -102,8 +124,10 @@ int sketch_matmul_fwd(const void* X, int x_dtype,
  *            [0, n_sets) are clamped to that range
  *   Y[t][i] = sum_j X[t][j] * luts[lut_set[t]][i][j/G][idx[i][j]]
  * Decode-sized batches (1 <= m <= 16, tables of a 16-row block within the
- * decode limit) with a 16-bit dtype pair; other sizes and the fp32 pair return
- * SKM_EUNSUPPORTED. The index stream is read from memory once; each set that
+ * decode limit) with a 16-bit dtype pair; other sizes, the fp32 pair and
+ * (BF16, F16) rows of more than 32768 columns return SKM_EUNSUPPORTED. Row
+ * exponents of the (BF16, F16) pair are found inside the kernel, so no
+ * workspace is needed. The index stream is read from memory once; each set that
  * some token uses adds its tables and one round of table lookups (one per
  * 32768 / d of its tokens when more of them than that share the set). lut_set must
  * be 4-byte aligned, the other pointers 16-byte aligned; Y must not overlap
@@ -124,7 +148,9 @@ int sketch_matmul_fwd_multi(const void* X, int x_dtype,
  *          accumulate == 0 overwrites dLUT, accumulate == 1 adds to it.
  *   dY [m][n] and X [m][d] are in io_dtype; X may be NULL when dLUT is NULL.
  * workspace/workspace_bytes: device scratch of at least
- * sketch_matmul_bwd_workspace(...) bytes (may be NULL when that is 0).
+ * sketch_matmul_bwd_workspace(...) bytes, 16-byte aligned, not overlapping
+ * any other buffer (may be NULL when that is 0). With (BF16, F16) it holds
+ * the row exponents of dY during the call; its contents are not kept.
  * Gradients are sums over the columns that share an entry (chain rule of the
  * corrected Eq. (6)), not averages. With m == 0 and accumulate == 0 the
  * requested gradients are written as zeros.

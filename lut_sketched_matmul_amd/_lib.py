@@ -41,7 +41,8 @@ _c_f32 = ctypes.c_float
 
 _SIGNATURES = {
     "sketch_matmul_fwd": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
-                                   _c_vp, _c_vp]),
+                                   _c_vp, _c_vp, _c_size, _c_vp]),
+    "sketch_matmul_fwd_workspace": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int]),
     "sketch_matmul_fwd_multi": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_vp, _c_int, _c_i64, _c_i64, _c_i64,
                                          _c_int, _c_int, _c_vp, _c_vp]),
     "sketch_matmul_bwd": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
@@ -174,11 +175,28 @@ def _matrix(t, name: str):
     return t.shape
 
 
-def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=None):
+def sketch_matmul_fwd_workspace(m: int, n: int, d: int, b: int, gpr: int, x_dtype: int, lut_dtype: int) -> int:
+    """Bytes of device workspace sketch_matmul_fwd needs for these sizes and dtypes."""
+    return int(lib().sketch_matmul_fwd_workspace(m, n, d, b, gpr, x_dtype, lut_dtype))
+
+
+def _workspace(ws, need: int, device):
+    """The caller's workspace (checked), or a new one of `need` bytes, or None."""
+    torch = _torch()
+    if ws is not None:
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, {need} needed")
+        return ws
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+
+
+def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, workspace=None, stream=None):
     """Y = X W^T with W[i, j] = lut[i, j // (d/gpr), idx[i, j]].
 
     X [m, d] (f32/f16/bf16), idx_packed [n, d*b/8] uint8, lut [n, gpr, 2^b].
-    Returns Y [m, n] in X's dtype.
+    Returns Y [m, n] in X's dtype. workspace: optional uint8 device buffer of
+    at least sketch_matmul_fwd_workspace(...) bytes (allocated here when
+    needed and omitted).
     """
     torch = _torch()
     m, d = _matrix(X, "X")
@@ -186,11 +204,15 @@ def sketch_matmul_fwd(X, idx_packed, lut, b: int, gpr: int, out=None, stream=Non
     _expect(X, "X", dtypes=_FLOAT_DTYPES)
     _check_sketch(idx_packed, lut, n, d, b, gpr)
     _expect(out, "out", shape=(m, n), dtypes=(_dtype_name(X),))
-    _require_device(X, idx_packed, lut, out)
+    _expect(workspace, "workspace", dtypes=("uint8",))
+    _require_device(X, idx_packed, lut, out, workspace)
     if out is None:
         out = torch.empty((m, n), dtype=X.dtype, device=X.device)
+    ws = _workspace(workspace, sketch_matmul_fwd_workspace(m, n, d, b, gpr, dtype_code(X), dtype_code(lut)),
+                    X.device)
     st = lib().sketch_matmul_fwd(X.data_ptr(), dtype_code(X), idx_packed.data_ptr(), lut.data_ptr(),
                                  dtype_code(lut), m, n, d, b, gpr, out.data_ptr() if out.numel() else None,
+                                 ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
                                  _stream_ptr(stream))
     _check("sketch_matmul_fwd", st)
     return out
@@ -260,9 +282,8 @@ def sketch_matmul_bwd(dY, X, idx_packed, lut, b: int, gpr: int, d: Optional[int]
     dL = None
     if need_dlut:
         dL = dlut_out if dlut_out is not None else torch.empty((n, gpr, K), dtype=torch.float32, device=dY.device)
-    ws_bytes = lib().sketch_matmul_bwd_workspace(m, n, d, b, gpr, dtype_code(dY), dtype_code(lut))
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dY.device)
+    workspace = _workspace(workspace, sketch_matmul_bwd_workspace(m, n, d, b, gpr, dtype_code(dY), dtype_code(lut)),
+                           dY.device)
     st = lib().sketch_matmul_bwd(
         dY.data_ptr() if dY.numel() else None, X.data_ptr() if (X is not None and X.numel()) else None,
         dtype_code(dY), idx_packed.data_ptr(), lut.data_ptr(), dtype_code(lut), m, n, d, b, gpr,

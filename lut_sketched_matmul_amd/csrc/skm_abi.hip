@@ -53,6 +53,20 @@ int status_of(hipError_t e) { return e == hipSuccess ? SKM_OK : SKM_EHIP; }
 // finite and at least lo
 bool finite_in(float v, float lo) { return std::isfinite(v) && v >= lo; }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// bf16 activations with f16 tables: the matrix-core operands are f16, and
+// the activations (forward) or output gradients (dX) are prescaled per row
+bool prescaled_pair(int x_dt, int lut_dt) { return x_dt == SKM_BF16 && lut_dt == SKM_F16; }
+
+// whether a forward call of these sizes reads row exponents of X from the
+// workspace (the GEMM, and the decode when it does not stage its activations)
+bool fwd_reads_rexp(const Problem& p, int x_dt, int lut_dt) {
+  if (!prescaled_pair(x_dt, lut_dt) || p.m < 1) return false;
+  if (skm::decode_supported(p)) return !skm::decode_stages_activations(p, false, 1, true);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,27 +112,45 @@ int sketch_dequant(const uint8_t* idx_packed, const void* lut, int lut_dtype, in
   return status_of(skm::launch_dequant(idx_packed, lut, lut_dtype, p, W, stream));
 }
 
+size_t sketch_matmul_fwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr, int x_dtype, int lut_dtype) {
+  if (check_shape(m, n, d, b, gpr) != SKM_OK || !supported_pair(x_dtype, lut_dtype)) return 0;
+  const Problem p{m, n, d, b, gpr};
+  return fwd_reads_rexp(p, x_dtype, lut_dtype) ? align256((size_t)m * 4) : 0;
+}
+
 int sketch_matmul_fwd(const void* X, int x_dtype, const uint8_t* idx_packed, const void* lut, int lut_dtype,
-                      int64_t m, int64_t n, int64_t d, int b, int gpr, void* Y, hipStream_t stream) {
+                      int64_t m, int64_t n, int64_t d, int b, int gpr, void* Y, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   int st = check_shape(m, n, d, b, gpr);
   if (st != SKM_OK) return st;
   if (!supported_pair(x_dtype, lut_dtype)) return SKM_EUNSUPPORTED;
   if (!idx_packed || !lut) return SKM_EINVAL;
   if (m > 0 && (!X || !Y)) return SKM_EINVAL;
-  if (!aligned16(idx_packed) || !aligned16(lut) || (X && !aligned16(X)) || (Y && !aligned16(Y))) return SKM_EALIGN;
+  if (!aligned16(idx_packed) || !aligned16(lut) || (X && !aligned16(X)) || (Y && !aligned16(Y)) ||
+      (workspace && !aligned16(workspace)))
+    return SKM_EALIGN;
+  const size_t ws_need = sketch_matmul_fwd_workspace(m, n, d, b, gpr, x_dtype, lut_dtype);
+  if (workspace_bytes < ws_need || (ws_need && !workspace)) return SKM_EWORKSPACE;
   const int xs = elem_bytes(x_dtype), ls = elem_bytes(lut_dtype);
-  const Range out{Y, m * n * xs};
-  if (overlap(out, {X, m * d * xs}) || overlap(out, {idx_packed, n * d * b / 8}) ||
-      overlap(out, {lut, n * gpr * (int64_t(1) << b) * ls}))
-    return SKM_EALIAS;
+  const Range out{Y, m * n * xs}, ws{workspace, (int64_t)ws_need};
+  const Range ins[3] = {{X, m * d * xs}, {idx_packed, n * d * b / 8}, {lut, n * gpr * (int64_t(1) << b) * ls}};
+  for (const Range& r : ins)
+    if (overlap(out, r) || overlap(ws, r)) return SKM_EALIAS;
+  if (overlap(out, ws)) return SKM_EALIAS;
   if (m == 0) return SKM_OK;
   const Problem p{m, n, d, b, gpr};
   if (x_dtype == SKM_F32)
     return status_of(skm::launch_fwd_f32((const float*)X, idx_packed, (const float*)lut, p, (float*)Y, stream));
+  int32_t* rexp = nullptr;
+  if (ws_need) {
+    rexp = static_cast<int32_t*>(workspace);
+    st = status_of(skm::launch_row_exp(X, m, d, rexp, stream));
+    if (st != SKM_OK) return st;
+  }
   if (skm::decode_supported(p))
-    return status_of(skm::launch_decode(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, stream));
+    return status_of(skm::launch_decode(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, rexp, stream));
   if (skm::gemm_fwd_supported(p))
-    return status_of(skm::launch_gemm_fwd(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, stream));
+    return status_of(skm::launch_gemm_fwd(X, x_dtype, idx_packed, lut, lut_dtype, p, Y, rexp, stream));
   return SKM_EUNSUPPORTED;
 }
 
@@ -140,13 +172,20 @@ int sketch_matmul_fwd_multi(const void* X, int x_dtype, const uint8_t* idx_packe
     return SKM_EALIAS;
   if (m == 0) return SKM_OK;
   const Problem p{m, n, d, b, gpr};
-  if (x_dtype == SKM_F32 || !skm::decode_supported(p)) return SKM_EUNSUPPORTED;
+  if (x_dtype == SKM_F32 || !skm::decode_multi_supported(p, prescaled_pair(x_dtype, lut_dtype)))
+    return SKM_EUNSUPPORTED;
   return status_of(skm::launch_decode_multi(X, x_dtype, idx_packed, luts, lut_dtype, lut_set, n_sets, p, Y, stream));
 }
 
+// Backward workspace: [row exponents of dY: m int32, 256-byte aligned]
+// (bf16 dY with f16 tables, read by dX)
+size_t bwd_rexp_bytes(int64_t m, int io_dtype, int lut_dtype) {
+  return prescaled_pair(io_dtype, lut_dtype) && m > 0 ? align256((size_t)m * 4) : 0;
+}
+
 size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr, int io_dtype, int lut_dtype) {
-  (void)m; (void)n; (void)d; (void)b; (void)gpr; (void)io_dtype; (void)lut_dtype;
-  return 0;
+  if (check_shape(m, n, d, b, gpr) != SKM_OK || !supported_pair(io_dtype, lut_dtype)) return 0;
+  return bwd_rexp_bytes(m, io_dtype, lut_dtype);
 }
 
 int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t* idx_packed, const void* lut,
@@ -160,17 +199,17 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
   if (m > 0 && !dY && (dX || dLUT)) return SKM_EINVAL;
   if (m > 0 && dLUT && !X) return SKM_EINVAL;
   if (!aligned16(idx_packed) || !aligned16(lut) || (dY && !aligned16(dY)) || (X && !aligned16(X)) ||
-      (dX && !aligned16(dX)) || (dLUT && !aligned16(dLUT)))
+      (dX && !aligned16(dX)) || (dLUT && !aligned16(dLUT)) || (workspace && !aligned16(workspace)))
     return SKM_EALIGN;
-  if (workspace_bytes < sketch_matmul_bwd_workspace(m, n, d, b, gpr, io_dtype, lut_dtype)) return SKM_EWORKSPACE;
-  (void)workspace;
+  const size_t ws_need = sketch_matmul_bwd_workspace(m, n, d, b, gpr, io_dtype, lut_dtype);
+  if (workspace_bytes < ws_need || (ws_need && !workspace)) return SKM_EWORKSPACE;
   const int xs = elem_bytes(io_dtype), ls = elem_bytes(lut_dtype);
   const int64_t K = int64_t(1) << b;
   const Range ins[4] = {{dY, m * n * xs}, {X, m * d * xs}, {idx_packed, n * d * b / 8}, {lut, n * gpr * K * ls}};
-  const Range odx{dX, m * d * 4}, odl{dLUT, n * gpr * K * 4};
+  const Range odx{dX, m * d * 4}, odl{dLUT, n * gpr * K * 4}, ows{workspace, (int64_t)ws_need};
   for (const Range& r : ins)
-    if (overlap(odx, r) || overlap(odl, r)) return SKM_EALIAS;
-  if (overlap(odx, odl)) return SKM_EALIAS;
+    if (overlap(odx, r) || overlap(odl, r) || overlap(ows, r)) return SKM_EALIAS;
+  if (overlap(odx, odl) || overlap(odx, ows) || overlap(odl, ows)) return SKM_EALIAS;
 
   const Problem p{m, n, d, b, gpr};
   if (m == 0) {
@@ -189,7 +228,13 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
   }
   if (!skm::gemm_bwd_supported(p)) return SKM_EUNSUPPORTED;
   if (dX) {
-    st = status_of(skm::launch_gemm_dx(dY, io_dtype, idx_packed, lut, lut_dtype, p, dX, stream));
+    int32_t* rexp = nullptr;
+    if (prescaled_pair(io_dtype, lut_dtype)) {
+      rexp = static_cast<int32_t*>(workspace);
+      st = status_of(skm::launch_row_exp(dY, m, n, rexp, stream));
+      if (st != SKM_OK) return st;
+    }
+    st = status_of(skm::launch_gemm_dx(dY, io_dtype, idx_packed, lut, lut_dtype, p, dX, rexp, stream));
     if (st != SKM_OK) return st;
   }
   if (dLUT) return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, stream));

@@ -97,4 +97,40 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ row_ptr, i
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// ---- per-row power-of-two prescale (bf16 activations on f16 matrix cores) ----
+// The matrix cores take both operands in one dtype. With bf16 activations and
+// f16 tables the activations are converted to f16, whose range is far
+// narrower than bf16's (largest 65504, normal values from 2^-14). A bf16 value
+// has 8 significant bits, so once scaled into f16's normal range it converts
+// exactly. Each token row therefore gets an exponent e, taken from its largest
+// magnitude: the row is multiplied by 2^-e before the conversion and each fp32
+// result of that row by 2^e after the contraction (exact: powers of two).
+// e = clamp(E - 141, -126, 113), E the biased exponent field of the row's
+// largest |value|, puts that magnitude into [2^14, 2^15): no value overflows,
+// and values down to 2^-31 of the row's largest convert exactly (smaller ones
+// round to f16 subnormals, an error below 2^-38 of the largest). Both scale
+// factors are normal fp32 numbers for every e in that range.
+constexpr bool scaled_pair(bool x_is_bf16, bool lut_is_f16) { return x_is_bf16 && lut_is_f16; }
+
+__device__ __forceinline__ int row_exp_of(uint32_t absmax_bits) {
+  const int e = (int)(absmax_bits >> 7) - 141;
+  return e < -126 ? -126 : (e > 113 ? 113 : e);
+}
+
+// 2^e as fp32 for -126 <= e <= 127
+__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23); }
+
+// largest magnitude pattern (|bf16| bits, 15 bits; NaN above infinity) of the
+// two bf16 values in a word, and of eight in four words
+__device__ __forceinline__ uint32_t absmax2_bf16(uint32_t w) {
+  const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  return lo > hi ? lo : hi;
+}
+__device__ __forceinline__ uint32_t absmax8_bf16(u32x4 v) {
+  uint32_t a = absmax2_bf16(v[0]), b = absmax2_bf16(v[1]), c = absmax2_bf16(v[2]), d = absmax2_bf16(v[3]);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
+}
+
 }  // namespace skm

@@ -32,6 +32,12 @@
 // slots s = w, w + NW, ... (slot = 4 units = 128 columns), so the waves of a
 // block read adjacent pieces of each row. The NW partial 16x16 tiles are
 // summed in LDS in wave order (deterministic) and stored once.
+//
+// bf16 activations with f16 tables take the per-row prescale of skm_common.h.
+// When the activations are staged in LDS, the block finds each staged row's
+// largest magnitude itself while staging (each wave writes its own maxima,
+// one barrier, every lane reduces the row of lane % 16); otherwise the row
+// exponents come from the caller's workspace.
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -73,6 +79,19 @@ template <int B> struct tab_entries { static constexpr int value = (B == 2) ? 16
 // through fp32 (exact widening, then one packed round-to-nearest-even convert)
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 -> f16 with every value multiplied by s (a power of two) first
+__device__ __forceinline__ u32x4 x_to_tc_scaled(u32x4 v, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f16x2_t r;
+    r.x = (half_t)(__builtin_bit_cast(float, v[q] << 16) * s);
+    r.y = (half_t)(__builtin_bit_cast(float, v[q] & 0xFFFF0000u) * s);
+    o[q] = __builtin_bit_cast(uint32_t, r);
+  }
+  return o;
+}
 
 template <typename TX, typename TC>
 __device__ __forceinline__ u32x4 x_to_tc(u32x4 v) {
@@ -286,13 +305,16 @@ template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool MU
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
          int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, TX* __restrict__ Y,
-         const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride) {
+         const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride, const int32_t* __restrict__ rexp) {
   // Dynamic LDS only (this kernel has no static LDS, so it starts at address
-  // 0): [entries][64 lanes] table dwords, [m][d] activations (XL), then the
-  // [NW][16][16] fp32 partials.
+  // 0): [entries][64 lanes] table dwords, [m][d] activations (XL), the
+  // [NW][16][16] fp32 partials, then (SC with XL) the [16 rows][NW waves]
+  // largest magnitudes of the staged activation rows.
   extern __shared__ uint32_t smem[];
   constexpr int T = tab_entries<B>::value;
   typedef mfma16<TL> MF;
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
+  static_assert(!(SC && MULTI && !XL), "prescaled multi-set decode stages its activations");
 
   const int lane = lane_id();
   // wave index as a scalar, so that the slot loop's branches are scalar
@@ -316,6 +338,11 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int64_t xl_elems =
       (int64_t)((MULTI && XL) ? (m < (int)(DEC_XL_MAX / d) ? m : (int)(DEC_XL_MAX / d)) : m) * d;
   constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
+  // SC + XL: magnitude slots [16 rows][NW] after the partials
+  const uint32_t mag_base = xl_base + (XL ? (uint32_t)((xl_elems + 7) / 8) * 16u : 0u) + (uint32_t)NW * 1024u;
+  // SC: e of the activation row (staged row with XL, token otherwise) of lane % 16
+  int erow = 0;
+  if constexpr (SC && !XL) erow = rexp[(lane & 15) < m ? (lane & 15) : m - 1];
 
   // MULTI: the block's passes, worked out once in lanes. A pass covers the
   // tokens of one set, at most `cap` of them (with XL the pass stages only its
@@ -424,27 +451,65 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     for (int c = 0; c < XCH; ++c) {
       const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
       if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
+      else xs[c] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   s0 = wave;
   if constexpr (!MULTI) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
-  if constexpr (XL && !MULTI) {
+  if constexpr (SC && XL) {
+    // largest magnitude of every staged row: per wave into its own slots
+    // (zeroed first; a wave's LDS accesses stay in order), one barrier, then
+    // lane l reduces row l % 16 over the waves
+    typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+    if (lane < 16) *(lds_u32_t*)(uintptr_t)(mag_base + ((uint32_t)lane * NW + wave) * 4u) = 0u;
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-      if (e < xl_elems) {
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+      const bool ok = MULTI ? xok[c] : e < xl_elems;
+      const uint32_t row = ok ? (uint32_t)e / (uint32_t)d : 0u;
+      const uint32_t v = ok ? absmax8_bf16(xs[c]) : 0u;
+      const uint64_t vm = __ballot(ok);
+      if (vm == 0) continue;  // wave-uniform
+      const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)row, (int)__builtin_ctzll(vm));
+      if (__ballot(ok && row != r0) == 0) {
+        uint32_t mx = v;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const uint32_t w = (uint32_t)__shfl_xor((int)mx, o, 64);
+          mx = mx > w ? mx : w;
+        }
+        if (lane == 0)
+          __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (r0 * NW + wave) * 4u), mx, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else if (ok) {
+        __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (row * NW + wave) * 4u), v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
+    __syncthreads();
+    uint32_t mx = 0;
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      const u32x4 w = lds_q16<TL>(mag_base + ((uint32_t)(lane & 15) * NW + 4u * q) * 4u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mx = mx > w[k] ? mx : w[k];
+    }
+    erow = row_exp_of(mx);
   }
-  if constexpr (XL && MULTI) {
+  if constexpr (XL) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-      if (xok[c]) {
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = x_to_tc<TX, TL>(xs[c]);
+      const bool ok = MULTI ? xok[c] : e < xl_elems;
+      u32x4 v;
+      if constexpr (SC) {
+        const int row = ok ? (int)((uint32_t)e / (uint32_t)d) : 0;
+        v = x_to_tc_scaled(xs[c], pow2f(-__shfl(erow, row, 64)));
+      } else {
+        v = x_to_tc<TX, TL>(xs[c]);
       }
+      if (ok) *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = v;
     }
   }
   // Every table and activation load has been consumed by now on the paths
@@ -476,6 +541,9 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // SC without staging: 2^-e of this lane's A row (its token)
+  const float xsc = SC && !XL ? pow2f(-erow) : 1.0f;
+  (void)xsc;
   // compute(R, first slot, tail): a batch can be partial only when it is a
   // wave's last one (tail = true); full batches carry no early exits, so every
   // path through them consumes all of their loads.
@@ -495,6 +563,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
         }
         u32x4 xv;
         if constexpr (XL) xv = lds_q16<TL>(xl_row + (Rc.u[p] * 32u + 8u * h) * 2u);
+        else if constexpr (SC) xv = x_to_tc_scaled(Rc.x[p][h], xsc);
         else xv = x_to_tc<TX, TL>(Rc.x[p][h]);
         if constexpr (RAGGED) {
           if (!Rc.ok[p]) xv = u32x4{0u, 0u, 0u, 0u};
@@ -548,7 +617,10 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool in = lpos[r] >= pstart && lpos[r] < pstart + pcnt;
-      out[r] = in ? acc[r] : out[r];
+      float v = acc[r];
+      // SC: the output row's staged row (its position in the pass) carries its exponent
+      if constexpr (SC) v *= pow2f(__shfl(erow, in ? lpos[r] - pstart : 0, 64));
+      out[r] = in ? v : out[r];
     }
     // the next pass's first index batch (from the L2), issued before the exit
     // test so that every path into the next pass has it in flight (after the
@@ -570,51 +642,61 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int t = threadIdx.x;
   if (t < 256) {
     const int token = t >> 4, rr = t & 15;
+    // SC (one set): the token's exponent from lane `token` of this wave
+    float u = 1.0f;
+    if constexpr (SC && !MULTI) u = pow2f(__shfl(erow, token, 64));
     if (token < m && row0 + rr < n) {
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < NW; ++wv) sum += red[wv * 256 + t];
+      if constexpr (SC && !MULTI) sum *= u;
       Y[(int64_t)token * n + row0 + rr] = from_f32<TX>(sum);
     }
   }
 }
 
 template <int B, int NW>
-size_t decode_lds_bytes(int gpr, int64_t x_elems) {
+size_t decode_lds_bytes(int gpr, int64_t x_elems, bool mags) {
   // x_elems is rounded up to whole 16-byte chunks so the partials stay aligned
   return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (size_t)((x_elems + 7) / 8) * 16 +
-         (size_t)NW * 256 * 4;
+         (size_t)NW * 256 * 4 + (mags ? (size_t)16 * NW * 4 : 0);
 }
 
 // Table sets for the MULTI kernel (a single set: lut_set == nullptr)
 struct SetArgs {
   const int32_t* lut_set = nullptr;
   int n_sets = 1;
-  int64_t set_stride = 0;  // table elements per set
+  int64_t set_stride = 0;          // table elements per set
+  const int32_t* rexp = nullptr;   // row exponents of X (prescaled pair without staging)
 };
 
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
 hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
                          uint32_t magic, const SetArgs& sa) {
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   // MULTI + XL stages one pass's tokens: at most min(m, DEC_XL_MAX / d) of them
   const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
-  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0);
+  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
   // (the gathers address the tables with absolute LDS addresses, see gaddr:
   // checked once per kernel, which also raises its LDS limit to 160 KB)
   if (sa.lut_set) {
-    const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
-    static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
-    if (prep != hipSuccess) return prep;
-    hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
-                       sa.lut_set, sa.n_sets, sa.set_stride);
-    return hipGetLastError();
+    if constexpr (SC && !XL) {
+      return hipErrorNotSupported;  // (the ABI routes no such call here)
+    } else {
+      const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
+      static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
+      if (prep != hipSuccess) return prep;
+      hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
+                         sa.lut_set, sa.n_sets, sa.set_stride, sa.rexp);
+      return hipGetLastError();
+    }
   }
   const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false>;
   static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
   if (prep != hipSuccess) return prep;
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
-                     sa.lut_set, sa.n_sets, sa.set_stride);
+                     sa.lut_set, sa.n_sets, sa.set_stride, sa.rexp);
   return hipGetLastError();
 }
 
@@ -624,7 +706,8 @@ hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Probl
   // one table set: stage the activations when all m rows fit. Several sets:
   // each pass stages its own tokens, so it suffices that one row fits (with a
   // single set in use, the m rows then take several passes)
-  const bool xl = p.m * p.d <= DEC_XL_MAX || (sa.lut_set && sa.n_sets > 1 && p.d <= DEC_XL_MAX);
+  const bool xl = decode_stages_activations(p, sa.lut_set != nullptr, sa.n_sets,
+                                            scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t)));
   if (p.units() % 4 != 0)
     return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic, sa)
               : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic, sa);
@@ -672,6 +755,16 @@ hipError_t decode_dispatch(const void* X, int x_dtype, const uint8_t* idx, const
 
 int decode_max_m() { return 16; }
 
+bool decode_stages_activations(const Problem& p, bool multi, int n_sets, bool scaled) {
+  // the prescaled multi-set decode always stages (it finds the exponents of
+  // the staged rows itself)
+  return p.m * p.d <= DEC_XL_MAX || (multi && (n_sets > 1 || scaled) && p.d <= DEC_XL_MAX);
+}
+
+bool decode_multi_supported(const Problem& p, bool scaled) {
+  return decode_supported(p) && (!scaled || p.d <= DEC_XL_MAX);
+}
+
 bool decode_supported(const Problem& p) {
   const int T = p.b == 2 ? 16 : p.k();
   // the magic-number division by units-per-group is exact while U * UG < 2^32
@@ -679,8 +772,10 @@ bool decode_supported(const Problem& p) {
 }
 
 hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                         const Problem& p, void* Y, hipStream_t s) {
-  return decode_dispatch(X, x_dtype, idx, lut, lut_dtype, p, Y, s, SetArgs{});
+                         const Problem& p, void* Y, const int32_t* rexp, hipStream_t s) {
+  SetArgs sa;
+  sa.rexp = rexp;
+  return decode_dispatch(X, x_dtype, idx, lut, lut_dtype, p, Y, s, sa);
 }
 
 hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,

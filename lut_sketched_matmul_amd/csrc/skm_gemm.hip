@@ -37,6 +37,10 @@
 // registers during K-step k and staged in K-step k+2 (two register stages);
 // one barrier per K-step; LDS tables (b = 2, 3) are staged one group ahead
 // into the other table buffer.
+//
+// bf16 activations with f16 tables: each token row is prescaled by 2^-e[t]
+// while it is converted (row exponents from the caller's workspace, see
+// skm_common.h) and its outputs are multiplied by 2^e[t] before rounding.
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -179,11 +183,51 @@ __device__ __forceinline__ void store_lut(const LutRegs<B>& L, uint32_t base, in
   }
 }
 
+// Store a wave's 128 x 64 outputs (acc[i][jj]: a 32 x 32 tile whose D[r][c]
+// sits in lane c (+32 for the second 4-row band) at register 4 (r / 8) + r % 4,
+// i.e. row 8 (e / 4) + 4 (lane / 32) + e % 4) rounded to TX. SC: row r of
+// the block's 256 tokens is first multiplied by 2^e[r]; the 256 factors go
+// through LDS (free after the last K-step's barrier), four tokens per read.
+template <typename TX, bool SC>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], TX* __restrict__ Y,
+                                           const int32_t* __restrict__ rexp, int64_t m, int64_t n, int64_t m0,
+                                           int64_t n0, int wm, int wn, int lane, int t) {
+  if constexpr (SC) {
+    if (t < G_BM) {
+      const int64_t tok = m0 + t < m ? m0 + t : m - 1;
+      st_w((uint32_t)t * 4u, __builtin_bit_cast(uint32_t, pow2f(rexp[tok])));
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x4 uq[4];
+    if constexpr (SC) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) uq[q] = mm::ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
+      if (col >= n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        float v = acc[i][jj][e];
+        if constexpr (SC) v *= uq[e >> 2][e & 3];
+        if (tok < m) Y[tok * n + col] = from_f32<TX>(v);
+      }
+    }
+  }
+}
+
 template <int B, typename TX, typename TL>
 __global__ void __launch_bounds__(G_THREADS, 1)
 k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
-           int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y) {
+           int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y,
+           const int32_t* __restrict__ rexp) {
   typedef mm::mfma32<TL> MF;
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
   (void)smem;
 
@@ -215,10 +259,12 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
     Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
   };
   const TX* xrow[2];
+  float xsc[2] = {1.0f, 1.0f};  // SC: 2^-e of the two staged token rows
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int64_t tok = m0 + 128 * c + (t >> 2);
     xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 3);
+    if constexpr (SC) xsc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
   }
   const uint32_t b_st0 = swz((uint32_t)r, 2u * hh), b_st1 = swz((uint32_t)r, 2u * hh + 1u);
   const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
@@ -240,8 +286,13 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
       }
       st_q(bb + b_st0, mm::dequant8_b4(S.w[0], P));
       st_q(bb + b_st1, mm::dequant8_b4(S.w[1], P));
-      st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(S.x[0]));
-      st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(S.x[1]));
+      if constexpr (SC) {
+        st_q(ab + a_st0, mm::cvt_quad_perm_scaled(S.x[0], xsc[0]));
+        st_q(ab + a_st1, mm::cvt_quad_perm_scaled(S.x[1], xsc[1]));
+      } else {
+        st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(S.x[0]));
+        st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(S.x[1]));
+      }
     } else {
       uint32_t o[8];
       const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
@@ -249,8 +300,13 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
       else dequant16<B, 0>(S, tb, lane4, o);
       st_q(bb + b_st0, u32x4{o[0], o[1], o[2], o[3]});
       st_q(bb + b_st1, u32x4{o[4], o[5], o[6], o[7]});
-      st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
-      st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
+      if constexpr (SC) {
+        st_q(ab + a_st0, mm::cvt_quad_scaled(S.x[0], xsc[0]));
+        st_q(ab + a_st1, mm::cvt_quad_scaled(S.x[1], xsc[1]));
+      } else {
+        st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
+        st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
+      }
     }
   };
   // staging work of K-step k: tile k+1 from Sn into LDS, Sn refilled with
@@ -359,18 +415,7 @@ k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, con
 
   // ---- epilogue: D[i][j] of a 32x32 tile sits in lane j (+32 for the second
   // 4-row band) at register 4*(i/8) + i%4, i.e. row 8*(e/4) + 4*(lane/32) + e%4
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
-      if (col >= n) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < m) Y[tok * n + col] = from_f32<TX>(acc[i][jj][e]);
-      }
-    }
+  store_tile<TX, SC>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
 }
 
 // ---- 64-column K-steps ------------------------------------------------------
@@ -401,8 +446,10 @@ template <int B> struct Stage64 {
 template <int B, typename TX, typename TL>
 __global__ void __launch_bounds__(G_THREADS, 1)
 k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
-             int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y) {
+             int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y,
+             const int32_t* __restrict__ rexp) {
   typedef mm::mfma32<TL> MF;
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   extern __shared__ uint32_t smem[];
   (void)smem;
 
@@ -428,10 +475,12 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
   const uint8_t* rowp = idx_packed + grow * (d * B / 8) + hh * (4 * B);
   const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
   const TX* xrow[4];
+  float xsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // SC: 2^-e of the four staged token rows
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int64_t tok = m0 + 64 * c + (t >> 3);
     xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 7);
+    if constexpr (SC) xsc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
   }
   auto load_stage = [&](Stage64<B>& S, int j) {
     const uint8_t* p = rowp + (int64_t)j * (8 * B);
@@ -476,8 +525,11 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
 #pragma unroll
       for (int q = 0; q < 4; ++q) st_q(bb + swz128((uint32_t)r, 4u * hh + q), mm::dequant8_b4(St.w[q], P));
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad_perm<TX, TL>(St.x[c]));
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+        if constexpr (SC) st_q(a, mm::cvt_quad_perm_scaled(St.x[c], xsc[c]));
+        else st_q(a, mm::cvt_quad_perm<TX, TL>(St.x[c]));
+      }
     } else {
       const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
       uint32_t o0[8], o1[8];
@@ -497,8 +549,11 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
       st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
       st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), mm::cvt_quad<TX, TL>(St.x[c]));
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+        if constexpr (SC) st_q(a, mm::cvt_quad_scaled(St.x[c], xsc[c]));
+        else st_q(a, mm::cvt_quad<TX, TL>(St.x[c]));
+      }
     }
   };
   // staging work of step k: tile k+1 into the other buffer, S refilled with
@@ -598,22 +653,12 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     __syncthreads();
   }
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
-      if (col >= n) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < m) Y[tok * n + col] = from_f32<TX>(acc[i][jj][e]);
-      }
-    }
+  store_tile<TX, SC>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
 }
 
 template <int B, typename TX, typename TL>
-hipError_t gemm_fwd_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
+hipError_t gemm_fwd_b(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y,
+                      const int32_t* rexp, hipStream_t s) {
   const int64_t mb = (p.m + G_BM - 1) / G_BM;
   const int64_t nb = (p.n + G_BN - 1) / G_BN;
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
@@ -623,23 +668,24 @@ hipError_t gemm_fwd_b(const TX* X, const uint8_t* idx, const TL* lut, const Prob
     static const hipError_t prep = prepare_kernel((const void*)kern, LDS64_TOTAL);
     if (prep != hipSuccess) return prep;
     hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(G_THREADS), LDS64_TOTAL, s, X, idx, lut, p.m, p.n,
-                       p.d, p.gpr, magic, mb, Y);
+                       p.d, p.gpr, magic, mb, Y, rexp);
     return hipGetLastError();
   }
   const auto kern = k_gemm_fwd<B, TX, TL>;
   static const hipError_t prep = prepare_kernel((const void*)kern, LDS_TOTAL);
   if (prep != hipSuccess) return prep;
   hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(G_THREADS), LDS_TOTAL, s, X, idx, lut, p.m, p.n, p.d,
-                     p.gpr, magic, mb, Y);
+                     p.gpr, magic, mb, Y, rexp);
   return hipGetLastError();
 }
 
 template <typename TX, typename TL>
-hipError_t gemm_fwd_t(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s) {
+hipError_t gemm_fwd_t(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, const int32_t* rexp,
+                      hipStream_t s) {
   switch (p.b) {
-    case 2: return gemm_fwd_b<2>(X, idx, lut, p, Y, s);
-    case 3: return gemm_fwd_b<3>(X, idx, lut, p, Y, s);
-    default: return gemm_fwd_b<4>(X, idx, lut, p, Y, s);
+    case 2: return gemm_fwd_b<2>(X, idx, lut, p, Y, rexp, s);
+    case 3: return gemm_fwd_b<3>(X, idx, lut, p, Y, rexp, s);
+    default: return gemm_fwd_b<4>(X, idx, lut, p, Y, rexp, s);
   }
 }
 
@@ -651,14 +697,14 @@ bool gemm_fwd_supported(const Problem& p) {
 }
 
 hipError_t launch_gemm_fwd(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                           const Problem& p, void* Y, hipStream_t s) {
+                           const Problem& p, void* Y, const int32_t* rexp, hipStream_t s) {
   if (x_dtype == DT_F16 && lut_dtype == DT_F16)
-    return gemm_fwd_t((const half_t*)X, idx, (const half_t*)lut, p, (half_t*)Y, s);
+    return gemm_fwd_t((const half_t*)X, idx, (const half_t*)lut, p, (half_t*)Y, nullptr, s);
   if (x_dtype == DT_BF16 && lut_dtype == DT_F16)
-    return gemm_fwd_t((const bf16_t*)X, idx, (const half_t*)lut, p, (bf16_t*)Y, s);
+    return gemm_fwd_t((const bf16_t*)X, idx, (const half_t*)lut, p, (bf16_t*)Y, rexp, s);
   if (x_dtype == DT_F16 && lut_dtype == DT_BF16)
-    return gemm_fwd_t((const half_t*)X, idx, (const bf16_t*)lut, p, (half_t*)Y, s);
-  return gemm_fwd_t((const bf16_t*)X, idx, (const bf16_t*)lut, p, (bf16_t*)Y, s);
+    return gemm_fwd_t((const half_t*)X, idx, (const bf16_t*)lut, p, (half_t*)Y, nullptr, s);
+  return gemm_fwd_t((const bf16_t*)X, idx, (const bf16_t*)lut, p, (bf16_t*)Y, nullptr, s);
 }
 
 }  // namespace skm

@@ -20,6 +20,10 @@
 // columns; with b = 4 it looks its weights up in registers (mm::dequant8_b4)
 // from a table loaded with each step's index words.
 //
+// bf16 dY with f16 tables: each token row of dY is prescaled by 2^-e[t]
+// while it is converted to f16 (row exponents from the caller's workspace,
+// see skm_common.h) and its dX row is multiplied by 2^e[t] when stored.
+//
 // k_gemm_dlut: one block owns 128 rows x one group. For each chunk of up to
 // 512 columns of the group it accumulates the dW = dY^T X tile over all
 // tokens (K = 32 tokens per step; the operand tiles are stored as loaded,
@@ -64,6 +68,17 @@ template <int NG> struct DxLds {
   static constexpr uint32_t B = A + 2u * DX_TA;
   static constexpr uint32_t TOTAL = B + 2u * DX_TB;
 };
+
+// Per-token factors 2^e of the block's 256 tokens into LDS at 0 (the table
+// area, free once the last K-step's barrier has passed), then the factors of
+// four consecutive tokens per read.
+__device__ __forceinline__ void dx_factors_to_lds(const int32_t* __restrict__ rexp, int64_t m, int64_t m0, int t) {
+  if (t < 256) {
+    const int64_t tok = m0 + t < m ? m0 + t : m - 1;
+    st_w((uint32_t)t * 4u, __builtin_bit_cast(uint32_t, pow2f(rexp[tok])));
+  }
+  __syncthreads();
+}
 
 template <int B> struct DxStage {
   u32x4 y[2];
@@ -147,8 +162,10 @@ __device__ __forceinline__ void dx_lut_store(const DxLutWord<B>& L, uint32_t eba
 template <int B, int NG, typename TX, typename TL>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut, int64_t m,
-          int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX) {
+          int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX,
+          const int32_t* __restrict__ rexp) {
   typedef mfma32<TL> MF;
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   typedef DxLds<NG> LDS;
   constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
   extern __shared__ uint32_t smem[];
@@ -181,10 +198,12 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
   const int part = wave;
   // ---- dY role: chunk t % 4 of token rows t / 4 + 128 c
   const TX* yrow[2];
+  float ysc[2] = {1.0f, 1.0f};  // SC: 2^-e of the two staged token rows
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int64_t tok = m0 + 128 * c + (t >> 2);
     yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+    if constexpr (SC) ysc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
   }
   const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
   const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
@@ -234,8 +253,13 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
     st_q(bb, ok ? u32x4{o[0], o[1], o[2], o[3]} : z);
     st_q(bb + 16u, ok ? u32x4{o[4], o[5], o[6], o[7]} : z);
     const uint32_t ab = LDS::A + buf * DX_TA;
-    st_q(ab + a_st0, cvt_quad<TX, TL>(S.y[0]));
-    st_q(ab + a_st1, cvt_quad<TX, TL>(S.y[1]));
+    if constexpr (SC) {
+      st_q(ab + a_st0, cvt_quad_scaled(S.y[0], ysc[0]));
+      st_q(ab + a_st1, cvt_quad_scaled(S.y[1], ysc[1]));
+    } else {
+      st_q(ab + a_st0, cvt_quad<TX, TL>(S.y[0]));
+      st_q(ab + a_st1, cvt_quad<TX, TL>(S.y[1]));
+    }
   };
   DxLutWord<B> LW[NG];
   auto lut_load = [&](int j) {
@@ -342,8 +366,14 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
   }
   if (k < KS) step(k, S1);
 
+  if constexpr (SC) dx_factors_to_lds(rexp, m, m0, t);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    f32x4 uq[4];
+    if constexpr (SC) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
+    }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
@@ -351,9 +381,12 @@ k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, con
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < m) dX[tok * d + col] = acc[i][jj][e];
+        float v = acc[i][jj][e];
+        if constexpr (SC) v *= uq[e >> 2][e & 3];
+        if (tok < m) dX[tok * d + col] = v;
       }
     }
+  }
 }
 
 // dX with 64 weight rows per step, for groups of >= 256 columns (a 256-column
@@ -381,8 +414,10 @@ template <int B> struct Dx6Stage {
 template <int B, typename TX, typename TL>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
-            int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX) {
+            int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX,
+            const int32_t* __restrict__ rexp) {
   typedef mfma32<TL> MF;
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   constexpr int NG = 2;
   constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
   extern __shared__ uint32_t smem[];
@@ -417,10 +452,12 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
   const int part = wave;
   // ---- dY role: chunk t % 8 of token rows t / 8 + 64 c
   const TX* yrow[4];
+  float ysc[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // SC: 2^-e of the four staged token rows
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int64_t tok = m0 + 64 * c + (t >> 3);
     yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+    if constexpr (SC) ysc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
   }
 
   const uint8_t* urow = ucol + (int64_t)r * rbytes;  // row r of step 0
@@ -514,8 +551,11 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     }
     const uint32_t ab = D6_A + buf * D6_TA;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st_q(ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7)), cvt_quad<TX, TL>(S.y[c]));
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+      if constexpr (SC) st_q(a, cvt_quad_scaled(S.y[c], ysc[c]));
+      else st_q(a, cvt_quad<TX, TL>(S.y[c]));
+    }
   };
   DxLutWord<B> LW[NG];
   auto lut_load = [&](int j) {
@@ -618,8 +658,14 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     __syncthreads();
   }
 
+  if constexpr (SC) dx_factors_to_lds(rexp, m, m0, t);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    f32x4 uq[4];
+    if constexpr (SC) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
+    }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       // b = 4: tile column p holds column (p & ~7) + (2 (p & 3) | (p & 7) >> 2)
@@ -630,9 +676,12 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < m) dX[tok * d + col] = acc[i][jj][e];
+        float v = acc[i][jj][e];
+        if constexpr (SC) v *= uq[e >> 2][e & 3];
+        if (tok < m) dX[tok * d + col] = v;
       }
     }
+  }
 }
 
 // ============================================================================
@@ -1115,19 +1164,21 @@ uint32_t ug_magic_of(const Problem& p) {
 }
 
 template <int B, int NG, typename TX, typename TL>
-hipError_t dx_launch(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+hipError_t dx_launch(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX,
+                     const int32_t* rexp, hipStream_t s) {
   const auto kern = k_gemm_dx<B, NG, TX, TL>;
   static const hipError_t prep = prepare_kernel((const void*)kern, DxLds<NG>::TOTAL);
   if (prep != hipSuccess) return prep;
   const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
   const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
   hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), DxLds<NG>::TOTAL, s, dY, idx, lut, p.m, p.n, p.d,
-                     p.gpr, ug_magic_of(p), mb, dX);
+                     p.gpr, ug_magic_of(p), mb, dX, rexp);
   return hipGetLastError();
 }
 
 template <int B, typename TX, typename TL>
-hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, const int32_t* rexp,
+                hipStream_t s) {
   // a 256-column tile touches at most 2 groups when groups are >= 256 columns
   // wide, at most 8 (one per 32-column unit) otherwise
   if (p.group_cols() >= 256) {
@@ -1137,18 +1188,19 @@ hipError_t dx_b(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& 
     const int64_t mb = (p.m + DX_BM - 1) / DX_BM;
     const int64_t nb = (p.d + DX_BN - 1) / DX_BN;
     hipLaunchKernelGGL(kern, dim3((unsigned)(mb * nb)), dim3(512), D6_LDS, s, dY, idx, lut, p.m, p.n, p.d, p.gpr,
-                       ug_magic_of(p), mb, dX);
+                       ug_magic_of(p), mb, dX, rexp);
     return hipGetLastError();
   }
-  return dx_launch<B, 8>(dY, idx, lut, p, dX, s);
+  return dx_launch<B, 8>(dY, idx, lut, p, dX, rexp, s);
 }
 
 template <typename TX, typename TL>
-hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, hipStream_t s) {
+hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& p, float* dX, const int32_t* rexp,
+                hipStream_t s) {
   switch (p.b) {
-    case 2: return dx_b<2>(dY, idx, lut, p, dX, s);
-    case 3: return dx_b<3>(dY, idx, lut, p, dX, s);
-    default: return dx_b<4>(dY, idx, lut, p, dX, s);
+    case 2: return dx_b<2>(dY, idx, lut, p, dX, rexp, s);
+    case 3: return dx_b<3>(dY, idx, lut, p, dX, rexp, s);
+    default: return dx_b<4>(dY, idx, lut, p, dX, rexp, s);
   }
 }
 
@@ -1203,11 +1255,14 @@ hipError_t dlut_t(const TX* dY, const TX* X, const uint8_t* idx, const Problem& 
 bool gemm_bwd_supported(const Problem& p) { return p.d <= (int64_t(1) << 20); }
 
 hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                          const Problem& p, float* dX, hipStream_t s) {
-  if (io_dtype == DT_F16 && lut_dtype == DT_F16) return dx_t((const half_t*)dY, idx, (const half_t*)lut, p, dX, s);
-  if (io_dtype == DT_BF16 && lut_dtype == DT_F16) return dx_t((const bf16_t*)dY, idx, (const half_t*)lut, p, dX, s);
-  if (io_dtype == DT_F16 && lut_dtype == DT_BF16) return dx_t((const half_t*)dY, idx, (const bf16_t*)lut, p, dX, s);
-  return dx_t((const bf16_t*)dY, idx, (const bf16_t*)lut, p, dX, s);
+                          const Problem& p, float* dX, const int32_t* rexp, hipStream_t s) {
+  if (io_dtype == DT_F16 && lut_dtype == DT_F16)
+    return dx_t((const half_t*)dY, idx, (const half_t*)lut, p, dX, nullptr, s);
+  if (io_dtype == DT_BF16 && lut_dtype == DT_F16)
+    return dx_t((const bf16_t*)dY, idx, (const half_t*)lut, p, dX, rexp, s);
+  if (io_dtype == DT_F16 && lut_dtype == DT_BF16)
+    return dx_t((const half_t*)dY, idx, (const bf16_t*)lut, p, dX, nullptr, s);
+  return dx_t((const bf16_t*)dY, idx, (const bf16_t*)lut, p, dX, nullptr, s);
 }
 
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,

@@ -21,6 +21,11 @@ __device__ __forceinline__ u32x4 ld_q(uint32_t a) { return *(const lds_u32x4*)(u
 __device__ __forceinline__ void st_h(uint32_t a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (uint16_t)v; }
 __device__ __forceinline__ void st_w(uint32_t a, uint32_t v) { *(lds_u32*)(uintptr_t)a = v; }
 __device__ __forceinline__ void st_q(uint32_t a, u32x4 v) { *(lds_u32x4*)(uintptr_t)a = v; }
+// four floats (read as a float vector: this hipcc turns a bit-cast of an
+// element of a loaded integer vector, indexed in an unrolled loop, into a
+// splat of element 0)
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+__device__ __forceinline__ f32x4 ld_f4(uint32_t a) { return *(const lds_f32x4*)(uintptr_t)a; }
 
 // 64-byte rows of four 16-byte chunks; chunk c of row r is stored at
 // c ^ f(r) with f(r) = ((r >> 1) ^ (r >> 2)) & 3. gfx950's LDS serves a
@@ -192,6 +197,28 @@ __device__ __forceinline__ u32x4 cvt_quad_perm(u32x4 v) {
     }
     return u32x4{pack_tc<TC>(f[0], f[2]), pack_tc<TC>(f[4], f[6]), pack_tc<TC>(f[1], f[3]), pack_tc<TC>(f[5], f[7])};
   }
+}
+
+// The prescaled conversions of bf16 activations to f16 operands (the row
+// prescale of skm_common.h): every value is multiplied by s = 2^-e of its
+// row (exact) and then rounded to f16. cvt_quad_scaled keeps the order,
+// cvt_quad_perm_scaled produces the K order of cvt_quad_perm.
+__device__ __forceinline__ u32x4 cvt_quad_scaled(u32x4 v, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = pack_tc<half_t>(__builtin_bit_cast(float, v[q] << 16) * s, __builtin_bit_cast(float, v[q] & 0xFFFF0000u) * s);
+  return o;
+}
+__device__ __forceinline__ u32x4 cvt_quad_perm_scaled(u32x4 v, float s) {
+  float f[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __builtin_bit_cast(float, v[q] << 16) * s;
+    f[2 * q + 1] = __builtin_bit_cast(float, v[q] & 0xFFFF0000u) * s;
+  }
+  return u32x4{pack_tc<half_t>(f[0], f[2]), pack_tc<half_t>(f[4], f[6]), pack_tc<half_t>(f[1], f[3]),
+               pack_tc<half_t>(f[5], f[7])};
 }
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16

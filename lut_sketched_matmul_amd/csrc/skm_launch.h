@@ -55,21 +55,31 @@ hipError_t launch_zero_f32(float* dst, int64_t count, hipStream_t s);
 // decode: m <= decode_max_m(), tables of one 16-row block must fit in LDS
 int decode_max_m();
 bool decode_supported(const Problem& p);
+// whether the decode stages the activations in LDS (then, for bf16
+// activations with f16 tables, it finds the row exponents itself; otherwise
+// it reads them from rexp)
+bool decode_stages_activations(const Problem& p, bool multi, int n_sets, bool scaled);
+bool decode_multi_supported(const Problem& p, bool scaled);
 hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                         const Problem& p, void* Y, hipStream_t s);
+                         const Problem& p, void* Y, const int32_t* rexp, hipStream_t s);
 // decode with one table set per token: luts [n_sets][n][gpr][2^b], lut_set [m]
 hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
                                const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s);
 
-// prefill / training forward: m > 16, tiled matrix-core GEMM
+// per-row exponents of the bf16 -> f16 operand prescale (skm_common.h) of a
+// bf16 matrix A [rows][cols] into e [rows]
+hipError_t launch_row_exp(const void* A, int64_t rows, int64_t cols, int32_t* e, hipStream_t s);
+
+// prefill / training forward: m > 16, tiled matrix-core GEMM. rexp: the row
+// exponents of X (read only for bf16 activations with f16 tables)
 bool gemm_fwd_supported(const Problem& p);
 hipError_t launch_gemm_fwd(const void* X, int x_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                           const Problem& p, void* Y, hipStream_t s);
+                           const Problem& p, void* Y, const int32_t* rexp, hipStream_t s);
 
 // backward on the matrix cores (16-bit operands, fp32 results)
 bool gemm_bwd_supported(const Problem& p);
 hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
-                          const Problem& p, float* dX, hipStream_t s);
+                          const Problem& p, float* dX, const int32_t* rexp, hipStream_t s);
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
                             float* dLUT, int accumulate, hipStream_t s);
 

@@ -37,7 +37,7 @@ def test_status_strings(lib):
 
 
 def fwd(lib, X=A, xdt=1, idx=B_, lut=C, ldt=1, m=4, n=64, d=512, b=4, gpr=1, Y=Dp):
-    return lib.sketch_matmul_fwd(X, xdt, idx, lut, ldt, m, n, d, b, gpr, Y, None)
+    return lib.sketch_matmul_fwd(X, xdt, idx, lut, ldt, m, n, d, b, gpr, Y, None, 0, None)
 
 
 def test_fwd_rejects_bad_shapes(lib):

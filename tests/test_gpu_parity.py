@@ -248,6 +248,12 @@ def _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype):
 def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     idx, luts, X = _multi_case(f"multi/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}", n, d, b, gpr, len(sets),
                                n_sets, x_dtype, lut_dtype)
+    if (x_dtype, lut_dtype) == ("bf16", "f16") and d > 32768:
+        # prescaled rows are staged in LDS, which holds at most 32768 columns of a row
+        with pytest.raises(skm().SketchError) as e:
+            _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype)
+        assert e.value.status == -2
+        return
     got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype))
     want = oracle.forward_multi(syn.to_float64(X, x_dtype), idx, syn.to_float64(luts, lut_dtype), sets, b, gpr)
     assert oracle.rel_err(got, want) <= TOL16
@@ -446,3 +452,89 @@ def test_finetune_workload_sampled(wname, b):
         assert oracle.rel_err(dX[np.ix_(toks, cols)], dY64[toks] @ W[:, cols]) <= w.tol, s.name
         want_dl = oracle.backward_dlut(dY64[:, rows], X64, t["idx_packed"][rows], b, w.gpr)
         assert oracle.rel_err(dL[rows], want_dl) <= w.tol, s.name
+
+
+# ---------------------------------------------------------------------------
+# bf16 activations with f16 tables: the matrix cores take f16 operands, so the
+# activations (forward) and output gradients (dX) are prescaled per token row
+# by a power of two before the conversion. These inputs lie outside f16's
+# range (entries above 65504, rows of gradients far below 2^-14).
+# ---------------------------------------------------------------------------
+
+def _scaled_rows(tag, shape, scales):
+    """bf16 N(0, 1) rows, row t multiplied by scales[t % len(scales)] (bits)."""
+    z = syn.random_normal(tag, shape, 1.0, "f32").astype(np.float64)
+    s = np.asarray([scales[t % len(scales)] for t in range(shape[0])], dtype=np.float64)[:, None]
+    return syn.to_storage((z * s).astype(np.float32), "bf16")
+
+
+def _row_errs(got, want):
+    return [oracle.rel_err(got[t], want[t]) for t in range(want.shape[0])]
+
+
+@pytest.mark.parametrize("b,gpr,d", [(4, 8, 4096), (4, 32, 4096), (2, 8, 4096), (3, 4, 1536)])
+@pytest.mark.parametrize("sigma", [1e-6, 1e-8, 1e-20, 1e4])
+def test_dx_gradient_scales_bf16_f16(b, gpr, d, sigma):
+    """dY ~ N(0, sigma) in bf16: dX within the 16-bit tolerance at gradient scales far below f16's normal
+    range (and above its largest value). Groups of 512 and 384 columns take the 64-row dX steps, groups of
+    128 columns the 32-row steps."""
+    n, m = 256, 96
+    idx, lut, X, _ = make_case(f"dxscale/{b}/{gpr}/{d}", n, d, b, gpr, m, "bf16", "f16")
+    dY = syn.random_normal(f"dxscale/{b}/{gpr}/{d}/{sigma}", (m, n), sigma, "bf16")
+    gdx, gdl = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
+    dY64, L64 = syn.to_float64(dY, "bf16"), syn.to_float64(lut, "f16")
+    want = oracle.backward_dx(dY64, idx, L64, d, b, gpr)
+    assert oracle.rel_err(gdx, want) <= TOL16
+    assert max(_row_errs(gdx, want)) <= TOL16
+    assert oracle.rel_err(gdl, oracle.backward_dlut(dY64, syn.to_float64(X, "bf16"), idx, b, gpr)) <= TOL16
+
+
+def test_dx_rows_of_different_scales_bf16_f16():
+    """Each token row of dY at its own scale (2^-60 .. 2^40): every row of dX within the tolerance."""
+    b, gpr, n, d, m = 4, 8, 300, 4096, 70
+    idx, lut, X, _ = make_case("dxrows", n, d, b, gpr, m, "bf16", "f16")
+    dY = _scaled_rows("dxrows/dY", (m, n), [2.0 ** k for k in range(-60, 41, 10)])
+    gdx, _ = _bwd16(idx, lut, X, dY, b, gpr, d, "bf16", "f16")
+    want = oracle.backward_dx(syn.to_float64(dY, "bf16"), idx, syn.to_float64(lut, "f16"), d, b, gpr)
+    assert max(_row_errs(gdx, want)) <= TOL16
+
+
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 8, 256, 4096, 1), (4, 4, 64, 8192, 4),       # decode, activations staged in LDS
+    (4, 8, 64, 4096, 16), (3, 4, 40, 16384, 3),      # decode, activations read per slot (row exponents from the workspace)
+    (4, 8, 200, 4096, 300), (2, 8, 130, 11008, 40),  # GEMM, 64- and 32-column K-steps
+    (3, 1, 33, 96, 19),
+])
+@pytest.mark.parametrize("scale", [3e4, 1e-6])
+def test_fwd_activation_scales_bf16_f16(b, gpr, n, d, m, scale):
+    """X ~ N(0, scale) in bf16: entries up to ~1e5 (beyond f16's largest) or rows far below f16's normal
+    range, through every forward path; every output row within the tolerance."""
+    idx, lut, _, _ = make_case(f"fwdscale/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, 1, "bf16", "f16")
+    X = syn.random_normal(f"fwdscale/{b}/{gpr}/{n}/{d}/{m}/{scale}", (m, d), scale, "bf16")
+    if scale > 1:
+        X[0, :4] = syn.to_storage(np.array([1e5, -1e5, 7e4, -9e4], dtype=np.float32), "bf16")
+    got, want = _fwd16(idx, lut, X, b, gpr, "bf16", "f16")
+    assert np.all(np.isfinite(got))
+    assert max(_row_errs(got, want)) <= TOL16
+
+
+@pytest.mark.parametrize("m,d", [(1, 4096), (16, 2048), (16, 4096), (300, 4096)])
+def test_fwd_rows_of_different_scales_bf16_f16(m, d):
+    """Each token row at its own scale (2^-70 .. 2^60): every output row within the tolerance."""
+    b, gpr, n = 4, 8, 96
+    idx, lut, _, _ = make_case(f"fwdrows/{m}/{d}", n, d, b, gpr, 1, "bf16", "f16")
+    X = _scaled_rows(f"fwdrows/{m}/{d}/X", (m, d), [2.0 ** k for k in range(-70, 61, 10)])
+    got, want = _fwd16(idx, lut, X, b, gpr, "bf16", "f16")
+    assert max(_row_errs(got, want)) <= TOL16
+
+
+@pytest.mark.parametrize("sets,d", [([0, 1, 2, 1], 4096), ([1] * 12 + [0] * 4, 4096), ([0, 1, 0], 16384)])
+def test_fwd_multi_scales_bf16_f16(sets, d):
+    """Several table sets: token rows at their own scales, staged pass by pass; every row within the tolerance."""
+    b, gpr, n = 4, 8, 64
+    m = len(sets)
+    idx, luts, _ = _multi_case(f"multiscale/{m}/{d}", n, d, b, gpr, 1, 3, "bf16", "f16")
+    X = _scaled_rows(f"multiscale/{m}/{d}/X", (m, d), [2.0 ** k for k in (-40, 17, -3, 30, -66, 8)])
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, "bf16", "f16"))
+    want = oracle.forward_multi(syn.to_float64(X, "bf16"), idx, syn.to_float64(luts, "f16"), sets, b, gpr)
+    assert max(_row_errs(got, want)) <= TOL16
