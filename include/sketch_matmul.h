@@ -84,7 +84,7 @@ typedef enum {
   SKM_EINVAL = -1,        /* bad size, bit width, group count or NULL pointer */
   SKM_EUNSUPPORTED = -2,  /* dtype combination not provided                   */
   SKM_EALIGN = -3,        /* a pointer is not 16-byte aligned                  */
-  SKM_EWORKSPACE = -4,    /* workspace smaller than sketch_matmul_bwd_workspace */
+  SKM_EWORKSPACE = -4,    /* workspace smaller than the size query returns      */
   SKM_EHIP = -5,          /* the HIP runtime reported a launch error           */
   SKM_EALIAS = -6         /* an output buffer overlaps an input buffer         */
 } skm_status;
@@ -149,8 +149,12 @@ int sketch_matmul_fwd_multi(const void* X, int x_dtype,
  *   dY [m][n] and X [m][d] are in io_dtype; X may be NULL when dLUT is NULL.
  * workspace/workspace_bytes: device scratch of at least
  * sketch_matmul_bwd_workspace(...) bytes, 16-byte aligned, not overlapping
- * any other buffer (may be NULL when that is 0). With (BF16, F16) it holds
- * the row exponents of dY during the call; its contents are not kept.
+ * any other buffer (may be NULL when that is 0). It holds, during the call
+ * only: with (BF16, F16), the row exponents of dY; and, when the table
+ * gradient's grid of (128-row block, group) pairs has fewer than 256 blocks
+ * (e.g. 4096 rows in one group), one partial dLUT per range of tokens the
+ * gradient is split into, added in range order at the end (deterministic; no
+ * atomics).
  * Gradients are sums over the columns that share an entry (chain rule of the
  * corrected Eq. (6)), not averages. With m == 0 and accumulate == 0 the
  * requested gradients are written as zeros.

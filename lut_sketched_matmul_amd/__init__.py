@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     sketch_lut_sgd_step,
     sketch_map,
     sketch_matmul_bwd,
+    sketch_matmul_bwd_workspace,
     sketch_matmul_fwd,
+    sketch_matmul_fwd_workspace,
     sketch_matmul_fwd_multi,
     sketch_unpack_indices,
 )

@@ -178,14 +178,17 @@ int sketch_matmul_fwd_multi(const void* X, int x_dtype, const uint8_t* idx_packe
 }
 
 // Backward workspace: [row exponents of dY: m int32, 256-byte aligned]
-// (bf16 dY with f16 tables, read by dX)
+// (bf16 dY with f16 tables, read by dX), then [partial dLUT tables of the
+// token ranges] (16-bit path, when the table gradient is split over tokens)
 size_t bwd_rexp_bytes(int64_t m, int io_dtype, int lut_dtype) {
   return prescaled_pair(io_dtype, lut_dtype) && m > 0 ? align256((size_t)m * 4) : 0;
 }
 
 size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr, int io_dtype, int lut_dtype) {
   if (check_shape(m, n, d, b, gpr) != SKM_OK || !supported_pair(io_dtype, lut_dtype)) return 0;
-  return bwd_rexp_bytes(m, io_dtype, lut_dtype);
+  const Problem p{m, n, d, b, gpr};
+  const size_t part = io_dtype == SKM_F32 || m < 1 ? 0 : skm::dlut_partial_bytes(p);
+  return bwd_rexp_bytes(m, io_dtype, lut_dtype) + part;
 }
 
 int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t* idx_packed, const void* lut,
@@ -237,7 +240,10 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
     st = status_of(skm::launch_gemm_dx(dY, io_dtype, idx_packed, lut, lut_dtype, p, dX, rexp, stream));
     if (st != SKM_OK) return st;
   }
-  if (dLUT) return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, stream));
+  if (dLUT) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_rexp_bytes(m, io_dtype, lut_dtype));
+    return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, part, stream));
+  }
   return SKM_OK;
 }
 

@@ -35,6 +35,11 @@
 // k_gemm_dlut_dma (whole 32-token steps, the common case) copies the operand
 // tiles from global memory into a three-stage LDS ring with global_load_lds
 // instead of staging them through registers.
+// When the (row block, group) grid alone has fewer blocks than the GPU has
+// CUs (e.g. 4096 rows in one group: 32 blocks), the tokens are split into
+// ranges: each block then sums one range and stores its bins into a partial
+// table of the caller's workspace, and k_dlut_reduce adds the partial tables
+// in range order (deterministic, still no atomics).
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -823,7 +828,8 @@ struct DlStage {
 template <int B, typename TX, bool VEC>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
-            int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate) {
+            int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate, int splits,
+            int64_t split_tokens, int64_t part_stride) {
   typedef mfma32<TX> MF;
   extern __shared__ uint32_t smem[];
   (void)smem;
@@ -831,8 +837,18 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int t = threadIdx.x;
   const uint32_t lane = (uint32_t)(t & 63);
   const int wave = t >> 6;
-  // the gpr groups of one row block (same dY strip) share an XCD's L2
-  const uint32_t lb = xcd_block(blockIdx.x, gridDim.x);
+  // token range (varying slowest, so an XCD's co-resident blocks share it),
+  // then the gpr groups of one row block (same dY strip) share an XCD's L2
+  const uint32_t lba = xcd_block(blockIdx.x, gridDim.x);
+  const uint32_t nb0 = gridDim.x / (uint32_t)splits;
+  const uint32_t sp = lba / nb0, lb = lba % nb0;
+  {
+    const int64_t tok0 = (int64_t)sp * split_tokens;
+    dY += tok0 * n;
+    X += tok0 * d;
+    m = m - tok0 < split_tokens ? m - tok0 : split_tokens;
+    dLUT += (int64_t)sp * part_stride;
+  }
   const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
   const int g = (int)(lb % (uint32_t)gpr);
   const int64_t G = d / gpr;
@@ -1027,7 +1043,8 @@ __device__ __forceinline__ void dd_wait_vmcnt() {
 template <int B, typename TX>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed,
-                int64_t m, int64_t n, int64_t d, int gpr, int gband, float* __restrict__ dLUT, int accumulate) {
+                int64_t m, int64_t n, int64_t d, int gpr, int gband, float* __restrict__ dLUT, int accumulate,
+                int splits, int64_t split_tokens, int64_t part_stride) {
   typedef mfma32<TX> MF;
   extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
   (void)smem;
@@ -1035,11 +1052,21 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
   const int t = threadIdx.x;
   const uint32_t lane = (uint32_t)(t & 63);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  // Consecutive logical blocks (one XCD's share, see xcd_block) take `gband`
-  // groups of consecutive row blocks: an XCD's co-resident blocks then share
-  // dY strips (same row block) and X slabs (same group) in its L2.
-  const uint32_t lb = xcd_block(blockIdx.x, gridDim.x);
-  const uint32_t rblocks = gridDim.x / (uint32_t)gpr;
+  // Consecutive logical blocks (one XCD's share, see xcd_block) take one
+  // token range (varying slowest) and in it `gband` groups of consecutive row
+  // blocks: an XCD's co-resident blocks then share dY strips (same row block)
+  // and X slabs (same group) in its L2.
+  const uint32_t lba = xcd_block(blockIdx.x, gridDim.x);
+  const uint32_t nb0 = gridDim.x / (uint32_t)splits;
+  const uint32_t sp = lba / nb0, lb = lba % nb0;
+  {
+    const int64_t tok0 = (int64_t)sp * split_tokens;
+    dY += tok0 * n;
+    X += tok0 * d;
+    m = m - tok0 < split_tokens ? m - tok0 : split_tokens;
+    dLUT += (int64_t)sp * part_stride;
+  }
+  const uint32_t rblocks = nb0 / (uint32_t)gpr;
   const uint32_t gi = lb % (uint32_t)gband, rest = lb / (uint32_t)gband;
   const int64_t i0 = (int64_t)(rest % rblocks) * DL_BM;
   const int g = (int)((rest / rblocks) * (uint32_t)gband + gi);
@@ -1204,55 +1231,106 @@ hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& 
   }
 }
 
+// Token ranges of the table gradient (see the header of this file): split
+// when the (row block, group) grid has fewer than 256 blocks, into ranges of
+// at least 4 steps of 32 tokens, none of them empty.
+struct DlutSplit {
+  int splits;
+  int64_t tokens;  // tokens per range (a multiple of 32)
+};
+DlutSplit dlut_split_of(const Problem& p) {
+  const int64_t nb0 = (p.n + DL_BM - 1) / DL_BM * p.gpr;
+  const int64_t steps = (p.m + DL_BK - 1) / DL_BK;
+  int64_t sp = nb0 >= 256 ? 1 : (256 + nb0 - 1) / nb0;
+  if (sp > steps / 4) sp = steps / 4;
+  if (sp <= 1) return {1, steps * DL_BK};
+  const int64_t per = (steps + sp - 1) / sp;
+  return {(int)((steps + per - 1) / per), per * DL_BK};
+}
+
+// dLUT = (accumulate ? dLUT : 0) + sum over the ranges of the partial tables,
+// in range order; four entries per thread (the entry count n * gpr * 2^b is a
+// multiple of 4)
+__global__ void __launch_bounds__(256) k_dlut_reduce(const float* __restrict__ part, int splits, int64_t count,
+                                                     float* __restrict__ dLUT, int accumulate) {
+  const int64_t q = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (q >= count) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + q);
+  for (int k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(part + (int64_t)k * count + q);
+  f32x4* dst = reinterpret_cast<f32x4*>(dLUT + q);
+  *dst = accumulate ? *dst + s : s;
+}
+
+hipError_t dlut_reduce(const float* part, int splits, int64_t count, float* dLUT, int accumulate, hipStream_t s) {
+  const int64_t threads = count / 4;
+  hipLaunchKernelGGL(k_dlut_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, splits, count,
+                     dLUT, accumulate);
+  return hipGetLastError();
+}
+
 template <int B, typename TX, bool VEC>
 hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
-                       hipStream_t s) {
+                       float* part, hipStream_t s) {
   const auto kern = k_gemm_dlut<B, TX, VEC>;
   static const hipError_t prep = prepare_kernel((const void*)kern, DL_LDS);
   if (prep != hipSuccess) return prep;
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr, dLUT,
-                     accumulate);
-  return hipGetLastError();
+  const DlutSplit sp = dlut_split_of(p);
+  const int64_t count = p.n * p.gpr * p.k();
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.splits)), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n, p.d,
+                     p.gpr, sp.splits > 1 ? part : dLUT, sp.splits > 1 ? 0 : accumulate, sp.splits, sp.tokens, count);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sp.splits > 1) e = dlut_reduce(part, sp.splits, count, dLUT, accumulate, s);
+  return e;
 }
 
 template <int B, typename TX>
 hipError_t dlut_dma_launch(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT,
-                           int accumulate, hipStream_t s) {
+                           int accumulate, float* part, hipStream_t s) {
   const auto kern = k_gemm_dlut_dma<B, TX>;
   static const hipError_t prep = prepare_kernel((const void*)kern, DD_LDS);
   if (prep != hipSuccess) return prep;
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
   // bands of 4 groups (or 2, or 1) in the XCD-local block order
   const int gband = p.gpr % 4 == 0 ? 4 : (p.gpr % 2 == 0 ? 2 : 1);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d, p.gpr,
-                     gband, dLUT, accumulate);
-  return hipGetLastError();
+  const DlutSplit sp = dlut_split_of(p);
+  const int64_t count = p.n * p.gpr * p.k();
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.splits)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d,
+                     p.gpr, gband, sp.splits > 1 ? part : dLUT, sp.splits > 1 ? 0 : accumulate, sp.splits, sp.tokens,
+                     count);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sp.splits > 1) e = dlut_reduce(part, sp.splits, count, dLUT, accumulate, s);
+  return e;
 }
 
 template <int B, typename TX>
 hipError_t dlut_b(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
-                  hipStream_t s) {
+                  float* part, hipStream_t s) {
   // DMA staging: whole 32-token steps and 16-byte aligned dY rows
   if (p.m % DL_BK == 0 && p.n % 8 == 0)
-    return dlut_dma_launch<B, TX>(dY, X, idx, p, dLUT, accumulate, s);
-  if (p.n % 8 == 0) return dlut_launch<B, TX, true>(dY, X, idx, p, dLUT, accumulate, s);
-  return dlut_launch<B, TX, false>(dY, X, idx, p, dLUT, accumulate, s);
+    return dlut_dma_launch<B, TX>(dY, X, idx, p, dLUT, accumulate, part, s);
+  if (p.n % 8 == 0) return dlut_launch<B, TX, true>(dY, X, idx, p, dLUT, accumulate, part, s);
+  return dlut_launch<B, TX, false>(dY, X, idx, p, dLUT, accumulate, part, s);
 }
 
 template <typename TX>
 hipError_t dlut_t(const TX* dY, const TX* X, const uint8_t* idx, const Problem& p, float* dLUT, int accumulate,
-                  hipStream_t s) {
+                  float* part, hipStream_t s) {
   switch (p.b) {
-    case 2: return dlut_b<2>(dY, X, idx, p, dLUT, accumulate, s);
-    case 3: return dlut_b<3>(dY, X, idx, p, dLUT, accumulate, s);
-    default: return dlut_b<4>(dY, X, idx, p, dLUT, accumulate, s);
+    case 2: return dlut_b<2>(dY, X, idx, p, dLUT, accumulate, part, s);
+    case 3: return dlut_b<3>(dY, X, idx, p, dLUT, accumulate, part, s);
+    default: return dlut_b<4>(dY, X, idx, p, dLUT, accumulate, part, s);
   }
 }
 
 }  // namespace
 
 bool gemm_bwd_supported(const Problem& p) { return p.d <= (int64_t(1) << 20); }
+
+size_t dlut_partial_bytes(const Problem& p) {
+  const DlutSplit sp = dlut_split_of(p);
+  return sp.splits > 1 ? (size_t)sp.splits * (size_t)(p.n * p.gpr * p.k()) * 4 : 0;
+}
 
 hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
                           const Problem& p, float* dX, const int32_t* rexp, hipStream_t s) {
@@ -1266,9 +1344,9 @@ hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, cons
 }
 
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
-                            float* dLUT, int accumulate, hipStream_t s) {
-  if (io_dtype == DT_F16) return dlut_t((const half_t*)dY, (const half_t*)X, idx, p, dLUT, accumulate, s);
-  return dlut_t((const bf16_t*)dY, (const bf16_t*)X, idx, p, dLUT, accumulate, s);
+                            float* dLUT, int accumulate, float* part, hipStream_t s) {
+  if (io_dtype == DT_F16) return dlut_t((const half_t*)dY, (const half_t*)X, idx, p, dLUT, accumulate, part, s);
+  return dlut_t((const bf16_t*)dY, (const bf16_t*)X, idx, p, dLUT, accumulate, part, s);
 }
 
 }  // namespace skm

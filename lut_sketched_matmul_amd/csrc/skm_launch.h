@@ -80,8 +80,12 @@ hipError_t launch_gemm_fwd(const void* X, int x_dtype, const uint8_t* idx, const
 bool gemm_bwd_supported(const Problem& p);
 hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,
                           const Problem& p, float* dX, const int32_t* rexp, hipStream_t s);
+// dLUT; when the (128-row block, group) grid is small the tokens are split
+// into ranges whose partial tables (dlut_partial_bytes(p) bytes, 0 when not
+// split) go to `part` and are then added in range order
+size_t dlut_partial_bytes(const Problem& p);
 hipError_t launch_gemm_dlut(const void* dY, const void* X, int io_dtype, const uint8_t* idx, const Problem& p,
-                            float* dLUT, int accumulate, hipStream_t s);
+                            float* dLUT, int accumulate, float* part, hipStream_t s);
 
 // sketch construction: column weights 1 / [H^-1]_jj from the factor U, the
 // weighted Lloyd tables, and the error-compensated mapping (Wc is overwritten;

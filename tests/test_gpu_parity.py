@@ -538,3 +538,56 @@ def test_fwd_multi_scales_bf16_f16(sets, d):
     got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, "bf16", "f16"))
     want = oracle.forward_multi(syn.to_float64(X, "bf16"), idx, syn.to_float64(luts, "f16"), sets, b, gpr)
     assert max(_row_errs(got, want)) <= TOL16
+
+
+# ---------------------------------------------------------------------------
+# table gradient split over token ranges (small (row block, group) grids)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("b,gpr,n,d,m", [
+    (4, 1, 256, 512, 640),     # 2 row blocks in one group: split, whole 32-token steps (DMA kernel)
+    (2, 1, 130, 1024, 1000),   # ragged rows and a ragged last token range (register-staged kernel)
+    (3, 2, 64, 1536, 4096),    # 2 blocks, 3-bit
+    (4, 1, 96, 256, 200),      # too few tokens to split (fewer than 8 steps)
+])
+def test_dlut_split_tokens(io, b, gpr, n, d, m):
+    idx, lut, X, dY = make_case(f"dlsplit/{io}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, io)
+    gdx, gdl = _bwd16(idx, lut, X, dY, b, gpr, d, io, io)
+    L64, X64, dY64 = syn.to_float64(lut, io), syn.to_float64(X, io), syn.to_float64(dY, io)
+    assert oracle.rel_err(gdl, oracle.backward_dlut(dY64, X64, idx, b, gpr)) <= TOL16
+    assert oracle.rel_err(gdx, oracle.backward_dx(dY64, idx, L64, d, b, gpr)) <= TOL16
+    # deterministic, and accumulate adds to the given table
+    _, gdl2 = _bwd16(idx, lut, X, dY, b, gpr, d, io, io)
+    assert np.array_equal(gdl, gdl2)
+    base = np.random.default_rng(5).normal(size=gdl.shape).astype(np.float32)
+    _, acc = _bwd16(idx, lut, X, dY, b, gpr, d, io, io, accumulate=True, dlut_init=base)
+    assert np.allclose(acc, base.astype(np.float64) + gdl, rtol=0, atol=1e-6 * max(1.0, np.abs(gdl).max()))
+
+
+def test_dlut_split_bins_exact():
+    """Integer dY, one-hot X, split over token ranges: every bin sum is the exact integer."""
+    b, gpr, n, d, m = 4, 1, 256, 2048, 1024
+    idx, lut, _, _ = make_case("dlsplitbins", n, d, b, gpr, 1, "bf16", "bf16")
+    cols = np.random.default_rng(77).choice(d, m, replace=True)
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    dY = syn.random_int_valued("dlsplitbins/dY", (m, n), -3, 3, "bf16")
+    _, gdl = _bwd16(idx, lut, syn.to_storage(X, "bf16"), dY, b, gpr, d, "bf16", "bf16")
+    want = oracle.backward_dlut(syn.to_float64(dY, "bf16"), X.astype(np.float64), idx, b, gpr)
+    assert np.array_equal(gdl, want)
+
+
+def test_dlut_split_7b_gpr1_sampled():
+    """4096 x 4096 at one group per row (32 row blocks) and 8192 tokens: the gradient split over token
+    ranges, checked on sampled rows against the oracle."""
+    b, gpr, n, d, m = 4, 1, 4096, 4096, 8192
+    idx, lut, X, dY = make_case("dlsplit7b", n, d, b, gpr, m, "bf16", "f16", dy_sigma=1e-2)
+    ws = skm().sketch_matmul_bwd_workspace(m, n, d, b, gpr, skm().SKM_BF16, skm().SKM_F16)
+    assert ws >= 8 * n * 16 * 4     # the partial tables of the token ranges
+    _, dL = skm().sketch_matmul_bwd(to_dev(dY, "bf16"), to_dev(X, "bf16"), to_dev(idx, "u8"), to_dev(lut, "f16"),
+                                    b, gpr, need_dx=False)
+    dL = to_f64(dL)
+    rows = _workload_rows(n, 99)
+    want = oracle.backward_dlut(syn.to_float64(dY, "bf16")[:, rows], syn.to_float64(X, "bf16"), idx[rows], b, gpr)
+    assert oracle.rel_err(dL[rows], want) <= TOL16
