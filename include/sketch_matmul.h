@@ -168,6 +168,28 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * sketch_matmul_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid allocation). Same arguments, results
+ * and errors as sketch_matmul_bwd, whose kernels it runs; the workspace is a
+ * library-owned scratch array of 8 MiB per GPU (a static device array, held
+ * until the process ends; its address is looked up once per device on the
+ * first call). Sizes whose sketch_matmul_bwd_workspace(...) exceeds 8 MiB
+ * return SKM_EWORKSPACE (the need is 4 bytes per token with (BF16, F16) plus
+ * at most 4 MiB of split table-gradient partials, so up to about a million
+ * tokens). Allocates nothing. Calls that overlap in time on one GPU (several
+ * host threads, or streams running concurrently) share that GPU's array and
+ * race; serialise them. Nothing from an earlier call is read back (every
+ * scratch entry a call reads was written by that call).
+ */
+int sketch_matmul_bwd_noalloc(const void* dY, const void* X, int io_dtype,
+                              const uint8_t* idx_packed,
+                              const void* lut, int lut_dtype,
+                              int64_t m, int64_t n, int64_t d, int b, int gpr,
+                              float* dX, float* dLUT, int accumulate,
+                              hipStream_t stream);
+
 /* Bytes of device workspace sketch_matmul_bwd needs for these sizes (>= 0). */
 size_t sketch_matmul_bwd_workspace(int64_t m, int64_t n, int64_t d, int b, int gpr,
                                    int io_dtype, int lut_dtype);

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "sketch_matmul_bwd": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_vp, _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
     "sketch_matmul_bwd_workspace": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "sketch_matmul_bwd_noalloc": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int,
+                                           _c_int, _c_vp, _c_vp, _c_int, _c_vp]),
     "sketch_dequant": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp]),
     "sketch_unpack_indices": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
     "sketch_lut_adam_step": (_c_int, [_c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_f32, _c_f32,
@@ -292,6 +294,32 @@ def sketch_matmul_bwd(dY, X, idx_packed, lut, b: int, gpr: int, d: Optional[int]
         workspace.numel() if workspace is not None else 0, _stream_ptr(stream))
     _check("sketch_matmul_bwd", st)
     return dX, dL
+
+
+def sketch_matmul_bwd_noalloc(dY, X, idx_packed, lut, b: int, gpr: int, dx_out=None, dlut_out=None,
+                              accumulate: bool = False, stream=None) -> None:
+    """The backward pass into caller-given outputs with the library's own scratch (no allocation at all).
+
+    dY [m, n], X [m, d] in the same dtype, idx_packed [n, d*b/8] uint8, lut [n, gpr, 2^b]; dx_out fp32
+    [m, d] and dlut_out fp32 [n, gpr, 2^b] are written when given (at least one of them). Nothing is
+    allocated here or in the library; calls that overlap in time on one GPU race on its scratch.
+    """
+    m, n = _matrix(dY, "dY")
+    mx, d = _matrix(X, "X")
+    _expect(dY, "dY", dtypes=_FLOAT_DTYPES)
+    _expect(X, "X", shape=(m, d), dtypes=(_dtype_name(dY),))
+    _check_sketch(idx_packed, lut, n, d, b, gpr)
+    _expect(dx_out, "dx_out", shape=(m, d), dtypes=("float32",))
+    _expect(dlut_out, "dlut_out", shape=(n, gpr, 1 << b), dtypes=("float32",))
+    if dx_out is None and dlut_out is None:
+        raise ValueError("give dx_out, dlut_out or both")
+    _require_device(dY, X, idx_packed, lut, dx_out, dlut_out)
+    st = lib().sketch_matmul_bwd_noalloc(
+        dY.data_ptr() if dY.numel() else None, X.data_ptr() if X.numel() else None, dtype_code(dY),
+        idx_packed.data_ptr(), lut.data_ptr(), dtype_code(lut), m, n, d, b, gpr,
+        dx_out.data_ptr() if (dx_out is not None and dx_out.numel()) else None,
+        dlut_out.data_ptr() if dlut_out is not None else None, 1 if accumulate else 0, _stream_ptr(stream))
+    _check("sketch_matmul_bwd_noalloc", st)
 
 
 def sketch_dequant(idx_packed, lut, d: int, b: int, gpr: int, stream=None):

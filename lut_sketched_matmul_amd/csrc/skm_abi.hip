@@ -3,9 +3,17 @@
 #include "sketch_matmul.h"
 
 #include <cmath>
+#include <mutex>
 
 #include "skm_common.h"
 #include "skm_launch.h"
+
+// Scratch of sketch_matmul_bwd_noalloc: one array per GPU, held until the
+// process ends. Host code never uses this name as a device address: the
+// address comes from hipGetSymbolAddress, looked up once per device (see
+// noalloc_scratch below).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -245,6 +253,39 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype, const uint8_t
     return status_of(skm::launch_gemm_dlut(dY, X, io_dtype, idx_packed, p, dLUT, accumulate, part, stream));
   }
   return SKM_OK;
+}
+
+// Device address of this GPU's scratch array (the current device), looked up
+// with that device current on its first use and kept per device; nullptr on
+// failure.
+static void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+int sketch_matmul_bwd_noalloc(const void* dY, const void* X, int io_dtype, const uint8_t* idx_packed,
+                              const void* lut, int lut_dtype, int64_t m, int64_t n, int64_t d, int b, int gpr,
+                              float* dX, float* dLUT, int accumulate, hipStream_t stream) {
+  // (invalid arguments give a size of 0 and are rejected by sketch_matmul_bwd)
+  const size_t need = sketch_matmul_bwd_workspace(m, n, d, b, gpr, io_dtype, lut_dtype);
+  if (need > kScratchBytes) return SKM_EWORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = noalloc_scratch();
+    if (!ws) return SKM_EHIP;
+  }
+  return sketch_matmul_bwd(dY, X, io_dtype, idx_packed, lut, lut_dtype, m, n, d, b, gpr, dX, dLUT, accumulate, ws,
+                           ws ? kScratchBytes : 0, stream);
 }
 
 int sketch_column_weights(const float* U, int64_t d, float* h, hipStream_t stream) {

@@ -181,3 +181,9 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("SKETCHMM_LIB", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    # bf16 dY with f16 tables at 3 million tokens: 12 MB of row exponents > 8 MiB of scratch (no GPU call)
+    assert lib.sketch_matmul_bwd_noalloc(A, B_, 2, C, Dp, 1, 3_000_000, 256, 1024, 4, 1, A, None, 0, None) == EWS
+    assert lib.sketch_matmul_bwd_noalloc(A, B_, 2, C, Dp, 1, 64, 256, 1024, 5, 1, A, None, 0, None) == EINVAL
