@@ -39,21 +39,24 @@
  * activations' own dtype.
  *
  * Range of the (BF16, F16) pair: f16 holds a far narrower range than bf16,
- * so before the conversion every token row of X (forward) or dY (dX) is
- * multiplied by a power of two 2^-e chosen from the row's largest magnitude
- * (which lands in [2^14, 2^15)), and the fp32 results of that row are
- * multiplied by 2^e afterwards. Both steps are exact, and every bf16 value at
- * most 2^31 below its row's largest converts exactly (smaller ones to f16
- * subnormals, an absolute error below 2^-38 of that largest), for any finite
- * bf16 input; infinities and NaNs propagate. The exponents are computed by a
- * pre-pass into the workspace (forward GEMM, dX, and the decode when m * d >
- * 32768) or inside the decode kernel.
+ * so every token row of X (forward) or dY (dX) whose largest magnitude M
+ * lies outside [2^-2, 2^16) is multiplied by a power of two 2^-e before the
+ * conversion, with e = floor(log2 M) - 14 clamped to [-126, 113] (so that
+ * M 2^-e lands in [2^14, 2^15)), and the fp32 results of that row are
+ * multiplied by 2^e afterwards; rows inside the window are converted as they
+ * are (e = 0). Both steps are exact. After them every bf16 value of the row
+ * at or above 2^-17 (in the scaled row) converts to f16 exactly, and a
+ * smaller one with an absolute error below 2^-23 M, for any finite bf16
+ * input; infinities and NaNs propagate. The exponents come from a pre-pass
+ * into the workspace (forward GEMM, dX, and the decode when m * d > 32768)
+ * or are found inside the decode kernel.
  *
  * Alignment: every pointer must be 16-byte aligned.
  *
  * Ownership and threading: the caller allocates and owns every buffer; the
- * library never allocates, frees or keeps device memory and holds no mutable
- * global state, so calls are thread-safe. Work is enqueued on `stream`
+ * library never allocates or frees device memory and, apart from
+ * sketch_matmul_bwd_noalloc's static scratch array, keeps none and holds no
+ * mutable global state, so calls are thread-safe. Work is enqueued on `stream`
  * (NULL = the default stream) and runs asynchronously; no call synchronises.
  *
  * Errors: argument checks run on the host before anything is launched; a

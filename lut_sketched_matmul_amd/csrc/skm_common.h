@@ -101,21 +101,41 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 // The matrix cores take both operands in one dtype. With bf16 activations and
 // f16 tables the activations are converted to f16, whose range is far
 // narrower than bf16's (largest 65504, normal values from 2^-14). A bf16 value
-// has 8 significant bits, so once scaled into f16's normal range it converts
+// has 8 significant bits, so once inside f16's normal range it converts
 // exactly. Each token row therefore gets an exponent e, taken from its largest
-// magnitude: the row is multiplied by 2^-e before the conversion and each fp32
-// result of that row by 2^e after the contraction (exact: powers of two).
-// e = clamp(E - 141, -126, 113), E the biased exponent field of the row's
-// largest |value|, puts that magnitude into [2^14, 2^15): no value overflows,
-// and values down to 2^-31 of the row's largest convert exactly (smaller ones
-// round to f16 subnormals, an error below 2^-38 of the largest). Both scale
-// factors are normal fp32 numbers for every e in that range.
+// magnitude M (biased exponent field E): the row is multiplied by 2^-e before
+// the conversion and each fp32 result of that row by 2^e after the
+// contraction (exact: powers of two).
+//   * 2^-2 <= M < 2^16 (E in [125, 142]): e = 0. Every bf16 value below 2^16
+//     is a finite f16; values from 2^-14 up convert exactly, smaller ones
+//     round to f16 subnormals with an absolute error below 2^-23 M.
+//   * otherwise e = clamp(E - 141, -126, 113), which puts M into [2^14, 2^15):
+//     values down to 2^-31 M convert exactly, smaller ones round to f16
+//     subnormals with an error below 2^-38 M.
+// Both scale factors are normal fp32 numbers for every e in that range.
 constexpr bool scaled_pair(bool x_is_bf16, bool lut_is_f16) { return x_is_bf16 && lut_is_f16; }
 
 __device__ __forceinline__ int row_exp_of(uint32_t absmax_bits) {
-  const int e = (int)(absmax_bits >> 7) - 141;
+  const int E = (int)(absmax_bits >> 7);
+  if (E >= 125 && E <= 142) return 0;
+  const int e = E - 141;
   return e < -126 ? -126 : (e > 113 ? 113 : e);
 }
+
+// Rows of exponent -101 <= e <= 0 (and no others in a block) may be scaled by
+// raising the exponent field of every bf16 value by k = -e: exact for normal
+// values (their exponent stays <= 142), and a zero or subnormal becomes a
+// value below 2^-25, which rounds to f16 zero as its true scaled value does
+// (or would round to at most 2^-24). scale_mode_of gives the conversion a
+// block uses: 0 none (all e == 0), 1 exponent add (all -101 <= e <= 0),
+// 2 multiply by 2^-e.
+__device__ __forceinline__ uint32_t scale_flags_of(int e) {
+  return (e != 0 ? 1u : 0u) | ((e > 0 || e < -101) ? 2u : 0u);
+}
+__device__ __forceinline__ int scale_mode_of(uint32_t flags) { return (flags & 2u) ? 2 : (int)(flags & 1u); }
+// the word added to a pair of bf16 values (two 16-bit halves) to raise both
+// exponent fields by k (no carry leaves either half: the fields stay <= 142)
+__device__ __forceinline__ uint32_t exp_add_word(int e) { return ((uint32_t)(-e) << 7) * 0x00010001u; }
 
 // 2^e as fp32 for -126 <= e <= 127
 __device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23); }
@@ -126,6 +146,30 @@ __device__ __forceinline__ uint32_t absmax2_bf16(uint32_t w) {
   const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
   return lo > hi ? lo : hi;
 }
+// op(v) over the wave, in lane 63, with DPP row shifts and row broadcasts
+// (vector ALU only; lanes shifted in from outside a row read 0, the identity
+// of an unsigned maximum and of a bitwise or).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_to_lane63(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, true));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, true));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_to_lane63(uint32_t v) {
+  return wave_reduce_to_lane63(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_or_to_lane63(uint32_t v) {
+  return wave_reduce_to_lane63(v, [](uint32_t a, uint32_t b) { return a | b; });
+}
+
+// magnitude patterns (|bf16| bits) of 2^-2 and 2^16: rows whose largest
+// magnitude lies in [2^-2, 2^16) take no prescale (row_exp_of gives 0)
+constexpr uint32_t kNoScaleLo = 125u << 7, kNoScaleHi = 143u << 7;
+
 __device__ __forceinline__ uint32_t absmax8_bf16(u32x4 v) {
   uint32_t a = absmax2_bf16(v[0]), b = absmax2_bf16(v[1]), c = absmax2_bf16(v[2]), d = absmax2_bf16(v[3]);
   a = a > b ? a : b;

@@ -34,9 +34,20 @@
 // summed in LDS in wave order (deterministic) and stored once.
 //
 // bf16 activations with f16 tables take the per-row prescale of skm_common.h.
-// When the activations are staged in LDS, the block finds each staged row's
-// largest magnitude itself while staging (each wave writes its own maxima,
-// one barrier, every lane reduces the row of lane % 16); otherwise the row
+// When the activations are staged in LDS, the block finds the exponents
+// itself. One table set: the activations are staged unscaled and every wave
+// records, beside them, whether any value reaches 2^16 and which rows hold a
+// value of at least 2^-2; after the staging barrier every row lying in
+// [2^-2, 2^16) (row_exp_of gives 0, the common case) means nothing more is
+// done. Otherwise (block-uniform) the block re-reads its activations, finds
+// each row's largest magnitude (below), stages them again prescaled and
+// passes one more barrier. Several sets: each pass takes that exact path
+// directly. The exact path: every lane folds the maxima of its chunks in
+// registers; when all of a wave's chunks lie in one row (always for one
+// token) a DPP reduction leaves the wave's maximum in one lane, which writes
+// it to the wave's own LDS slot, else every lane adds its running maximum
+// with an LDS atomic max per run of chunks in one row; one barrier, then each
+// lane reduces the slots of the rows it needs. Without staging, the row
 // exponents come from the caller's workspace.
 #include "skm_common.h"
 #include "skm_launch.h"
@@ -304,12 +315,13 @@ __device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
 template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool MULTI>
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
-         int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, TX* __restrict__ Y,
+         int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, uint32_t d_magic, TX* __restrict__ Y,
          const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride, const int32_t* __restrict__ rexp) {
   // Dynamic LDS only (this kernel has no static LDS, so it starts at address
   // 0): [entries][64 lanes] table dwords, [m][d] activations (XL), the
-  // [NW][16][16] fp32 partials, then (SC with XL) the [16 rows][NW waves]
-  // largest magnitudes of the staged activation rows.
+  // [NW][16][16] fp32 partials; SC with XL: the partials in the activations'
+  // place at the end, then the [16 rows][NW waves] largest magnitudes of the
+  // staged activation rows and the [NW] range records.
   extern __shared__ uint32_t smem[];
   constexpr int T = tab_entries<B>::value;
   typedef mfma16<TL> MF;
@@ -338,8 +350,14 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int64_t xl_elems =
       (int64_t)((MULTI && XL) ? (m < (int)(DEC_XL_MAX / d) ? m : (int)(DEC_XL_MAX / d)) : m) * d;
   constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
-  // SC + XL: magnitude slots [16 rows][NW] after the partials
-  const uint32_t mag_base = xl_base + (XL ? (uint32_t)((xl_elems + 7) / 8) * 16u : 0u) + (uint32_t)NW * 1024u;
+  // SC + XL: the partials overlay the staged activations (after a barrier
+  // at the end), and the magnitude slots [16 rows][NW] and the waves' range
+  // records [NW] follow that region (keeping the block's LDS near the f16
+  // pair's, so as many blocks fit on a CU)
+  const uint32_t xl_bytes = XL ? (uint32_t)((xl_elems + 7) / 8) * 16u : 0u;
+  const uint32_t mag_base =
+      xl_base + (SC && XL ? (xl_bytes > (uint32_t)NW * 1024u ? xl_bytes : (uint32_t)NW * 1024u)
+                          : xl_bytes + (uint32_t)NW * 1024u);
   // SC: e of the activation row (staged row with XL, token otherwise) of lane % 16
   int erow = 0;
   if constexpr (SC && !XL) erow = rexp[(lane & 15) < m ? (lane & 15) : m - 1];
@@ -416,7 +434,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // compiler's load counts stay exact
   auto stage_src = [&](int c, int st, int cnt, bool& ok) -> const TX* {
     const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-    const int slot = (int)((uint32_t)e / (uint32_t)d);
+    const int slot = (int)__umulhi((uint32_t)e, d_magic);  // e / d
     const int col = (int)(e - (int64_t)slot * d);
     ok = slot < cnt;
     const int t = __shfl(sorted_tok, ok ? st + slot : 0, 64);
@@ -446,71 +464,114 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // the LDS stores of the first two (their loads complete first). MULTI passes
   // find their tables, activations and first index batch loaded.
   if constexpr (!MULTI) tab_load<B, NW, TL>(TR, lut, row_ok ? grow : n - 1, gpr, wave);
-  if constexpr (XL && !MULTI) {
+  // (a chunk past m*d is neither loaded nor read: giving it a value would
+  // merge it with the load at a branch, which waits for the load there)
+  auto load_x = [&]() {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
       if (e < xl_elems) xs[c] = *reinterpret_cast<const u32x4*>(X + e);
-      else xs[c] = u32x4{0u, 0u, 0u, 0u};
     }
-  }
+  };
+  if constexpr (XL && !MULTI) load_x();
   s0 = wave;
   if constexpr (!MULTI) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
-  if constexpr (SC && XL) {
-    // largest magnitude of every staged row: per wave into its own slots
-    // (zeroed first; a wave's LDS accesses stay in order), one barrier, then
-    // lane l reduces row l % 16 over the waves
-    typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
-    if (lane < 16) *(lds_u32_t*)(uintptr_t)(mag_base + ((uint32_t)lane * NW + wave) * 4u) = 0u;
-#pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
-      const bool ok = MULTI ? xok[c] : e < xl_elems;
-      const uint32_t row = ok ? (uint32_t)e / (uint32_t)d : 0u;
-      const uint32_t v = ok ? absmax8_bf16(xs[c]) : 0u;
-      const uint64_t vm = __ballot(ok);
-      if (vm == 0) continue;  // wave-uniform
-      const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)row, (int)__builtin_ctzll(vm));
-      if (__ballot(ok && row != r0) == 0) {
-        uint32_t mx = v;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const uint32_t w = (uint32_t)__shfl_xor((int)mx, o, 64);
-          mx = mx > w ? mx : w;
-        }
-        if (lane == 0)
-          __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (r0 * NW + wave) * 4u), mx, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else if (ok) {
-        __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (row * NW + wave) * 4u), v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
-    __syncthreads();
+  // SC + XL: the exponent of a staged row from the waves' slots (NW maxima)
+  auto row_slots_exp = [&](uint32_t row) -> int {
     uint32_t mx = 0;
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
-      const u32x4 w = lds_q16<TL>(mag_base + ((uint32_t)(lane & 15) * NW + 4u * q) * 4u);
+      const u32x4 w = lds_q16<TL>(mag_base + (row * NW + 4u * q) * 4u);
 #pragma unroll
       for (int k = 0; k < 4; ++k) mx = mx > w[k] ? mx : w[k];
     }
-    erow = row_exp_of(mx);
-  }
-  if constexpr (XL) {
+    return row_exp_of(mx);
+  };
+  // SC + XL, exact path: the largest magnitude of every staged row into the
+  // waves' slots, one barrier, then erow for the row of lane % 16
+  auto exact_exponents = [&]() {
+    // a wave's LDS accesses stay in order, so it zeroes its own slots first;
+    // a lane's chunks lie in non-decreasing rows, so it keeps a running
+    // maximum and adds it with one atomic max whenever the row changes
+    typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+    if (lane < 16) *(lds_u32_t*)(uintptr_t)(mag_base + ((uint32_t)lane * NW + wave) * 4u) = 0u;
+    // the row of the wave's first element: when every valid chunk of the
+    // wave lies in it, one DPP reduction and one store suffice
+    const uint32_t row0 = __umulhi((uint32_t)(64 * wave * 8), d_magic);
+    uint32_t run_row = 0u, run_max = 0u;
+    bool one_row = true;
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
       const bool ok = MULTI ? xok[c] : e < xl_elems;
-      u32x4 v;
-      if constexpr (SC) {
-        const int row = ok ? (int)((uint32_t)e / (uint32_t)d) : 0;
-        v = x_to_tc_scaled(xs[c], pow2f(-__shfl(erow, row, 64)));
-      } else {
-        v = x_to_tc<TX, TL>(xs[c]);
+      const uint32_t row = __umulhi((uint32_t)e, d_magic);  // e / d
+      if (ok) {
+        one_row = one_row && row == row0;
+        if (row != run_row && run_max != 0u)
+          __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (run_row * NW + wave) * 4u), run_max,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (row != run_row) run_max = 0u;
+        run_row = row;
+        const uint32_t v = absmax8_bf16(xs[c]);
+        run_max = run_max > v ? run_max : v;
       }
-      if (ok) *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = v;
     }
+    if (__ballot(!one_row) == 0) {  // wave-uniform: the whole wave's chunks lie in row0
+      const uint32_t mx = wave_max_to_lane63(run_max);
+      // (mx == 0: no valid chunk, or only zeros; then row0 may lie past the staged rows and the slot stays 0)
+      if (lane == 63 && mx != 0u) *(lds_u32_t*)(uintptr_t)(mag_base + (row0 * NW + wave) * 4u) = mx;
+    } else if (run_max != 0u) {
+      __hip_atomic_fetch_max((lds_u32_t*)(uintptr_t)(mag_base + (run_row * NW + wave) * 4u), run_max,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    erow = row_slots_exp((uint32_t)(lane & 15));  // for the outputs of the row of lane % 16
+  };
+  // stage the activation chunks (prescaled by their rows' exponents, looked
+  // up in the slots, or converted as they are)
+  auto store_x = [&](auto scaled) {
+    int crow = -1, cexp = 0;  // the exponent of the last chunk row looked up
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      const bool ok = MULTI ? xok[c] : e < xl_elems;
+      if (ok) {
+        u32x4 v;
+        if constexpr (decltype(scaled)::value) {
+          const int row = (int)__umulhi((uint32_t)e, d_magic);  // e / d
+          if (row != crow) {
+            crow = row;
+            cexp = row_slots_exp((uint32_t)row);
+          }
+          v = x_to_tc_scaled(xs[c], pow2f(-cexp));
+        } else {
+          v = x_to_tc<TX, TL>(xs[c]);
+        }
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xl_base + (uint32_t)e * 2u) = v;
+      }
+    }
+  };
+  if constexpr (SC && XL && MULTI) {
+    exact_exponents();
+    store_x(btag<true>{});
+  } else if constexpr (SC && XL) {
+    // range record of this wave: bit r = row r holds a magnitude >= 2^-2,
+    // bit 31 = some magnitude >= 2^16 (or an infinity or NaN)
+    uint32_t rec = 0u;
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int64_t e = ((int64_t)c * NW * 64 + threadIdx.x) * 8;
+      if (e < xl_elems) {
+        const uint32_t v = absmax8_bf16(xs[c]);
+        rec |= (v >= kNoScaleLo ? 1u << __umulhi((uint32_t)e, d_magic) : 0u) | (v >= kNoScaleHi ? 1u << 31 : 0u);
+      }
+    }
+    rec = wave_or_to_lane63(rec);
+    if (lane == 63) *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(mag_base + 64u * NW + wave * 4u) = rec;
+    store_x(btag<false>{});
+  } else if constexpr (XL) {
+    store_x(btag<false>{});
   }
   // Every table and activation load has been consumed by now on the paths
   // that store it; the ones past the row's tables (or past m*d) were issued
@@ -519,6 +580,23 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // load counting below starts from the first batch alone.
   wait_vmcnt<PF * ((B == 3 ? 3 : 1) + (XL ? 0 : 4))>();
   __syncthreads();
+  if constexpr (SC && XL && !MULTI) {
+    // every staged row inside [2^-2, 2^16): no prescale (erow stays 0);
+    // otherwise (block-uniform) re-read the activations and take the exact path
+    uint32_t all = 0u;
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      const u32x4 w = lds_q16<TL>(mag_base + 64u * NW + 16u * q);
+      all |= w[0] | w[1] | w[2] | w[3];
+    }
+    const uint32_t rows = (1u << m) - 1u;  // m <= 16 staged rows
+    if ((all >> 31) != 0u || (all & rows) != rows) {
+      load_x();
+      exact_exponents();
+      store_x(btag<true>{});
+      __syncthreads();
+    }
+  }
   // this lane's A row: its token's staged row (MULTI + XL: the token's slot in
   // the pass, or slot 0 for a token outside the pass, whose results are not kept)
   int aslot = tokc;
@@ -635,7 +713,9 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
 
   // ---- sum the NW partial tiles in wave order, then store Y[token][row]
   // lane l holds D[token 4*(l/16)+r][row l%16]
-  float* red = reinterpret_cast<float*>(smem) + (xl_base + (XL ? (uint32_t)xl_elems * 2u : 0u)) / 4u;
+  // (SC + XL: in the staged activations, once every wave is done with them)
+  if constexpr (SC && XL) __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + (xl_base + (SC && XL ? 0u : xl_bytes)) / 4u;
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave * 256 + (4 * q + r) * 16 + j] = out[r];
   __syncthreads();
@@ -657,9 +737,10 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
 
 template <int B, int NW>
 size_t decode_lds_bytes(int gpr, int64_t x_elems, bool mags) {
-  // x_elems is rounded up to whole 16-byte chunks so the partials stay aligned
-  return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (size_t)((x_elems + 7) / 8) * 16 +
-         (size_t)NW * 256 * 4 + (mags ? (size_t)16 * NW * 4 : 0);
+  // x_elems is rounded up to whole 16-byte chunks so the partials stay
+  // aligned; with the magnitude slots the partials overlay the activations
+  const size_t xb = (size_t)((x_elems + 7) / 8) * 16, pb = (size_t)NW * 256 * 4;
+  return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (mags ? (xb > pb ? xb : pb) + (size_t)17 * NW * 4 : xb + pb);
 }
 
 // Table sets for the MULTI kernel (a single set: lut_set == nullptr)
@@ -678,6 +759,9 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
   const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
+  // element e of the staged activations lies in row e / d = umulhi(e, ceil(2^32 / d)), exact for e * d < 2^32
+  // (staged elements number at most 32768 and d <= 32768 when staging)
+  const uint32_t d_magic = p.d <= DEC_XL_MAX ? (uint32_t)(((uint64_t)1 << 32) / (uint64_t)p.d) + 1u : 0u;
   // (the gathers address the tables with absolute LDS addresses, see gaddr:
   // checked once per kernel, which also raises its LDS limit to 160 KB)
   if (sa.lut_set) {
@@ -687,7 +771,7 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
       const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
       static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
       if (prep != hipSuccess) return prep;
-      hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
+      hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, d_magic, Y,
                          sa.lut_set, sa.n_sets, sa.set_stride, sa.rexp);
       return hipGetLastError();
     }
@@ -695,7 +779,7 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false>;
   static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, Y,
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, d_magic, Y,
                      sa.lut_set, sa.n_sets, sa.set_stride, sa.rexp);
   return hipGetLastError();
 }

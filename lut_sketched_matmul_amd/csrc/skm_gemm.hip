@@ -41,6 +41,11 @@
 // bf16 activations with f16 tables: each token row is prescaled by 2^-e[t]
 // while it is converted (row exponents from the caller's workspace, see
 // skm_common.h) and its outputs are multiplied by 2^e[t] before rounding.
+// The block takes one conversion for all its rows (block_scale_mode): none
+// when every e is 0 (the common case), an exponent-field add, or a multiply;
+// the prologue, K loop and store are compiled once per conversion (run<MD>),
+// so the common case runs the same loop as 16-bit activations of the table
+// dtype would.
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -201,7 +206,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], TX* __rest
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f32x4 uq[4];
+    f32x4 uq[4] = {};
     if constexpr (SC) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) uq[q] = mm::ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
@@ -226,196 +231,234 @@ __global__ void __launch_bounds__(G_THREADS, 1)
 k_gemm_fwd(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
            int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y,
            const int32_t* __restrict__ rexp) {
-  typedef mm::mfma32<TL> MF;
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
-  extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
-  (void)smem;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int64_t bm = blockIdx.x % mblocks;
-  const int64_t bn = blockIdx.x / mblocks;
-  const int64_t m0 = bm * G_BM, n0 = bn * G_BN;
-  const int U = (int)(d / 32);
-  auto group_of = [&](int k) -> uint32_t { return mm::group_of((uint32_t)k, ug_magic); };
-
-  // ---- staging state (b = 4: the two threads of a row are adjacent lanes and
-  // the tables stay in registers, as in k_gemm_fwd64)
-  const int r = B == 4 ? (t >> 1) : (t & 255);
-  const int hh = B == 4 ? (t & 1) : (t >> 8);  // wave-uniform for b = 2, 3
-  const uint32_t rq = (uint32_t)(wave & 3);    // row quarter of r (b = 2, 3)
-  const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
-  const uint8_t* rowp = idx_packed + grow * (d * B / 8);
-  const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
-  mm::Planes16 P;
-  uint32_t Ln[8];
-  uint32_t cur_g = 0xFFFFFFFFu;
-  auto load_tab = [&](uint32_t g) {
-    const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
-    const u32x4 a = tp[0], b = tp[1];
-    Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
-    Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
-  };
-  const TX* xrow[2];
-  float xsc[2] = {1.0f, 1.0f};  // SC: 2^-e of the two staged token rows
+  // The block's conversion mode of its activation rows (bf16 with f16 tables:
+  // block_scale_mode). Everything after it is compiled once per mode (run<MD>),
+  // each copy with its own registers: only the kernel arguments cross the
+  // dispatch, so the common mode 0 runs the loop 16-bit operands of the table
+  // dtype would, and the modes that convert do not squeeze its registers.
+  int mode = 0;
+  if constexpr (SC) {
+    const int64_t mb0 = (int64_t)(blockIdx.x % mblocks) * G_BM;
+    uint32_t flags = 0u;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int64_t tok = m0 + 128 * c + (t >> 2);
-    xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 3);
-    if constexpr (SC) xsc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
+    for (int c = 0; c < 2; ++c) {
+      const int64_t tok = mb0 + 128 * c + (threadIdx.x >> 2);
+      flags |= scale_flags_of(rexp[tok < m ? tok : m - 1]);
+    }
+    mode = mm::block_scale_mode(flags, LDS_B + B_TILE);
   }
-  const uint32_t b_st0 = swz((uint32_t)r, 2u * hh), b_st1 = swz((uint32_t)r, 2u * hh + 1u);
-  const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
-  const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
-  Stage<B> S0, S1;
-  LutRegs<B> L;
+  auto run = [&](auto md) __attribute__((always_inline)) {
+    constexpr int MD = decltype(md)::value;
+    typedef mm::mfma32<TL> MF;
+    extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
+    (void)smem;
 
-  // stage tile j (raw operands in S) into LDS buffer j & 1
-  auto stage = [&](const Stage<B>& S, int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-    const uint32_t bb = LDS_B + buf * B_TILE;
-    const uint32_t ab = LDS_A + buf * A_TILE;
-    if constexpr (B == 4) {
-      const uint32_t g = group_of(j);
-      if (g != cur_g) {
-        mm::planes16(Ln, P);
-        cur_g = g;
-        load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
-      }
-      st_q(bb + b_st0, mm::dequant8_b4(S.w[0], P));
-      st_q(bb + b_st1, mm::dequant8_b4(S.w[1], P));
-      if constexpr (SC) {
-        st_q(ab + a_st0, mm::cvt_quad_perm_scaled(S.x[0], xsc[0]));
-        st_q(ab + a_st1, mm::cvt_quad_perm_scaled(S.x[1], xsc[1]));
-      } else {
-        st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(S.x[0]));
-        st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(S.x[1]));
-      }
-    } else {
-      uint32_t o[8];
-      const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
-      if (hh) dequant16<B, 1>(S, tb, lane4, o);
-      else dequant16<B, 0>(S, tb, lane4, o);
-      st_q(bb + b_st0, u32x4{o[0], o[1], o[2], o[3]});
-      st_q(bb + b_st1, u32x4{o[4], o[5], o[6], o[7]});
-      if constexpr (SC) {
-        st_q(ab + a_st0, mm::cvt_quad_scaled(S.x[0], xsc[0]));
-        st_q(ab + a_st1, mm::cvt_quad_scaled(S.x[1], xsc[1]));
-      } else {
-        st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
-        st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
-      }
-    }
-  };
-  // staging work of K-step k: tile k+1 from Sn into LDS, Sn refilled with
-  // tile k+3, tables kept one group ahead (the table of tile k+2's group is
-  // in L and goes to LDS now; the table of tile k+3's group is loaded)
-  auto stage_step = [&](int k, Stage<B>& Sn) {
-    if (k + 1 >= U) return;
-    stage(Sn, k + 1);
-    if (k + 3 < U) load_stage<B, TX>(Sn, rowp, xrow, (uint32_t)(k + 3), hh);
-    if (B != 4 && k + 2 < U) {
-      const uint32_t g2 = group_of(k + 2);
-      if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
-      if (k + 3 < U && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
-    }
-  };
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const uint32_t lane4 = (uint32_t)lane * 4u;
+    const int64_t bm = blockIdx.x % mblocks;
+    const int64_t bn = blockIdx.x / mblocks;
+    const int64_t m0 = bm * G_BM, n0 = bn * G_BN;
+    const int U = (int)(d / 32);
+    auto group_of = [&](int k) -> uint32_t { return mm::group_of((uint32_t)k, ug_magic); };
 
-  // ---- matrix state
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
-  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
-  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-    const uint32_t buf = (uint32_t)(k & 1);
-    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS_A + buf * A_TILE + swz(arow + 32u * i, ch));
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS_B + buf * B_TILE + swz(brow + 32u * jj, ch));
-  };
-  // matrix work of K-step k. The scheduling groups issue the first half's
-  // fragment reads, then alternate MFMAs of the first half with the second
-  // half's reads (each read reuses the registers of an A fragment whose MFMAs
-  // have been issued), then the second half's MFMAs.
-  auto mfma_step = [&](int k) {
-    u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
-    load_frags(fa0, fb0, k, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa0[i], fb0[jj], acc[i][jj]);
-    load_frags(fa1, fb1, k, 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa1[i], fb1[jj], acc[i][jj]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // reads of the first half
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of the second half
+    // ---- staging state (b = 4: the two threads of a row are adjacent lanes and
+    // the tables stay in registers, as in k_gemm_fwd64)
+    const int r = B == 4 ? (t >> 1) : (t & 255);
+    const int hh = B == 4 ? (t & 1) : (t >> 8);  // wave-uniform for b = 2, 3
+    const uint32_t rq = (uint32_t)(wave & 3);    // row quarter of r (b = 2, 3)
+    const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
+    const uint8_t* rowp = idx_packed + grow * (d * B / 8);
+    const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
+    mm::Planes16 P;
+    uint32_t Ln[8];
+    uint32_t cur_g = 0xFFFFFFFFu;
+    auto load_tab = [&](uint32_t g) {
+      const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
+      const u32x4 a = tp[0], b = tp[1];
+      Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
+      Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
+    };
+    const TX* xrow[2];
+    int xe[2] = {0, 0};  // SC: exponents of the two staged token rows
+  #pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t tok = m0 + 128 * c + (t >> 2);
+      xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 3);
+      if constexpr (SC && MD != 0) xe[c] = rexp[tok < m ? tok : m - 1];
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  const bool mfma_first = wave < 4;  // the other wave of this SIMD stages first
-  auto step = [&](int k, Stage<B>& Sn) {
-    if (mfma_first) {
-      mfma_step(k);
-      stage_step(k, Sn);
-    } else {
-      stage_step(k, Sn);
+    float xsc[2] = {1.0f, 1.0f};
+    uint32_t xk[2] = {0u, 0u};
+  #pragma unroll
+    for (int c = 0; c < (int)(sizeof(xe) / sizeof(xe[0])); ++c) {
+      if constexpr (MD == 2) xsc[c] = pow2f(-xe[c]);
+      if constexpr (MD == 1) xk[c] = exp_add_word(xe[c]);
+    }
+    (void)xsc;
+    (void)xk;
+    const uint32_t b_st0 = swz((uint32_t)r, 2u * hh), b_st1 = swz((uint32_t)r, 2u * hh + 1u);
+    const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
+    const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
+    Stage<B> S0, S1;
+    LutRegs<B> L;
+
+    // stage tile j (raw operands in S) into LDS buffer j & 1
+    auto stage = [&](const Stage<B>& S, int j, auto md) __attribute__((always_inline)) {
+      constexpr int MD = decltype(md)::value;
+      const uint32_t buf = (uint32_t)(j & 1);
+      const uint32_t bb = LDS_B + buf * B_TILE;
+      const uint32_t ab = LDS_A + buf * A_TILE;
+      if constexpr (B == 4) {
+        const uint32_t g = group_of(j);
+        if (g != cur_g) {
+          mm::planes16(Ln, P);
+          cur_g = g;
+          load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
+        }
+        st_q(bb + b_st0, mm::dequant8_b4(S.w[0], P));
+        st_q(bb + b_st1, mm::dequant8_b4(S.w[1], P));
+        if constexpr (SC && MD == 2) {
+          st_q(ab + a_st0, mm::cvt_quad_perm_scaled(S.x[0], xsc[0]));
+          st_q(ab + a_st1, mm::cvt_quad_perm_scaled(S.x[1], xsc[1]));
+        } else if constexpr (SC && MD == 1) {
+          st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(mm::add_quad(S.x[0], xk[0])));
+          st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(mm::add_quad(S.x[1], xk[1])));
+        } else {
+          st_q(ab + a_st0, mm::cvt_quad_perm<TX, TL>(S.x[0]));
+          st_q(ab + a_st1, mm::cvt_quad_perm<TX, TL>(S.x[1]));
+        }
+      } else {
+        uint32_t o[8];
+        const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
+        if (hh) dequant16<B, 1>(S, tb, lane4, o);
+        else dequant16<B, 0>(S, tb, lane4, o);
+        st_q(bb + b_st0, u32x4{o[0], o[1], o[2], o[3]});
+        st_q(bb + b_st1, u32x4{o[4], o[5], o[6], o[7]});
+        if constexpr (SC && MD == 2) {
+          st_q(ab + a_st0, mm::cvt_quad_scaled(S.x[0], xsc[0]));
+          st_q(ab + a_st1, mm::cvt_quad_scaled(S.x[1], xsc[1]));
+        } else if constexpr (SC && MD == 1) {
+          st_q(ab + a_st0, mm::cvt_quad<TX, TL>(mm::add_quad(S.x[0], xk[0])));
+          st_q(ab + a_st1, mm::cvt_quad<TX, TL>(mm::add_quad(S.x[1], xk[1])));
+        } else {
+          st_q(ab + a_st0, mm::cvt_quad<TX, TL>(S.x[0]));
+          st_q(ab + a_st1, mm::cvt_quad<TX, TL>(S.x[1]));
+        }
+      }
+    };
+    // staging work of K-step k: tile k+1 from Sn into LDS, Sn refilled with
+    // tile k+3, tables kept one group ahead (the table of tile k+2's group is
+    // in L and goes to LDS now; the table of tile k+3's group is loaded)
+    auto stage_step = [&](int k, Stage<B>& Sn, auto md) __attribute__((always_inline)) {
+      if (k + 1 >= U) return;
+      stage(Sn, k + 1, md);
+      if (k + 3 < U) load_stage<B, TX>(Sn, rowp, xrow, (uint32_t)(k + 3), hh);
+      if (B != 4 && k + 2 < U) {
+        const uint32_t g2 = group_of(k + 2);
+        if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
+        if (k + 3 < U && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+      }
+    };
+
+    // ---- matrix state
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+    const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
+    const uint32_t khalf = (uint32_t)(lane >> 5);
+    f32x16 acc[4][2];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
+    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+      const uint32_t buf = (uint32_t)(k & 1);
+      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS_A + buf * A_TILE + swz(arow + 32u * i, ch));
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS_B + buf * B_TILE + swz(brow + 32u * jj, ch));
+    };
+    // matrix work of K-step k. The scheduling groups issue the first half's
+    // fragment reads, then alternate MFMAs of the first half with the second
+    // half's reads (each read reuses the registers of an A fragment whose MFMAs
+    // have been issued), then the second half's MFMAs.
+    auto mfma_step = [&](int k) {
+      u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+      load_frags(fa0, fb0, k, 0);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa0[i], fb0[jj], acc[i][jj]);
+      load_frags(fa1, fb1, k, 1);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa1[i], fb1[jj], acc[i][jj]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // reads of the first half
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of the second half
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step(k);
+    };
+    const bool mfma_first = wave < 4;  // the other wave of this SIMD stages first
+    auto step = [&](int k, Stage<B>& Sn, auto md) __attribute__((always_inline)) {
+      if (mfma_first) {
+        mfma_step(k);
+        stage_step(k, Sn, md);
+      } else {
+        stage_step(k, Sn, md);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(k);
+      }
+      __syncthreads();
+    };
+
+    // ---- prologue: tables of group 0 (group 1's in registers), tile 0 staged,
+    // tiles 1 and 2 in registers, then the table of group 1 and of tile 2's
+    // group staged / loaded as in a K-step
+    if constexpr (B == 4) {
+      load_tab(group_of(0));
+      load_stage<B, TX>(S0, rowp, xrow, 0, hh);
+      if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
+      stage(S0, 0, md);
+      if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
+    } else {
+      load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
+      load_stage<B, TX>(S0, rowp, xrow, 0, hh);
+      if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
+      store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
+      const bool new1 = U > 1 && group_of(1) != group_of(0);
+      if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
+      __syncthreads();
+      stage(S0, 0, md);
+      if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
+      if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
+      if (U > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
     }
     __syncthreads();
+
+    // ---- main loop: two K-steps per trip so each register stage keeps its
+    // role; an odd last step is peeled
+    int k = 0;
+    for (; k + 1 < U; k += 2) {
+      step(k, S1, md);
+      step(k + 1, S0, md);
+    }
+    if (k < U) step(k, S1, md);
+
+    // ---- epilogue: D[i][j] of a 32x32 tile sits in lane j (+32 for the second
+    // 4-row band) at register 4*(i/8) + i%4, i.e. row 8*(e/4) + 4*(lane/32) + e%4
+    store_tile<TX, SC && MD != 0>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
   };
-
-  // ---- prologue: tables of group 0 (group 1's in registers), tile 0 staged,
-  // tiles 1 and 2 in registers, then the table of group 1 and of tile 2's
-  // group staged / loaded as in a K-step
-  if constexpr (B == 4) {
-    load_tab(group_of(0));
-    load_stage<B, TX>(S0, rowp, xrow, 0, hh);
-    if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
-    stage(S0, 0);
-    if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
-  } else {
-    load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
-    load_stage<B, TX>(S0, rowp, xrow, 0, hh);
-    if (U > 1) load_stage<B, TX>(S1, rowp, xrow, 1, hh);
-    store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
-    const bool new1 = U > 1 && group_of(1) != group_of(0);
-    if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
-    __syncthreads();
-    stage(S0, 0);
-    if (U > 2) load_stage<B, TX>(S0, rowp, xrow, 2, hh);
-    if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
-    if (U > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
-  }
-  __syncthreads();
-
-  // ---- main loop: two K-steps per trip so each register stage keeps its
-  // role; an odd last step is peeled
-  int k = 0;
-  for (; k + 1 < U; k += 2) {
-    step(k, S1);
-    step(k + 1, S0);
-  }
-  if (k < U) step(k, S1);
-
-  // ---- epilogue: D[i][j] of a 32x32 tile sits in lane j (+32 for the second
-  // 4-row band) at register 4*(i/8) + i%4, i.e. row 8*(e/4) + 4*(lane/32) + e%4
-  store_tile<TX, SC>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
+  if (!SC || mode == 0) run(mm::mode_tag<0>{});
+  else if (mode == 1) run(mm::mode_tag<1>{});
+  else run(mm::mode_tag<2>{});
 }
 
 // ---- 64-column K-steps ------------------------------------------------------
@@ -448,212 +491,245 @@ __global__ void __launch_bounds__(G_THREADS, 1)
 k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
              int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, TX* __restrict__ Y,
              const int32_t* __restrict__ rexp) {
-  typedef mm::mfma32<TL> MF;
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
-  extern __shared__ uint32_t smem[];
-  (void)smem;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int64_t bm = blockIdx.x % mblocks;
-  const int64_t bn = blockIdx.x / mblocks;
-  const int64_t m0 = bm * G_BM, n0 = bn * G_BN;
-  const int KS = (int)(d / 64);
-  // group of tile j (both of its units are in it)
-  auto group_of = [&](int j) -> uint32_t { return mm::group_of((uint32_t)(2 * j), ug_magic); };
-
-  // ---- staging state: weight row r, unit hh of the step; activation chunk
-  // t % 8 of token rows t / 8 + 64 c. b = 4 pairs adjacent lanes on one row
-  // (32 contiguous index bytes per row and step); the LDS tables of b = 2, 3
-  // need hh wave-uniform (threads t and t + 256 fill one lane's table copy).
-  const int r = B == 4 ? (t >> 1) : (t & 255);
-  const int hh = B == 4 ? (t & 1) : (t >> 8);
-  const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r (b = 2, 3)
-  const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
-  const uint8_t* rowp = idx_packed + grow * (d * B / 8) + hh * (4 * B);
-  const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
-  const TX* xrow[4];
-  float xsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // SC: 2^-e of the four staged token rows
+  // The block's conversion mode of its activation rows (bf16 with f16 tables:
+  // block_scale_mode). Everything after it is compiled once per mode (run<MD>),
+  // each copy with its own registers: only the kernel arguments cross the
+  // dispatch, so the common mode 0 runs the loop 16-bit operands of the table
+  // dtype would, and the modes that convert do not squeeze its registers.
+  int mode = 0;
+  if constexpr (SC) {
+    const int64_t mb0 = (int64_t)(blockIdx.x % mblocks) * G_BM;
+    uint32_t flags = 0u;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int64_t tok = m0 + 64 * c + (t >> 3);
-    xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 7);
-    if constexpr (SC) xsc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
-  }
-  auto load_stage = [&](Stage64<B>& S, int j) {
-    const uint8_t* p = rowp + (int64_t)j * (8 * B);
-    if constexpr (B == 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-      S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
-    } else if constexpr (B == 2) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-      S.w[0] = v.x; S.w[1] = v.y;
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-      S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
+    for (int c = 0; c < 4; ++c) {
+      const int64_t tok = mb0 + 64 * c + (threadIdx.x >> 3);
+      flags |= scale_flags_of(rexp[tok < m ? tok : m - 1]);
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) S.x[c] = *reinterpret_cast<const u32x4*>(xrow[c] + (int64_t)j * 64);
-  };
-  Stage64<B> S;
-  // b = 4: the table of the group being staged, as byte planes (P), and the
-  // next group's table as loaded (Ln); the group changes every UG/2 steps
-  mm::Planes16 P;
-  uint32_t Ln[8];
-  uint32_t cur_g = 0xFFFFFFFFu;
-  auto load_tab = [&](uint32_t g) {
-    const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
-    const u32x4 a = tp[0], b = tp[1];
-    Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
-    Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
-  };
-  LutRegs<B> L;
-  auto stage = [&](const Stage64<B>& St, int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-    const uint32_t bb = LDS64_B + buf * B64_TILE;
-    const uint32_t ab = LDS64_A + buf * A64_TILE;
-    if constexpr (B == 4) {
-      // tables in registers; both operands in the K order of dequant8_b4
-      const uint32_t g = group_of(j);
-      if (g != cur_g) {
-        mm::planes16(Ln, P);
-        cur_g = g;
-        load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st_q(bb + swz128((uint32_t)r, 4u * hh + q), mm::dequant8_b4(St.w[q], P));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
-        if constexpr (SC) st_q(a, mm::cvt_quad_perm_scaled(St.x[c], xsc[c]));
-        else st_q(a, mm::cvt_quad_perm<TX, TL>(St.x[c]));
-      }
-    } else {
-      const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
-      uint32_t o0[8], o1[8];
-      Stage<B> h0, h1;  // the two half units in the layout dequant16 expects
-      if constexpr (B == 2) {
-        h0.w[0] = St.w[0];
-        h1.w[0] = St.w[1];
+    mode = mm::block_scale_mode(flags, LDS64_B + B64_TILE);
+  }
+  auto run = [&](auto md) __attribute__((always_inline)) {
+    constexpr int MD = decltype(md)::value;
+    typedef mm::mfma32<TL> MF;
+    extern __shared__ uint32_t smem[];
+    (void)smem;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const uint32_t lane4 = (uint32_t)lane * 4u;
+    const int64_t bm = blockIdx.x % mblocks;
+    const int64_t bn = blockIdx.x / mblocks;
+    const int64_t m0 = bm * G_BM, n0 = bn * G_BN;
+    const int KS = (int)(d / 64);
+    // group of tile j (both of its units are in it)
+    auto group_of = [&](int j) -> uint32_t { return mm::group_of((uint32_t)(2 * j), ug_magic); };
+
+    // ---- staging state: weight row r, unit hh of the step; activation chunk
+    // t % 8 of token rows t / 8 + 64 c. b = 4 pairs adjacent lanes on one row
+    // (32 contiguous index bytes per row and step); the LDS tables of b = 2, 3
+    // need hh wave-uniform (threads t and t + 256 fill one lane's table copy).
+    const int r = B == 4 ? (t >> 1) : (t & 255);
+    const int hh = B == 4 ? (t & 1) : (t >> 8);
+    const uint32_t rq = (uint32_t)(wave & 3);  // row quarter of r (b = 2, 3)
+    const int64_t grow = (n0 + r < n) ? n0 + r : n - 1;
+    const uint8_t* rowp = idx_packed + grow * (d * B / 8) + hh * (4 * B);
+    const uint16_t* lutrow = reinterpret_cast<const uint16_t*>(lut) + grow * (int64_t)gpr * (1 << B);
+    const TX* xrow[4];
+    int xe[4] = {0, 0, 0, 0};  // SC: exponents of the four staged token rows
+  #pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t tok = m0 + 64 * c + (t >> 3);
+      xrow[c] = X + (tok < m ? tok : m - 1) * d + 8 * (t & 7);
+      if constexpr (SC && MD != 0) xe[c] = rexp[tok < m ? tok : m - 1];
+    }
+    float xsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    uint32_t xk[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+    for (int c = 0; c < (int)(sizeof(xe) / sizeof(xe[0])); ++c) {
+      if constexpr (MD == 2) xsc[c] = pow2f(-xe[c]);
+      if constexpr (MD == 1) xk[c] = exp_add_word(xe[c]);
+    }
+    (void)xsc;
+    (void)xk;
+    auto load_stage = [&](Stage64<B>& S, int j) {
+      const uint8_t* p = rowp + (int64_t)j * (8 * B);
+      if constexpr (B == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+      } else if constexpr (B == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        S.w[0] = v.x; S.w[1] = v.y;
       } else {
-        h0.w[0] = h1.w[0] = St.w[0];
-        h0.w[1] = h1.w[1] = St.w[1];
-        h0.w[2] = h1.w[2] = St.w[2];
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
       }
-      dequant16<B, 0>(h0, tb, lane4, o0);
-      dequant16<B, 1>(h1, tb, lane4, o1);
-      st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
-      st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
-      st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
-      st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
-        if constexpr (SC) st_q(a, mm::cvt_quad_scaled(St.x[c], xsc[c]));
-        else st_q(a, mm::cvt_quad<TX, TL>(St.x[c]));
+  #pragma unroll
+      for (int c = 0; c < 4; ++c) S.x[c] = *reinterpret_cast<const u32x4*>(xrow[c] + (int64_t)j * 64);
+    };
+    Stage64<B> S;
+    // b = 4: the table of the group being staged, as byte planes (P), and the
+    // next group's table as loaded (Ln); the group changes every UG/2 steps
+    mm::Planes16 P;
+    uint32_t Ln[8];
+    uint32_t cur_g = 0xFFFFFFFFu;
+    auto load_tab = [&](uint32_t g) {
+      const u32x4* tp = reinterpret_cast<const u32x4*>(lutrow + g * 16u);
+      const u32x4 a = tp[0], b = tp[1];
+      Ln[0] = a.x; Ln[1] = a.y; Ln[2] = a.z; Ln[3] = a.w;
+      Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
+    };
+    LutRegs<B> L;
+    auto stage = [&](const Stage64<B>& St, int j, auto md) __attribute__((always_inline)) {
+      constexpr int MD = decltype(md)::value;
+      const uint32_t buf = (uint32_t)(j & 1);
+      const uint32_t bb = LDS64_B + buf * B64_TILE;
+      const uint32_t ab = LDS64_A + buf * A64_TILE;
+      if constexpr (B == 4) {
+        // tables in registers; both operands in the K order of dequant8_b4
+        const uint32_t g = group_of(j);
+        if (g != cur_g) {
+          mm::planes16(Ln, P);
+          cur_g = g;
+          load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
+        }
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) st_q(bb + swz128((uint32_t)r, 4u * hh + q), mm::dequant8_b4(St.w[q], P));
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+          if constexpr (SC && MD == 2) st_q(a, mm::cvt_quad_perm_scaled(St.x[c], xsc[c]));
+          else if constexpr (SC && MD == 1) st_q(a, mm::cvt_quad_perm<TX, TL>(mm::add_quad(St.x[c], xk[c])));
+          else st_q(a, mm::cvt_quad_perm<TX, TL>(St.x[c]));
+        }
+      } else {
+        const uint32_t tb = tab_base<B>(group_of(j) & 1u, rq);
+        uint32_t o0[8], o1[8];
+        Stage<B> h0, h1;  // the two half units in the layout dequant16 expects
+        if constexpr (B == 2) {
+          h0.w[0] = St.w[0];
+          h1.w[0] = St.w[1];
+        } else {
+          h0.w[0] = h1.w[0] = St.w[0];
+          h0.w[1] = h1.w[1] = St.w[1];
+          h0.w[2] = h1.w[2] = St.w[2];
+        }
+        dequant16<B, 0>(h0, tb, lane4, o0);
+        dequant16<B, 1>(h1, tb, lane4, o1);
+        st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
+        st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
+        st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
+        st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+          if constexpr (SC && MD == 2) st_q(a, mm::cvt_quad_scaled(St.x[c], xsc[c]));
+          else if constexpr (SC && MD == 1) st_q(a, mm::cvt_quad<TX, TL>(mm::add_quad(St.x[c], xk[c])));
+          else st_q(a, mm::cvt_quad<TX, TL>(St.x[c]));
+        }
       }
-    }
-  };
-  // staging work of step k: tile k+1 into the other buffer, S refilled with
-  // tile k+2, tables kept one group ahead
-  auto stage_step = [&](int k) {
-    if (k + 1 >= KS) return;
-    stage(S, k + 1);
-    if (k + 2 < KS) {
-      load_stage(S, k + 2);
-      if constexpr (B != 4) {
-        const uint32_t g2 = group_of(k + 2);
-        if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
-        if (k + 3 < KS && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+    };
+    // staging work of step k: tile k+1 into the other buffer, S refilled with
+    // tile k+2, tables kept one group ahead
+    auto stage_step = [&](int k, auto md) __attribute__((always_inline)) {
+      if (k + 1 >= KS) return;
+      stage(S, k + 1, md);
+      if (k + 2 < KS) {
+        load_stage(S, k + 2);
+        if constexpr (B != 4) {
+          const uint32_t g2 = group_of(k + 2);
+          if (g2 != group_of(k + 1)) store_lut<B>(L, tab_base<B>(g2 & 1u, rq), hh, lane4);
+          if (k + 3 < KS && group_of(k + 3) != g2) load_lut<B, TL>(L, lut, grow, gpr, group_of(k + 3), hh);
+        }
       }
-    }
-  };
+    };
 
-  // ---- matrix state
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
-  const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
-  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-    const uint32_t buf = (uint32_t)(k & 1);
-    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS64_A + buf * A64_TILE + swz128(arow + 32u * i, ch));
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS64_B + buf * B64_TILE + swz128(brow + 32u * jj, ch));
-  };
-  auto mfma_step = [&](int k) {
-    u32x4 fa[4][4], fb[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
-    // each quarter's fragment reads interleaved with the previous quarter's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int ks = 1; ks < 4; ++ks) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // ---- matrix state
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+    const uint32_t brow = (uint32_t)(64 * wn + (lane & 31));
+    const uint32_t khalf = (uint32_t)(lane >> 5);
+    f32x16 acc[4][2];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
+    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+      const uint32_t buf = (uint32_t)(k & 1);
+      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS64_A + buf * A64_TILE + swz128(arow + 32u * i, ch));
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS64_B + buf * B64_TILE + swz128(brow + 32u * jj, ch));
+    };
+    auto mfma_step = [&](int k) {
+      u32x4 fa[4][4], fb[4][2];
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
+      // each quarter's fragment reads interleaved with the previous quarter's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  #pragma unroll
+      for (int ks = 1; ks < 4; ++ks) {
+  #pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+  #pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  const bool mfma_first = wave < 4;
-
-  // ---- prologue: tables of tile 0's group (tile 1's in registers if new),
-  // tile 0 staged, tile 1 in registers, then tile 1's table staged and tile
-  // 2's loaded as in a step
-  if constexpr (B == 4) {
-    load_tab(group_of(0));
-    load_stage(S, 0);
-    stage(S, 0);
-    if (KS > 1) load_stage(S, 1);
-  } else {
-    load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
-    load_stage(S, 0);
-    store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
-    const bool new1 = KS > 1 && group_of(1) != group_of(0);
-    if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
-    __syncthreads();
-    stage(S, 0);
-    if (KS > 1) load_stage(S, 1);
-    if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
-    if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
-  }
-  __syncthreads();
-
-  for (int k = 0; k < KS; ++k) {
-    if (mfma_first) {
-      mfma_step(k);
-      stage_step(k);
-    } else {
-      stage_step(k);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step(k);
+    };
+    const bool mfma_first = wave < 4;
+
+    // ---- prologue: tables of tile 0's group (tile 1's in registers if new),
+    // tile 0 staged, tile 1 in registers, then tile 1's table staged and tile
+    // 2's loaded as in a step
+    if constexpr (B == 4) {
+      load_tab(group_of(0));
+      load_stage(S, 0);
+      stage(S, 0, md);
+      if (KS > 1) load_stage(S, 1);
+    } else {
+      load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
+      load_stage(S, 0);
+      store_lut<B>(L, tab_base<B>(group_of(0) & 1u, rq), hh, lane4);
+      const bool new1 = KS > 1 && group_of(1) != group_of(0);
+      if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
+      __syncthreads();
+      stage(S, 0, md);
+      if (KS > 1) load_stage(S, 1);
+      if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
+      if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
     }
     __syncthreads();
-  }
 
-  store_tile<TX, SC>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
+    for (int k = 0; k < KS; ++k) {
+      if (mfma_first) {
+        mfma_step(k);
+        stage_step(k, md);
+      } else {
+        stage_step(k, md);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(k);
+      }
+      __syncthreads();
+    }
+    store_tile<TX, SC && MD != 0>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
+  };
+  if (!SC || mode == 0) run(mm::mode_tag<0>{});
+  else if (mode == 1) run(mm::mode_tag<1>{});
+  else run(mm::mode_tag<2>{});
 }
 
 template <int B, typename TX, typename TL>

@@ -22,7 +22,10 @@
 //
 // bf16 dY with f16 tables: each token row of dY is prescaled by 2^-e[t]
 // while it is converted to f16 (row exponents from the caller's workspace,
-// see skm_common.h) and its dX row is multiplied by 2^e[t] when stored.
+// see skm_common.h) and its dX row is multiplied by 2^e[t] when stored; the
+// block takes one conversion for all its rows (none, exponent-field add or
+// multiply, mm::block_scale_mode), and its prologue, K loop and store are
+// compiled once per conversion.
 //
 // k_gemm_dlut: one block owns 128 rows x one group. For each chunk of up to
 // 512 columns of the group it accumulates the dW = dY^T X tile over all
@@ -169,229 +172,264 @@ __global__ void __launch_bounds__(512, 1)
 k_gemm_dx(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut, int64_t m,
           int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX,
           const int32_t* __restrict__ rexp) {
-  typedef mfma32<TL> MF;
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
-  typedef DxLds<NG> LDS;
-  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
-  extern __shared__ uint32_t smem[];
-  (void)smem;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
-  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;  // token / column tile origins
-  const bool vec = (n % 8) == 0;
-  const int KS = (int)((n + DX_BK - 1) / DX_BK);   // K-steps over the weight rows
-
-  // ---- dequant role: weight row r of the step, 16-column chunk cc
-  const int r = t & 31;
-  const int cc = t >> 5;
-  const int hh = cc & 1;
-  const int64_t jc = n0 + 16 * cc;  // first column of the chunk
-  const bool col_ok = jc < d;
-  const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
-  const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
-  const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
-  const int ng = (int)(ghi - glo + 1);  // groups touched by the column tile (<= NG)
-  const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
-  const int64_t rbytes = d * B / 8;
-  const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B) + (B == 3 ? 0 : hh * 2 * B);
-  const uint32_t b_st = (uint32_t)r * DX_RSB + 32u * (uint32_t)cc;
-  // ---- table role: lane slot `lane` (row lane % 32 of a step), part = wave
-  const int part = wave;
-  // ---- dY role: chunk t % 4 of token rows t / 4 + 128 c
-  const TX* yrow[2];
-  float ysc[2] = {1.0f, 1.0f};  // SC: 2^-e of the two staged token rows
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int64_t tok = m0 + 128 * c + (t >> 2);
-    yrow[c] = dY + (tok < m ? tok : m - 1) * n;
-    if constexpr (SC) ysc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
-  }
-  const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
-  const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
-
-  auto load_stage = [&](DxStage<B>& S, int j) {
-    const int64_t k0 = (int64_t)j * DX_BK;
-    const int64_t e0 = k0 + 8 * (t & 3);
+  // The block's conversion mode of its activation rows (bf16 with f16 tables:
+  // block_scale_mode). Everything after it is compiled once per mode (run<MD>),
+  // each copy with its own registers: only the kernel arguments cross the
+  // dispatch, so the common mode 0 runs the loop 16-bit operands of the table
+  // dtype would, and the modes that convert do not squeeze its registers.
+  int mode = 0;
+  if constexpr (SC) {
+    const int64_t mb0 = (int64_t)(blockIdx.x % mblocks) * DX_BM;
+    uint32_t flags = 0u;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      if (vec) {
-        const bool in = e0 < n;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
-        S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+      const int64_t tok = mb0 + 128 * c + (threadIdx.x >> 2);
+      flags |= scale_flags_of(rexp[tok < m ? tok : m - 1]);
+    }
+    mode = block_scale_mode(flags, DxLds<NG>::B + DX_TB);
+  }
+  auto run = [&](auto md) __attribute__((always_inline)) {
+    constexpr int MD = decltype(md)::value;
+    typedef mfma32<TL> MF;
+    typedef DxLds<NG> LDS;
+    constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
+    extern __shared__ uint32_t smem[];
+    (void)smem;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const uint32_t lane4 = (uint32_t)lane * 4u;
+    const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
+    const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;  // token / column tile origins
+    const bool vec = (n % 8) == 0;
+    const int KS = (int)((n + DX_BK - 1) / DX_BK);   // K-steps over the weight rows
+
+    // ---- dequant role: weight row r of the step, 16-column chunk cc
+    const int r = t & 31;
+    const int cc = t >> 5;
+    const int hh = cc & 1;
+    const int64_t jc = n0 + 16 * cc;  // first column of the chunk
+    const bool col_ok = jc < d;
+    const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
+    const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
+    const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
+    const int ng = (int)(ghi - glo + 1);  // groups touched by the column tile (<= NG)
+    const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
+    const int64_t rbytes = d * B / 8;
+    const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B) + (B == 3 ? 0 : hh * 2 * B);
+    const uint32_t b_st = (uint32_t)r * DX_RSB + 32u * (uint32_t)cc;
+    // ---- table role: lane slot `lane` (row lane % 32 of a step), part = wave
+    const int part = wave;
+    // ---- dY role: chunk t % 4 of token rows t / 4 + 128 c
+    const TX* yrow[2];
+    int ye[2] = {0, 0};  // SC: exponents of the two staged token rows
+  #pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t tok = m0 + 128 * c + (t >> 2);
+      yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+      if constexpr (SC && MD != 0) ye[c] = rexp[tok < m ? tok : m - 1];
+    }
+    float ysc[2] = {1.0f, 1.0f};
+    uint32_t yk[2] = {0u, 0u};
+  #pragma unroll
+    for (int c = 0; c < (int)(sizeof(ye) / sizeof(ye[0])); ++c) {
+      if constexpr (MD == 2) ysc[c] = pow2f(-ye[c]);
+      if constexpr (MD == 1) yk[c] = exp_add_word(ye[c]);
+    }
+    (void)ysc;
+    (void)yk;
+    const uint32_t a_st0 = swz((uint32_t)(t >> 2), (uint32_t)(t & 3));
+    const uint32_t a_st1 = swz((uint32_t)(128 + (t >> 2)), (uint32_t)(t & 3));
+
+    auto load_stage = [&](DxStage<B>& S, int j) {
+      const int64_t k0 = (int64_t)j * DX_BK;
+      const int64_t e0 = k0 + 8 * (t & 3);
+  #pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (vec) {
+          const bool in = e0 < n;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
+          S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(yrow[c]);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t i = e0 + 2 * q;
+            S.y[c][q] = (i < n ? p[i] : 0u) | ((i + 1 < n ? p[i + 1] : 0u) << 16);
+          }
+        }
+      }
+      const int64_t row = k0 + r;
+      const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
+      if constexpr (B == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+        S.w[0] = v.x;
+        S.w[1] = v.y;
+      } else if constexpr (B == 2) {
+        S.w[0] = *reinterpret_cast<const uint32_t*>(src);
       } else {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(yrow[c]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t i = e0 + 2 * q;
-          S.y[c][q] = (i < n ? p[i] : 0u) | ((i + 1 < n ? p[i + 1] : 0u) << 16);
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
+        S.w[0] = q[0];
+        S.w[1] = q[1];
+        S.w[2] = q[2];
+      }
+    };
+    // dequantise / convert tile j into buffer j & 1 (tables of tile j are in
+    // table buffer j & 1)
+    auto stage = [&](const DxStage<B>& S, int j, auto md) __attribute__((always_inline)) {
+      constexpr int MD = decltype(md)::value;
+      const uint32_t buf = (uint32_t)(j & 1);
+      const bool ok = (int64_t)j * DX_BK + r < n && col_ok;
+      uint32_t o[8];
+      dx_dequant<B>(S.w, hh, (buf * NG + gsel) * T, lane4, o);
+      const uint32_t bb = LDS::B + buf * DX_TB + b_st;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      st_q(bb, ok ? u32x4{o[0], o[1], o[2], o[3]} : z);
+      st_q(bb + 16u, ok ? u32x4{o[4], o[5], o[6], o[7]} : z);
+      const uint32_t ab = LDS::A + buf * DX_TA;
+      if constexpr (SC && MD == 2) {
+        st_q(ab + a_st0, cvt_quad_scaled(S.y[0], ysc[0]));
+        st_q(ab + a_st1, cvt_quad_scaled(S.y[1], ysc[1]));
+      } else if constexpr (SC && MD == 1) {
+        st_q(ab + a_st0, cvt_quad<TX, TL>(add_quad(S.y[0], yk[0])));
+        st_q(ab + a_st1, cvt_quad<TX, TL>(add_quad(S.y[1], yk[1])));
+      } else {
+        st_q(ab + a_st0, cvt_quad<TX, TL>(S.y[0]));
+        st_q(ab + a_st1, cvt_quad<TX, TL>(S.y[1]));
+      }
+    };
+    DxLutWord<B> LW[NG];
+    auto lut_load = [&](int j) {
+      const int64_t row = (int64_t)j * DX_BK + (lane & 31);
+      const bool ok = row < n;
+  #pragma unroll
+      for (int gs = 0; gs < NG; ++gs)
+        if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
+    };
+    auto lut_store = [&](int j) {
+      const uint32_t buf = (uint32_t)(j & 1);
+  #pragma unroll
+      for (int gs = 0; gs < NG; ++gs)
+        if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
+    };
+
+    // ---- matrix roles
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+    const uint32_t khalf = (uint32_t)(lane >> 5);
+    f32x16 acc[4][2];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
+    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+      const uint32_t buf = (uint32_t)(k & 1);
+      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS::A + buf * DX_TA + swz(arow + 32u * i, ch));
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        fb[jj] = ld_frag_tr(LDS::B + buf * DX_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
+                            (uint32_t)lane);
+    };
+    auto mfma_step = [&](int k) {
+      u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+      load_frags(fa0, fb0, k, 0);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa0[i], fb0[jj], acc[i][jj]);
+      load_frags(fa1, fb1, k, 1);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa1[i], fb1[jj], acc[i][jj]);
+      // first half's 8 reads (4 A + 2 x 2 transposing B), then its MFMAs
+      // interleaved with the second half's reads, then the second half's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // staging work of step k: the tables of tile k+2 (loaded during step k-1)
+    // go to LDS and those of tile k+3 are loaded; tile k+1 goes from Sn into
+    // LDS and Sn is refilled with tile k+3
+    auto stage_step = [&](int k, DxStage<B>& Sn, auto md) __attribute__((always_inline)) {
+      if (k + 2 < KS) lut_store(k + 2);
+      if (k + 3 < KS) lut_load(k + 3);
+      if (k + 1 < KS) {
+        stage(Sn, k + 1, md);
+        if (k + 3 < KS) load_stage(Sn, k + 3);
+      }
+    };
+    const bool mfma_first = wave < 4;
+    DxStage<B> S0, S1;
+    auto step = [&](int k, DxStage<B>& Sn, auto md) __attribute__((always_inline)) {
+      if (mfma_first) {
+        mfma_step(k);
+        stage_step(k, Sn, md);
+      } else {
+        stage_step(k, Sn, md);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(k);
+      }
+      __syncthreads();
+    };
+
+    // ---- prologue: tables of tiles 0 and 1, tile 0 staged, tiles 1 and 2 in
+    // registers
+    lut_load(0);
+    load_stage(S0, 0);
+    if (KS > 1) load_stage(S1, 1);
+    lut_store(0);
+    if (KS > 1) {
+      lut_load(1);
+      lut_store(1);
+    }
+    if (KS > 2) lut_load(2);
+    __syncthreads();
+    stage(S0, 0, md);
+    if (KS > 2) load_stage(S0, 2);
+    __syncthreads();
+
+    int k = 0;
+    for (; k + 1 < KS; k += 2) {
+      step(k, S1, md);
+      step(k + 1, S0, md);
+    }
+    if (k < KS) step(k, S1, md);
+
+    if constexpr (SC && MD != 0) dx_factors_to_lds(rexp, m, m0, t);  // block-uniform
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 uq[4] = {};
+      if constexpr (SC && MD != 0) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
+      }
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
+        if (col >= d) continue;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          float v = acc[i][jj][e];
+          if constexpr (SC && MD != 0) v *= uq[e >> 2][e & 3];
+          if (tok < m) dX[tok * d + col] = v;
         }
       }
     }
-    const int64_t row = k0 + r;
-    const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
-    if constexpr (B == 4) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-      S.w[0] = v.x;
-      S.w[1] = v.y;
-    } else if constexpr (B == 2) {
-      S.w[0] = *reinterpret_cast<const uint32_t*>(src);
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
-      S.w[0] = q[0];
-      S.w[1] = q[1];
-      S.w[2] = q[2];
-    }
   };
-  // dequantise / convert tile j into buffer j & 1 (tables of tile j are in
-  // table buffer j & 1)
-  auto stage = [&](const DxStage<B>& S, int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-    const bool ok = (int64_t)j * DX_BK + r < n && col_ok;
-    uint32_t o[8];
-    dx_dequant<B>(S.w, hh, (buf * NG + gsel) * T, lane4, o);
-    const uint32_t bb = LDS::B + buf * DX_TB + b_st;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    st_q(bb, ok ? u32x4{o[0], o[1], o[2], o[3]} : z);
-    st_q(bb + 16u, ok ? u32x4{o[4], o[5], o[6], o[7]} : z);
-    const uint32_t ab = LDS::A + buf * DX_TA;
-    if constexpr (SC) {
-      st_q(ab + a_st0, cvt_quad_scaled(S.y[0], ysc[0]));
-      st_q(ab + a_st1, cvt_quad_scaled(S.y[1], ysc[1]));
-    } else {
-      st_q(ab + a_st0, cvt_quad<TX, TL>(S.y[0]));
-      st_q(ab + a_st1, cvt_quad<TX, TL>(S.y[1]));
-    }
-  };
-  DxLutWord<B> LW[NG];
-  auto lut_load = [&](int j) {
-    const int64_t row = (int64_t)j * DX_BK + (lane & 31);
-    const bool ok = row < n;
-#pragma unroll
-    for (int gs = 0; gs < NG; ++gs)
-      if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
-  };
-  auto lut_store = [&](int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-#pragma unroll
-    for (int gs = 0; gs < NG; ++gs)
-      if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
-  };
-
-  // ---- matrix roles
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
-  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-    const uint32_t buf = (uint32_t)(k & 1);
-    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS::A + buf * DX_TA + swz(arow + 32u * i, ch));
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      fb[jj] = ld_frag_tr(LDS::B + buf * DX_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
-                          (uint32_t)lane);
-  };
-  auto mfma_step = [&](int k) {
-    u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
-    load_frags(fa0, fb0, k, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa0[i], fb0[jj], acc[i][jj]);
-    load_frags(fa1, fb1, k, 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa1[i], fb1[jj], acc[i][jj]);
-    // first half's 8 reads (4 A + 2 x 2 transposing B), then its MFMAs
-    // interleaved with the second half's reads, then the second half's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // staging work of step k: the tables of tile k+2 (loaded during step k-1)
-  // go to LDS and those of tile k+3 are loaded; tile k+1 goes from Sn into
-  // LDS and Sn is refilled with tile k+3
-  auto stage_step = [&](int k, DxStage<B>& Sn) {
-    if (k + 2 < KS) lut_store(k + 2);
-    if (k + 3 < KS) lut_load(k + 3);
-    if (k + 1 < KS) {
-      stage(Sn, k + 1);
-      if (k + 3 < KS) load_stage(Sn, k + 3);
-    }
-  };
-  const bool mfma_first = wave < 4;
-  DxStage<B> S0, S1;
-  auto step = [&](int k, DxStage<B>& Sn) {
-    if (mfma_first) {
-      mfma_step(k);
-      stage_step(k, Sn);
-    } else {
-      stage_step(k, Sn);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(k);
-    }
-    __syncthreads();
-  };
-
-  // ---- prologue: tables of tiles 0 and 1, tile 0 staged, tiles 1 and 2 in
-  // registers
-  lut_load(0);
-  load_stage(S0, 0);
-  if (KS > 1) load_stage(S1, 1);
-  lut_store(0);
-  if (KS > 1) {
-    lut_load(1);
-    lut_store(1);
-  }
-  if (KS > 2) lut_load(2);
-  __syncthreads();
-  stage(S0, 0);
-  if (KS > 2) load_stage(S0, 2);
-  __syncthreads();
-
-  int k = 0;
-  for (; k + 1 < KS; k += 2) {
-    step(k, S1);
-    step(k + 1, S0);
-  }
-  if (k < KS) step(k, S1);
-
-  if constexpr (SC) dx_factors_to_lds(rexp, m, m0, t);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f32x4 uq[4];
-    if constexpr (SC) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t col = n0 + 64 * wn + 32 * jj + (lane & 31);
-      if (col >= d) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        float v = acc[i][jj][e];
-        if constexpr (SC) v *= uq[e >> 2][e & 3];
-        if (tok < m) dX[tok * d + col] = v;
-      }
-    }
-  }
+  if (!SC || mode == 0) run(mode_tag<0>{});
+  else if (mode == 1) run(mode_tag<1>{});
+  else run(mode_tag<2>{});
 }
 
 // dX with 64 weight rows per step, for groups of >= 256 columns (a 256-column
@@ -421,73 +459,130 @@ __global__ void __launch_bounds__(512, 1)
 k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
             int64_t m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, int64_t mblocks, float* __restrict__ dX,
             const int32_t* __restrict__ rexp) {
-  typedef mfma32<TL> MF;
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
-  constexpr int NG = 2;
-  constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
-  extern __shared__ uint32_t smem[];
-  (void)smem;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
-  const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;
-  const bool vec = (n % 8) == 0;
-  const int KS = (int)((n + D6_BK - 1) / D6_BK);
-
-  // ---- dequant role: weight row r = lane of the step, unit uu = wave of the
-  // column tile (32 columns, 4 * B bytes). b = 4 keeps the tables in
-  // registers instead (mm::dequant8_b4); then 4 adjacent lanes take 4
-  // adjacent units of one row (64 contiguous index bytes per row), 16 rows
-  // per wave.
-  const int r = B == 4 ? 16 * (wave & 3) + (lane >> 2) : lane;
-  const int uu = B == 4 ? 4 * (wave >> 2) + (lane & 3) : wave;
-  const int64_t jc = n0 + 32 * uu;
-  const bool col_ok = jc < d;
-  const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
-  const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
-  const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
-  const int ng = (int)(ghi - glo + 1);
-  const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
-  const int64_t rbytes = d * B / 8;
-  const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B);
-  const uint32_t b_st = (uint32_t)r * DX_RSB + 64u * (uint32_t)uu;
-  const int part = wave;
-  // ---- dY role: chunk t % 8 of token rows t / 8 + 64 c
-  const TX* yrow[4];
-  float ysc[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // SC: 2^-e of the four staged token rows
+  // The block's conversion mode of its activation rows (bf16 with f16 tables:
+  // block_scale_mode). Everything after it is compiled once per mode (run<MD>),
+  // each copy with its own registers: only the kernel arguments cross the
+  // dispatch, so the common mode 0 runs the loop 16-bit operands of the table
+  // dtype would, and the modes that convert do not squeeze its registers.
+  int mode = 0;
+  if constexpr (SC) {
+    const int64_t mb0 = (int64_t)(blockIdx.x % mblocks) * DX_BM;
+    uint32_t flags = 0u;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int64_t tok = m0 + 64 * c + (t >> 3);
-    yrow[c] = dY + (tok < m ? tok : m - 1) * n;
-    if constexpr (SC) ysc[c] = pow2f(-rexp[tok < m ? tok : m - 1]);
-  }
-
-  const uint8_t* urow = ucol + (int64_t)r * rbytes;  // row r of step 0
-  // b = 4: the table of (row, this thread's group), 16 entries
-  const uint32_t gabs = glo + gsel;
-  auto load_tab = [&](Dx6Stage<B>& S, int64_t row) {
-    if constexpr (B == 4) {
-      const u32x4* tp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lut) +
-                                                        (row * gpr + gabs) * 16);
-      const u32x4 a = tp[0], b = tp[1];
-      S.lut[0] = a.x; S.lut[1] = a.y; S.lut[2] = a.z; S.lut[3] = a.w;
-      S.lut[4] = b.x; S.lut[5] = b.y; S.lut[6] = b.z; S.lut[7] = b.w;
+    for (int c = 0; c < 4; ++c) {
+      const int64_t tok = mb0 + 64 * c + (threadIdx.x >> 3);
+      flags |= scale_flags_of(rexp[tok < m ? tok : m - 1]);
     }
-  };
-  auto load_stage = [&](Dx6Stage<B>& S, int j) {
-    const int64_t k0 = (int64_t)j * D6_BK;
-    const int64_t e0 = k0 + 8 * (t & 7);
-    if (vec && k0 + D6_BK <= n) {  // wave-uniform: every row of the step exists
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S.y[c] = *reinterpret_cast<const u32x4*>(yrow[c] + e0);
-      const uint8_t* src = urow + k0 * rbytes;
+    mode = block_scale_mode(flags, D6_B + D6_TB);
+  }
+  auto run = [&](auto md) __attribute__((always_inline)) {
+    constexpr int MD = decltype(md)::value;
+    typedef mfma32<TL> MF;
+    constexpr int NG = 2;
+    constexpr uint32_t T = (uint32_t)tab_entries<B>::value;
+    extern __shared__ uint32_t smem[];
+    (void)smem;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const uint32_t lane4 = (uint32_t)lane * 4u;
+    const int64_t bm = blockIdx.x % mblocks, bn = blockIdx.x / mblocks;
+    const int64_t m0 = bm * DX_BM, n0 = bn * DX_BN;
+    const bool vec = (n % 8) == 0;
+    const int KS = (int)((n + D6_BK - 1) / D6_BK);
+
+    // ---- dequant role: weight row r = lane of the step, unit uu = wave of the
+    // column tile (32 columns, 4 * B bytes). b = 4 keeps the tables in
+    // registers instead (mm::dequant8_b4); then 4 adjacent lanes take 4
+    // adjacent units of one row (64 contiguous index bytes per row), 16 rows
+    // per wave.
+    const int r = B == 4 ? 16 * (wave & 3) + (lane >> 2) : lane;
+    const int uu = B == 4 ? 4 * (wave >> 2) + (lane & 3) : wave;
+    const int64_t jc = n0 + 32 * uu;
+    const bool col_ok = jc < d;
+    const uint32_t u = (uint32_t)((col_ok ? jc : 0) / 32);
+    const uint32_t glo = group_of((uint32_t)(n0 / 32), ug_magic);
+    const uint32_t ghi = group_of((uint32_t)((n0 + DX_BN < d ? n0 + DX_BN : d) / 32 - 1), ug_magic);
+    const int ng = (int)(ghi - glo + 1);
+    const uint32_t gsel = col_ok ? group_of(u, ug_magic) - glo : 0u;
+    const int64_t rbytes = d * B / 8;
+    const uint8_t* ucol = idx_packed + (int64_t)u * (4 * B);
+    const uint32_t b_st = (uint32_t)r * DX_RSB + 64u * (uint32_t)uu;
+    const int part = wave;
+    // ---- dY role: chunk t % 8 of token rows t / 8 + 64 c
+    const TX* yrow[4];
+    int ye[4] = {0, 0, 0, 0};  // SC: exponents of the four staged token rows
+  #pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t tok = m0 + 64 * c + (t >> 3);
+      yrow[c] = dY + (tok < m ? tok : m - 1) * n;
+      if constexpr (SC && MD != 0) ye[c] = rexp[tok < m ? tok : m - 1];
+    }
+    float ysc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    uint32_t yk[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+    for (int c = 0; c < (int)(sizeof(ye) / sizeof(ye[0])); ++c) {
+      if constexpr (MD == 2) ysc[c] = pow2f(-ye[c]);
+      if constexpr (MD == 1) yk[c] = exp_add_word(ye[c]);
+    }
+    (void)ysc;
+    (void)yk;
+
+    const uint8_t* urow = ucol + (int64_t)r * rbytes;  // row r of step 0
+    // b = 4: the table of (row, this thread's group), 16 entries
+    const uint32_t gabs = glo + gsel;
+    auto load_tab = [&](Dx6Stage<B>& S, int64_t row) {
+      if constexpr (B == 4) {
+        const u32x4* tp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lut) +
+                                                          (row * gpr + gabs) * 16);
+        const u32x4 a = tp[0], b = tp[1];
+        S.lut[0] = a.x; S.lut[1] = a.y; S.lut[2] = a.z; S.lut[3] = a.w;
+        S.lut[4] = b.x; S.lut[5] = b.y; S.lut[6] = b.z; S.lut[7] = b.w;
+      }
+    };
+    auto load_stage = [&](Dx6Stage<B>& S, int j) {
+      const int64_t k0 = (int64_t)j * D6_BK;
+      const int64_t e0 = k0 + 8 * (t & 7);
+      if (vec && k0 + D6_BK <= n) {  // wave-uniform: every row of the step exists
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) S.y[c] = *reinterpret_cast<const u32x4*>(yrow[c] + e0);
+        const uint8_t* src = urow + k0 * rbytes;
+        if constexpr (B == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
+          load_tab(S, k0 + r);
+        } else if constexpr (B == 2) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+          S.w[0] = v.x; S.w[1] = v.y;
+        } else {
+          const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
+          S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
+        }
+        return;
+      }
+  #pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (vec) {
+          const bool in = e0 < n;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
+          S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          const uint16_t* pp = reinterpret_cast<const uint16_t*>(yrow[c]);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t i = e0 + 2 * q;
+            S.y[c][q] = (i < n ? pp[i] : 0u) | ((i + 1 < n ? pp[i + 1] : 0u) << 16);
+          }
+        }
+      }
+      const int64_t row = k0 + r;
+      const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
       if constexpr (B == 4) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src);
         S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
-        load_tab(S, k0 + r);
+        load_tab(S, row < n ? row : n - 1);
       } else if constexpr (B == 2) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(src);
         S.w[0] = v.x; S.w[1] = v.y;
@@ -495,198 +590,174 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
         const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
         S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
       }
-      return;
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (vec) {
-        const bool in = e0 < n;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(yrow[c] + (in ? e0 : 0));
-        S.y[c] = in ? v : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto stage = [&](const Dx6Stage<B>& S, int j, auto md) __attribute__((always_inline)) {
+      constexpr int MD = decltype(md)::value;
+      const uint32_t buf = (uint32_t)(j & 1);
+      const bool ok = (int64_t)j * D6_BK + r < n && col_ok;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if constexpr (B == 4) {
+        // columns of each 8-column chunk in the order of mm::dequant8_b4 (undone
+        // when dX is stored)
+        mm::Planes16 P;
+        mm::planes16(S.lut, P);
+        const uint32_t bb = D6_B + buf * D6_TB + b_st;
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) st_q(bb + 16u * q, ok ? mm::dequant8_b4(S.w[q], P) : z);
       } else {
-        const uint16_t* pp = reinterpret_cast<const uint16_t*>(yrow[c]);
-#pragma unroll
+      const uint32_t gk = (buf * NG + gsel) * T;
+      uint32_t o0[8], o1[8];
+      if constexpr (B == 3) {
+        dx_dequant<B>(S.w, 0, gk, lane4, o0);
+        dx_dequant<B>(S.w, 1, gk, lane4, o1);
+      } else {
+        dx_dequant<B>(S.w, 0, gk, lane4, o0);
+        dx_dequant<B>(S.w + (B == 4 ? 2 : 1), 1, gk, lane4, o1);
+      }
+      const uint32_t bb = D6_B + buf * D6_TB + b_st;
+      st_q(bb, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
+      st_q(bb + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
+      st_q(bb + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
+      st_q(bb + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
+      }
+      const uint32_t ab = D6_A + buf * D6_TA;
+  #pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+        if constexpr (SC && MD == 2) st_q(a, cvt_quad_scaled(S.y[c], ysc[c]));
+        else if constexpr (SC && MD == 1) st_q(a, cvt_quad<TX, TL>(add_quad(S.y[c], yk[c])));
+        else st_q(a, cvt_quad<TX, TL>(S.y[c]));
+      }
+    };
+    DxLutWord<B> LW[NG];
+    auto lut_load = [&](int j) {
+      const int64_t row = (int64_t)j * D6_BK + lane;
+      const bool ok = row < n;
+  #pragma unroll
+      for (int gs = 0; gs < NG; ++gs)
+        if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
+    };
+    auto lut_store = [&](int j) {
+      const uint32_t buf = (uint32_t)(j & 1);
+  #pragma unroll
+      for (int gs = 0; gs < NG; ++gs)
+        if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
+    };
+
+    // ---- matrix roles
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
+    const uint32_t khalf = (uint32_t)(lane >> 5);
+    f32x16 acc[4][2];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
+    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
+      const uint32_t buf = (uint32_t)(k & 1);
+      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(D6_A + buf * D6_TA + swz128(arow + 32u * i, ch));
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        fb[jj] = ld_frag_tr(D6_B + buf * D6_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
+                            (uint32_t)lane);
+    };
+    // four 16-row quarters: each quarter's fragment reads are interleaved with
+    // the previous quarter's MFMAs
+    auto mfma_step = [&](int k) {
+      u32x4 fa[4][4], fb[4][2];
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  #pragma unroll
+      for (int ks = 1; ks < 4; ++ks) {
+  #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t i = e0 + 2 * q;
-          S.y[c][q] = (i < n ? pp[i] : 0u) | ((i + 1 < n ? pp[i + 1] : 0u) << 16);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    Dx6Stage<B> S;
+    // staging work of step k: tables of tile k+2 to LDS, tables of tile k+3
+    // loaded; tile k+1 from S into LDS, S refilled with tile k+2
+    auto stage_step = [&](int k, auto md) __attribute__((always_inline)) {
+      if constexpr (B != 4) {
+        if (k + 2 < KS) lut_store(k + 2);
+        if (k + 3 < KS) lut_load(k + 3);
+      }
+      if (k + 1 < KS) {
+        stage(S, k + 1, md);
+        if (k + 2 < KS) load_stage(S, k + 2);
+      }
+    };
+    const bool mfma_first = wave < 4;
+
+    // ---- prologue
+    if constexpr (B != 4) lut_load(0);
+    load_stage(S, 0);
+    if constexpr (B != 4) {
+      lut_store(0);
+      if (KS > 1) {
+        lut_load(1);
+        lut_store(1);
+      }
+      if (KS > 2) lut_load(2);
+      __syncthreads();
+    }
+    stage(S, 0, md);
+    if (KS > 1) load_stage(S, 1);
+    __syncthreads();
+
+    for (int k = 0; k < KS; ++k) {
+      if (mfma_first) {
+        mfma_step(k);
+        stage_step(k, md);
+      } else {
+        stage_step(k, md);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(k);
+      }
+      __syncthreads();
+    }
+
+    if constexpr (SC && MD != 0) dx_factors_to_lds(rexp, m, m0, t);  // block-uniform
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 uq[4] = {};
+      if constexpr (SC && MD != 0) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
+      }
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        // b = 4: tile column p holds column (p & ~7) + (2 (p & 3) | (p & 7) >> 2)
+        const int p = 64 * wn + 32 * jj + (lane & 31);
+        const int pc = B == 4 ? (p & ~7) | ((p & 3) << 1) | ((p >> 2) & 1) : p;
+        const int64_t col = n0 + pc;
+        if (col >= d) continue;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          float v = acc[i][jj][e];
+          if constexpr (SC && MD != 0) v *= uq[e >> 2][e & 3];
+          if (tok < m) dX[tok * d + col] = v;
         }
       }
     }
-    const int64_t row = k0 + r;
-    const uint8_t* src = ucol + (row < n ? row : n - 1) * rbytes;
-    if constexpr (B == 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-      S.w[0] = v.x; S.w[1] = v.y; S.w[2] = v.z; S.w[3] = v.w;
-      load_tab(S, row < n ? row : n - 1);
-    } else if constexpr (B == 2) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-      S.w[0] = v.x; S.w[1] = v.y;
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(src);
-      S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
-    }
   };
-  auto stage = [&](const Dx6Stage<B>& S, int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-    const bool ok = (int64_t)j * D6_BK + r < n && col_ok;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if constexpr (B == 4) {
-      // columns of each 8-column chunk in the order of mm::dequant8_b4 (undone
-      // when dX is stored)
-      mm::Planes16 P;
-      mm::planes16(S.lut, P);
-      const uint32_t bb = D6_B + buf * D6_TB + b_st;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st_q(bb + 16u * q, ok ? mm::dequant8_b4(S.w[q], P) : z);
-    } else {
-    const uint32_t gk = (buf * NG + gsel) * T;
-    uint32_t o0[8], o1[8];
-    if constexpr (B == 3) {
-      dx_dequant<B>(S.w, 0, gk, lane4, o0);
-      dx_dequant<B>(S.w, 1, gk, lane4, o1);
-    } else {
-      dx_dequant<B>(S.w, 0, gk, lane4, o0);
-      dx_dequant<B>(S.w + (B == 4 ? 2 : 1), 1, gk, lane4, o1);
-    }
-    const uint32_t bb = D6_B + buf * D6_TB + b_st;
-    st_q(bb, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
-    st_q(bb + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
-    st_q(bb + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
-    st_q(bb + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
-    }
-    const uint32_t ab = D6_A + buf * D6_TA;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
-      if constexpr (SC) st_q(a, cvt_quad_scaled(S.y[c], ysc[c]));
-      else st_q(a, cvt_quad<TX, TL>(S.y[c]));
-    }
-  };
-  DxLutWord<B> LW[NG];
-  auto lut_load = [&](int j) {
-    const int64_t row = (int64_t)j * D6_BK + lane;
-    const bool ok = row < n;
-#pragma unroll
-    for (int gs = 0; gs < NG; ++gs)
-      if (gs < ng) dx_lut_load<B, TL>(LW[gs], lut, ok ? row : 0, ok, gpr, glo + gs, part);
-  };
-  auto lut_store = [&](int j) {
-    const uint32_t buf = (uint32_t)(j & 1);
-#pragma unroll
-    for (int gs = 0; gs < NG; ++gs)
-      if (gs < ng) dx_lut_store<B>(LW[gs], (buf * NG + gs) * T, part, lane4);
-  };
-
-  // ---- matrix roles
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint32_t arow = (uint32_t)(128 * wm + (lane & 31));
-  const uint32_t khalf = (uint32_t)(lane >> 5);
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
-  auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-    const uint32_t buf = (uint32_t)(k & 1);
-    const uint32_t ch = (uint32_t)(2 * ks) + khalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = ld_q(D6_A + buf * D6_TA + swz128(arow + 32u * i, ch));
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      fb[jj] = ld_frag_tr(D6_B + buf * D6_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
-                          (uint32_t)lane);
-  };
-  // four 16-row quarters: each quarter's fragment reads are interleaved with
-  // the previous quarter's MFMAs
-  auto mfma_step = [&](int k) {
-    u32x4 fa[4][4], fb[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = MF::run(fa[ks][i], fb[ks][jj], acc[i][jj]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int ks = 1; ks < 4; ++ks) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  Dx6Stage<B> S;
-  // staging work of step k: tables of tile k+2 to LDS, tables of tile k+3
-  // loaded; tile k+1 from S into LDS, S refilled with tile k+2
-  auto stage_step = [&](int k) {
-    if constexpr (B != 4) {
-      if (k + 2 < KS) lut_store(k + 2);
-      if (k + 3 < KS) lut_load(k + 3);
-    }
-    if (k + 1 < KS) {
-      stage(S, k + 1);
-      if (k + 2 < KS) load_stage(S, k + 2);
-    }
-  };
-  const bool mfma_first = wave < 4;
-
-  // ---- prologue
-  if constexpr (B != 4) lut_load(0);
-  load_stage(S, 0);
-  if constexpr (B != 4) {
-    lut_store(0);
-    if (KS > 1) {
-      lut_load(1);
-      lut_store(1);
-    }
-    if (KS > 2) lut_load(2);
-    __syncthreads();
-  }
-  stage(S, 0);
-  if (KS > 1) load_stage(S, 1);
-  __syncthreads();
-
-  for (int k = 0; k < KS; ++k) {
-    if (mfma_first) {
-      mfma_step(k);
-      stage_step(k);
-    } else {
-      stage_step(k);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(k);
-    }
-    __syncthreads();
-  }
-
-  if constexpr (SC) dx_factors_to_lds(rexp, m, m0, t);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f32x4 uq[4];
-    if constexpr (SC) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) uq[q] = ld_f4((uint32_t)(128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)) * 4u);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      // b = 4: tile column p holds column (p & ~7) + (2 (p & 3) | (p & 7) >> 2)
-      const int p = 64 * wn + 32 * jj + (lane & 31);
-      const int pc = B == 4 ? (p & ~7) | ((p & 3) << 1) | ((p >> 2) & 1) : p;
-      const int64_t col = n0 + pc;
-      if (col >= d) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t tok = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        float v = acc[i][jj][e];
-        if constexpr (SC) v *= uq[e >> 2][e & 3];
-        if (tok < m) dX[tok * d + col] = v;
-      }
-    }
-  }
+  if (!SC || mode == 0) run(mode_tag<0>{});
+  else if (mode == 1) run(mode_tag<1>{});
+  else run(mode_tag<2>{});
 }
 
 // ============================================================================

@@ -210,6 +210,28 @@ __device__ __forceinline__ u32x4 cvt_quad_scaled(u32x4 v, float s) {
     o[q] = pack_tc<half_t>(__builtin_bit_cast(float, v[q] << 16) * s, __builtin_bit_cast(float, v[q] & 0xFFFF0000u) * s);
   return o;
 }
+// the same with the exponent fields raised by an exp_add_word (block mode 1)
+__device__ __forceinline__ u32x4 add_quad(u32x4 v, uint32_t k) {
+  return u32x4{v[0] + k, v[1] + k, v[2] + k, v[3] + k};
+}
+
+// compile-time tag of a block's prescale mode (0 none, 1 exponent add, 2 multiply)
+template <int V> struct mode_tag { static constexpr int value = V; };
+
+// Block-uniform prescale mode (skm_common.h scale_mode_of) from each thread's
+// flags: the waves OR their ballots into an LDS word at `word` (an address no
+// thread touches before the block's first K-step), two barriers.
+__device__ __forceinline__ int block_scale_mode(uint32_t flags, uint32_t word) {
+  if (threadIdx.x == 0) st_w(word, 0u);
+  __syncthreads();
+  const uint64_t b1 = __ballot(flags & 1u), b2 = __ballot(flags & 2u);
+  if ((threadIdx.x & 63) == 0 && (b1 | b2))
+    __hip_atomic_fetch_or((lds_u32*)(uintptr_t)word, (b1 ? 1u : 0u) | (b2 ? 2u : 0u), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  return scale_mode_of(ld_w(word));
+}
+
 __device__ __forceinline__ u32x4 cvt_quad_perm_scaled(u32x4 v, float s) {
   float f[8];
 #pragma unroll

@@ -473,10 +473,11 @@ def _row_errs(got, want):
 
 
 @pytest.mark.parametrize("b,gpr,d", [(4, 8, 4096), (4, 32, 4096), (2, 8, 4096), (3, 4, 1536)])
-@pytest.mark.parametrize("sigma", [1e-6, 1e-8, 1e-20, 1e4])
+@pytest.mark.parametrize("sigma", [1e-6, 1e-8, 1e-20, 1e-33, 1e4])
 def test_dx_gradient_scales_bf16_f16(b, gpr, d, sigma):
     """dY ~ N(0, sigma) in bf16: dX within the 16-bit tolerance at gradient scales far below f16's normal
-    range (and above its largest value). Groups of 512 and 384 columns take the 64-row dX steps, groups of
+    range (and up to f16's largest value). The scales take each conversion of a block: none (1e4),
+    exponent-field add (1e-6 .. 1e-20), multiply (1e-33, rows below 2^-87). Groups of 512 and 384 columns take the 64-row dX steps, groups of
     128 columns the 32-row steps."""
     n, m = 256, 96
     idx, lut, X, _ = make_case(f"dxscale/{b}/{gpr}/{d}", n, d, b, gpr, m, "bf16", "f16")
@@ -505,10 +506,11 @@ def test_dx_rows_of_different_scales_bf16_f16():
     (4, 8, 200, 4096, 300), (2, 8, 130, 11008, 40),  # GEMM, 64- and 32-column K-steps
     (3, 1, 33, 96, 19),
 ])
-@pytest.mark.parametrize("scale", [3e4, 1e-6])
+@pytest.mark.parametrize("scale", [3e4, 1e-6, 1e-32])
 def test_fwd_activation_scales_bf16_f16(b, gpr, n, d, m, scale):
     """X ~ N(0, scale) in bf16: entries up to ~1e5 (beyond f16's largest) or rows far below f16's normal
-    range, through every forward path; every output row within the tolerance."""
+    range, through every forward path; every output row within the tolerance. The GEMM blocks take the
+    multiply (3e4 with 1e5 entries; 1e-32, rows below 2^-87) and exponent-add (1e-6) conversions."""
     idx, lut, _, _ = make_case(f"fwdscale/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, 1, "bf16", "f16")
     X = syn.random_normal(f"fwdscale/{b}/{gpr}/{n}/{d}/{m}/{scale}", (m, d), scale, "bf16")
     if scale > 1:
@@ -525,6 +527,48 @@ def test_fwd_rows_of_different_scales_bf16_f16(m, d):
     idx, lut, _, _ = make_case(f"fwdrows/{m}/{d}", n, d, b, gpr, 1, "bf16", "f16")
     X = _scaled_rows(f"fwdrows/{m}/{d}/X", (m, d), [2.0 ** k for k in range(-70, 61, 10)])
     got, want = _fwd16(idx, lut, X, b, gpr, "bf16", "f16")
+    assert max(_row_errs(got, want)) <= TOL16
+
+
+# bf16 row maxima at the edges of [2^-2, 2^16), the window of rows converted without a prescale:
+# 2^-2 and 65280 (the largest bf16 below 2^16) lie inside it, 2^-2 - 2^-10 and 2^16 outside
+_WINDOW_EDGES = [0.25, 0.25 - 2.0 ** -10, 65280.0, 65536.0]
+
+
+@pytest.mark.parametrize("peak", _WINDOW_EDGES)
+@pytest.mark.parametrize("d", [4096, 28672])
+def test_decode_window_edge_rows_bf16_f16(peak, d):
+    """One token whose largest magnitude sits at an edge of the unscaled window (the staging decode checks
+    the window and, outside it, re-stages the activations prescaled): the output within the tolerance."""
+    b, gpr, n = 4, 4, 80
+    idx, lut, _, _ = make_case(f"window/{d}", n, d, b, gpr, 1, "bf16", "f16")
+    z = syn.random_normal(f"window/{d}/{peak}", (1, d), 1.0, "f32").astype(np.float64)
+    x = np.clip(z / 4.0, -0.999, 0.999) * peak
+    x[0, d // 3] = -peak
+    X = syn.to_storage(x.astype(np.float32), "bf16")
+    assert np.max(np.abs(syn.to_float64(X, "bf16"))) == peak
+    got, want = _fwd16(idx, lut, X, b, gpr, "bf16", "f16")
+    assert np.all(np.isfinite(got))
+    assert max(_row_errs(got, want)) <= TOL16
+
+
+@pytest.mark.parametrize("zero_row", [False, True])
+def test_decode_window_mixed_rows_bf16_f16(zero_row):
+    """Staged rows at every window edge together (one row outside it sends the whole block to the exact
+    path), and optionally a row of zeros (whose outputs must be exactly 0): every output row within the
+    tolerance."""
+    b, gpr, n, d = 4, 8, 96, 4096
+    m = len(_WINDOW_EDGES) + 2
+    idx, lut, _, _ = make_case("windowmix", n, d, b, gpr, 1, "bf16", "f16")
+    z = syn.random_normal("windowmix/X", (m, d), 1.0, "f32").astype(np.float64)
+    peaks = _WINDOW_EDGES + [1.0, 0.0 if zero_row else 3.0]
+    x = np.clip(z / 4.0, -0.999, 0.999) * np.asarray(peaks)[:, None]
+    x[np.arange(m), (np.arange(m) * 37) % d] = peaks
+    X = syn.to_storage(x.astype(np.float32), "bf16")
+    got, want = _fwd16(idx, lut, X, b, gpr, "bf16", "f16")
+    if zero_row:
+        assert np.all(got[-1] == 0.0)
+        got, want = got[:-1], want[:-1]
     assert max(_row_errs(got, want)) <= TOL16
 
 
