@@ -11,9 +11,12 @@ The same JSON line carries the other measured parts of the hot path (16-token
 forward, the 7B MLP at 2 and 3 bits, decode with one table set per token over
 one index stream, 70B-shaped decode and prefill GEMM, the 7B decoder-layer
 fine-tuning step, the fused table optimizer steps and a grouped q/k/v decode,
-LLaMA-2-13B decode at one group per row, the backward at 2 and 3 bits, sketch
-construction of a 4096 x 4096 layer)
-and the CPU oracle timed on this host as a baseline.
+LLaMA-2-13B decode at one group per row, the backward at 2 and 3 bits and at
+one group per row, sketch construction of a 4096 x 4096 layer, a rotated
+read-only stream of the decode calls' sizes) and the CPU oracle timed on this
+host as a baseline. The CPU leg also scores each part's outputs (sampled rows,
+tokens and columns) against the oracle: ``parity_err`` = max |gpu - oracle| /
+max |oracle| on the sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -34,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "LUT-GEMV GB/s (% HBM peak) at 7B shapes; LUT-GEMM + bwd TFLOP/s (% MFMA)"
 ROTATE_BYTES = 1 << 30
-SPIN_CYCLES_PER_LAUNCH = 100_000  # > host enqueue time of one launch at the GPU timer rate
+SPIN_MIN_MS = 0.5  # shortest hold of the stream before the timed launches
 # rocprofv3 summary of the headline kernel (FETCH_SIZE / WRITE_SIZE counters)
 DECODE_PROFILE = os.path.join(ROOT, "profiles", "k_decode_llama2_7b_attn_4096x4096_b4_m1.md")
 
@@ -45,8 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="all",
-                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,13b,bwdlowbit,construct,"
-                         "dense,copy "
+                    help="comma list of decode,fwd16,lowbit,multilut,decode70b,prefill,finetune,glue,13b,bwdlowbit,"
+                         "bwdgpr1,construct,dense,copy,readref "
                          "(default all; decode always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
@@ -74,41 +77,129 @@ class Rotation:
         return self.idx[k], self.lut[k]
 
 
+_SPIN_RATE = []  # cycles of torch.cuda._sleep per millisecond, measured once
+
+
+def spin_cycles_per_ms(torch):
+    if not _SPIN_RATE:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_RATE.append(2_000_000 / max(e0.elapsed_time(e1), 1e-3))
+    return _SPIN_RATE[0]
+
+
 def time_launches(torch, launch, steps, warmup, launches_per_step=1):
     """GPU time (ms) of `steps` back-to-back launches, from HIP events on the launch stream.
 
     The stream is held by a spin kernel while the host enqueues every timed
     launch, so the GPU then runs them back to back: the events measure the
     kernels and the dispatch gaps between them, not the host's submission time.
+    The spin is sized from the host's own submission time per launch (twice
+    the warm-up's median, measured here) at the spin kernel's measured rate; when the
+    timed submissions still outlast it, the run is repeated with a spin sized
+    from them.
     """
+    del launches_per_step  # the spin is sized from measured host time
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    rate = spin_cycles_per_ms(torch)
+    per = []
+    for _ in range(max(1, warmup)):
+        t0 = time.perf_counter()
         launch()
+        per.append((time.perf_counter() - t0) * 1e3)
+    host_ms = float(np.median(per))  # (the first calls may load code objects)
     torch.cuda.synchronize()
-    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(SPIN_CYCLES_PER_LAUNCH * steps * launches_per_step))
-    first.record(stream)
-    for _ in range(steps):
-        launch()
-    last.record(stream)
-    torch.cuda.synchronize()
+    for attempt in range(2):
+        spin_ms = SPIN_MIN_MS + 2.0 * host_ms * steps
+        first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(rate * spin_ms))
+        t0 = time.perf_counter()
+        first.record(stream)
+        for _ in range(steps):
+            launch()
+        last.record(stream)
+        submit_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        if submit_ms < spin_ms:
+            break
+        host_ms = submit_ms / max(1, steps)
+    else:
+        print(f"time_launches: host submission ({submit_ms:.2f} ms) outlasted the spin ({spin_ms:.2f} ms); "
+              "the time may include host gaps", file=sys.stderr)
     return first.elapsed_time(last)
 
 
-def bench_fwd(torch, skm, w, shape, b, m, steps, warmup, rotate=True):
+def sample_ids(count, k, seed):
+    """Sorted sample of indices in [0, count): the first and last 16 and k random ones."""
+    r = np.random.default_rng(seed)
+    ids = np.concatenate([np.arange(min(16, count)), np.arange(max(0, count - 16), count),
+                          r.choice(count, min(k, count), replace=False)])
+    return np.unique(ids)
+
+
+def fwd_workspace(torch, skm, X, lut, n, d, b, gpr):
+    nb = skm.sketch_matmul_fwd_workspace(X.shape[0], n, d, b, gpr, skm._lib.dtype_code(X), skm._lib.dtype_code(lut))
+    return torch.empty(nb, dtype=torch.uint8, device="cuda:0") if nb else None
+
+
+def bwd_workspace(torch, skm, dY, lut, n, d, b, gpr):
+    nb = skm.sketch_matmul_bwd_workspace(dY.shape[0], n, d, b, gpr, skm._lib.dtype_code(dY),
+                                         skm._lib.dtype_code(lut))
+    return torch.empty(nb, dtype=torch.uint8, device="cuda:0") if nb else None
+
+
+def fwd_check(name, t, Y, b, gpr, x_dtype, lut_dtype, seed):
+    """A parity sample of a forward output (scored by the CPU leg): sampled tokens x sampled rows."""
+    m, n = Y.shape
+    toks = sample_ids(m, 96, seed) if m > 128 else np.arange(m)
+    rows = sample_ids(n, 224, seed + 1)
+    got = Y.float().cpu().numpy()[np.ix_(toks, rows)].astype(np.float64)
+    return {"name": name, "kind": "fwd", "X": t["X"][toks], "idx": t["idx_packed"][rows], "lut": t["lut"][rows],
+            "b": b, "gpr": gpr, "x_dtype": x_dtype, "lut_dtype": lut_dtype, "got": got}
+
+
+def bwd_checks(name, t, dX, dL, b, gpr, x_dtype, lut_dtype, seed):
+    """Parity samples of dX (sampled tokens x sampled columns) and dLUT (sampled rows)."""
+    out = []
+    if dX is not None:
+        m, d = dX.shape
+        toks, cols = sample_ids(m, 96, seed), sample_ids(d, 224, seed + 1)
+        out.append({"name": name + ".dx", "kind": "dx", "dY": t["dY"][toks], "idx": t["idx_packed"],
+                    "lut": t["lut"], "cols": cols, "b": b, "gpr": gpr, "x_dtype": x_dtype, "lut_dtype": lut_dtype,
+                    "got": dX.cpu().numpy()[np.ix_(toks, cols)].astype(np.float64)})
+    if dL is not None:
+        rows = sample_ids(dL.shape[0], 96, seed + 2)
+        out.append({"name": name + ".dlut", "kind": "dlut", "dY": t["dY"][:, rows], "X": t["X"],
+                    "idx": t["idx_packed"][rows], "b": b, "gpr": gpr, "x_dtype": x_dtype, "lut_dtype": lut_dtype,
+                    "got": dL.cpu().numpy()[rows].astype(np.float64)})
+    return out
+
+
+CHECKS = []   # parity samples of the parts, scored against the oracle by the CPU leg
+
+
+def bench_fwd(torch, skm, w, shape, b, m, steps, warmup, rotate=True, check=None):
     from lut_sketched_matmul_amd import workloads as wl
     t = w.make(shape, b, m)
     X = dev(torch, t["X"], w.x_dtype)
     idx = dev(torch, t["idx_packed"], "u8")
     lut = dev(torch, t["lut"], w.lut_dtype)
     Y = torch.empty((m, shape.n), dtype=X.dtype, device="cuda:0")
+    ws = fwd_workspace(torch, skm, X, lut, shape.n, shape.d, b, w.gpr)
     rot = Rotation(torch, idx, lut) if rotate else None
 
     def launch():
         i, l = rot.next() if rot else (idx, lut)
-        skm.sketch_matmul_fwd(X, i, l, b, w.gpr, out=Y)
+        skm.sketch_matmul_fwd(X, i, l, b, w.gpr, out=Y, workspace=ws)
 
     total = time_launches(torch, launch, steps, warmup)
+    if check:
+        skm.sketch_matmul_fwd(X, idx, lut, b, w.gpr, out=Y, workspace=ws)
+        CHECKS.append(fwd_check(check, t, Y, b, w.gpr, w.x_dtype, w.lut_dtype, shape.n + m + b))
     xb = wl.DTYPE_BYTES[w.x_dtype]
     lb = wl.DTYPE_BYTES[w.lut_dtype]
     nbytes = wl.algorithmic_bytes_fwd(shape.n, shape.d, b, w.gpr, m, lb, xb)
@@ -244,6 +335,10 @@ def bench_finetune(torch, skm, steps, warmup):
             Y=torch.empty((m, s.n), dtype=torch.bfloat16, device="cuda:0"),
             dL=torch.empty((s.n, w.gpr, 16), dtype=torch.float32, device="cuda:0")))
         p = projs[-1]
+        p["wsf"] = fwd_workspace(torch, skm, p["X"], p["lut"], s.n, s.d, 4, w.gpr)
+        p["wsb"] = bwd_workspace(torch, skm, p["dY"], p["lut"], s.n, s.d, 4, w.gpr)
+        if s.name == "gate":
+            p["host"] = {k: t[k] for k in ("X", "dY", "idx_packed", "lut")}
         # fp32 master tables and Adam moments; the step refreshes the f16 copy the kernels read
         p["master"] = p["lut"].float()
         p["m1"], p["m2"] = torch.zeros_like(p["master"]), torch.zeros_like(p["master"])
@@ -253,8 +348,9 @@ def bench_finetune(torch, skm, steps, warmup):
     def step():
         it[0] += 1
         for p in projs:
-            skm.sketch_matmul_fwd(p["X"], p["idx"], p["lut"], 4, w.gpr, out=p["Y"])
-            skm.sketch_matmul_bwd(p["dY"], p["X"], p["idx"], p["lut"], 4, w.gpr, dlut_out=p["dL"])
+            skm.sketch_matmul_fwd(p["X"], p["idx"], p["lut"], 4, w.gpr, out=p["Y"], workspace=p["wsf"])
+            skm.sketch_matmul_bwd(p["dY"], p["X"], p["idx"], p["lut"], 4, w.gpr, dlut_out=p["dL"],
+                                  workspace=p["wsb"])
         for p in projs:
             skm.sketch_lut_adam_step(p["master"], p["dL"], p["m1"], p["m2"], it[0], 1e-5, grad_scale=1.0 / m,
                                      lut=p["lut"])
@@ -264,13 +360,23 @@ def bench_finetune(torch, skm, steps, warmup):
     ms = total / steps
     # per-pass split, timed the same way on the largest projection (gate)
     g = projs[4]
-    t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(g["X"], g["idx"], g["lut"], 4, w.gpr, out=g["Y"]),
-                          steps, warmup) / steps
+    t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(g["X"], g["idx"], g["lut"], 4, w.gpr, out=g["Y"],
+                                                               workspace=g["wsf"]), steps, warmup) / steps
     t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(g["dY"], g["X"], g["idx"], g["lut"], 4, w.gpr,
-                                                               need_dlut=False), steps, warmup) / steps
+                                                               need_dlut=False, workspace=g["wsb"]),
+                         steps, warmup) / steps
     t_dl = time_launches(torch, lambda: skm.sketch_matmul_bwd(g["dY"], g["X"], g["idx"], g["lut"], 4, w.gpr,
-                                                               need_dx=False, dlut_out=g["dL"]), steps, warmup) / steps
+                                                               need_dx=False, dlut_out=g["dL"], workspace=g["wsb"]),
+                         steps, warmup) / steps
     fg = wl.flops_pass(g["s"].n, g["s"].d, m)
+    # parity samples of the gate projection (forward, dX, dLUT), on its original tables (the timed Adam
+    # steps have moved the device copy)
+    g["lut"].copy_(dev(torch, g["host"]["lut"], w.lut_dtype))
+    skm.sketch_matmul_fwd(g["X"], g["idx"], g["lut"], 4, w.gpr, out=g["Y"], workspace=g["wsf"])
+    gdx, _ = skm.sketch_matmul_bwd(g["dY"], g["X"], g["idx"], g["lut"], 4, w.gpr, dlut_out=g["dL"],
+                                   workspace=g["wsb"])
+    CHECKS.append(fwd_check("finetune_7b_layer.gate.y", g["host"], g["Y"], 4, w.gpr, w.x_dtype, w.lut_dtype, 41))
+    CHECKS.extend(bwd_checks("finetune_7b_layer.gate", g["host"], gdx, g["dL"], 4, w.gpr, w.x_dtype, w.lut_dtype, 43))
     return {
         "workload": w.name, "m": m, "ms_per_step": ms, "flops": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
         "frac_mfma_peak": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
@@ -336,18 +442,83 @@ def bench_bwd_lowbit(torch, skm, steps, warmup):
             idx, lut = dev(torch, t["idx_packed"], "u8"), dev(torch, t["lut"], w.lut_dtype)
             Y = torch.empty((m, s_.n), dtype=X.dtype, device="cuda:0")
             dL = torch.empty((s_.n, w.gpr, 1 << b), dtype=torch.float32, device="cuda:0")
-            del t
-            t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(X, idx, lut, b, w.gpr, out=Y),
+            wf = fwd_workspace(torch, skm, X, lut, s_.n, s_.d, b, w.gpr)
+            wb = bwd_workspace(torch, skm, dY, lut, s_.n, s_.d, b, w.gpr)
+            t_fwd = time_launches(torch, lambda: skm.sketch_matmul_fwd(X, idx, lut, b, w.gpr, out=Y, workspace=wf),
                                   steps, warmup) / steps
-            t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, need_dlut=False),
-                                 steps, warmup) / steps
+            t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, need_dlut=False,
+                                                                       workspace=wb), steps, warmup) / steps
             t_dl = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, need_dx=False,
-                                                                       dlut_out=dL), steps, warmup) / steps
+                                                                       dlut_out=dL, workspace=wb),
+                                 steps, warmup) / steps
+            if s_.name == "down":
+                gdx, _ = skm.sketch_matmul_bwd(dY, X, idx, lut, b, w.gpr, dlut_out=dL, workspace=wb)
+                CHECKS.extend(bwd_checks(f"finetune_lowbit_7b_m8192.down_b{b}", t, gdx, dL, b, w.gpr, w.x_dtype,
+                                         w.lut_dtype, 50 + b))
+            del t
             f = wl.flops_pass(s_.n, s_.d, m)
             out[f"{s_.name}_{s_.n}x{s_.d}_b{b}"] = {
                 "fwd_ms": t_fwd, "dx_ms": t_dx, "dlut_ms": t_dl,
                 "fwd_TFLOPs": f / (t_fwd * 1e-3) / 1e12, "dx_TFLOPs": f / (t_dx * 1e-3) / 1e12,
                 "dlut_TFLOPs": f / (t_dl * 1e-3) / 1e12}
+    return out
+
+
+def bench_bwd_gpr1(torch, skm, steps, warmup):
+    """dX and dLUT at one group per row on the 7B q and gate projections (m = 8192): the (128-row block,
+    group) grid alone has 32 / 86 blocks, so the table gradient is split over token ranges into the
+    workspace and the partial tables are added in range order."""
+    from lut_sketched_matmul_amd import workloads as wl
+    w = wl.LLAMA2_7B_FINETUNE_GPR1
+    m = w.tokens[0]
+    out = {}
+    for s_ in w.shapes:
+        t = w.make(s_, 4, m)
+        X, dY = dev(torch, t["X"], w.x_dtype), dev(torch, t["dY"], w.x_dtype)
+        idx, lut = dev(torch, t["idx_packed"], "u8"), dev(torch, t["lut"], w.lut_dtype)
+        dL = torch.empty((s_.n, 1, 16), dtype=torch.float32, device="cuda:0")
+        wb = bwd_workspace(torch, skm, dY, lut, s_.n, s_.d, 4, 1)
+        t_dx = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, 4, 1, need_dlut=False,
+                                                                   workspace=wb), steps, warmup) / steps
+        t_dl = time_launches(torch, lambda: skm.sketch_matmul_bwd(dY, X, idx, lut, 4, 1, need_dx=False,
+                                                                   dlut_out=dL, workspace=wb), steps, warmup) / steps
+        f = wl.flops_pass(s_.n, s_.d, m)
+        rb = (s_.n + 127) // 128
+        # the workspace holds the row exponents of dY (bf16 with f16 tables), then one partial table per range
+        rexp_bytes = -(-m * 4 // 256) * 256
+        ranges = (wb.numel() - rexp_bytes) // (s_.n * 16 * 4)
+        out[f"{s_.name}_{s_.n}x{s_.d}_gpr1"] = {
+            "dx_ms": t_dx, "dlut_ms": t_dl, "dx_TFLOPs": f / (t_dx * 1e-3) / 1e12,
+            "dlut_TFLOPs": f / (t_dl * 1e-3) / 1e12, "dlut_row_blocks": rb, "dlut_token_ranges": int(ranges),
+            "dlut_blocks": int(rb * ranges)}
+        if s_.name == "q":
+            gdx, _ = skm.sketch_matmul_bwd(dY, X, idx, lut, 4, 1, dlut_out=dL, workspace=wb)
+            CHECKS.extend(bwd_checks("finetune_7b_gpr1.q", t, gdx, dL, 4, 1, w.x_dtype, w.lut_dtype, 61))
+        del t
+    return out
+
+
+def bench_read_reference(torch, steps, warmup):
+    """A rotated read-only stream of the headline decode's and the 70B up decode's byte counts per call
+    (the vendor reduction torch.sum over fp16 buffers, >= 1 GiB in rotation): the per-call cost of reading
+    that many bytes once from HBM, launch and ramp included. Context for the decode rates, not a roof."""
+    from lut_sketched_matmul_amd import workloads as wl
+    out = {}
+    for name, nbytes in (("7b_attn_decode_9.45MB", wl.algorithmic_bytes_fwd(4096, 4096, 4, 8, 1, 2, 2)),
+                         ("70b_up_decode_121MB", wl.algorithmic_bytes_fwd(28672, 8192, 4, 4, 1, 2, 2))):
+        elems = nbytes // 2
+        count = max(2, -(-ROTATE_BYTES // nbytes))
+        bufs = [torch.ones(elems, dtype=torch.float16, device="cuda:0") for _ in range(count)]
+        it = [0]
+
+        def launch():
+            torch.sum(bufs[it[0] % count])
+            it[0] += 1
+
+        ms = time_launches(torch, launch, steps, warmup) / steps
+        out[name] = {"bytes": int(elems * 2), "ms_per_call": ms, "GBps": elems * 2 / (ms * 1e-3) / 1e9,
+                     "rotation_copies": count}
+        del bufs
     return out
 
 
@@ -424,8 +595,10 @@ def bench_copy(torch, steps, warmup):
             "GBps_read_plus_write": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, shape, b, m, budget_s=12.0):
-    """The CPU oracle (float64 numpy) on the same decode workload."""
+def cpu_baseline(w, shape, b, m, checks, budget_s=12.0):
+    """The CPU oracle (float64 numpy) on the same decode workload, and on the backward (dX, dW and the
+    binning into dLUT) of one fine-tuning projection; then the parity samples of the parts scored against
+    it."""
     import oracle
     from lut_sketched_matmul_amd import synthetic as syn
     from lut_sketched_matmul_amd import workloads as wl
@@ -446,13 +619,49 @@ def cpu_baseline(w, shape, b, m, budget_s=12.0):
     nbytes = wl.algorithmic_bytes_fwd(shape.n, shape.d, b, w.gpr, m, wl.DTYPE_BYTES[w.lut_dtype],
                                       wl.DTYPE_BYTES[w.x_dtype])
     med = float(np.median(times))
-    return {
+    out = {
         "value": nbytes / med / 1e9, "unit": "GB/s",
         "cores": int(blas_threads), "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{len(times)} oracle forward calls (unpack + float64 dequant + matvec) on the full "
                   f"{shape.n}x{shape.d} b={b} m={m} layer, median {med * 1e3:.1f} ms",
     }
+    # backward of the 7B fine-tuning q projection (4096 x 4096, 8192 tokens): dX = dY W, then dW = dY^T X
+    # binned into dLUT, in float64; one run (about 2 x 0.27 TFLOP)
+    wf = wl.LLAMA2_7B_FINETUNE
+    sq = wf.shapes[0]
+    tq = wf.make(sq, 4, wf.tokens[0])
+    dY64, X64 = syn.to_float64(tq["dY"], wf.x_dtype), syn.to_float64(tq["X"], wf.x_dtype)
+    L64 = syn.to_float64(tq["lut"], wf.lut_dtype)
+    t0 = time.perf_counter()
+    oracle.backward_dx(dY64, tq["idx_packed"], L64, sq.d, 4, wf.gpr)
+    oracle.backward_dlut(dY64, X64, tq["idx_packed"], 4, wf.gpr)
+    tb = time.perf_counter() - t0
+    fb = 2 * wl.flops_pass(sq.n, sq.d, wf.tokens[0])
+    out["backward"] = {"value": fb / tb / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+                       "seconds": tb,
+                       "sample": f"one oracle backward (dX, dW, binning) of the {sq.n}x{sq.d} b=4 gpr={wf.gpr} "
+                                 f"q projection at {wf.tokens[0]} tokens"}
+    del tq, dY64, X64
+    return out, _score_checks(oracle, syn, checks)
+
+
+def _score_checks(oracle, syn, checks):
+    """max |gpu - oracle| / max |oracle| of each part's parity sample (part of the CPU leg)."""
+    errs = {}
+    for c in checks:
+        L64 = syn.to_float64(c["lut"], c["lut_dtype"]) if "lut" in c else None
+        if c["kind"] == "fwd":
+            want = oracle.forward(syn.to_float64(c["X"], c["x_dtype"]), c["idx"], L64, c["b"], c["gpr"])
+        elif c["kind"] == "dx":
+            d = c["idx"].shape[1] * 8 // c["b"]
+            W = oracle.dequantize(c["idx"], L64, d, c["b"], c["gpr"])
+            want = syn.to_float64(c["dY"], c["x_dtype"]) @ W[:, c["cols"]]
+        else:
+            want = oracle.backward_dlut(syn.to_float64(c["dY"], c["x_dtype"]), syn.to_float64(c["X"], c["x_dtype"]),
+                                        c["idx"], c["b"], c["gpr"])
+        errs[c["name"]] = oracle.rel_err(c["got"], want)
+    return errs
 
 
 def main():
@@ -470,17 +679,18 @@ def main():
     skm.lib()
     want = set(args.parts.split(",")) if args.parts != "all" else {"decode", "fwd16", "lowbit", "multilut",
                                                                    "decode70b", "prefill", "finetune", "glue",
-                                                                   "13b", "bwdlowbit", "construct", "dense", "copy"}
+                                                                   "13b", "bwdlowbit", "bwdgpr1", "construct",
+                                                                   "dense", "copy", "readref"}
     w = wl.LLAMA2_7B_ATTN
     shape = w.shapes[0]
     parts = {}
     log = lambda msg: print("# " + msg, file=sys.stderr, flush=True)
 
-    dec = bench_fwd(torch, skm, w, shape, 4, 1, args.steps, args.warmup)
+    dec = bench_fwd(torch, skm, w, shape, 4, 1, args.steps, args.warmup, check="decode_m1")
     parts["decode_m1"] = dec
     log(f"decode 4096x4096 b=4 m=1: {dec['ms_per_launch'] * 1e3:.2f} us/launch, {dec['GBps']:.0f} GB/s")
     if "fwd16" in want:
-        f16 = bench_fwd(torch, skm, w, shape, 4, 16, args.steps, args.warmup)
+        f16 = bench_fwd(torch, skm, w, shape, 4, 16, args.steps, args.warmup, check="fwd_m16")
         parts["fwd_m16"] = f16
         log(f"forward 4096x4096 b=4 m=16: {f16['ms_per_launch'] * 1e3:.2f} us/launch, {f16['GBps']:.0f} GB/s")
     if "lowbit" in want:
@@ -488,9 +698,11 @@ def main():
         wlb = wl.LLAMA2_7B_MLP_LOWBIT
         lb = {}
         for s_, b_, m_ in wl.runs(wlb):
-            r = bench_fwd(torch, skm, wlb, s_, b_, m_, args.steps, args.warmup)
+            key = f"{s_.name}_b{b_}_m{m_}"
+            r = bench_fwd(torch, skm, wlb, s_, b_, m_, args.steps, args.warmup,
+                          check=f"decode_lowbit_7b_mlp.{key}")
             r["frac_hbm_peak"] = r["GBps"] / HBM_PEAK_GBS
-            lb[f"{s_.name}_b{b_}_m{m_}"] = r
+            lb[key] = r
         parts["decode_lowbit_7b_mlp"] = lb
         log("7B MLP b=2/3 decode: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in lb.items()))
     if "multilut" in want:
@@ -503,7 +715,8 @@ def main():
         w7 = wl.LLAMA3_70B_MLP
         d7 = {}
         for s_ in w7.shapes:
-            r = bench_fwd(torch, skm, w7, s_, 4, 1, max(20, args.steps // 4), max(2, args.warmup // 4))
+            r = bench_fwd(torch, skm, w7, s_, 4, 1, max(20, args.steps // 4), max(2, args.warmup // 4),
+                          check=f"decode_70b_mlp_m1.{s_.name}")
             r["frac_hbm_peak"] = r["GBps"] / HBM_PEAK_GBS
             d7[s_.name] = r
         parts["decode_70b_mlp_m1"] = d7
@@ -514,7 +727,8 @@ def main():
     if "prefill" in want:
         w4 = wl.LLAMA3_70B_MLP
         for s4 in w4.shapes:
-            r = bench_fwd(torch, skm, w4, s4, 4, 2048, big_steps, big_warm, rotate=False)
+            r = bench_fwd(torch, skm, w4, s4, 4, 2048, big_steps, big_warm, rotate=False,
+                          check=f"prefill_70b_{s4.name}_m2048")
             r["frac_mfma_peak"] = r["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
             parts[f"prefill_70b_{s4.name}_m2048"] = r
             log(f"prefill 70B {s4.name} m=2048: {r['ms_per_launch']:.3f} ms, {r['TFLOPs']:.0f} TFLOP/s")
@@ -534,6 +748,17 @@ def main():
         parts["finetune_lowbit_7b_m8192"] = rb
         log("7B b=2/3 m=8192 fwd/dX/dLUT TFLOP/s: " + ", ".join(
             f"{k} {v['fwd_TFLOPs']:.0f}/{v['dx_TFLOPs']:.0f}/{v['dlut_TFLOPs']:.0f}" for k, v in rb.items()))
+    if "bwdgpr1" in want:
+        rg = bench_bwd_gpr1(torch, skm, big_steps, big_warm)
+        parts["finetune_7b_gpr1_m8192"] = rg
+        log("7B gpr=1 m=8192 dX/dLUT TFLOP/s: " + ", ".join(
+            f"{k} {v['dx_TFLOPs']:.0f}/{v['dlut_TFLOPs']:.0f} ({v['dlut_blocks']} dLUT blocks)" for k, v in rg.items()))
+    if "readref" in want:
+        rr = bench_read_reference(torch, max(20, args.steps // 2), max(2, args.warmup // 2))
+        rr["decode_m1_over_read_ref"] = dec["ms_per_launch"] / rr["7b_attn_decode_9.45MB"]["ms_per_call"]
+        parts["read_reference_torch_sum"] = rr
+        log("read-only reference (torch.sum, rotated): " + ", ".join(
+            f"{k} {v['ms_per_call'] * 1e3:.2f} us {v['GBps']:.0f} GB/s" for k, v in rr.items() if isinstance(v, dict)))
     if "construct" in want:
         cs = bench_construct(torch, skm)
         parts["sketch_construction_4096x4096_b4_gpr4"] = cs
@@ -558,7 +783,12 @@ def main():
         parts["copy_1GiB"] = cp
         log(f"device copy 1 GiB: {cp['ms_per_launch']:.3f} ms, {cp['GBps_read_plus_write']:.0f} GB/s read+write")
 
-    cpu = None if args.no_cpu else cpu_baseline(w, shape, 4, 1)
+    cpu = None
+    if not args.no_cpu:
+        cpu, errs = cpu_baseline(w, shape, 4, 1, CHECKS)
+        parts["parity_err"] = errs
+        log("parity (max|gpu - oracle| / max|oracle| on sampled outputs): " + ", ".join(
+            f"{k} {v:.2e}" for k, v in errs.items()))
     value = dec["GBps"]
     from lut_sketched_matmul_amd import profiling
     # measured HBM bytes per launch (scaled counters); None once the kernel sources changed

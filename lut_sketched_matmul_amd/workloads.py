@@ -117,8 +117,17 @@ LLAMA2_7B_FINETUNE_LOWBIT = Workload(
     notes="forward, dX and dLUT at 2- and 3-bit indices (m = 8192)",
 )
 
+LLAMA2_7B_FINETUNE_GPR1 = Workload(
+    name="llama2-7b-finetune-gpr1",
+    shapes=(Shape("q", 4096, 4096), Shape("gate", 11008, 4096)),
+    bits=(4,), gpr=1, lut_dtype="f16", lut_sigma=0.02, x_dtype="bf16",
+    tokens=(8192,), backward=True, dy_sigma=1e-2,
+    notes="dX and dLUT at one group per row (the 7B setting of the decode comparison): 32 and 86 row "
+          "blocks, so the table gradient is split over token ranges",
+)
+
 ALL: List[Workload] = [TINY, LLAMA2_7B_ATTN, LLAMA2_7B_MLP_LOWBIT, LLAMA3_70B_MLP, LLAMA2_7B_FINETUNE,
-                       LLAMA2_13B_DECODE, LLAMA2_7B_FINETUNE_LOWBIT]
+                       LLAMA2_13B_DECODE, LLAMA2_7B_FINETUNE_LOWBIT, LLAMA2_7B_FINETUNE_GPR1]
 BY_NAME = {w.name: w for w in ALL}
 
 
