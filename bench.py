@@ -484,12 +484,13 @@ def bench_bwd_gpr1(torch, skm, steps, warmup):
                                                                    dlut_out=dL, workspace=wb), steps, warmup) / steps
         f = wl.flops_pass(s_.n, s_.d, m)
         rb = (s_.n + 127) // 128
-        # the workspace holds the row exponents of dY (bf16 with f16 tables), then one partial table per range
+        # the workspace holds the row exponents of dY (bf16 with f16 tables), then one partial table per
+        # (column range, token range) of the split
         rexp_bytes = -(-m * 4 // 256) * 256
         ranges = (wb.numel() - rexp_bytes) // (s_.n * 16 * 4)
         out[f"{s_.name}_{s_.n}x{s_.d}_gpr1"] = {
             "dx_ms": t_dx, "dlut_ms": t_dl, "dx_TFLOPs": f / (t_dx * 1e-3) / 1e12,
-            "dlut_TFLOPs": f / (t_dl * 1e-3) / 1e12, "dlut_row_blocks": rb, "dlut_token_ranges": int(ranges),
+            "dlut_TFLOPs": f / (t_dl * 1e-3) / 1e12, "dlut_row_blocks": rb, "dlut_partial_tables": int(ranges),
             "dlut_blocks": int(rb * ranges)}
         if s_.name == "q":
             gdx, _ = skm.sketch_matmul_bwd(dY, X, idx, lut, 4, 1, dlut_out=dL, workspace=wb)

@@ -155,9 +155,9 @@ int sketch_matmul_fwd_multi(const void* X, int x_dtype,
  * any other buffer (may be NULL when that is 0). It holds, during the call
  * only: with (BF16, F16), the row exponents of dY; and, when the table
  * gradient's grid of (128-row block, group) pairs has fewer than 256 blocks
- * (e.g. 4096 rows in one group), one partial dLUT per range of tokens the
- * gradient is split into, added in range order at the end (deterministic; no
- * atomics).
+ * (e.g. 4096 rows in one group), one partial dLUT per (column range, token
+ * range) the gradient is split into, at most 6 MiB in all, added in range
+ * order at the end (deterministic; no atomics).
  * Gradients are sums over the columns that share an entry (chain rule of the
  * corrected Eq. (6)), not averages. With m == 0 and accumulate == 0 the
  * requested gradients are written as zeros.
@@ -179,9 +179,9 @@ int sketch_matmul_bwd(const void* dY, const void* X, int io_dtype,
  * library-owned scratch array of 8 MiB per GPU (a static device array, held
  * until the process ends; its address is looked up once per device on the
  * first call). Sizes whose sketch_matmul_bwd_workspace(...) exceeds 8 MiB
- * return SKM_EWORKSPACE (the need is 4 bytes per token with (BF16, F16) plus
- * at most 4 MiB of split table-gradient partials, so up to about a million
- * tokens). Allocates nothing. Calls that overlap in time on one GPU (several
+ * return SKM_EWORKSPACE (the need is 4 bytes per token with (BF16, F16),
+ * rounded up to 256, plus at most 6 MiB of split table-gradient partials, so
+ * every call with up to 524288 tokens fits). Allocates nothing. Calls that overlap in time on one GPU (several
  * host threads, or streams running concurrently) share that GPU's array and
  * race; serialise them. Nothing from an earlier call is read back (every
  * scratch entry a call reads was written by that call).

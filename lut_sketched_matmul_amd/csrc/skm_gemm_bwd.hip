@@ -39,10 +39,11 @@
 // tiles from global memory into a three-stage LDS ring with global_load_lds
 // instead of staging them through registers.
 // When the (row block, group) grid alone has fewer blocks than the GPU has
-// CUs (e.g. 4096 rows in one group: 32 blocks), the tokens are split into
-// ranges: each block then sums one range and stores its bins into a partial
-// table of the caller's workspace, and k_dlut_reduce adds the partial tables
-// in range order (deterministic, still no atomics).
+// CUs (e.g. 4096 rows in one group: 32 blocks), the group's columns are split
+// into ranges of whole 512-column chunks and, if that is not enough, the
+// tokens into ranges: each block then bins one (column range, token range)
+// into a partial table of the caller's workspace, and k_dlut_reduce adds the
+// partial tables in range order (deterministic, still no atomics).
 #include "skm_gemm_common.h"
 #include "skm_launch.h"
 
@@ -899,8 +900,8 @@ struct DlStage {
 template <int B, typename TX, bool VEC>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, int64_t m,
-            int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate, int splits,
-            int64_t split_tokens, int64_t part_stride) {
+            int64_t n, int64_t d, int gpr, float* __restrict__ dLUT, int accumulate, int tsplits, int csplits,
+            int64_t split_tokens, int64_t split_cols, int64_t part_stride) {
   typedef mfma32<TX> MF;
   extern __shared__ uint32_t smem[];
   (void)smem;
@@ -908,13 +909,15 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int t = threadIdx.x;
   const uint32_t lane = (uint32_t)(t & 63);
   const int wave = t >> 6;
-  // token range (varying slowest, so an XCD's co-resident blocks share it),
-  // then the gpr groups of one row block (same dY strip) share an XCD's L2
+  // split (column range, token range; varying slowest, so an XCD's
+  // co-resident blocks share it), then the gpr groups of one row block (same
+  // dY strip) share an XCD's L2
   const uint32_t lba = xcd_block(blockIdx.x, gridDim.x);
-  const uint32_t nb0 = gridDim.x / (uint32_t)splits;
+  const uint32_t nb0 = gridDim.x / (uint32_t)(tsplits * csplits);
   const uint32_t sp = lba / nb0, lb = lba % nb0;
+  const uint32_t cr = sp / (uint32_t)tsplits;  // column range of the group
   {
-    const int64_t tok0 = (int64_t)sp * split_tokens;
+    const int64_t tok0 = (int64_t)(sp % (uint32_t)tsplits) * split_tokens;
     dY += tok0 * n;
     X += tok0 * d;
     m = m - tok0 < split_tokens ? m - tok0 : split_tokens;
@@ -923,8 +926,9 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const int64_t i0 = (int64_t)(lb / (uint32_t)gpr) * DL_BM;
   const int g = (int)(lb % (uint32_t)gpr);
   const int64_t G = d / gpr;
-  const int64_t jg0 = (int64_t)g * G;  // first column of the group
-  const int64_t jend = jg0 + G;
+  // this block's columns of the group: column range cr (whole chunks)
+  const int64_t jg0 = (int64_t)g * G + (int64_t)cr * split_cols;
+  const int64_t jend = (int64_t)g * G + G < jg0 + split_cols ? (int64_t)g * G + G : jg0 + split_cols;
   const int KS = (int)((m + DL_BK - 1) / DL_BK);
 
   for (uint32_t q = (uint32_t)t; q < 4u * DL_BCOPY / 4u; q += 512u) st_w(DL_BINS + q * 4u, 0u);
@@ -942,7 +946,7 @@ k_gemm_dlut(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* 
   const TX* yfast = dY + (int64_t)ytok * n + yrow;
   auto load_step = [&](DlStage& S, int k, int64_t j0) {
     const int64_t t0 = (int64_t)k * DL_BK;
-    // (columns past the group but inside the row are read too: binning leaves them out)
+    // (columns past the block's range but inside the row are read too: binning leaves them out)
     if (rows_full && j0 + DL_BN <= d && t0 + DL_BK <= m) {  // wave-uniform
       S.y = *reinterpret_cast<const u32x4*>(yfast + t0 * n);
       const TX* xb = X + t0 * d + j0 + 8 * (t & 63);
@@ -1115,7 +1119,7 @@ template <int B, typename TX>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed,
                 int64_t m, int64_t n, int64_t d, int gpr, int gband, float* __restrict__ dLUT, int accumulate,
-                int splits, int64_t split_tokens, int64_t part_stride) {
+                int tsplits, int csplits, int64_t split_tokens, int64_t split_cols, int64_t part_stride) {
   typedef mfma32<TX> MF;
   extern __shared__ uint32_t smem[];  // dynamic LDS only: starts at address 0
   (void)smem;
@@ -1124,14 +1128,15 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
   const uint32_t lane = (uint32_t)(t & 63);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // Consecutive logical blocks (one XCD's share, see xcd_block) take one
-  // token range (varying slowest) and in it `gband` groups of consecutive row
+  // split (varying slowest) and in it `gband` groups of consecutive row
   // blocks: an XCD's co-resident blocks then share dY strips (same row block)
   // and X slabs (same group) in its L2.
   const uint32_t lba = xcd_block(blockIdx.x, gridDim.x);
-  const uint32_t nb0 = gridDim.x / (uint32_t)splits;
+  const uint32_t nb0 = gridDim.x / (uint32_t)(tsplits * csplits);
   const uint32_t sp = lba / nb0, lb = lba % nb0;
+  const uint32_t cr = sp / (uint32_t)tsplits;  // column range of the group
   {
-    const int64_t tok0 = (int64_t)sp * split_tokens;
+    const int64_t tok0 = (int64_t)(sp % (uint32_t)tsplits) * split_tokens;
     dY += tok0 * n;
     X += tok0 * d;
     m = m - tok0 < split_tokens ? m - tok0 : split_tokens;
@@ -1142,8 +1147,9 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
   const int64_t i0 = (int64_t)(rest % rblocks) * DL_BM;
   const int g = (int)((rest / rblocks) * (uint32_t)gband + gi);
   const int64_t G = d / gpr;
-  const int64_t jg0 = (int64_t)g * G;
-  const int64_t jend = jg0 + G;
+  // this block's columns of the group: column range cr (whole chunks)
+  const int64_t jg0 = (int64_t)g * G + (int64_t)cr * split_cols;
+  const int64_t jend = (int64_t)g * G + G < jg0 + split_cols ? (int64_t)g * G + G : jg0 + split_cols;
   const int KS = (int)(m / DL_BK);
 
   for (uint32_t q = (uint32_t)t; q < 4u * DD_BCOPY / 4u; q += 512u) st_w(DD_BINS + q * 4u, 0u);
@@ -1302,21 +1308,55 @@ hipError_t dx_t(const TX* dY, const uint8_t* idx, const TL* lut, const Problem& 
   }
 }
 
-// Token ranges of the table gradient (see the header of this file): split
-// when the (row block, group) grid has fewer than 256 blocks, into ranges of
-// at least 4 steps of 32 tokens, none of them empty.
+// Splits of the table gradient (see the header of this file) when the (row
+// block, group) grid has fewer than 256 blocks: first into column ranges of
+// whole 512-column chunks of the group (each block still sums every token, so
+// the binning is not repeated per token), then, when the chunks alone cannot
+// fill the CUs, into token ranges of at least 4 steps of 32 tokens. Each
+// count is the one that minimises rounds of 256 blocks times the chunks (or
+// steps) per block, the fewer ranges on a tie, with the partial tables
+// (parts * n * gpr * 2^b floats) within DLUT_PART_MAX bytes. No range is empty.
+constexpr size_t DLUT_PART_MAX = size_t(6) << 20;
 struct DlutSplit {
-  int splits;
+  int tsplits, csplits;
   int64_t tokens;  // tokens per range (a multiple of 32)
+  int64_t cols;    // columns per range (a multiple of 512, or the whole group)
+  int parts() const { return tsplits * csplits; }
 };
+// the count in [1, most] minimising ceil(blocks * c / 256) * ceil(units / c)
+inline int64_t best_split(int64_t blocks, int64_t units, int64_t most) {
+  int64_t best = 1, cost = ((blocks + 255) / 256) * units;
+  for (int64_t c = 2; c <= most; ++c) {
+    const int64_t k = ((blocks * c + 255) / 256) * ((units + c - 1) / c);
+    if (k < cost) {
+      cost = k;
+      best = c;
+    }
+  }
+  return best;
+}
 DlutSplit dlut_split_of(const Problem& p) {
   const int64_t nb0 = (p.n + DL_BM - 1) / DL_BM * p.gpr;
   const int64_t steps = (p.m + DL_BK - 1) / DL_BK;
-  int64_t sp = nb0 >= 256 ? 1 : (256 + nb0 - 1) / nb0;
-  if (sp > steps / 4) sp = steps / 4;
-  if (sp <= 1) return {1, steps * DL_BK};
-  const int64_t per = (steps + sp - 1) / sp;
-  return {(int)((steps + per - 1) / per), per * DL_BK};
+  const int64_t G = p.group_cols();
+  if (nb0 >= 256) return {1, 1, steps * DL_BK, G};
+  const int64_t want = (256 + nb0 - 1) / nb0;  // ranges that fill the CUs once
+  const int64_t nch = (G + DL_BN - 1) / DL_BN;
+  const int64_t cap = (int64_t)(DLUT_PART_MAX / ((size_t)(p.n * p.gpr * p.k()) * 4));  // most partial tables
+  if (cap < 2) return {1, 1, steps * DL_BK, G};
+  int64_t most = nch < 4 * want ? nch : 4 * want;
+  int64_t cs = best_split(nb0, nch, most < cap ? most : cap);
+  const int64_t per_c = (nch + cs - 1) / cs;
+  cs = (nch + per_c - 1) / per_c;
+  int64_t ts = 1, per_t = steps;
+  if (nb0 * cs < 256 && steps / 4 > 1 && cap / cs > 1) {
+    const int64_t tw = (256 + nb0 * cs - 1) / (nb0 * cs);
+    most = steps / 4 < 4 * tw ? steps / 4 : 4 * tw;
+    ts = best_split(nb0 * cs, steps, most < cap / cs ? most : cap / cs);
+    per_t = (steps + ts - 1) / ts;
+    ts = (steps + per_t - 1) / per_t;
+  }
+  return {(int)ts, (int)cs, per_t * DL_BK, cs > 1 ? per_c * DL_BN : G};
 }
 
 // dLUT = (accumulate ? dLUT : 0) + sum over the ranges of the partial tables,
@@ -1348,10 +1388,12 @@ hipError_t dlut_launch(const TX* dY, const TX* X, const uint8_t* idx, const Prob
   const int64_t rb = (p.n + DL_BM - 1) / DL_BM;
   const DlutSplit sp = dlut_split_of(p);
   const int64_t count = p.n * p.gpr * p.k();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.splits)), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n, p.d,
-                     p.gpr, sp.splits > 1 ? part : dLUT, sp.splits > 1 ? 0 : accumulate, sp.splits, sp.tokens, count);
+  const bool split = sp.parts() > 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.parts())), dim3(512), DL_LDS, s, dY, X, idx, p.m, p.n,
+                     p.d, p.gpr, split ? part : dLUT, split ? 0 : accumulate, sp.tsplits, sp.csplits, sp.tokens,
+                     sp.cols, count);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && sp.splits > 1) e = dlut_reduce(part, sp.splits, count, dLUT, accumulate, s);
+  if (e == hipSuccess && split) e = dlut_reduce(part, sp.parts(), count, dLUT, accumulate, s);
   return e;
 }
 
@@ -1366,11 +1408,12 @@ hipError_t dlut_dma_launch(const TX* dY, const TX* X, const uint8_t* idx, const 
   const int gband = p.gpr % 4 == 0 ? 4 : (p.gpr % 2 == 0 ? 2 : 1);
   const DlutSplit sp = dlut_split_of(p);
   const int64_t count = p.n * p.gpr * p.k();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.splits)), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n, p.d,
-                     p.gpr, gband, sp.splits > 1 ? part : dLUT, sp.splits > 1 ? 0 : accumulate, sp.splits, sp.tokens,
-                     count);
+  const bool split = sp.parts() > 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rb * p.gpr * sp.parts())), dim3(512), DD_LDS, s, dY, X, idx, p.m, p.n,
+                     p.d, p.gpr, gband, split ? part : dLUT, split ? 0 : accumulate, sp.tsplits, sp.csplits,
+                     sp.tokens, sp.cols, count);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && sp.splits > 1) e = dlut_reduce(part, sp.splits, count, dLUT, accumulate, s);
+  if (e == hipSuccess && split) e = dlut_reduce(part, sp.parts(), count, dLUT, accumulate, s);
   return e;
 }
 
@@ -1400,7 +1443,7 @@ bool gemm_bwd_supported(const Problem& p) { return p.d <= (int64_t(1) << 20); }
 
 size_t dlut_partial_bytes(const Problem& p) {
   const DlutSplit sp = dlut_split_of(p);
-  return sp.splits > 1 ? (size_t)sp.splits * (size_t)(p.n * p.gpr * p.k()) * 4 : 0;
+  return sp.parts() > 1 ? (size_t)sp.parts() * (size_t)(p.n * p.gpr * p.k()) * 4 : 0;
 }
 
 hipError_t launch_gemm_dx(const void* dY, int io_dtype, const uint8_t* idx, const void* lut, int lut_dtype,

@@ -123,7 +123,7 @@ LLAMA2_7B_FINETUNE_GPR1 = Workload(
     bits=(4,), gpr=1, lut_dtype="f16", lut_sigma=0.02, x_dtype="bf16",
     tokens=(8192,), backward=True, dy_sigma=1e-2,
     notes="dX and dLUT at one group per row (the 7B setting of the decode comparison): 32 and 86 row "
-          "blocks, so the table gradient is split over token ranges",
+          "blocks, so the table gradient is split over column ranges of the group",
 )
 
 ALL: List[Workload] = [TINY, LLAMA2_7B_ATTN, LLAMA2_7B_MLP_LOWBIT, LLAMA3_70B_MLP, LLAMA2_7B_FINETUNE,

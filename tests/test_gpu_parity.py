@@ -429,7 +429,9 @@ def test_bwd_accumulate_and_deterministic(m):
 @pytest.mark.parametrize("wname,b", [(wl.LLAMA2_7B_FINETUNE.name, 4), (wl.LLAMA2_7B_FINETUNE_LOWBIT.name, 2),
                                      (wl.LLAMA2_7B_FINETUNE_LOWBIT.name, 3)])
 def test_finetune_workload_sampled(wname, b):
-    """The 7B decoder layer's projections at full size (m = 8192): sampled outputs."""
+    """The 7B decoder layer at full size (m = 8192), forward + dX + dLUT on sampled outputs: the q, gate
+    and down projections at b = 4 (k, v and o have q's shape and up has gate's, so they run the same kernel
+    instances on the same grids) and gate and down at b = 2 and 3."""
     w = wl.BY_NAME[wname]
     r = np.random.default_rng(11 + b)
     shapes = (w.shapes[0], w.shapes[4], w.shapes[6]) if b == 4 else w.shapes   # q, gate, down
@@ -585,17 +587,18 @@ def test_fwd_multi_scales_bf16_f16(sets, d):
 
 
 # ---------------------------------------------------------------------------
-# table gradient split over token ranges (small (row block, group) grids)
+# table gradient split over column and token ranges (small (row block, group) grids)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
 @pytest.mark.parametrize("b,gpr,n,d,m", [
-    (4, 1, 256, 512, 640),     # 2 row blocks in one group: split, whole 32-token steps (DMA kernel)
-    (2, 1, 130, 1024, 1000),   # ragged rows and a ragged last token range (register-staged kernel)
+    (4, 1, 256, 512, 640),     # 2 row blocks in one group: token ranges, whole 32-token steps (DMA kernel)
+    (2, 1, 130, 1024, 1000),   # 2 column and 8 token ranges, ragged rows, ragged last token range (register-staged)
     (3, 2, 64, 1536, 4096),    # 2 blocks, 3-bit
     (4, 1, 96, 256, 200),      # too few tokens to split (fewer than 8 steps)
+    (3, 1, 8100, 2560, 256),   # 64 row blocks, ragged rows: column ranges of 2, 2 and 1 chunks
 ])
-def test_dlut_split_tokens(io, b, gpr, n, d, m):
+def test_dlut_split(io, b, gpr, n, d, m):
     idx, lut, X, dY = make_case(f"dlsplit/{io}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m, io, io)
     gdx, gdl = _bwd16(idx, lut, X, dY, b, gpr, d, io, io)
     L64, X64, dY64 = syn.to_float64(lut, io), syn.to_float64(X, io), syn.to_float64(dY, io)
@@ -610,7 +613,7 @@ def test_dlut_split_tokens(io, b, gpr, n, d, m):
 
 
 def test_dlut_split_bins_exact():
-    """Integer dY, one-hot X, split over token ranges: every bin sum is the exact integer."""
+    """Integer dY, one-hot X, split over 4 column and 8 token ranges: every bin sum is the exact integer."""
     b, gpr, n, d, m = 4, 1, 256, 2048, 1024
     idx, lut, _, _ = make_case("dlsplitbins", n, d, b, gpr, 1, "bf16", "bf16")
     cols = np.random.default_rng(77).choice(d, m, replace=True)
@@ -623,12 +626,12 @@ def test_dlut_split_bins_exact():
 
 
 def test_dlut_split_7b_gpr1_sampled():
-    """4096 x 4096 at one group per row (32 row blocks) and 8192 tokens: the gradient split over token
-    ranges, checked on sampled rows against the oracle."""
+    """4096 x 4096 at one group per row (32 row blocks) and 8192 tokens: the gradient split over 8 column
+    ranges of 512 columns, checked on sampled rows against the oracle."""
     b, gpr, n, d, m = 4, 1, 4096, 4096, 8192
     idx, lut, X, dY = make_case("dlsplit7b", n, d, b, gpr, m, "bf16", "f16", dy_sigma=1e-2)
     ws = skm().sketch_matmul_bwd_workspace(m, n, d, b, gpr, skm().SKM_BF16, skm().SKM_F16)
-    assert ws >= 8 * n * 16 * 4     # the partial tables of the token ranges
+    assert ws >= 8 * n * 16 * 4     # the partial tables of the column ranges
     _, dL = skm().sketch_matmul_bwd(to_dev(dY, "bf16"), to_dev(X, "bf16"), to_dev(idx, "u8"), to_dev(lut, "f16"),
                                     b, gpr, need_dx=False)
     dL = to_f64(dL)
