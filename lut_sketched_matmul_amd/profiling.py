@@ -30,11 +30,11 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {
     "decode": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
                "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
-               "lut_sketched_matmul_amd/csrc/skm_decode.hip"],
+               "lut_sketched_matmul_amd/csrc/skm_decode.hip", "lut_sketched_matmul_amd/csrc/skm_rowscale.hip"],
     "gemm": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
              "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
              "lut_sketched_matmul_amd/csrc/skm_gemm_common.h", "lut_sketched_matmul_amd/csrc/skm_gemm.hip",
-             "lut_sketched_matmul_amd/csrc/skm_gemm_bwd.hip"],
+             "lut_sketched_matmul_amd/csrc/skm_gemm_bwd.hip", "lut_sketched_matmul_amd/csrc/skm_rowscale.hip"],
     "optim": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
               "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
               "lut_sketched_matmul_amd/csrc/skm_optim.hip"],
@@ -143,7 +143,8 @@ XCDS, CUS_PER_XCD, SIMDS_PER_CU = 8, 32, 4
 MFMA16_PEAK_TFLOPS = 2500.0
 
 
-def summarize(stats_dir, pmc_dirs, kernel_regex, family, title, commands, copy_bytes, algorithmic_bytes=None):
+def summarize(stats_dir, pmc_dirs, kernel_regex, family, title, commands, copy_bytes, algorithmic_bytes=None,
+              grid_bytes=None):
     st = trace_stats(_one(os.path.join(stats_dir, "**", "*kernel_trace.csv")))
     counters = {}
     for d in pmc_dirs:
@@ -206,10 +207,13 @@ def summarize(stats_dir, pmc_dirs, kernel_regex, family, title, commands, copy_b
             e["mfma_busy_frac"] = round(e["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 4)
         summary["kernels"][label(k)] = e
         parts = []
+        algo = (grid_bytes or {}).get(k[1], algorithmic_bytes)
+        if algo and grid_bytes and k[1] in grid_bytes:
+            e["algorithmic_bytes"] = algo
         if "hbm_bytes" in e:
             parts.append(f"HBM bytes/launch {e['hbm_bytes']} ({e['hbm_GBps']} GB/s over the mean duration)")
-            if algorithmic_bytes:
-                parts.append(f"algorithmic {algorithmic_bytes} (ratio {e['hbm_bytes'] / algorithmic_bytes:.3f})")
+            if algo:
+                parts.append(f"algorithmic {algo} (ratio {e['hbm_bytes'] / algo:.3f})")
         if "mfma_TFLOPs" in e:
             parts.append(f"MFMA flops {e['mfma_flops']:.4g} -> {e['mfma_TFLOPs']} TFLOP/s "
                          f"({100 * e['mfma_frac_of_peak']:.1f}% of 2.5 PFLOP/s)")
@@ -259,15 +263,18 @@ def main():
     ap.add_argument("--command", action="append", default=[], help="command line to record (repeatable)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--algorithmic-bytes", type=int, default=None)
+    ap.add_argument("--grid-bytes", action="append", default=[],
+                    help="BLOCKS=BYTES: algorithmic bytes of the launches with that grid (repeatable)")
     ap.add_argument("--merge-grids", default=None, help="regex: report these kernels' launches together")
     ap.add_argument("-o", "--out", required=True)
     a = ap.parse_args()
     global MERGE_GRIDS
     MERGE_GRIDS = a.merge_grids
-    text = summarize(a.stats, a.pmc, a.kernels, a.family, a.title, a.command, a.copy_bytes, a.algorithmic_bytes)
+    grid_bytes = {int(g.split("=")[0]): int(g.split("=")[1]) for g in a.grid_bytes}
+    text = summarize(a.stats, a.pmc, a.kernels, a.family, a.title, a.command, a.copy_bytes, a.algorithmic_bytes,
+                     grid_bytes)
     with open(a.out, "w") as f:
         f.write(text)
-    print(text)
 
 
 if __name__ == "__main__":
