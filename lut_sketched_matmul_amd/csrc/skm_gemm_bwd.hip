@@ -1185,38 +1185,34 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
   for (int b = 0; b < 4; ++b) fb[b] = DD_TA + frow * 1024u + (((16u * wn + 4u * b + fin) ^ fx) << 4) + fw;
 
   f32x16 acc[2][4];
-  auto mfma_step = [&](uint32_t stage) {
-    u32x4 af[2][2], bf[2][4];
+  // one half step (16 tokens) of fragments: 12 transposing reads
+  auto read_half = [&](uint32_t stage, int ks, u32x4 (&af)[2], u32x4 (&bf)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const uint32_t p = stage + fa[a] + 16u * 256u * ks;
-        const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 256u);
-        af[ks][a] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t p = stage + fb[b] + 16u * 1024u * ks;
-        const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 1024u);
-        bf[ks][b] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t p = stage + fa[a] + 16u * 256u * (uint32_t)ks;
+      const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 256u);
+      af[a] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t p = stage + fb[b] + 16u * 1024u * (uint32_t)ks;
+      const u32x2 lo = ld_tr(p), hi = ld_tr(p + 4u * 1024u);
+      bf[b] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+  auto mfma_half = [&](const u32x4 (&af)[2], const u32x4 (&bf)[4]) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = MF::run(af[ks][a], bf[ks][b], acc[a][b]);
-    // the first half's 12 reads, then its 8 MFMAs interleaved with the second
-    // half's reads, then the second half's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      for (int b = 0; b < 4; ++b) acc[a][b] = MF::run(af[a], bf[b], acc[a][b]);
+  };
+  // a half step's 8 MFMAs interleaved with the other half's 12 reads
+  auto interleave = [&]() {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -1239,16 +1235,32 @@ k_gemm_dlut_dma(const TX* __restrict__ dY, const TX* __restrict__ X, const uint8
       dd_wait_vmcnt<0>();
     }
     dd_barrier();
+    // Pipelined across the step barrier: step k's second half of reads runs
+    // beside its first half of MFMAs; then every read of stage k has landed
+    // (lgkmcnt 0) and this wave's copy of step k+1 (vmcnt), the barrier, and
+    // step k+1's first half of reads runs beside step k's second half of
+    // MFMAs, so the matrix core has work while the waves meet.
+    u32x4 a0[2], b0[4], a1[2], b1[4];
     uint32_t st = 0u;  // stage of step k
+    read_half(st, 0, a0, b0);
     for (int k = 0; k < KS; ++k) {
       const uint32_t st2 = st >= DD_STAGE ? st - DD_STAGE : st + 2u * DD_STAGE;  // stage of step k+2
+      // (stage k+2 = stage k-1: every wave finished reading it before the last barrier)
       if (k + 2 < KS) dma(k + 2, st2);
-      mfma_step(st);
+      read_half(st, 1, a1, b1);
+      mfma_half(a0, b0);
+      interleave();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every read of stage k has landed
       // this wave's DMA of step k+1 has landed (the one of step k+2 may not)
       if (k + 2 < KS) dd_wait_vmcnt<5>();
       else dd_wait_vmcnt<0>();
       dd_barrier();
       st = st + DD_STAGE == 3u * DD_STAGE ? 0u : st + DD_STAGE;
+      // (unconditional, so that the reads interleave with the MFMAs: after
+      // the last step they read a stale stage and the values go unused)
+      read_half(st, 0, a0, b0);
+      mfma_half(a1, b1);
+      interleave();
     }
     dd_wait_vmcnt<0>();  // (no copy is in flight here; the compiler does not count them)
 
