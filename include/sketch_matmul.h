@@ -258,6 +258,26 @@ int sketch_map(float* W, const float* U, const void* lut, int lut_dtype,
                hipStream_t stream);
 
 /*
+ * The factor U that sketch_column_weights and sketch_map take, from the Gram
+ * matrix of the sample inputs (the mapping's error update of Frantar et al.
+ * needs the upper Cholesky factor of the inverse Hessian):
+ *   U upper triangular with U^T U = (H + damp * mean(diag H) * I)^-1.
+ * H: [d][d] float64, row-major, symmetric (H = X_s^T X_s; only entries with
+ * i <= j are read). damp >= 0 (1 % is the usual choice). U: [d][d] fp32,
+ * written in full (zeros below the diagonal). Computed in float64: with P the
+ * exchange matrix and P H P = L L^T, U = P L^-1 P (one blocked Cholesky
+ * factorization and one triangular inverse). workspace:
+ * sketch_hessian_factor_workspace(d) bytes (16-byte aligned; 8 (D^2 + D * 64
+ * + 32) bytes with D = d rounded up to a multiple of 64). 1 <= d <= 65536.
+ * A matrix that is not positive definite after the damping gives NaN entries
+ * in U (the factorization runs on the device; nothing is read back).
+ */
+size_t sketch_hessian_factor_workspace(int64_t d);
+
+int sketch_hessian_factor(const double* H, int64_t d, double damp, float* U,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Fused optimizer steps for the trainable tables (SpaLLM section 2.3: only the
  * table values are fine-tuned; the mapping stays frozen). The pages give the
  * learning rates searched (SpaLLM appendix B.1, Table 7) but no optimizer;

@@ -13,11 +13,13 @@ from ._lib import (  # noqa: F401
     lib,
     sketch_column_weights,
     sketch_dequant,
+    sketch_hessian_factor,
     sketch_lloyd,
     sketch_lut_adam_step,
     sketch_lut_sgd_step,
     sketch_map,
     sketch_matmul_bwd,
+    sketch_matmul_bwd_noalloc,
     sketch_matmul_bwd_workspace,
     sketch_matmul_fwd,
     sketch_matmul_fwd_workspace,

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "sketch_map_workspace": (_c_size, [_c_i64]),
     "sketch_map": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_size,
                             _c_vp]),
+    "sketch_hessian_factor_workspace": (_c_size, [_c_i64]),
+    "sketch_hessian_factor": (_c_int, [_c_vp, _c_i64, ctypes.c_double, _c_vp, _c_vp, _c_size, _c_vp]),
     "sketch_status_str": (ctypes.c_char_p, [_c_int]),
     "sketch_version": (_c_int, []),
 }
@@ -441,4 +443,25 @@ def sketch_map(W_work, U, lut, b: int, gpr: int, out=None, workspace=None, strea
                           out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_ptr(stream))
     _check("sketch_map", st)
+    return out
+
+
+def sketch_hessian_factor(H, damp: float = 0.01, out=None, workspace=None, stream=None):
+    """U [d, d] fp32, upper triangular, with U^T U = (H + damp * mean(diag H) * I)^-1, from the float64 Gram
+    matrix H [d, d] of the sample inputs (only its entries with i <= j are read)."""
+    torch = _torch()
+    d, d2 = _matrix(H, "H")
+    if d != d2:
+        raise ValueError(f"H must be square, got {tuple(H.shape)}")
+    _expect(H, "H", dtypes=("float64",))
+    _expect(out, "out", shape=(d, d), dtypes=("float32",))
+    _expect(workspace, "workspace", dtypes=("uint8",))
+    _require_device(H, out, workspace)
+    if out is None:
+        out = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    ws = _workspace(workspace, lib().sketch_hessian_factor_workspace(d), H.device)
+    st = lib().sketch_hessian_factor(H.data_ptr(), d, float(damp), out.data_ptr(),
+                                     ws.data_ptr() if ws is not None else None,
+                                     ws.numel() if ws is not None else 0, _stream_ptr(stream))
+    _check("sketch_hessian_factor", st)
     return out

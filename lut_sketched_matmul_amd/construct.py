@@ -9,10 +9,10 @@ its error over the later columns with the update of Frantar et al.
 
 H = X^T X of sample inputs X of the layer, plus a damping of ``damp`` times
 its mean diagonal (the pages do not say how H is kept invertible; 1 % is
-GPTQ's choice). The upper-triangular factor U (H^-1 = U^T U) is computed
-with torch.linalg on the GPU in float64 (library factorizations);
-the three sketching steps run in the HIP library: column weights, Lloyd, and
-the mapping sweep.
+GPTQ's choice). H is one plain float64 GEMM (the vendor BLAS through
+torch.matmul); the upper-triangular factor U (H^-1 = U^T U) and the three
+sketching steps run in the HIP library: the factor (blocked Cholesky and
+triangular inverse in float64), column weights, Lloyd, and the mapping sweep.
 """
 from __future__ import annotations
 
@@ -22,20 +22,9 @@ from . import _lib
 
 
 def hessian_factor(Xs, damp: float = 0.01):
-    """Upper-triangular U (fp32, [d, d]) with U^T U = (X^T X + damp * mean(diag) * I)^-1.
-
-    Without forming the inverse: with P the exchange matrix and P H P = L L^T (L lower triangular),
-    H^-1 = (P L^-T P)(P L^-1 P), and P L^-1 P is upper triangular with a positive diagonal, so it is
-    the factor. One Cholesky factorization and one triangular solve (half the time of inverting H
-    and factoring the inverse at d = 4096).
-    """
+    """Upper-triangular U (fp32, [d, d]) with U^T U = (X^T X + damp * mean(diag) * I)^-1."""
     X = Xs.to(torch.float64)
-    H = X.T @ X
-    H.diagonal().add_(damp * H.diagonal().mean())
-    L = torch.linalg.cholesky(H.flip(0, 1))
-    eye = torch.eye(H.shape[0], dtype=H.dtype, device=H.device)
-    U = torch.linalg.solve_triangular(L, eye, upper=False).flip(0, 1)
-    return U.to(torch.float32).contiguous()
+    return _lib.sketch_hessian_factor(X.T @ X, damp)
 
 
 def build_sketch(W, b: int, gpr: int, Xs=None, U=None, iters: int = 30, lut_dtype=torch.float16,

@@ -20,6 +20,7 @@ namespace {
 using skm::Problem;
 
 constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxFactorD = int64_t(1) << 16;  // sketch_hessian_factor: the tile grid stays below 2^31 blocks
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -308,6 +309,23 @@ int sketch_lloyd(const float* W, const float* h, int64_t n, int64_t d, int b, in
   if (overlap(o, {W, n * d * 4}) || overlap(o, {h, d * 4})) return SKM_EALIAS;
   const Problem p{0, n, d, b, gpr};
   return status_of(skm::launch_lloyd(W, h, p, iters, lut, lut_dtype, stream));
+}
+
+size_t sketch_hessian_factor_workspace(int64_t d) {
+  return d >= 1 && d <= kMaxFactorD ? skm::hessian_factor_workspace_bytes(d) : 0;
+}
+
+int sketch_hessian_factor(const double* H, int64_t d, double damp, float* U, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (d < 1 || d > kMaxFactorD) return SKM_EINVAL;
+  if (!(damp >= 0.0) || !std::isfinite(damp)) return SKM_EINVAL;
+  if (!H || !U || !workspace) return SKM_EINVAL;
+  if (!aligned16(H) || !aligned16(U) || !aligned16(workspace)) return SKM_EALIGN;
+  const size_t need = skm::hessian_factor_workspace_bytes(d);
+  if (workspace_bytes < need) return SKM_EWORKSPACE;
+  const Range h{H, d * d * 8}, u{U, d * d * 4}, w{workspace, (int64_t)need};
+  if (overlap(u, h) || overlap(w, h) || overlap(u, w)) return SKM_EALIAS;
+  return status_of(skm::launch_hessian_factor(H, d, damp, U, workspace, stream));
 }
 
 size_t sketch_map_workspace(int64_t n) { return n > 0 ? skm::map_workspace_bytes(n) : 0; }

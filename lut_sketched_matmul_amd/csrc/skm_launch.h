@@ -94,6 +94,10 @@ hipError_t launch_col_weights(const float* U, int64_t d, float* h, hipStream_t s
 hipError_t launch_lloyd(const float* W, const float* h, const Problem& p, int iters, void* lut, int lut_dtype,
                         hipStream_t s);
 size_t map_workspace_bytes(int64_t n);
+// the factor U of the damped inverse Hessian (skm_factor.hip); the workspace
+// holds hessian_factor_workspace_bytes(d)
+size_t hessian_factor_workspace_bytes(int64_t d);
+hipError_t launch_hessian_factor(const double* H, int64_t d, double damp, float* U, void* workspace, hipStream_t s);
 hipError_t launch_map(float* Wc, const float* U, const void* lut, int lut_dtype, const Problem& p, uint8_t* idx,
                       float* E, hipStream_t s);
 

@@ -169,6 +169,25 @@ def test_construction_rejects_bad_arguments(lib):
     assert mp(ldt=5) == EUNSUP
 
 
+def test_hessian_factor_rejects_bad_arguments(lib):
+    ws = lib.sketch_hessian_factor_workspace(100)
+    # D = 128: 8 (128^2 + 128 * 64 + 32) bytes
+    assert ws == 8 * (128 * 128 + 128 * 64 + 32)
+    assert lib.sketch_hessian_factor_workspace(0) == 0 and lib.sketch_hessian_factor_workspace(1 << 17) == 0
+    hf = lambda H=A, d=100, damp=0.01, U=B_, w=C, wsb=ws: lib.sketch_hessian_factor(H, d, damp, U, w, wsb, None)
+    assert hf(d=0) == EINVAL
+    assert hf(d=(1 << 16) + 1) == EINVAL
+    assert hf(damp=-0.1) == EINVAL
+    assert hf(damp=float("nan")) == EINVAL
+    assert hf(damp=float("inf")) == EINVAL
+    assert hf(H=0) == EINVAL
+    assert hf(w=0) == EINVAL
+    assert hf(wsb=ws - 1) == EWS
+    assert hf(U=B_ + 4) == EALIGN
+    assert hf(U=A + 8 * 100 * 100 - 16) == EALIAS       # U over the end of H
+    assert hf(w=B_ + 16) == EALIAS                      # workspace over U
+
+
 def test_dequant_and_unpack_reject(lib):
     assert lib.sketch_dequant(B_, C, 1, 64, 512, 7, 1, A, None) == EINVAL
     assert lib.sketch_dequant(B_, C, 9, 64, 512, 4, 1, A, None) == EUNSUP

@@ -54,6 +54,27 @@ def weights(tag, n, d):
     return syn.random_normal(f"{tag}/W", (n, d), 0.02, "f32")
 
 
+@pytest.mark.parametrize("d,s", [(1, 4), (5, 12), (63, 150), (64, 160), (65, 200), (200, 500), (1000, 2400)])
+@pytest.mark.parametrize("damp", [0.01, 0.0])
+def test_hessian_factor(d, s, damp):
+    """U from the float64 Gram matrix (blocked Cholesky and triangular inverse in 64-column steps, padded to a
+    multiple of 64) against the oracle's factor: float64 on both sides, so the fp32 result must equal the
+    rounding of the oracle's within a few fp32 units of its scale; U is upper triangular with exact zeros below."""
+    t = torch()
+    X = calib(f"factor/{d}", s, d)
+    H = to_dev(X.T @ X, "f64")
+    U = to_f64(skm().sketch_hessian_factor(H, damp))
+    want = oracle.hessian_factor(X, damp)
+    assert np.all(np.tril(U, -1) == 0.0)
+    assert float(np.max(np.abs(U - want))) <= 1e-6 * float(np.max(np.abs(want)))
+    # and UᵀU inverts the damped H
+    Hd = X.T @ X + damp * np.mean(np.diag(X.T @ X)) * np.eye(d)
+    assert float(np.max(np.abs(U.T @ U @ Hd - np.eye(d)))) <= 1e-4
+    # repeat calls are bit-identical (no atomics)
+    assert np.array_equal(to_f64(skm().sketch_hessian_factor(H, damp)), U)
+    del t
+
+
 @pytest.mark.parametrize("d", [1, 37, 256, 1024])
 def test_column_weights(d):
     U = factor32(f"cw/{d}", 2 * d + 8, d)
