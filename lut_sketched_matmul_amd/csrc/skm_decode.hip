@@ -33,6 +33,17 @@
 // block read adjacent pieces of each row. The NW partial 16x16 tiles are
 // summed in LDS in wave order (deterministic) and stored once.
 //
+// Activations. When m*d <= 32768 the block stages X in LDS once and reads its
+// fragments there. Otherwise they come from global memory with each slot:
+// below 8 tokens every lane loads its own fragment (64-byte runs of at most
+// m distinct rows). From 8 tokens on such a load spreads over 64 separate
+// 16-byte pieces of up to 16 rows, which the load unit handles piece by
+// piece, so each wave loads its slot's [16 tokens][256 bytes] with
+// neighbouring lanes on neighbouring pieces instead (four fully used 1 KB
+// loads), stores them in a private LDS buffer (rows padded by 16 bytes, so
+// the fragment reads hit distinct banks) and reads the four fragments back.
+// One wave's LDS operations complete in order, so no barrier is involved.
+//
 // bf16 activations with f16 tables take the per-row prescale of skm_common.h.
 // When the activations are staged in LDS, the block finds the exponents
 // itself. One table set: the activations are staged unscaled and every wave
@@ -63,6 +74,11 @@ constexpr int DEC_MAX_ENTRIES = 224;  // table entries per row kept in LDS (entr
 constexpr int DEC_LUT_CHUNKS = 2;     // 8-entry table chunks loaded per wave (16 * 2 * 8 >= 224)
 constexpr int64_t DEC_XL_MAX = 32768; // m * d elements staged in LDS (64 KB)
 constexpr int DEC_XL_CHUNKS = (int)(DEC_XL_MAX / 8 / (8 * 64));  // 16-byte chunks per thread (NW >= 8)
+// unstaged activations: every wave turns its slot's [16 tokens][16 pieces of
+// 16 bytes] around in a private LDS buffer, rows padded by one piece
+constexpr uint32_t DEC_XT_ROW = 17 * 16;
+constexpr uint32_t DEC_XT_WAVE = 16 * DEC_XT_ROW;
+constexpr int DEC_XT_MIN_M = 8;  // tokens from which unstaged single-set calls take the turn-around
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -240,6 +256,18 @@ __device__ __forceinline__ void tab_store(const TabRegs<B>& R, uint32_t* tabs, i
   }
 }
 
+// Sources of one wave's coalesced activation loads (unstaged, one table set):
+// load i of a slot brings token min(4i + l/16, m-1) (element offset off[i])
+// at columns 128 s + c8, c8 = 8 (l%16), clamped to dcol = d - 8 when the
+// row ends inside the slot.
+template <typename TX>
+struct XtSrc {
+  const TX* x = nullptr;
+  uint32_t off[4] = {0u, 0u, 0u, 0u};
+  uint32_t c8 = 0u;
+  uint32_t dcol = 0u;
+};
+
 template <int B, typename TX, int PF>
 struct SlotRegs {
   uint32_t w[PF][B];
@@ -256,10 +284,12 @@ struct SlotRegs {
 // token row >= m or a weight row >= n only feeds outputs that are never
 // stored, and a unit past the row end (RAGGED only) is zeroed by the caller.
 // g = u / UG is a multiply-high by the host's magic constant (exact for
-// u * UG < 2^32).
-template <int B, int NW, typename TX, bool RAGGED, bool XL, int PF>
+// u * UG < 2^32). XT: the activations arrive in load order (see XtSrc) and
+// are put into fragment order by the caller.
+template <int B, int NW, typename TX, bool RAGGED, bool XL, bool XT, int PF>
 __device__ __forceinline__ void load_batch(SlotRegs<B, TX, PF>& R, int64_t s0, int64_t S, uint32_t U,
-                                           uint32_t ug_magic, int q, const uint8_t* rowp, const TX* xrow) {
+                                           uint32_t ug_magic, int q, const uint8_t* rowp, const TX* xrow,
+                                           const XtSrc<TX>& xt) {
   constexpr int T = tab_entries<B>::value;
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
@@ -272,7 +302,12 @@ __device__ __forceinline__ void load_batch(SlotRegs<B, TX, PF>& R, int64_t s0, i
     }
     load_unit<B>(rowp, u, R.w[p]);
     R.u[p] = u;
-    if constexpr (!XL) {
+    if constexpr (XT) {
+      uint32_t col = 128u * (uint32_t)s + xt.c8;
+      if constexpr (RAGGED) col = col < xt.dcol ? col : xt.dcol;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.x[p][i] = *reinterpret_cast<const u32x4*>(xt.x + xt.off[i] + col);
+    } else if constexpr (!XL) {
       const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
 #pragma unroll
       for (int h = 0; h < 4; ++h) R.x[p][h] = xp[h];
@@ -312,7 +347,7 @@ __device__ __forceinline__ u32x4 lds_q16(uint32_t a) {
 // tables and one round of table lookups; the index stream is read from memory
 // once. A pass's tables, activations and first index batch are loaded during
 // the pass before it.
-template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool MULTI>
+template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool XT, bool MULTI>
 __global__ void __launch_bounds__(NW * 64)
 k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ lut,
          int m, int64_t n, int64_t d, int gpr, uint32_t ug_magic, uint32_t d_magic, TX* __restrict__ Y,
@@ -327,6 +362,9 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   typedef mfma16<TL> MF;
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   static_assert(!(SC && MULTI && !XL), "prescaled multi-set decode stages its activations");
+  // XT (one table set without staging, m >= 8): coalesced activation loads,
+  // turned into fragments through a per-wave LDS buffer
+  static_assert(!(XT && (XL || MULTI)), "the LDS turn-around serves unstaged single-set calls");
 
   const int lane = lane_id();
   // wave index as a scalar, so that the slot loop's branches are scalar
@@ -344,6 +382,17 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   const int64_t S = (U + 3) / 4;                 // slots per row
   const uint8_t* rowp = idx_packed + (row_ok ? grow : n - 1) * (d * B / 8);
   const TX* xrow = X + (int64_t)tokc * d;
+  XtSrc<TX> xts;
+  if constexpr (XT) {
+    xts.x = X;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + (lane >> 4);
+      xts.off[i] = (uint32_t)((t < m ? t : m - 1) * d);
+    }
+    xts.c8 = 8u * (uint32_t)(lane & 15);
+    xts.dcol = (uint32_t)d - 8u;
+  }
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const uint32_t xl_base = (uint32_t)gpr * T * 256u;  // byte offset of the staged activations
   // activation elements staged (MULTI + XL: one pass's tokens)
@@ -456,7 +505,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
 #pragma unroll
       for (int c = 0; c < XCH; ++c) xs[c] = *reinterpret_cast<const u32x4*>(stage_src(c, pstart, pcnt, xok[c]));
     }
-    load_batch<B, NW, TX, RAGGED, XL, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow);
+    load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow, xts);
   }
   while (true) {
   const bool has_next = MULTI && pass + 1 < npass;
@@ -475,7 +524,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   };
   if constexpr (XL && !MULTI) load_x();
   s0 = wave;
-  if constexpr (!MULTI) load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+  if constexpr (!MULTI) load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow, xts);
   tab_store<B, NW>(TR, smem, gpr, lane, wave);
   // SC + XL: the exponent of a staged row from the waves' slots (NW maxima)
   auto row_slots_exp = [&](uint32_t row) -> int {
@@ -619,6 +668,14 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // XT: this wave's buffer; a lane stores load i at row 4i + l/16, piece
+  // l%16, and reads step h of its fragment at row l%16 (its token), piece
+  // 4 (l/16) + h: columns 8h.. of unit 4s + q, as a direct load would give
+  const uint32_t xt_w = xl_base + (uint32_t)wave * DEC_XT_WAVE;
+  const uint32_t xt_st = xt_w + (uint32_t)(lane >> 4) * DEC_XT_ROW + (uint32_t)(lane & 15) * 16u;
+  const uint32_t xt_ld = xt_w + (uint32_t)(lane & 15) * DEC_XT_ROW + (uint32_t)(lane >> 4) * 64u;
+  (void)xt_st;
+  (void)xt_ld;
   // SC without staging: 2^-e of this lane's A row (its token)
   const float xsc = SC && !XL ? pow2f(-erow) : 1.0f;
   (void)xsc;
@@ -631,6 +688,17 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
       if (decltype(tail)::value && sb + (int64_t)p * NW >= S) break;  // wave-uniform
       const uint32_t gk = Rc.gk[p];
       const uint32_t gk4 = __builtin_amdgcn_perm(0u, gk, 0u);  // gk < 256 in all four bytes
+      // XT: the slot's activations through the wave's buffer (one wave's LDS
+      // accesses are carried out in order, so the next slot's stores cannot
+      // overtake these loads)
+      u32x4 xf[4];
+      if constexpr (XT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xt_st + (uint32_t)i * 4u * DEC_XT_ROW) = Rc.x[p][i];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) xf[h] = lds_q16<TL>(xt_ld + 16u * (uint32_t)h);
+      }
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         u32x4 wb = dequant_step<B>(Rc.w[p], h, gk4, gk, lane4);
@@ -641,8 +709,8 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
         }
         u32x4 xv;
         if constexpr (XL) xv = lds_q16<TL>(xl_row + (Rc.u[p] * 32u + 8u * h) * 2u);
-        else if constexpr (SC) xv = x_to_tc_scaled(Rc.x[p][h], xsc);
-        else xv = x_to_tc<TX, TL>(Rc.x[p][h]);
+        else if constexpr (SC) xv = x_to_tc_scaled(XT ? xf[h] : Rc.x[p][h], xsc);
+        else xv = x_to_tc<TX, TL>(XT ? xf[h] : Rc.x[p][h]);
         if constexpr (RAGGED) {
           if (!Rc.ok[p]) xv = u32x4{0u, 0u, 0u, 0u};
         }
@@ -664,14 +732,14 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     // on the next one's first load); the last one or two batches run after it.
     int64_t b = 0;
     for (; b + 2 < nb; b += 2) {
-      load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow);
+      load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow, xts);
       compute(R0, s0, btag<false>{});
-      load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0 + 2 * STEP, S, U, ug_magic, q, rowp, xrow);
+      load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R0, s0 + 2 * STEP, S, U, ug_magic, q, rowp, xrow, xts);
       compute(R1, s0 + STEP, btag<false>{});
       s0 += 2 * STEP;
     }
     if (nb - b == 2) {
-      load_batch<B, NW, TX, RAGGED, XL, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow);
+      load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R1, s0 + STEP, S, U, ug_magic, q, rowp, xrow, xts);
       compute(R0, s0, btag<false>{});
       compute(R1, s0 + STEP, btag<true>{});
     } else {
@@ -683,7 +751,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     for (int64_t b = 0; b + 1 < nb; ++b) {
       compute(R0, s0, btag<false>{});
       s0 += STEP;
-      load_batch<B, NW, TX, RAGGED, XL, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow);
+      load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R0, s0, S, U, ug_magic, q, rowp, xrow, xts);
     }
     compute(R0, s0, btag<true>{});
   }
@@ -704,7 +772,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     // test so that every path into the next pass has it in flight (after the
     // last pass it re-reads batch 0, unused); then every wave is done with
     // this pass's tables
-    load_batch<B, NW, TX, RAGGED, XL, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow);
+    load_batch<B, NW, TX, RAGGED, XL, XT, PF>(R0, (int64_t)wave, S, U, ug_magic, q, rowp, xrow, xts);
     if (!has_next) break;
     load_pass(++pass);
     __syncthreads();
@@ -714,10 +782,12 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // ---- sum the NW partial tiles in wave order, then store Y[token][row]
   // lane l holds D[token 4*(l/16)+r][row l%16]
   // (SC + XL: in the staged activations, once every wave is done with them)
+  // (XT: each wave's partials in its own buffer, which only it has used)
   if constexpr (SC && XL) __syncthreads();
   float* red = reinterpret_cast<float*>(smem) + (xl_base + (SC && XL ? 0u : xl_bytes)) / 4u;
+  constexpr int RS = XT ? (int)(DEC_XT_WAVE / 4) : 256;  // floats between the waves' partial tiles
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave * 256 + (4 * q + r) * 16 + j] = out[r];
+  for (int r = 0; r < 4; ++r) red[wave * RS + (4 * q + r) * 16 + j] = out[r];
   __syncthreads();
   const int t = threadIdx.x;
   if (t < 256) {
@@ -728,7 +798,7 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
     if (token < m && row0 + rr < n) {
       float sum = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < NW; ++wv) sum += red[wv * 256 + t];
+      for (int wv = 0; wv < NW; ++wv) sum += red[wv * RS + t];
       if constexpr (SC && !MULTI) sum *= u;
       Y[(int64_t)token * n + row0 + rr] = from_f32<TX>(sum);
     }
@@ -736,9 +806,11 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
 }
 
 template <int B, int NW>
-size_t decode_lds_bytes(int gpr, int64_t x_elems, bool mags) {
+size_t decode_lds_bytes(int gpr, int64_t x_elems, bool mags, bool xt) {
   // x_elems is rounded up to whole 16-byte chunks so the partials stay
-  // aligned; with the magnitude slots the partials overlay the activations
+  // aligned; with the magnitude slots the partials overlay the activations;
+  // the waves' transposition buffers (xt) hold their partials
+  if (xt) return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (size_t)NW * DEC_XT_WAVE;
   const size_t xb = (size_t)((x_elems + 7) / 8) * 16, pb = (size_t)NW * 256 * 4;
   return (size_t)gpr * tab_entries<B>::value * 64 * 4 + (mags ? (xb > pb ? xb : pb) + (size_t)17 * NW * 4 : xb + pb);
 }
@@ -751,13 +823,13 @@ struct SetArgs {
   const int32_t* rexp = nullptr;   // row exponents of X (prescaled pair without staging)
 };
 
-template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL>
+template <int B, int NW, typename TX, typename TL, bool RAGGED, bool XL, bool XT>
 hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const Problem& p, TX* Y, hipStream_t s,
                          uint32_t magic, const SetArgs& sa) {
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   // MULTI + XL stages one pass's tokens: at most min(m, DEC_XL_MAX / d) of them
   const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
-  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL);
+  const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL, XT);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
   // element e of the staged activations lies in row e / d = umulhi(e, ceil(2^32 / d)), exact for e * d < 2^32
   // (staged elements number at most 32768 and d <= 32768 when staging)
@@ -765,10 +837,10 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   // (the gathers address the tables with absolute LDS addresses, see gaddr:
   // checked once per kernel, which also raises its LDS limit to 160 KB)
   if (sa.lut_set) {
-    if constexpr (SC && !XL) {
+    if constexpr ((SC && !XL) || XT) {
       return hipErrorNotSupported;  // (the ABI routes no such call here)
     } else {
-      const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, true>;
+      const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false, true>;
       static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
       if (prep != hipSuccess) return prep;
       hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, d_magic, Y,
@@ -776,7 +848,7 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
       return hipGetLastError();
     }
   }
-  const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, false>;
+  const auto kern = k_decode<B, NW, TX, TL, RAGGED, XL, XT, false>;
   static const hipError_t prep = prepare_kernel((const void*)kern, 160 * 1024);
   if (prep != hipSuccess) return prep;
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, lut, (int)p.m, p.n, p.d, p.gpr, magic, d_magic, Y,
@@ -792,11 +864,17 @@ hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Probl
   // single set in use, the m rows then take several passes)
   const bool xl = decode_stages_activations(p, sa.lut_set != nullptr, sa.n_sets,
                                             scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t)));
+  // Unstaged, one set: from 8 tokens on, the coalesced loads and the LDS
+  // turn-around cost less than loading fragments directly (whose cost grows
+  // with the distinct token rows a load touches); below, the direct loads.
+  const bool xt = !xl && !sa.lut_set && p.m >= DEC_XT_MIN_M;
   if (p.units() % 4 != 0)
-    return xl ? decode_launch<B, NW, TX, TL, true, true>(X, idx, lut, p, Y, s, magic, sa)
-              : decode_launch<B, NW, TX, TL, true, false>(X, idx, lut, p, Y, s, magic, sa);
-  return xl ? decode_launch<B, NW, TX, TL, false, true>(X, idx, lut, p, Y, s, magic, sa)
-            : decode_launch<B, NW, TX, TL, false, false>(X, idx, lut, p, Y, s, magic, sa);
+    return xl ? decode_launch<B, NW, TX, TL, true, true, false>(X, idx, lut, p, Y, s, magic, sa)
+              : (xt ? decode_launch<B, NW, TX, TL, true, false, true>(X, idx, lut, p, Y, s, magic, sa)
+                    : decode_launch<B, NW, TX, TL, true, false, false>(X, idx, lut, p, Y, s, magic, sa));
+  return xl ? decode_launch<B, NW, TX, TL, false, true, false>(X, idx, lut, p, Y, s, magic, sa)
+            : (xt ? decode_launch<B, NW, TX, TL, false, false, true>(X, idx, lut, p, Y, s, magic, sa)
+                  : decode_launch<B, NW, TX, TL, false, false, false>(X, idx, lut, p, Y, s, magic, sa));
 }
 
 template <int B, typename TX, typename TL>

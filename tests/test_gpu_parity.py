@@ -117,6 +117,9 @@ def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 1, 8200, 1184, 3), (4, 4, 8200, 1152, 2), (3, 8, 9001, 2048, 1), (2, 8, 12000, 512, 16),
     (4, 1, 16400, 96, 7), (4, 8, 8400, 4096, 1),
+    # activations past the staging limit: from 8 tokens on turned around in LDS (one with a ragged
+    # slot), below that loaded per lane
+    (2, 8, 8200, 4096, 12), (4, 5, 8300, 2080, 16), (4, 4, 6400, 4736, 7),
 ])
 def test_fwd16_large_n_decode(x_dtype, lut_dtype, b, gpr, n, d, m):
     """Decode with more 16-row blocks than the GPU holds at once (8-wave
