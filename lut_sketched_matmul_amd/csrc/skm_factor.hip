@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(256) k_hf_init(const double* __restrict__ H, i
 // forward substitution L X = I taken with it; entries of L above the diagonal
 // are never read for the result). (One wave holding whole rows, with no
 // block barrier, was twice as slow: the column work then runs on one SIMD.)
-__global__ void __launch_bounds__(256) k_hf_diag(double* __restrict__ A, int64_t D, int k, double* __restrict__ Dinv) {
+__device__ __forceinline__ void hf_diag(double* __restrict__ A, int64_t D, int k, double* __restrict__ Dinv) {
   __shared__ double colb[2][HF], rowb[2][HF], piv[2][2];
   const int t = threadIdx.x, r = t >> 2, p = t & 3;
   double* Akk = A + (int64_t)k * HF * D + (int64_t)k * HF;
@@ -138,6 +138,12 @@ __global__ void __launch_bounds__(256) k_hf_diag(double* __restrict__ A, int64_t
   double* dst = Dinv + (int64_t)k * HF * HF;
 #pragma unroll
   for (int s = 0; s < HF / 4; ++s) dst[r * HF + p + 4 * s] = x[s];
+}
+
+// the first diagonal block (the later ones are factored by the update of the
+// step before, see k_hf_update)
+__global__ void __launch_bounds__(256) k_hf_diag(double* __restrict__ A, int64_t D, int k, double* __restrict__ Dinv) {
+  hf_diag(A, D, k, Dinv);
 }
 
 // A 64 x 64 matrix M in memory: element (r, c) at m + r * rs + c * cs
@@ -219,9 +225,12 @@ __global__ void __launch_bounds__(256) k_hf_panel(double* __restrict__ A, int64_
 }
 
 // ---- update of step k: blocks b < N1: A_ij -= L_ik L_jk^T over the trailing
-// lower triangle (k < j <= i); the others: R_pj -= L_pk X_kj (p > k, j <= k)
+// lower triangle (k < j <= i); the others: R_pj -= L_pk X_kj (p > k, j <= k).
+// Block 0 updates the next diagonal tile A_{k+1,k+1} and then factors and
+// inverts it (the diagonal step k+1), while the other blocks are still at
+// their tiles: no other block of this launch reads that tile or Dinv_{k+1}.
 __global__ void __launch_bounds__(256) k_hf_update(double* __restrict__ A, int64_t D, int T, int k,
-                                                   const double* __restrict__ Dinv) {
+                                                   double* __restrict__ Dinv) {
   __shared__ __attribute__((aligned(16))) double Ps[HF * HS], Qs[HF * HS];
   const int64_t m = T - k - 1;
   const int64_t n1 = m * (m + 1) / 2;
@@ -234,10 +243,14 @@ __global__ void __launch_bounds__(256) k_hf_update(double* __restrict__ A, int64
     const int64_t jp = b - ip * (ip + 1) / 2;
     const int64_t i = k + 1 + ip, j = k + 1 + jp;
     tile_mul<true>(blk(A, D, i, j), blk(A, D, i, k), blk_t(A, D, k, j), 1.0, -1.0, Ps, Qs);
+    if (b == 0) {
+      __syncthreads();  // the tile's stores (other threads') before its factorization reads them
+      hf_diag(A, D, k + 1, Dinv);
+    }
   } else {
     const int64_t b2 = b - n1;
     const int64_t p = k + 1 + b2 / (k + 1), j = b2 % (k + 1);
-    double* Dk = const_cast<double*>(Dinv) + (int64_t)k * HF * HF;
+    double* Dk = Dinv + (int64_t)k * HF * HF;
     const Tile X = j == k ? Tile{Dk, HF, 1} : blk_t(A, D, k, j);
     tile_mul<false>(blk_t(A, D, p, j), blk(A, D, p, k), X, 1.0, -1.0, Ps, Qs);
   }
@@ -287,8 +300,9 @@ hipError_t launch_hessian_factor(const double* H, int64_t d, double damp, float*
   double* mean = Dinv + (int64_t)T * HF * HF;
   hipLaunchKernelGGL(k_hf_mean, dim3(1), dim3(256), 0, s, H, d, mean);
   hipLaunchKernelGGL(k_hf_init, dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0, s, H, d, D, damp, mean, A);
+  hipLaunchKernelGGL(k_hf_diag, dim3(1), dim3(256), 0, s, A, D, 0, Dinv);
   for (int k = 0; k < T; ++k) {
-    hipLaunchKernelGGL(k_hf_diag, dim3(1), dim3(256), 0, s, A, D, k, Dinv);
+    // (the diagonal step k + 1 runs in block 0 of the update of step k)
     const int np = (T - 1 - k) + k;
     if (np > 0) hipLaunchKernelGGL(k_hf_panel, dim3((unsigned)np), dim3(256), 0, s, A, D, T, k, Dinv);
     const int64_t m = T - k - 1;
