@@ -14,8 +14,8 @@
 // Kernels: k_col_weights (one thread per column); k_lloyd (one wave per
 // (row, group), everything in registers and wave reductions); the mapping in
 // blocks of 64 columns: k_map_block runs the sequential sweep of one block
-// (four lanes per row, the block's 64 x 64 part of U in LDS) and writes the
-// packed indices and the block's errors; k_map_trail applies errors to later
+// (one wave per row, a lane per column with its column of the block's part
+// of U in registers) and writes the packed indices and the block's errors; k_map_trail applies errors to later
 // columns as fp32 rank-k updates (W[:, cols] -= E^T U[rows, cols]), in two
 // levels: each 64-column block's errors to the rest of its 512-column outer
 // block, each outer block's 512 errors to every column after it. The sum each
@@ -130,126 +130,84 @@ __global__ void __launch_bounds__(256) k_lloyd(const float* __restrict__ W, cons
   }
 }
 
-// One 64-column block of the mapping sweep. Four lanes per row (16 rows per
-// wave): lane `sub` of a row holds the row's columns 4 t + sub (t < 16) of the
-// block, so the updates of each step split over the four lanes. Column c is
-// owned by lane c % 4: a quad broadcast (DPP) hands the owner's weight to the
-// other three, each lane scans a quarter of the table and two DPP butterfly
-// steps leave the nearest entry (ties to the lower index) in all four. The
-// error is (w - q) times 1 / U[c][c] (the reciprocals are taken once per
-// block). Reads the compensated weights
-// Wc[:, j0 : j0 + cols] (all earlier blocks' errors applied), writes the
-// block's packed indices and its errors E [64][n]. The block's part of U sits
-// in LDS as [c][sub][t] so a lane's 16 coefficients of a step are contiguous.
-template <int OWN>
-__device__ __forceinline__ float quad_bcast(float v) {
-  constexpr int ctrl = OWN | (OWN << 2) | (OWN << 4) | (OWN << 6);  // quad_perm [OWN, OWN, OWN, OWN]
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+// One 64-column block of the mapping sweep, one wave per row (16 rows per
+// block). Lane j holds column j0 + j of the block: its compensated weight
+// and its column of the block's part of U, in registers. Lane e also holds
+// table entry e % K of the (at most two) groups the block spans, so lanes
+// 0 .. K-1 hold every entry once, in order. Step c: the owner's weight
+// reaches every lane by readlane; every lane takes its entry's distance, and
+// a 4-step DPP min over each 16-lane row leaves the smallest in all lanes;
+// the lowest lane holding it (ballot, first set bit) is the nearest entry,
+// ties going to the lower index. Every lane then subtracts err * U[c][j]
+// from its weight (for j <= c that term is zero or the column is done),
+// with err = (w_c - q) / U[c][c] (the reciprocal taken once per block).
+// Lane c keeps the step's error and the index goes into scalar registers,
+// so the errors E [64][n] and the packed indices are written once, at the
+// end. Reads the compensated weights Wc[:, j0 : j0 + cols] (all earlier
+// blocks' errors applied).
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 template <int CTRL>
-__device__ __forceinline__ float quad_perm_f(float v) {
+__device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int quad_perm_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-// merge with the quad partner given by CTRL: the partner's entry wins when it
-// is nearer, or as near with a lower index
-template <int CTRL>
-__device__ __forceinline__ void quad_min(float& best, float& q, int& a) {
-  const float pb = quad_perm_f<CTRL>(best), pq = quad_perm_f<CTRL>(q);
-  const int pa = quad_perm_i<CTRL>(a);
-  const bool take = pb < best || (pb == best && pa < a);
-  best = take ? pb : best;
-  q = take ? pq : q;
-  a = take ? pa : a;
-}
-
-template <int C, int B, int K>
-__device__ __forceinline__ void map_step(float (&w)[16], const float (&t0)[K / 4], const float (&t1)[K / 4],
-                                         const float (*ub)[MAP_COLS], const float* rdiag, int sub, int cols,
-                                         bool row_ok, int64_t n, int64_t i, float* __restrict__ E,
-                                         uint32_t (&pk)[MAP_COLS * B / 32]) {
-  if constexpr (C < MAP_COLS) {
-    constexpr int T = C / 4, OWN = C % 4;
-    if (C < cols) {  // uniform
-      // the owner's weight; each lane scans its quarter of the table (entries
-      // sub K/4 .. sub K/4 + K/4 - 1), then two butterfly steps over the quad
-      const float wv = quad_bcast<OWN>(w[T]);
-      float best = fabsf(wv - (C < 32 ? t0[0] : t1[0])), q = C < 32 ? t0[0] : t1[0];
-      int a = sub * (K / 4);
-#pragma unroll
-      for (int e = 1; e < K / 4; ++e) {
-        const float tvv = C < 32 ? t0[e] : t1[e];
-        const float dr = fabsf(wv - tvv);
-        const bool lt = dr < best;
-        best = lt ? dr : best;
-        q = lt ? tvv : q;
-        a = lt ? sub * (K / 4) + e : a;
-      }
-      quad_min<0xB1>(best, q, a);  // quad_perm [1, 0, 3, 2]
-      quad_min<0x4E>(best, q, a);  // quad_perm [2, 3, 0, 1]
-      const float err = (wv - q) * rdiag[C];  // the same on all four lanes
-      if (sub == OWN && row_ok) E[C * n + i] = err;
-      const float* u = ub[C] + sub * 16;
-#pragma unroll
-      for (int t2 = T + 1; t2 < 16; ++t2) w[t2] -= err * u[t2];
-      if (sub > OWN) w[T] -= err * u[T];
-      constexpr int p = B * C;
-      pk[p >> 5] |= (uint32_t)a << (p & 31);
-      if constexpr ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)a >> (32 - (p & 31));
-    }
-    map_step<C + 1, B, K>(w, t0, t1, ub, rdiag, sub, cols, row_ok, n, i, E, pk);
-  }
 }
 
 template <int B, typename TL>
-__global__ void __launch_bounds__(64) k_map_block(float* __restrict__ Wc, const float* __restrict__ U,
-                                                   const TL* __restrict__ lut, int64_t n, int64_t d, int gpr,
-                                                   int64_t j0, int cols, uint8_t* __restrict__ idx_packed,
-                                                   float* __restrict__ E) {
+__global__ void __launch_bounds__(1024) k_map_block(float* __restrict__ Wc, const float* __restrict__ U,
+                                                     const TL* __restrict__ lut, int64_t n, int64_t d, int gpr,
+                                                     int64_t j0, int cols, uint8_t* __restrict__ idx_packed,
+                                                     float* __restrict__ E) {
   constexpr int K = 1 << B;
-  __shared__ float ub[MAP_COLS][MAP_COLS];  // [c][sub * 16 + t] = U[j0 + c][j0 + 4 t + sub]
-  __shared__ float rdiag[MAP_COLS];         // 1 / U[j0 + c][j0 + c] (the steps multiply)
-  for (int e = threadIdx.x; e < MAP_COLS * MAP_COLS; e += 64) {
+  __shared__ float ub[MAP_COLS][MAP_COLS];  // U[j0 + c][j0 + j]
+  for (int e = threadIdx.x; e < MAP_COLS * MAP_COLS; e += 1024) {
     const int r = e / MAP_COLS, cc = e % MAP_COLS;
-    ub[r][(cc & 3) * 16 + (cc >> 2)] = (r < cols && cc < cols) ? U[(j0 + r) * d + j0 + cc] : 0.f;
+    ub[r][cc] = (r < cols && cc < cols) ? U[(j0 + r) * d + j0 + cc] : 0.f;
   }
-  rdiag[threadIdx.x] = threadIdx.x < cols ? 1.f / U[(j0 + threadIdx.x) * d + j0 + threadIdx.x] : 0.f;
   __syncthreads();
-  const int sub = threadIdx.x & 3;
-  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 2);
-  const bool row_ok = i < n;  // no early exit: the quad broadcasts need every lane
-  const int64_t ic = row_ok ? i : n - 1;
+  const int lane = (int)(threadIdx.x & 63);
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (i >= n) return;  // a whole wave; no barrier follows
+  float u[MAP_COLS];
+#pragma unroll
+  for (int c = 0; c < MAP_COLS; ++c) u[c] = ub[c][lane];
+  const float rd = lane < cols ? 1.f / ub[lane][lane] : 0.f;
+  float w = lane < cols ? Wc[i * d + j0 + lane] : 0.f;
+  // the block spans at most two groups, split at a multiple of 32 columns
   const int64_t G = d / gpr;
-  float w[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int col = 4 * t + sub;
-    w[t] = col < cols ? Wc[ic * d + j0 + col] : 0.f;
-  }
-  // the block spans at most two groups, split at a multiple of 32 columns;
-  // each lane keeps its quarter of both tables
-  float t0[K / 4], t1[K / 4];
   const int64_t g0 = j0 / G, g1 = (j0 + 32) / G;
-#pragma unroll
-  for (int e = 0; e < K / 4; ++e) {
-    t0[e] = to_f32(lut[(ic * gpr + g0) * K + sub * (K / 4) + e]);
-    t1[e] = to_f32(lut[(ic * gpr + (g1 < gpr ? g1 : g0)) * K + sub * (K / 4) + e]);
-  }
+  const float t0 = to_f32(lut[(i * gpr + g0) * K + (lane % K)]);
+  const float t1 = to_f32(lut[(i * gpr + (g1 < gpr ? g1 : g0)) * K + (lane % K)]);
   constexpr int WORDS = MAP_COLS * B / 32;
   uint32_t pk[WORDS];
 #pragma unroll
   for (int q = 0; q < WORDS; ++q) pk[q] = 0u;
-  map_step<0, B, K>(w, t0, t1, ub, rdiag, sub, cols, row_ok, n, i, E, pk);
-  if (sub == 0 && row_ok) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(idx_packed + i * (d * B / 8) + j0 * B / 8);
-    const int words = cols * B / 32;
+  float ekeep = 0.f;
 #pragma unroll
-    for (int q = 0; q < WORDS; ++q)
-      if (q < words) dst[q] = pk[q];
+  for (int c = 0; c < MAP_COLS; ++c) {
+    if (c < cols) {  // uniform
+      const float tv = c < 32 ? t0 : t1;
+      const float wv = readlane_f(w, c);
+      const float dist = fabsf(wv - tv);
+      float mn = fminf(dist, dpp_f<0xB1>(dist));  // quad_perm [1, 0, 3, 2]
+      mn = fminf(mn, dpp_f<0x4E>(mn));             // quad_perm [2, 3, 0, 1]
+      mn = fminf(mn, dpp_f<0x141>(mn));            // row_half_mirror
+      mn = fminf(mn, dpp_f<0x140>(mn));            // row_mirror
+      const int a = __builtin_ctzll(__ballot(dist == mn));  // < K: lane a holds entry a
+      const float err = (wv - readlane_f(tv, a)) * readlane_f(rd, c);
+      ekeep = lane == c ? err : ekeep;
+      w -= err * u[c];
+      const int p = B * c;
+      pk[p >> 5] |= (uint32_t)a << (p & 31);
+      if ((p & 31) + B > 32) pk[(p >> 5) + 1] |= (uint32_t)a >> (32 - (p & 31));
+    }
   }
+  if (lane < cols) E[(int64_t)lane * n + i] = ekeep;
+  const int words = cols * B / 32;
+  uint32_t v = 0u;
+#pragma unroll
+  for (int q = 0; q < WORDS; ++q) v = lane == q ? pk[q] : v;
+  if (lane < words) reinterpret_cast<uint32_t*>(idx_packed + i * (d * B / 8) + j0 * B / 8)[lane] = v;
 }
 
 // Wc[:, c0 : c1] -= E[e0 : e0 + k]^T * U[u0 : u0 + k, c0 : c1] (E is [rows][n],
@@ -318,7 +276,7 @@ hipError_t map_run(float* Wc, const float* U, const TL* lut, const Problem& p, u
     for (int64_t j0 = ob; j0 < oend; j0 += MAP_COLS) {
       const int cols = (int)(p.d - j0 < MAP_COLS ? p.d - j0 : MAP_COLS);
       float* Eb = E + (j0 - ob) * p.n;
-      hipLaunchKernelGGL((k_map_block<B, TL>), dim3((unsigned)((p.n + 15) / 16)), dim3(64), 0, s, Wc, U, lut, p.n,
+      hipLaunchKernelGGL((k_map_block<B, TL>), dim3((unsigned)((p.n + 15) / 16)), dim3(1024), 0, s, Wc, U, lut, p.n,
                          p.d, p.gpr, j0, cols, idx, Eb);
       const int64_t j1 = j0 + cols;
       if (j1 < oend) {
