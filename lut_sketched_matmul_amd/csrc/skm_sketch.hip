@@ -211,48 +211,75 @@ __global__ void __launch_bounds__(1024) k_map_block(float* __restrict__ Wc, cons
 }
 
 // Wc[:, c0 : c1] -= E[e0 : e0 + k]^T * U[u0 : u0 + k, c0 : c1] (E is [rows][n],
-// k a multiple of 64); 64 x 64 output tiles, 4 x 4 outputs per thread, the
-// k rows taken 64 at a time through LDS
+// k a multiple of 64) on the matrix cores: 64 x 64 output tiles, each wave a
+// 32 x 32 quarter as 2 x 2 v_mfma_f32_16x16x4 tiles; the k rows go through
+// LDS 64 at a time as [k][row] and [k][col] (the next 64 loaded into
+// registers meanwhile), rows padded to 80 floats so the four k rows of an
+// operand read land on distinct banks.
+constexpr int TRAIL_LD = 80;
 __global__ void __launch_bounds__(256) k_map_trail(float* __restrict__ Wc, const float* __restrict__ U,
                                                     const float* __restrict__ E, int64_t n, int64_t d, int64_t u0,
                                                     int k, int64_t cbeg, int64_t cend) {
-  __shared__ float es[MAP_COLS][MAP_COLS + 4];  // [k][row]
-  __shared__ float us[MAP_COLS][MAP_COLS + 4];  // [k][col]
+  __shared__ float es[MAP_COLS][TRAIL_LD];  // [k][row]
+  __shared__ float us[MAP_COLS][TRAIL_LD];  // [k][col]
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = cbeg + (int64_t)blockIdx.x * 64;
-  const int tid = threadIdx.x;
-  const int tr = tid / 16, tc = tid % 16;  // rows tr + 16 a, columns 4 tc + b
-  float acc[4][4] = {};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);  // the wave's quarter
+  const int lr = lane & 15, lk = lane >> 4;               // operand row / column, k within the step
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the next 64 k rows are loaded into registers while the current ones are
+  // multiplied (thread t: k rows t / 64 + 4 q, row / column t % 64)
+  const int x = tid & 63, k4 = tid >> 6;
+  const bool rok = r0 + x < n, cok = c0 + x < cend;
+  float pe[16], pu[16];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int kk = k4 + 4 * q;
+      pe[q] = rok ? E[(int64_t)(kb + kk) * n + r0 + x] : 0.f;
+      pu[q] = cok ? U[(u0 + kb + kk) * d + c0 + x] : 0.f;
+    }
+  };
+  fetch(0);
   for (int kb = 0; kb < k; kb += MAP_COLS) {
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int kk = e / 64, x = e % 64;  // error kb + kk of row r0 + x; U row u0 + kb + kk, column c0 + x
-      es[kk][x] = r0 + x < n ? E[(int64_t)(kb + kk) * n + r0 + x] : 0.f;
-      us[kk][x] = c0 + x < cend ? U[(u0 + kb + kk) * d + c0 + x] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      es[k4 + 4 * q][x] = pe[q];
+      us[k4 + 4 * q][x] = pu[q];
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < MAP_COLS; ++kk) {
-      float ev[4], uv[4];
+    if (kb + MAP_COLS < k) fetch(kb + MAP_COLS);
+#pragma unroll 4
+    for (int kk = 0; kk < MAP_COLS; kk += 4) {
+      float av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ev[a] = es[kk][tr + 16 * a];
+      for (int a = 0; a < 2; ++a) av[a] = es[kk + lk][wr + 16 * a + lr];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) uv[b] = us[kk][4 * tc + b];
+      for (int b = 0; b < 2; ++b) bv[b] = us[kk + lk][wc + 16 * b + lr];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] += ev[a] * uv[b];
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane l holds rows 4 (l / 16) + i, column l % 16 of each 16 x 16 tile
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t r = r0 + tr + 16 * a;
-    if (r >= n) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t c = c0 + 4 * tc + b;
-      if (c < cend) Wc[r * d + c] -= acc[a][b];
+    for (int b = 0; b < 2; ++b) {
+      const int64_t c = c0 + wc + 16 * b + lr;
+      if (c >= cend) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + wr + 16 * a + 4 * lk + i;
+        if (r < n) Wc[r * d + c] -= acc[a][b][i];
+      }
     }
-  }
 }
 
 hipError_t map_trail(float* Wc, const float* U, const float* E, const Problem& p, int64_t u0, int k, int64_t cbeg,
