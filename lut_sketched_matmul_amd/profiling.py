@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
               "lut_sketched_matmul_amd/csrc/skm_optim.hip"],
     "sketch": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
                "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
-               "lut_sketched_matmul_amd/csrc/skm_sketch.hip"],
+               "lut_sketched_matmul_amd/csrc/skm_sketch.hip", "lut_sketched_matmul_amd/csrc/skm_factor.hip"],
 }
 
 # torch.add(src, 1.0, out=dst) on fp32: reads and writes this many bytes per launch
