@@ -46,21 +46,37 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // [H^-1]_jj = sum_{k <= j} U_kj^2 (U is upper triangular). A block takes 64
-// columns; its 4 waves take every 4th row (each lane one column, so a wave
-// reads 256 contiguous bytes per row) and the 4 partial sums meet in LDS.
-__global__ void __launch_bounds__(256) k_col_weights(const float* __restrict__ U, int64_t d, float* __restrict__ h) {
-  __shared__ float part[4][64];
+// columns; its 16 waves take every 16th row (each lane one column, so a wave
+// reads 256 contiguous bytes per row), eight rows' loads in flight at a time,
+// and the 16 partial sums meet in LDS in wave order.
+constexpr int CW_WAVES = 16, CW_UNROLL = 8;
+__global__ void __launch_bounds__(CW_WAVES * 64) k_col_weights(const float* __restrict__ U, int64_t d,
+                                                                float* __restrict__ h) {
+  __shared__ float part[CW_WAVES][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t jc = j < d ? j : d - 1;
   float s = 0.f;
-  if (j < d)
-    for (int64_t k = w; k <= j; k += 4) {
-      const float u = U[k * d + j];
-      s += u * u;
+  // rows up to the block's last column (the lanes past their own column add 0)
+  const int64_t kend = ((int64_t)blockIdx.x * 64 + 63 < d ? (int64_t)blockIdx.x * 64 + 63 : d - 1) + 1;
+  for (int64_t k0 = w; k0 < kend; k0 += CW_WAVES * CW_UNROLL) {
+    float u[CW_UNROLL];
+#pragma unroll
+    for (int a = 0; a < CW_UNROLL; ++a) {
+      const int64_t k = k0 + (int64_t)a * CW_WAVES;
+      u[a] = (k < kend && k <= j && j < d) ? U[k * d + jc] : 0.f;
     }
+#pragma unroll
+    for (int a = 0; a < CW_UNROLL; ++a) s += u[a] * u[a];
+  }
   part[w][lane] = s;
   __syncthreads();
-  if (w == 0 && j < d) h[j] = 1.f / (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]);
+  if (w == 0 && j < d) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < CW_WAVES; ++q) t += part[q][lane];
+    h[j] = 1.f / t;
+  }
 }
 
 // one wave per (row, group); K = 2^b centroids
@@ -333,7 +349,7 @@ hipError_t lloyd_run(const float* W, const float* h, const Problem& p, int iters
 }  // namespace
 
 hipError_t launch_col_weights(const float* U, int64_t d, float* h, hipStream_t s) {
-  hipLaunchKernelGGL(k_col_weights, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, U, d, h);
+  hipLaunchKernelGGL(k_col_weights, dim3((unsigned)((d + 63) / 64)), dim3(CW_WAVES * 64), 0, s, U, d, h);
   return hipGetLastError();
 }
 
