@@ -60,35 +60,38 @@ __global__ void __launch_bounds__(256) k_hf_init(const double* __restrict__ H, i
 }
 
 // ---- diag: L_kk = chol(A_kk) in place (lower part), Dinv_k = L_kk^-1 ------
-// Thread (r, p) = (t / 4, t % 4) holds entries of row r of L and of X = L^-1
-// in registers (X starts as I): x[s] is X_rq for q = p + 4 s, and l[s] is L_rq
-// for q = p + 4 (s + cc) during column group cc (columns 4 cc .. 4 cc + 3):
-// after each group the thread stores l[0], whose column is then final, and
-// shifts l down, so every register index is a compile-time constant while
-// the loop over groups stays a loop (the kernel's code fits the instruction
-// cache). Column c, in one pass behind one barrier: the threads holding
-// column c of L and the four holding row c of X publish them (double-buffered
-// in LDS) beside the pivot g = sqrt(L_cc) and 1 / g, which the thread holding
-// L_cc worked out during column c - 1 as soon as that entry was final (so the
-// square root and division are off the path from one barrier to the next);
-// then for r > c
+// Thread (a, e) = (t / 16, t % 16) holds the 4 x 4 block of rows 4a .. 4a+3
+// and columns 4e .. 4e+3, of L and of X = L^-1 (X starts as I), in
+// registers. Column c, in one pass behind one barrier: the 16 threads of
+// column block c / 4 publish column c of L and the 16 of row block c / 4 row
+// c of X (double-buffered in LDS) beside the pivot g = sqrt(L_cc) and 1 / g,
+// which the thread holding L_cc worked out during column c - 1 as soon as that
+// entry was final (so the square root and division are off the path from one
+// barrier to the next); then for r > c
 //   L_rc = L_rc / g,  L_rq -= L_rc L_qc / g (q > c),  X_rq -= L_rc X_cq / g,
 // while row c sets L_cc = g and X_cq /= g (right-looking Cholesky, and the
 // forward substitution L X = I taken with it; entries of L above the diagonal
-// are never read for the result). (One wave holding whole rows, with no
-// block barrier, was twice as slow: the column work then runs on one SIMD.)
+// are never read for the result). Each thread reads 12 published values per
+// column (its rows' and its columns' entries of column c, its columns' of row
+// c), as 16-byte pairs. (Rows of 16 entries per thread needed 32 values per
+// column, and that LDS traffic set the pace; one wave holding whole rows,
+// with no block barrier, was slower still: the column work then runs on one
+// SIMD.)
 __device__ __forceinline__ void hf_diag(double* __restrict__ A, int64_t D, int k, double* __restrict__ Dinv) {
-  __shared__ double colb[2][HF], rowb[2][HF], piv[2][2];
-  const int t = threadIdx.x, r = t >> 2, p = t & 3;
+  __shared__ __attribute__((aligned(16))) double colb[2][HF], rowb[2][HF];
+  __shared__ double piv[2][2];
+  const int t = threadIdx.x, a = t >> 4, e = t & 15;
   double* Akk = A + (int64_t)k * HF * D + (int64_t)k * HF;
-  double l[HF / 4], x[HF / 4];
+  double l[4][4], x[4][4];
 #pragma unroll
-  for (int s = 0; s < HF / 4; ++s) {
-    l[s] = Akk[(int64_t)r * D + p + 4 * s];
-    x[s] = (p + 4 * s == r) ? 1.0 : 0.0;
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      l[i][jj] = Akk[(int64_t)(4 * a + i) * D + 4 * e + jj];
+      x[i][jj] = (4 * a + i == 4 * e + jj) ? 1.0 : 0.0;
+    }
   if (t == 0) {
-    const double g0 = sqrt(l[0]);
+    const double g0 = sqrt(l[0][0]);
     piv[0][0] = g0;
     piv[0][1] = 1.0 / g0;
   }
@@ -96,48 +99,69 @@ __device__ __forceinline__ void hf_diag(double* __restrict__ A, int64_t D, int k
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 4 * cc + j, b = j & 1;
-      if (p == j) colb[b][r] = l[0];
-      if (r == c) {
+      if (e == cc) {
+        colb[b][4 * a + 0] = l[0][j];
+        colb[b][4 * a + 1] = l[1][j];
+        colb[b][4 * a + 2] = l[2][j];
+        colb[b][4 * a + 3] = l[3][j];
+      }
+      if (a == cc) {
 #pragma unroll
-        for (int s = 0; s < HF / 4; ++s) rowb[b][p + 4 * s] = x[s];
+        for (int jj = 0; jj < 4; ++jj) rowb[b][4 * e + jj] = x[j][jj];
       }
       __syncthreads();
       const double g = piv[b][0], rg = piv[b][1];
-      if (r > c) {
-        const double lrc = colb[b][r] * rg;
-        if (p == j) l[0] = lrc;
-        const double f = lrc * rg;
-        // the next pivot first: L_{c+1,c+1} sits in l[0] (l[1] across a group
-        // boundary) of thread (c + 1, (c + 1) % 4)
-        const int sn = j == 3 ? 1 : 0;
-        if (r == c + 1 && p == ((j + 1) & 3) && c + 1 < HF) {
-          const double v = l[sn] - f * colb[b][c + 1];
-          const double gn = sqrt(v);
-          piv[b ^ 1][0] = gn;
-          piv[b ^ 1][1] = 1.0 / gn;
-        }
+      const double2* cb = reinterpret_cast<const double2*>(&colb[b][0]);
+      const double2* rb = reinterpret_cast<const double2*>(&rowb[b][0]);
+      const double2 cr0 = cb[2 * a], cr1 = cb[2 * a + 1];  // L_rc (unscaled) of this thread's rows
+      const double2 cq0 = cb[2 * e], cq1 = cb[2 * e + 1];  // L_qc (unscaled) of its columns
+      const double2 xq0 = rb[2 * e], xq1 = rb[2 * e + 1];  // X_cq (unscaled) of its columns
+      const double cr[4] = {cr0.x, cr0.y, cr1.x, cr1.y};
+      const double cq[4] = {cq0.x, cq0.y, cq1.x, cq1.y};
+      const double xq[4] = {xq0.x, xq0.y, xq1.x, xq1.y};
+      // the next pivot first: L_{c+1,c+1} is entry ((c+1) % 4, (c+1) % 4) of
+      // block ((c+1) / 4, (c+1) / 4), final once this column is applied
+      const int i1 = (j + 1) & 3;
+      const int b1 = j == 3 ? cc + 1 : cc;
+      if (a == b1 && e == b1 && c + 1 < HF) {
+        const double f1 = cr[i1] * rg * rg;
+        const double v = l[i1][i1] - f1 * cq[i1];
+        const double gn = sqrt(v);
+        piv[b ^ 1][0] = gn;
+        piv[b ^ 1][1] = 1.0 / gn;
+      }
 #pragma unroll
-        for (int s = 0; s < HF / 4; ++s) {
-          // column q = p + 4 (s + cc) of L, for q > c and q < 64
-          if (p + 4 * s > j && s + cc < HF / 4) l[s] -= f * colb[b][p + 4 * (s + cc)];
-          x[s] -= f * rowb[b][p + 4 * s];
-        }
-      } else if (r == c) {
-        if (p == j) l[0] = g;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * a + i;
+        if (r > c) {
+          const double lrc = cr[i] * rg;
+          const double f = lrc * rg;
+          if (e == cc) l[i][j] = lrc;
 #pragma unroll
-        for (int s = 0; s < HF / 4; ++s) x[s] *= rg;
+          for (int jj = 0; jj < 4; ++jj) {
+            if (4 * e + jj > c) l[i][jj] -= f * cq[jj];
+            x[i][jj] -= f * xq[jj];
+          }
+        } else if (r == c) {
+          if (e == cc) l[i][j] = g;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) x[i][jj] *= rg;
+        }
       }
     }
-    // column p + 4 cc of this row is final
-    const int q = p + 4 * cc;
-    if (q <= r) Akk[(int64_t)r * D + q] = l[0];
-#pragma unroll
-    for (int s = 0; s + 1 < HF / 4; ++s) l[s] = l[s + 1];
-    l[HF / 4 - 1] = 0.0;
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 4 * a + i, q = 4 * e + jj;
+      if (q <= r) Akk[(int64_t)r * D + q] = l[i][jj];
+    }
   double* dst = Dinv + (int64_t)k * HF * HF;
 #pragma unroll
-  for (int s = 0; s < HF / 4; ++s) dst[r * HF + p + 4 * s] = x[s];
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dst[(4 * a + i) * HF + 4 * e + jj] = x[i][jj];
 }
 
 // the first diagonal block (the later ones are factored by the update of the
