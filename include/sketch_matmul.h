@@ -48,8 +48,11 @@
  * at or above 2^-17 (in the scaled row) converts to f16 exactly, and a
  * smaller one with an absolute error below 2^-23 M, for any finite bf16
  * input; infinities and NaNs propagate. The exponents come from a pre-pass
- * into the workspace (forward GEMM, dX, and the decode when m * d > 32768)
- * or are found inside the decode kernel.
+ * into the workspace (forward GEMM, dX, and a decode that reads its
+ * activations per slot instead of staging them in LDS) or are found inside
+ * the decode kernel. The decode stages them when m * d <= 32768, and when
+ * m < 8, m * d <= 49152, n <= 4096 and the block's tables, activations and
+ * partial sums fit in 160 KB of LDS.
  *
  * Alignment: every pointer must be 16-byte aligned.
  *
@@ -100,7 +103,8 @@ typedef enum {
  * workspace/workspace_bytes: device scratch of at least
  * sketch_matmul_fwd_workspace(...) bytes, 16-byte aligned, not overlapping
  * any other buffer; may be NULL when that size is 0 (every dtype pair except
- * (BF16, F16), and that pair's decode-sized calls with m * d <= 32768). It
+ * (BF16, F16), and that pair's decode-sized calls that stage their
+ * activations, see "Range" above). It
  * holds the row exponents of X (see "Range" above) during the call only.
  * Decode-sized m streams the indices once; larger m runs a tiled matrix-core
  * GEMM. Returns SKM_OK or an error status (see above).

@@ -74,6 +74,10 @@ constexpr int DEC_MAX_ENTRIES = 224;  // table entries per row kept in LDS (entr
 constexpr int DEC_LUT_CHUNKS = 2;     // 8-entry table chunks loaded per wave (16 * 2 * 8 >= 224)
 constexpr int64_t DEC_XL_MAX = 32768; // m * d elements staged in LDS (64 KB)
 constexpr int DEC_XL_CHUNKS = (int)(DEC_XL_MAX / 8 / (8 * 64));  // 16-byte chunks per thread (NW >= 8)
+// one table set, at most one 16-row block per CU: up to 96 KB of staged
+// activations when the block's LDS still fits
+constexpr int64_t DEC_XL_MAX1 = 49152;
+constexpr int DEC_XL_CHUNKS1 = (int)(DEC_XL_MAX1 / 8 / (8 * 64));
 // unstaged activations: every wave turns its slot's [16 tokens][16 pieces of
 // 16 bytes] around in a private LDS buffer, rows padded by one piece
 constexpr uint32_t DEC_XT_ROW = 17 * 16;
@@ -398,7 +402,8 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // activation elements staged (MULTI + XL: one pass's tokens)
   const int64_t xl_elems =
       (int64_t)((MULTI && XL) ? (m < (int)(DEC_XL_MAX / d) ? m : (int)(DEC_XL_MAX / d)) : m) * d;
-  constexpr int XCH = XL ? DEC_XL_CHUNKS * 8 / NW : 1;  // 16-byte activation chunks per thread
+  // 16-byte activation chunks per thread (the larger staging only runs with 16 waves)
+  constexpr int XCH = XL ? ((MULTI || NW < 16) ? DEC_XL_CHUNKS : DEC_XL_CHUNKS1) * 8 / NW : 1;
   // SC + XL: the partials overlay the staged activations (after a barrier
   // at the end), and the magnitude slots [16 rows][NW] and the waves' range
   // records [NW] follow that region (keeping the block's LDS near the f16
@@ -832,8 +837,8 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL, XT);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
   // element e of the staged activations lies in row e / d = umulhi(e, ceil(2^32 / d)), exact for e * d < 2^32
-  // (staged elements number at most 32768 and d <= 32768 when staging)
-  const uint32_t d_magic = p.d <= DEC_XL_MAX ? (uint32_t)(((uint64_t)1 << 32) / (uint64_t)p.d) + 1u : 0u;
+  // (staged elements number at most 49152 and d <= 49152 when staging)
+  const uint32_t d_magic = p.d <= DEC_XL_MAX1 ? (uint32_t)(((uint64_t)1 << 32) / (uint64_t)p.d) + 1u : 0u;
   // (the gathers address the tables with absolute LDS addresses, see gaddr:
   // checked once per kernel, which also raises its LDS limit to 160 KB)
   if (sa.lut_set) {
@@ -919,8 +924,18 @@ int decode_max_m() { return 16; }
 
 bool decode_stages_activations(const Problem& p, bool multi, int n_sets, bool scaled) {
   // the prescaled multi-set decode always stages (it finds the exponents of
-  // the staged rows itself)
-  return p.m * p.d <= DEC_XL_MAX || (multi && (n_sets > 1 || scaled) && p.d <= DEC_XL_MAX);
+  // the staged rows itself). One set: up to 32768 elements, or, below the
+  // token count from which the LDS turn-around runs (staging 72-96 KB per
+  // block measured slower than that), up to 49152 when the grid has at most
+  // one 16-row block per CU (more LDS per block then costs no occupancy) and
+  // tables, activations, 16 partial tiles and the magnitude slots fit in
+  // 160 KB.
+  if (p.m * p.d <= DEC_XL_MAX) return true;
+  if (multi) return (n_sets > 1 || scaled) && p.d <= DEC_XL_MAX;
+  const int64_t T = p.b == 2 ? 16 : p.k();
+  const int64_t lds = p.gpr * T * 256 + p.m * p.d * 2 + 16 * 1024 + 17 * 16 * 4;
+  return p.m < DEC_XT_MIN_M && p.m * p.d <= DEC_XL_MAX1 && (p.n + DEC_ROWS - 1) / DEC_ROWS <= 256 &&
+         lds <= 160 * 1024;
 }
 
 bool decode_multi_supported(const Problem& p, bool scaled) {

@@ -51,6 +51,23 @@ def test_fwd_rejects_bad_shapes(lib):
     assert fwd(lib, n=0) == EINVAL
 
 
+def test_fwd_workspace_follows_activation_staging(lib):
+    """(BF16, F16): the decode needs the row-exponent workspace exactly when it reads its activations per
+    slot; it stages them up to 32768 elements, and below 8 tokens up to 49152 on at most 4096 rows when the
+    block's LDS holds them."""
+    BF16, F16 = 2, 1
+    ws = lambda m, n, d, b, gpr, x=BF16: lib.sketch_matmul_fwd_workspace(m, n, d, b, gpr, x, F16)
+    assert ws(8, 64, 4096, 4, 8) == 0                  # 32768 elements
+    assert ws(9, 64, 4096, 4, 8) == 256                # more, and 8 tokens or more: per slot
+    assert ws(4, 64, 11008, 2, 8) == 0                 # 44032 elements, few rows
+    assert ws(4, 4096, 11008, 2, 8) == 0
+    assert ws(4, 4112, 11008, 2, 8) == 256             # more than one 16-row block per CU
+    assert ws(3, 40, 16384, 3, 4) == 0                 # 49152 elements
+    assert ws(5, 40, 16384, 3, 4) == 256
+    assert ws(4, 64, 12096, 4, 14) == 256              # 224-entry tables: 168 KB of LDS would not fit
+    assert ws(4, 64, 11008, 2, 8, x=F16) == 0          # no prescale for the (F16, F16) pair
+
+
 def test_fwd_rejects_bad_pointers_and_dtypes(lib):
     assert fwd(lib, idx=0) == EINVAL
     assert fwd(lib, lut=0) == EINVAL

@@ -105,6 +105,9 @@ def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
     # just over the activation staging limit (m * d > 32768: activations read
     # per slot), and a ragged row
     (4, 8, 40, 4096, 16), (2, 8, 50, 3072, 16), (3, 2, 17, 4096, 12), (4, 8, 70, 4096, 9), (4, 1, 24, 2080, 16),
+    # up to 49152 activation elements staged when m < 8 and the grid is at most one block per CU (a ragged
+    # row among them), and just past that
+    (4, 1, 40, 8224, 5), (2, 8, 64, 11008, 4), (2, 8, 64, 11008, 5),
 ])
 def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
@@ -507,7 +510,8 @@ def test_dx_rows_of_different_scales_bf16_f16():
 
 @pytest.mark.parametrize("b,gpr,n,d,m", [
     (4, 8, 256, 4096, 1), (4, 4, 64, 8192, 4),       # decode, activations staged in LDS
-    (4, 8, 64, 4096, 16), (3, 4, 40, 16384, 3),      # decode, activations read per slot (row exponents from the workspace)
+    (3, 4, 40, 16384, 3),                            # decode, 96 KB of activations staged (few tokens, few rows)
+    (4, 8, 64, 4096, 16), (3, 4, 40, 16384, 5),      # decode, activations read per slot (row exponents from the workspace)
     (4, 8, 200, 4096, 300), (2, 8, 130, 11008, 40),  # GEMM, 64- and 32-column K-steps
     (3, 1, 33, 96, 19),
 ])
@@ -541,7 +545,7 @@ _WINDOW_EDGES = [0.25, 0.25 - 2.0 ** -10, 65280.0, 65536.0]
 
 
 @pytest.mark.parametrize("peak", _WINDOW_EDGES)
-@pytest.mark.parametrize("d", [4096, 28672])
+@pytest.mark.parametrize("d", [4096, 28672, 40960])
 def test_decode_window_edge_rows_bf16_f16(peak, d):
     """One token whose largest magnitude sits at an edge of the unscaled window (the staging decode checks
     the window and, outside it, re-stages the activations prescaled): the output within the tolerance."""
