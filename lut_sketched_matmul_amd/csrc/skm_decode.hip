@@ -34,7 +34,10 @@
 // summed in LDS in wave order (deterministic) and stored once.
 //
 // Activations. When m*d <= 32768 the block stages X in LDS once and reads its
-// fragments there. Otherwise they come from global memory with each slot:
+// fragments there (below 8 tokens also up to 49152 elements when the grid has
+// at most one block per CU and the LDS fits, see
+// decode_stages_activations). Otherwise they come from global memory with
+// each slot:
 // below 8 tokens every lane loads its own fragment (64-byte runs of at most
 // m distinct rows). From 8 tokens on such a load spreads over 64 separate
 // 16-byte pieces of up to 16 rows, which the load unit handles piece by
