@@ -108,6 +108,8 @@ def _fwd16(idx, lut, X, b, gpr, x_dtype, lut_dtype, rows=None):
     # up to 49152 activation elements staged when m < 8 and the grid is at most one block per CU (a ragged
     # row among them), and just past that
     (4, 1, 40, 8224, 5), (2, 8, 64, 11008, 4), (2, 8, 64, 11008, 5),
+    # the LDS turn-around from its first token count on, with a ragged row
+    (4, 1, 40, 4128, 8),
 ])
 def test_fwd16_small(x_dtype, lut_dtype, b, gpr, n, d, m):
     idx, lut, X, _ = make_case(f"fwd16/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{m}", n, d, b, gpr, m,
