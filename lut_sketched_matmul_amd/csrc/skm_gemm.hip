@@ -481,6 +481,9 @@ constexpr uint32_t LDS64_A = 2u * 4u * 16u * 64u * 4u;    // 32768
 constexpr uint32_t LDS64_B = LDS64_A + 2u * A64_TILE;     // 98304
 constexpr uint32_t LDS64_TOTAL = LDS64_B + 2u * B64_TILE; // 163840
 
+// compile-time LDS buffer index of a K-step
+template <int V> struct buf_tag { static constexpr uint32_t value = V; };
+
 template <int B> struct Stage64 {
   uint32_t w[B];  // one whole unit
   u32x4 x[4];
@@ -580,11 +583,18 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
       Ln[4] = b.x; Ln[5] = b.y; Ln[6] = b.z; Ln[7] = b.w;
     };
     LutRegs<B> L;
-    auto stage = [&](const Stage64<B>& St, int j, auto md) __attribute__((always_inline)) {
+    // LDS write addresses of the thread's four weight chunks and of its first
+    // activation chunk (the other three are 64 rows = 8 KB further: the
+    // swizzle of a row repeats every 16 rows); the buffer is a compile-time
+    // offset, so every write takes its address from one of these registers
+    // plus an immediate
+    uint32_t bst[4];
+  #pragma unroll
+    for (int q = 0; q < 4; ++q) bst[q] = LDS64_B + swz128((uint32_t)r, 4u * hh + q);
+    const uint32_t ast = LDS64_A + swz128((uint32_t)(t >> 3), (uint32_t)(t & 7));
+    auto stage = [&](const Stage64<B>& St, int j, auto md, auto bufc) __attribute__((always_inline)) {
       constexpr int MD = decltype(md)::value;
-      const uint32_t buf = (uint32_t)(j & 1);
-      const uint32_t bb = LDS64_B + buf * B64_TILE;
-      const uint32_t ab = LDS64_A + buf * A64_TILE;
+      constexpr uint32_t buf = decltype(bufc)::value;
       if constexpr (B == 4) {
         // tables in registers; both operands in the K order of dequant8_b4
         const uint32_t g = group_of(j);
@@ -594,10 +604,10 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
           load_tab(g + 1 < (uint32_t)gpr ? g + 1 : g);
         }
   #pragma unroll
-        for (int q = 0; q < 4; ++q) st_q(bb + swz128((uint32_t)r, 4u * hh + q), mm::dequant8_b4(St.w[q], P));
+        for (int q = 0; q < 4; ++q) st_q(bst[q] + buf * B64_TILE, mm::dequant8_b4(St.w[q], P));
   #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+          const uint32_t a = ast + buf * A64_TILE + 8192u * c;
           if constexpr (SC && MD == 2) st_q(a, mm::cvt_quad_perm_scaled(St.x[c], xsc[c]));
           else if constexpr (SC && MD == 1) st_q(a, mm::cvt_quad_perm<TX, TL>(mm::add_quad(St.x[c], xk[c])));
           else st_q(a, mm::cvt_quad_perm<TX, TL>(St.x[c]));
@@ -616,13 +626,13 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
         }
         dequant16<B, 0>(h0, tb, lane4, o0);
         dequant16<B, 1>(h1, tb, lane4, o1);
-        st_q(bb + swz128((uint32_t)r, 4u * hh + 0u), u32x4{o0[0], o0[1], o0[2], o0[3]});
-        st_q(bb + swz128((uint32_t)r, 4u * hh + 1u), u32x4{o0[4], o0[5], o0[6], o0[7]});
-        st_q(bb + swz128((uint32_t)r, 4u * hh + 2u), u32x4{o1[0], o1[1], o1[2], o1[3]});
-        st_q(bb + swz128((uint32_t)r, 4u * hh + 3u), u32x4{o1[4], o1[5], o1[6], o1[7]});
+        st_q(bst[0] + buf * B64_TILE, u32x4{o0[0], o0[1], o0[2], o0[3]});
+        st_q(bst[1] + buf * B64_TILE, u32x4{o0[4], o0[5], o0[6], o0[7]});
+        st_q(bst[2] + buf * B64_TILE, u32x4{o1[0], o1[1], o1[2], o1[3]});
+        st_q(bst[3] + buf * B64_TILE, u32x4{o1[4], o1[5], o1[6], o1[7]});
   #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+          const uint32_t a = ast + buf * A64_TILE + 8192u * c;
           if constexpr (SC && MD == 2) st_q(a, mm::cvt_quad_scaled(St.x[c], xsc[c]));
           else if constexpr (SC && MD == 1) st_q(a, mm::cvt_quad<TX, TL>(mm::add_quad(St.x[c], xk[c])));
           else st_q(a, mm::cvt_quad<TX, TL>(St.x[c]));
@@ -631,9 +641,9 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     };
     // staging work of step k: tile k+1 into the other buffer, S refilled with
     // tile k+2, tables kept one group ahead
-    auto stage_step = [&](int k, auto md) __attribute__((always_inline)) {
+    auto stage_step = [&](int k, auto md, auto bufc) __attribute__((always_inline)) {
       if (k + 1 >= KS) return;
-      stage(S, k + 1, md);
+      stage(S, k + 1, md, bufc);
       if (k + 2 < KS) {
         load_stage(S, k + 2);
         if constexpr (B != 4) {
@@ -654,18 +664,30 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     for (int i = 0; i < 4; ++i)
   #pragma unroll
       for (int jj = 0; jj < 2; ++jj) mm::zero16(acc[i][jj]);
-    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-      const uint32_t buf = (uint32_t)(k & 1);
-      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+    // fragment read addresses of quarter ks in buffer 0; fragments 32 rows
+    // apart are 4 KB apart (the swizzle repeats every 16 rows), and the buffer
+    // is a compile-time offset: every read is one of these plus an immediate
+    uint32_t ard[4], brd[4];
   #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = ld_q(LDS64_A + buf * A64_TILE + swz128(arow + 32u * i, ch));
+    for (int ks = 0; ks < 4; ++ks) {
+      ard[ks] = LDS64_A + swz128(arow, (uint32_t)(2 * ks) + khalf);
+      brd[ks] = LDS64_B + swz128(brow, (uint32_t)(2 * ks) + khalf);
+    }
+    auto load_frags = [&](u32x4* fa, u32x4* fb, uint32_t buf, int ks) __attribute__((always_inline)) {
   #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(LDS64_B + buf * B64_TILE + swz128(brow + 32u * jj, ch));
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(ard[ks] + buf * A64_TILE + 4096u * i);
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) fb[jj] = ld_q(brd[ks] + buf * B64_TILE + 4096u * jj);
     };
-    auto mfma_step = [&](int k) {
+    // The matrix phase runs at raised wave priority, so that while the other
+    // wave of the SIMD stages, its vector work does not hold back the next
+    // MFMA issue.
+    auto mfma_step = [&](auto bufc) __attribute__((always_inline)) {
+      constexpr uint32_t buf = decltype(bufc)::value;
+      __builtin_amdgcn_s_setprio(1);
       u32x4 fa[4][4], fb[4][2];
   #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], buf, ks);
   #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
   #pragma unroll
@@ -689,6 +711,7 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     };
     const bool mfma_first = wave < 4;
 
@@ -698,7 +721,7 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
     if constexpr (B == 4) {
       load_tab(group_of(0));
       load_stage(S, 0);
-      stage(S, 0, md);
+      stage(S, 0, md, buf_tag<0>{});
       if (KS > 1) load_stage(S, 1);
     } else {
       load_lut<B, TL>(L, lut, grow, gpr, group_of(0), hh);
@@ -707,24 +730,32 @@ k_gemm_fwd64(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, c
       const bool new1 = KS > 1 && group_of(1) != group_of(0);
       if (new1) load_lut<B, TL>(L, lut, grow, gpr, group_of(1), hh);
       __syncthreads();
-      stage(S, 0, md);
+      stage(S, 0, md, buf_tag<0>{});
       if (KS > 1) load_stage(S, 1);
       if (new1) store_lut<B>(L, tab_base<B>(group_of(1) & 1u, rq), hh, lane4);
       if (KS > 2 && group_of(2) != group_of(1)) load_lut<B, TL>(L, lut, grow, gpr, group_of(2), hh);
     }
     __syncthreads();
 
-    for (int k = 0; k < KS; ++k) {
+    // step k multiplies buffer k & 1 and stages the other; two steps per trip
+    // keep both buffer offsets compile-time
+    auto step = [&](int k, auto cur, auto nxt) __attribute__((always_inline)) {
       if (mfma_first) {
-        mfma_step(k);
-        stage_step(k, md);
+        mfma_step(cur);
+        stage_step(k, md, nxt);
       } else {
-        stage_step(k, md);
+        stage_step(k, md, nxt);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(k);
+        mfma_step(cur);
       }
       __syncthreads();
+    };
+    int k = 0;
+    for (; k + 1 < KS; k += 2) {
+      step(k, buf_tag<0>{}, buf_tag<1>{});
+      step(k + 1, buf_tag<1>{}, buf_tag<0>{});
     }
+    if (k < KS) step(k, buf_tag<0>{}, buf_tag<1>{});
     store_tile<TX, SC && MD != 0>(acc, Y, rexp, m, n, m0, n0, wm, wn, lane, t);
   };
   if (!SC || mode == 0) run(mm::mode_tag<0>{});
