@@ -53,6 +53,10 @@ namespace {
 
 using namespace mm;
 
+// LDS buffer index of a K-step, known at compile time (buf_tag) or not (buf_rt)
+template <int V> struct buf_tag { static constexpr uint32_t value = V; };
+struct buf_rt { uint32_t value; };
+
 // ============================================================================
 // dX
 // ============================================================================
@@ -592,9 +596,14 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
         S.w[0] = q[0]; S.w[1] = q[1]; S.w[2] = q[2];
       }
     };
-    auto stage = [&](const Dx6Stage<B>& S, int j, auto md) __attribute__((always_inline)) {
+    // activation chunk c of the thread sits 64 rows = 8 KB after chunk 0 (the
+    // swizzle repeats every 16 rows); the buffer (bufc) is known at compile
+    // time, so every write is a register plus an immediate
+    const uint32_t ast = D6_A + swz128((uint32_t)(t >> 3), (uint32_t)(t & 7));
+    const uint32_t bst = D6_B + b_st;
+    auto stage = [&](const Dx6Stage<B>& S, int j, auto md, auto bufc) __attribute__((always_inline)) {
       constexpr int MD = decltype(md)::value;
-      const uint32_t buf = (uint32_t)(j & 1);
+      const uint32_t buf = bufc.value;
       const bool ok = (int64_t)j * D6_BK + r < n && col_ok;
       const u32x4 z = {0u, 0u, 0u, 0u};
       if constexpr (B == 4) {
@@ -602,9 +611,8 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
         // when dX is stored)
         mm::Planes16 P;
         mm::planes16(S.lut, P);
-        const uint32_t bb = D6_B + buf * D6_TB + b_st;
   #pragma unroll
-        for (int q = 0; q < 4; ++q) st_q(bb + 16u * q, ok ? mm::dequant8_b4(S.w[q], P) : z);
+        for (int q = 0; q < 4; ++q) st_q(bst + buf * D6_TB + 16u * q, ok ? mm::dequant8_b4(S.w[q], P) : z);
       } else {
       const uint32_t gk = (buf * NG + gsel) * T;
       uint32_t o0[8], o1[8];
@@ -615,16 +623,14 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
         dx_dequant<B>(S.w, 0, gk, lane4, o0);
         dx_dequant<B>(S.w + (B == 4 ? 2 : 1), 1, gk, lane4, o1);
       }
-      const uint32_t bb = D6_B + buf * D6_TB + b_st;
-      st_q(bb, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
-      st_q(bb + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
-      st_q(bb + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
-      st_q(bb + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
+      st_q(bst + buf * D6_TB, ok ? u32x4{o0[0], o0[1], o0[2], o0[3]} : z);
+      st_q(bst + buf * D6_TB + 16u, ok ? u32x4{o0[4], o0[5], o0[6], o0[7]} : z);
+      st_q(bst + buf * D6_TB + 32u, ok ? u32x4{o1[0], o1[1], o1[2], o1[3]} : z);
+      st_q(bst + buf * D6_TB + 48u, ok ? u32x4{o1[4], o1[5], o1[6], o1[7]} : z);
       }
-      const uint32_t ab = D6_A + buf * D6_TA;
   #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t a = ab + swz128((uint32_t)(64 * c + (t >> 3)), (uint32_t)(t & 7));
+        const uint32_t a = ast + buf * D6_TA + 8192u * c;
         if constexpr (SC && MD == 2) st_q(a, cvt_quad_scaled(S.y[c], ysc[c]));
         else if constexpr (SC && MD == 1) st_q(a, cvt_quad<TX, TL>(add_quad(S.y[c], yk[c])));
         else st_q(a, cvt_quad<TX, TL>(S.y[c]));
@@ -654,22 +660,34 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     for (int i = 0; i < 4; ++i)
   #pragma unroll
       for (int jj = 0; jj < 2; ++jj) zero16(acc[i][jj]);
-    auto load_frags = [&](u32x4* fa, u32x4* fb, int k, int ks) {
-      const uint32_t buf = (uint32_t)(k & 1);
-      const uint32_t ch = (uint32_t)(2 * ks) + khalf;
+    // Read addresses in buffer 0: A fragment rows of quarter ks (fragments 32
+    // rows apart are 4 KB apart), and the lane's element of the transposing
+    // weight reads (as ld_frag_tr places it). Buffer, quarter and fragment
+    // are compile-time offsets added to these registers.
+    uint32_t ard[4];
   #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = ld_q(D6_A + buf * D6_TA + swz128(arow + 32u * i, ch));
+    for (int ks = 0; ks < 4; ++ks) ard[ks] = D6_A + swz128(arow, (uint32_t)(2 * ks) + khalf);
+    const uint32_t ls = (uint32_t)lane & 15u;
+    const uint32_t btr = D6_B + (8u * ((uint32_t)lane >> 5) + (ls >> 2)) * DX_RSB +
+                         (16u * (((uint32_t)lane >> 4) & 1u) + 4u * (ls & 3u)) * 2u + 128u * (uint32_t)wn;
+    auto load_frags = [&](u32x4* fa, u32x4* fb, uint32_t buf, int ks) __attribute__((always_inline)) {
   #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        fb[jj] = ld_frag_tr(D6_B + buf * D6_TB + 16u * ks * DX_RSB + (64u * wn + 32u * jj) * 2u, DX_RSB,
-                            (uint32_t)lane);
+      for (int i = 0; i < 4; ++i) fa[i] = ld_q(ard[ks] + buf * D6_TA + 4096u * i);
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t a = btr + buf * D6_TB + 16u * ks * DX_RSB + 64u * jj;
+        const u32x2 lo = ld_tr(a), hi = ld_tr(a + 4u * DX_RSB);
+        fb[jj] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
     };
     // four 16-row quarters: each quarter's fragment reads are interleaved with
-    // the previous quarter's MFMAs
-    auto mfma_step = [&](int k) {
+    // the previous quarter's MFMAs (raising the wave priority of this phase, as
+    // the forward kernels do, measured no change here)
+    auto mfma_step = [&](auto bufc) __attribute__((always_inline)) {
+      const uint32_t buf = bufc.value;
       u32x4 fa[4][4], fb[4][2];
   #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], k, ks);
+      for (int ks = 0; ks < 4; ++ks) load_frags(fa[ks], fb[ks], buf, ks);
   #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
   #pragma unroll
@@ -691,13 +709,13 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
     Dx6Stage<B> S;
     // staging work of step k: tables of tile k+2 to LDS, tables of tile k+3
     // loaded; tile k+1 from S into LDS, S refilled with tile k+2
-    auto stage_step = [&](int k, auto md) __attribute__((always_inline)) {
+    auto stage_step = [&](int k, auto md, auto bufc) __attribute__((always_inline)) {
       if constexpr (B != 4) {
         if (k + 2 < KS) lut_store(k + 2);
         if (k + 3 < KS) lut_load(k + 3);
       }
       if (k + 1 < KS) {
-        stage(S, k + 1, md);
+        stage(S, k + 1, md, bufc);
         if (k + 2 < KS) load_stage(S, k + 2);
       }
     };
@@ -715,21 +733,24 @@ k_gemm_dx64(const TX* __restrict__ dY, const uint8_t* __restrict__ idx_packed, c
       if (KS > 2) lut_load(2);
       __syncthreads();
     }
-    stage(S, 0, md);
+    stage(S, 0, md, buf_tag<0>{});
     if (KS > 1) load_stage(S, 1);
     __syncthreads();
 
-    for (int k = 0; k < KS; ++k) {
+    // step k multiplies buffer k & 1 and stages the other (a one-step loop:
+    // unrolled by two, with compile-time buffer offsets, it measured slower)
+    auto step = [&](int k, auto cur, auto nxt) __attribute__((always_inline)) {
       if (mfma_first) {
-        mfma_step(k);
-        stage_step(k, md);
+        mfma_step(cur);
+        stage_step(k, md, nxt);
       } else {
-        stage_step(k, md);
+        stage_step(k, md, nxt);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(k);
+        mfma_step(cur);
       }
       __syncthreads();
-    }
+    };
+    for (int k = 0; k < KS; ++k) step(k, buf_rt{(uint32_t)(k & 1)}, buf_rt{(uint32_t)((k + 1) & 1)});
 
     if constexpr (SC && MD != 0) dx_factors_to_lds(rexp, m, m0, t);  // block-uniform
   #pragma unroll
