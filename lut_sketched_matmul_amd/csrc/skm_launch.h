@@ -65,6 +65,11 @@ hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const v
 // decode with one table set per token: luts [n_sets][n][gpr][2^b], lut_set [m]
 hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
                                const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s);
+// the same with set-interleaved tables (one LDS read looks up a weight for up
+// to 8 sets; at most 16 sets in use); not for the prescaled (BF16, F16) pair
+bool decode_sets_supported(const Problem& p, int n_sets, bool scaled);
+hipError_t launch_decode_sets(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
+                              const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s);
 
 // per-row exponents of the bf16 -> f16 operand prescale (skm_common.h) of a
 // bf16 matrix A [rows][cols] into e [rows]

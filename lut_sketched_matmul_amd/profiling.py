@@ -30,7 +30,8 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {
     "decode": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
                "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
-               "lut_sketched_matmul_amd/csrc/skm_decode.hip", "lut_sketched_matmul_amd/csrc/skm_rowscale.hip"],
+               "lut_sketched_matmul_amd/csrc/skm_decode.hip", "lut_sketched_matmul_amd/csrc/skm_decode_sets.hip",
+               "lut_sketched_matmul_amd/csrc/skm_rowscale.hip"],
     "gemm": ["include/sketch_matmul.h", "lut_sketched_matmul_amd/csrc/skm_abi.hip",
              "lut_sketched_matmul_amd/csrc/skm_common.h", "lut_sketched_matmul_amd/csrc/skm_launch.h",
              "lut_sketched_matmul_amd/csrc/skm_gemm_common.h", "lut_sketched_matmul_amd/csrc/skm_gemm.hip",

@@ -289,13 +289,18 @@ def test_fwd_multi_random_patterns(seed):
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("m", [5, 16])
 def test_fwd_multi_one_set_is_fwd(dt, m):
-    """All tokens on one set: the same numbers as the single-set forward (m = 16: the set takes two
-    passes of 8 staged tokens, the single-set kernel reads all 16 from memory)."""
+    """All tokens on one set: the single-set forward's numbers up to the rounding of the outputs. The
+    multi-set kernel with set-interleaved tables adds each token's products in MFMAs of 16 columns (its
+    contraction runs over column and set-parity pairs), the single-set decode in MFMAs of 32, so the fp32
+    sums round differently before the 16-bit output; both stay within the parity bound of the oracle."""
     b, gpr, n, d = 4, 8, 80, 4096
     idx, luts, X = _multi_case(f"multi1/{dt}/{m}", n, d, b, gpr, m, 3, dt, dt)
-    got = _fwd_multi(idx, luts, X, [1] * m, b, gpr, dt, dt)
-    ref = skm().sketch_matmul_fwd(to_dev(X, dt), to_dev(idx, "u8"), to_dev(luts[1], dt), b, gpr)
-    assert bool((got == ref).all())
+    got = to_f64(_fwd_multi(idx, luts, X, [1] * m, b, gpr, dt, dt))
+    ref = to_f64(skm().sketch_matmul_fwd(to_dev(X, dt), to_dev(idx, "u8"), to_dev(luts[1], dt), b, gpr))
+    want = oracle.forward(syn.to_float64(X, dt), idx, syn.to_float64(luts[1], dt), b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16 and oracle.rel_err(ref, want) <= TOL16
+    # no output differs by more than one unit in the last place of the largest output
+    assert oracle.rel_err(got, ref) <= 2.0 ** (-10 if dt == "f16" else -7), dt
 
 
 def test_fwd_multi_clamps_set_indices():
