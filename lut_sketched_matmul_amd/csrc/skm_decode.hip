@@ -960,9 +960,12 @@ hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const v
 
 hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
                                const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s) {
+  // one set: the single-set decode (every token on set 0); else
   // set-interleaved tables whenever they apply (every pair but the
   // prescaled one); otherwise one pass per set in use
-  if (decode_sets_supported(p, n_sets, x_dtype == DT_BF16 && lut_dtype == DT_F16))
+  const bool scaled = x_dtype == DT_BF16 && lut_dtype == DT_F16;
+  if (n_sets == 1 && !scaled) return decode_dispatch(X, x_dtype, idx, luts, lut_dtype, p, Y, s, SetArgs{});
+  if (decode_sets_supported(p, n_sets, scaled))
     return launch_decode_sets(X, x_dtype, idx, luts, lut_dtype, lut_set, n_sets, p, Y, s);
   SetArgs sa;
   sa.lut_set = lut_set;

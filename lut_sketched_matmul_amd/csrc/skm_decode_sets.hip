@@ -40,8 +40,12 @@
 // Work split as in the single-set decode: wave w handles slots (4 units = 128
 // columns) w, w + NW, ..., lane (j, q) loads unit 4s+q of row j with one
 // index load, and the A fragments of token t = lane % 16 come from global
-// memory (four 16-byte loads per slot). The waves' partial tiles are summed in
-// LDS in wave order (deterministic) and stored once.
+// memory: below 8 tokens each lane loads its own 64 bytes, from 8 tokens on
+// the wave loads the slot's [16 tokens][256 bytes] with neighbouring lanes on
+// neighbouring 16-byte pieces and turns them around in a private LDS buffer
+// (a load whose lanes touch 16 separate rows is served piece by piece). The
+// waves' partial tiles are summed in LDS in wave order (deterministic) and
+// stored once.
 //
 // Set slots: each wave computes the same schedule from lut_set: set indices
 // are clamped into [0, n_sets), the distinct sets are numbered in order of
@@ -57,8 +61,14 @@ constexpr int DS_ROWS = 16;     // weight rows per block
 constexpr int DS_NW = 16;       // waves per block
 constexpr int DS_MAX_ENTRIES = 224;   // table entries per row (entry byte: 8 bits)
 constexpr int DS_MAX_ENTRIES2 = 128;  // with two cells per (entry, row): doubled entry byte
+// XT: every wave turns its slot's [16 tokens][16 pieces of 16 bytes] around
+// in a private LDS buffer, rows padded by one piece (conflict-free reads)
+constexpr uint32_t DS_XT_ROW = 17 * 16;
+constexpr uint32_t DS_XT_WAVE = 16 * DS_XT_ROW;
+constexpr int DS_XT_MIN_M = 8;  // tokens from which the activations take the turn-around
 
 template <bool V> struct btag_ds { static constexpr bool value = V; };
+template <int V> struct ival_ds { static constexpr int value = V; };
 
 typedef __attribute__((address_space(3))) uint32_t ds_u32;
 typedef __attribute__((address_space(3))) u32x2 ds_u32x2;
@@ -124,11 +134,25 @@ struct DsSlot {
   bool ok;         // unit inside the row (RAGGED)
 };
 
+// Sources of the coalesced activation loads (XT): load i of a slot brings
+// token min(4i + l/16, m-1) (element offset off[i]) at columns 128 s + c8,
+// c8 = 8 (l % 16), clamped to dcol = d - 8 when the row ends inside the slot.
+template <typename TX>
+struct DsXt {
+  const TX* x = nullptr;
+  uint32_t off[4] = {0u, 0u, 0u, 0u};
+  uint32_t c8 = 0u;
+  uint32_t dcol = 0u;
+};
+
 // Index and activation loads of slot s (clamped to the last slot, and to the
 // last unit with RAGGED, so every load is unconditional and in range).
-template <int B, typename TX, bool RAGGED>
+// Without XT, lane (token t, quarter q) loads its own 32 activations of unit
+// 4s+q; with XT, the wave's four loads cover the slot's [16 tokens][128
+// columns] with neighbouring lanes on neighbouring 16-byte pieces.
+template <int B, typename TX, bool RAGGED, bool XT>
 __device__ __forceinline__ void ds_load(DsSlot<B, TX>& R, int64_t s, int64_t S, uint32_t U, uint32_t ug_magic,
-                                        int q, const uint8_t* rowp, const TX* xrow) {
+                                        int q, const uint8_t* rowp, const TX* xrow, const DsXt<TX>& xt) {
   const int64_t sc = s < S ? s : S - 1;
   uint32_t u = 4u * (uint32_t)sc + (uint32_t)q;
   R.ok = true;
@@ -137,9 +161,16 @@ __device__ __forceinline__ void ds_load(DsSlot<B, TX>& R, int64_t s, int64_t S, 
     u = u < U ? u : U - 1u;
   }
   load_unit<B>(rowp, u, R.w);
-  const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
+  if constexpr (XT) {
+    uint32_t col = 128u * (uint32_t)sc + xt.c8;
+    if constexpr (RAGGED) col = col < xt.dcol ? col : xt.dcol;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) R.x[h] = xp[h];
+    for (int i = 0; i < 4; ++i) R.x[i] = *reinterpret_cast<const u32x4*>(xt.x + xt.off[i] + col);
+  } else {
+    const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) R.x[h] = xp[h];
+  }
   R.gk = (ug_magic ? __umulhi(u, ug_magic) : u) << B;
 }
 
@@ -152,14 +183,15 @@ __device__ __forceinline__ void ds_wait_vmcnt() {
 
 // GW: sets per cell read (2, 4 or 8); OCT2: a second cell per (entry, row)
 // for set slots 8..15 (GW == 8 only).
-template <int B, int GW, bool OCT2, typename TX, typename TL, bool RAGGED>
+template <int B, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
 __global__ void __launch_bounds__(DS_NW * 64)
 k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ luts,
               const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride, int m, int64_t n, int64_t d,
               int gpr, uint32_t ug_magic, TX* __restrict__ Y) {
   // Dynamic LDS only (no static LDS: absolute addresses from 0): the cells
   // [entry][cell][row] of 16 bytes; after the last lookup, the waves'
-  // [NW][16][16] fp32 partial tiles in the same place.
+  // [NW][16][16] fp32 partial tiles in the same place; XT: the waves'
+  // activation buffers above both.
   extern __shared__ uint32_t smem[];
   constexpr int NW = DS_NW;
   constexpr int NP = (OCT2 ? 16 : GW) / 2;  // set pairs (accumulators)
@@ -178,9 +210,34 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   const int tokc = j < m ? j : m - 1;  // A operand row = token (clamped)
   const int E = gpr << B;              // table entries per row
 
-  // ---- set slots (every wave computes the same)
+  const uint32_t U = (uint32_t)(d / 32);
+  const int64_t S = (U + 3) / 4;  // slots per row
+  const uint8_t* rowp = idx_packed + (row_ok ? grow : n - 1) * (d * B / 8);
+  const TX* xrow = X + (int64_t)tokc * d;
+  DsXt<TX> xts;
+  if constexpr (XT) {
+    xts.x = X;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + q;
+      xts.off[i] = (uint32_t)((t < m ? t : m - 1) * d);
+    }
+    xts.c8 = 8u * (uint32_t)j;
+    xts.dcol = (uint32_t)d - 8u;
+  }
+
+  // The set indices are loaded first and the first slot's index and
+  // activation loads right after them, so that the index stream is under way
+  // while the table loads wait for the set indices (the loads complete in
+  // order, so waiting for the set indices does not wait for the slot's).
   const int tl = lane < m ? lane : m - 1;
   const int sv = lut_set[tl];
+  int64_t s0 = wave;
+  DsSlot<B, TX> R0, R1;
+  ds_load<B, TX, RAGGED, XT>(R0, s0, S, U, ug_magic, q, rowp, xrow, xts);
+  ds_load<B, TX, RAGGED, XT>(R1, s0 + NW, S, U, ug_magic, q, rowp, xrow, xts);
+
+  // ---- set slots (every wave computes the same)
   const int setv = sv < 0 ? 0 : (sv >= n_sets ? n_sets - 1 : sv);
   int ftok = tl;  // first token on this token's set
   for (int u = 0; u < m; ++u) {
@@ -193,16 +250,10 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   // lane k: the set of slot k (k < nd), then the last slot's set
   const int pushed = __builtin_amdgcn_ds_permute(slot * 4, setv);
   const int setk = __shfl(pushed, lane < nd ? lane : nd - 1, 64);
-  const int npairs = (nd + 1) >> 1;
-
-  const uint32_t U = (uint32_t)(d / 32);
-  const int64_t S = (U + 3) / 4;  // slots per row
-  const uint8_t* rowp = idx_packed + (row_ok ? grow : n - 1) * (d * B / 8);
-  const TX* xrow = X + (int64_t)tokc * d;
 
   // ---- table loads: unit (cell c, row jj, 4-entry chunk ec); rows vary
   // fastest, so a wave's cell writes cover 256 contiguous bytes per chunk
-  constexpr int UPT = 2;  // units per thread (the host checks the count)
+  constexpr int UPT = 1;  // units per thread (the host checks the count)
   const int EC = E >> 2;
   const int units = (OCT2 ? 2 : 1) * 16 * EC;
   u32x2 tv[UPT][GW];
@@ -219,10 +270,6 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
       tv[k][kk] = *reinterpret_cast<const u32x2*>(luts + (int64_t)st * set_stride + tr * E + 4 * ec);
     }
   }
-  // first slot's loads
-  int64_t s0 = wave;
-  DsSlot<B, TX> R0, R1;
-  ds_load<B, TX, RAGGED>(R0, s0, S, U, ug_magic, q, rowp, xrow);
   // cells: entry 4 ec + e of row jj for the set slots of cell c
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
@@ -243,12 +290,18 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
       }
     }
   }
-  // the table loads are consumed; settle them on every path, leaving the
-  // first slot's index and activation loads in flight
-  ds_wait_vmcnt<(B == 3 ? 3 : 1) + 4>();
+  // every load is consumed by now, the slots' (issued before the table
+  // loads) included, or has landed
   __syncthreads();
 
   const uint32_t jc = (uint32_t)j * 16u;
+  // XT: this wave's buffer, above the cells and the partial tiles
+  const uint32_t cells = (uint32_t)E * ES;
+  const uint32_t xt_w = (cells > NW * 1024u ? cells : NW * 1024u) + (uint32_t)wave * DS_XT_WAVE;
+  const uint32_t xt_st = xt_w + (uint32_t)q * DS_XT_ROW + (uint32_t)j * 16u;
+  const uint32_t xt_ld = xt_w + (uint32_t)j * DS_XT_ROW + (uint32_t)q * 64u;
+  (void)xt_st;
+  (void)xt_ld;
   // A fragment selectors: token's value into the half of its set's parity
   const int par = __shfl(slot, tokc, 64) & 1;
   const uint32_t sel_lo = par ? 0x01000C0Cu : 0x0C0C0100u;
@@ -259,8 +312,13 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   for (int p = 0; p < NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one MFMA chunk: 4 cell addresses (byte p of ent for p = 0..3, or given
-  // addresses for b = 3) and the 4 A dwords
-  auto chunk = [&](const uint32_t (&addr)[4], const u32x4& a, bool ok) {
+  // addresses for b = 3) and the 4 A dwords. NPA (compile time) pairs run
+  // without branches, so lookups and MFMAs of successive chunks overlap;
+  // pairs past the sets in use read valid (clamped) cells and their
+  // accumulators are never selected.
+  auto chunk = [&](auto npa, const uint32_t (&addr)[4], const u32x4& a, bool ok) {
+    constexpr int NPA = decltype(npa)::value;
+    constexpr int P1 = NPA < GW / 2 ? NPA : GW / 2;  // pairs in the first cell
     uint32_t g[4][GW / 2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ds_cell<GW>(addr[i], g[i]);
@@ -269,44 +327,50 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
       if (!ok) av = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int p = 0; p < (GW / 2 < NP ? GW / 2 : NP); ++p) {
-      if (p < npairs) {
-        u32x4 bv{g[0][p], g[1][p], g[2][p], g[3][p]};
+    for (int p = 0; p < P1; ++p) {
+      u32x4 bv{g[0][p], g[1][p], g[2][p], g[3][p]};
+      if constexpr (RAGGED) {
+        if (!ok) bv = u32x4{0u, 0u, 0u, 0u};
+      }
+      acc[p] = MF::run(__builtin_bit_cast(typename MF::vec, av), __builtin_bit_cast(typename MF::vec, bv), acc[p]);
+    }
+    if constexpr (NPA > 4) {
+      // (the second cells' lookups after the first cells' MFMAs: one set of
+      // lookup registers at a time)
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t g2[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds_cell<8>(addr[i] + 256u, g2[i]);
+#pragma unroll
+      for (int p = 0; p < NPA - 4; ++p) {
+        u32x4 bv{g2[0][p], g2[1][p], g2[2][p], g2[3][p]};
         if constexpr (RAGGED) {
           if (!ok) bv = u32x4{0u, 0u, 0u, 0u};
         }
-        acc[p] = MF::run(__builtin_bit_cast(typename MF::vec, av), __builtin_bit_cast(typename MF::vec, bv), acc[p]);
+        acc[4 + p] = MF::run(__builtin_bit_cast(typename MF::vec, av), __builtin_bit_cast(typename MF::vec, bv),
+                             acc[4 + p]);
       }
     }
-    if constexpr (OCT2) {
-      if (npairs > 4) {
-        uint32_t g2[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ds_cell<8>(addr[i] + 256u, g2[i]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (4 + p < npairs) {
-            u32x4 bv{g2[0][p], g2[1][p], g2[2][p], g2[3][p]};
-            if constexpr (RAGGED) {
-              if (!ok) bv = u32x4{0u, 0u, 0u, 0u};
-            }
-            acc[4 + p] =
-                MF::run(__builtin_bit_cast(typename MF::vec, av), __builtin_bit_cast(typename MF::vec, bv), acc[4 + p]);
-          }
-        }
-      }
-    }
+    // keep the next chunk's lookups behind this one's (bounded registers;
+    // the other waves of the SIMD cover the lookup latency)
+    if constexpr (GW > 2) __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto compute = [&](const DsSlot<B, TX>& Rc, int64_t s, auto tail) {
+  auto compute = [&](auto npa, const DsSlot<B, TX>& Rc, int64_t s, auto tail) {
     if (decltype(tail)::value && s >= S) return;  // wave-uniform
-    // the unit's 32 activations in the compute dtype: xd[k] = columns 2k, 2k+1
-    uint32_t xd[16];
+    if constexpr (XT) {
+      // a lane stores load i at row 4i + l/16, piece l%16, and reads its
+      // token's (row l%16) pieces 4q..4q+3: unit 4s+q, as a direct load
+      // would give (one wave's LDS accesses are carried out in order)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x4 v = ds_convert<TX, TL>(Rc.x[h]);
-      xd[4 * h] = v[0]; xd[4 * h + 1] = v[1]; xd[4 * h + 2] = v[2]; xd[4 * h + 3] = v[3];
+      for (int i = 0; i < 4; ++i) *(ds_u32x4*)(uintptr_t)(xt_st + (uint32_t)i * 4u * DS_XT_ROW) = Rc.x[i];
     }
+    // columns 8h..8h+7 of the unit in the compute dtype (dword i = columns
+    // 8h + 2i, 8h + 2i + 1), read where first needed
+    auto xq = [&](int h) -> u32x4 {
+      if constexpr (XT) return ds_convert<TX, TL>(*(const ds_u32x4*)(uintptr_t)(xt_ld + 16u * (uint32_t)h));
+      else return ds_convert<TX, TL>(Rc.x[h]);
+    };
     const uint32_t gk = OCT2 ? Rc.gk * 2u : Rc.gk;
     const uint32_t gk4 = __builtin_amdgcn_perm(0u, gk, 0u);  // gk (< 256) in all four bytes
     if constexpr (B == 4) {
@@ -314,22 +378,30 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t w = Rc.w[k];
-        const uint32_t ev = OCT2 ? (((w << 1) & 0x1E1E1E1Eu) | gk4) : ((w & 0x0F0F0F0Fu) | gk4);
-        const uint32_t od = OCT2 ? (((w >> 3) & 0x1E1E1E1Eu) | gk4) : (((w >> 4) & 0x0F0F0F0Fu) | gk4);
-        const uint32_t ae[4] = {ds_addr(ev, jc, 0), ds_addr(ev, jc, 1), ds_addr(ev, jc, 2), ds_addr(ev, jc, 3)};
-        const uint32_t ao[4] = {ds_addr(od, jc, 0), ds_addr(od, jc, 1), ds_addr(od, jc, 2), ds_addr(od, jc, 3)};
-        // columns 8k + 2i (low halves of xd[4k+i]) and 8k + 2i + 1 (high halves)
-        const u32x4 xe{__builtin_amdgcn_perm(0u, xd[4 * k], sel_lo), __builtin_amdgcn_perm(0u, xd[4 * k + 1], sel_lo),
-                       __builtin_amdgcn_perm(0u, xd[4 * k + 2], sel_lo), __builtin_amdgcn_perm(0u, xd[4 * k + 3], sel_lo)};
-        const u32x4 xo{__builtin_amdgcn_perm(0u, xd[4 * k], sel_hi), __builtin_amdgcn_perm(0u, xd[4 * k + 1], sel_hi),
-                       __builtin_amdgcn_perm(0u, xd[4 * k + 2], sel_hi), __builtin_amdgcn_perm(0u, xd[4 * k + 3], sel_hi)};
-        chunk(ae, xe, Rc.ok);
-        chunk(ao, xo, Rc.ok);
+        const u32x4 xk = xq(k);
+        // columns 8k + 2i (low halves of xk[i]), then 8k + 2i + 1 (high halves)
+        {
+          const uint32_t ev = OCT2 ? (((w << 1) & 0x1E1E1E1Eu) | gk4) : ((w & 0x0F0F0F0Fu) | gk4);
+          const uint32_t ae[4] = {ds_addr(ev, jc, 0), ds_addr(ev, jc, 1), ds_addr(ev, jc, 2), ds_addr(ev, jc, 3)};
+          const u32x4 xe{__builtin_amdgcn_perm(0u, xk[0], sel_lo), __builtin_amdgcn_perm(0u, xk[1], sel_lo),
+                         __builtin_amdgcn_perm(0u, xk[2], sel_lo), __builtin_amdgcn_perm(0u, xk[3], sel_lo)};
+          chunk(npa, ae, xe, Rc.ok);
+        }
+        {
+          const uint32_t od = OCT2 ? (((w >> 3) & 0x1E1E1E1Eu) | gk4) : (((w >> 4) & 0x0F0F0F0Fu) | gk4);
+          const uint32_t ao[4] = {ds_addr(od, jc, 0), ds_addr(od, jc, 1), ds_addr(od, jc, 2), ds_addr(od, jc, 3)};
+          const u32x4 xo{__builtin_amdgcn_perm(0u, xk[0], sel_hi), __builtin_amdgcn_perm(0u, xk[1], sel_hi),
+                         __builtin_amdgcn_perm(0u, xk[2], sel_hi), __builtin_amdgcn_perm(0u, xk[3], sel_hi)};
+          chunk(npa, ao, xo, Rc.ok);
+        }
       }
     } else if constexpr (B == 2) {
       // word k: fields 16k..16k+15; chunk i: fields 16k + i + 4c in byte c
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
+        const u32x4 xa = xq(2 * k), xb = xq(2 * k + 1);
+        // column 16k + i + 4c = half (i & 1) of local dword 2c + (i >> 1)
+        const uint32_t xl[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t w = Rc.w[k];
@@ -337,29 +409,33 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
                                   : ((w >> (2 * i)) & 0x03030303u);
           const uint32_t ent = f | gk4;
           const uint32_t a[4] = {ds_addr(ent, jc, 0), ds_addr(ent, jc, 1), ds_addr(ent, jc, 2), ds_addr(ent, jc, 3)};
-          // column 16k + i + 4c = half (i & 1) of xd[8k + 2c + (i >> 1)]
           const uint32_t sl = (i & 1) ? sel_hi : sel_lo;
-          const u32x4 xa{__builtin_amdgcn_perm(0u, xd[8 * k + (i >> 1)], sl),
-                         __builtin_amdgcn_perm(0u, xd[8 * k + 2 + (i >> 1)], sl),
-                         __builtin_amdgcn_perm(0u, xd[8 * k + 4 + (i >> 1)], sl),
-                         __builtin_amdgcn_perm(0u, xd[8 * k + 6 + (i >> 1)], sl)};
-          chunk(a, xa, Rc.ok);
+          const u32x4 xv{__builtin_amdgcn_perm(0u, xl[(i >> 1)], sl), __builtin_amdgcn_perm(0u, xl[2 + (i >> 1)], sl),
+                         __builtin_amdgcn_perm(0u, xl[4 + (i >> 1)], sl), __builtin_amdgcn_perm(0u, xl[6 + (i >> 1)], sl)};
+          chunk(npa, a, xv, Rc.ok);
         }
       }
     } else {
       // 3-bit fields at any bit offset: chunk h = fields 4h..4h+3
       const uint32_t base = (gk << 8) | jc;
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        uint32_t a[4];
+      for (int hp = 0; hp < 4; ++hp) {
+        const u32x4 xk = xq(hp);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t e = unit_field<3>(Rc.w, 4 * h + i);
-          a[i] = base + (e << (OCT2 ? 9 : 8));
+        for (int hh = 0; hh < 2; ++hh) {
+          const int h = 2 * hp + hh;
+          uint32_t a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t e = unit_field<3>(Rc.w, 4 * h + i);
+            a[i] = base + (e << (OCT2 ? 9 : 8));
+          }
+          // columns 4h..4h+3: dwords 2hh, 2hh + 1 of xk
+          const u32x4 xv{__builtin_amdgcn_perm(0u, xk[2 * hh], sel_lo), __builtin_amdgcn_perm(0u, xk[2 * hh], sel_hi),
+                         __builtin_amdgcn_perm(0u, xk[2 * hh + 1], sel_lo),
+                         __builtin_amdgcn_perm(0u, xk[2 * hh + 1], sel_hi)};
+          chunk(npa, a, xv, Rc.ok);
         }
-        const u32x4 xa{__builtin_amdgcn_perm(0u, xd[2 * h], sel_lo), __builtin_amdgcn_perm(0u, xd[2 * h], sel_hi),
-                       __builtin_amdgcn_perm(0u, xd[2 * h + 1], sel_lo), __builtin_amdgcn_perm(0u, xd[2 * h + 1], sel_hi)};
-        chunk(a, xa, Rc.ok);
       }
     }
   };
@@ -367,22 +443,24 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   // slots of this wave: at least one (possibly past the row end: skipped)
   const int64_t nb_raw = (S - s0 + NW - 1) / NW;
   const int64_t nb = nb_raw > 1 ? nb_raw : 1;
-  // two register sets, one exit, unconditional loads (exact load counts)
-  int64_t bi = 0;
-  for (; bi + 2 < nb; bi += 2) {
-    ds_load<B, TX, RAGGED>(R1, s0 + NW, S, U, ug_magic, q, rowp, xrow);
-    compute(R0, s0, btag_ds<false>{});
-    ds_load<B, TX, RAGGED>(R0, s0 + 2 * NW, S, U, ug_magic, q, rowp, xrow);
-    compute(R1, s0 + NW, btag_ds<false>{});
-    s0 += 2 * NW;
-  }
-  if (nb - bi == 2) {
-    ds_load<B, TX, RAGGED>(R1, s0 + NW, S, U, ug_magic, q, rowp, xrow);
-    compute(R0, s0, btag_ds<false>{});
-    compute(R1, s0 + NW, btag_ds<true>{});
-  } else {
-    compute(R0, s0, btag_ds<true>{});
-  }
+  // two register sets, two slots in flight, one exit, unconditional loads
+  // (exact load counts; the last iteration's loads of slots past the end
+  // are clamped and left unused)
+  auto run = [&](auto npa) {
+    int64_t bi = 0;
+    for (; bi + 2 < nb; bi += 2) {
+      compute(npa, R0, s0, btag_ds<false>{});
+      ds_load<B, TX, RAGGED, XT>(R0, s0 + 2 * NW, S, U, ug_magic, q, rowp, xrow, xts);
+      compute(npa, R1, s0 + NW, btag_ds<false>{});
+      ds_load<B, TX, RAGGED, XT>(R1, s0 + 3 * NW, S, U, ug_magic, q, rowp, xrow, xts);
+      s0 += 2 * NW;
+    }
+    compute(npa, R0, s0, btag_ds<true>{});
+    if (nb - bi == 2) compute(npa, R1, s0 + NW, btag_ds<true>{});
+  };
+  // every pair of the capacity (chosen on the host from min(m, n_sets)), in
+  // use or not: one branch-free instance of the slot loop
+  run(ival_ds<NP>{});
 
   // ---- each output keeps its token's pair: lane l holds D[token 4q + r][row j]
   f32x4 out = acc[0];
@@ -412,32 +490,38 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   }
 }
 
+template <int B, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
+hipError_t sets_kernel(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
+                       const Problem& p, TX* Y, hipStream_t s, uint32_t magic, size_t lds) {
+  const auto kern = k_decode_sets<B, GW, OCT2, TX, TL, RAGGED, XT>;
+  static const hipError_t prep = prepare_kernel((const void*)kern, lds);
+  if (prep != hipSuccess) return prep;
+  const dim3 grid((unsigned)((p.n + DS_ROWS - 1) / DS_ROWS));
+  hipLaunchKernelGGL(kern, grid, dim3(DS_NW * 64), lds, s, X, idx, luts, lut_set, n_sets, p.n * ((int64_t)p.gpr << p.b),
+                     (int)p.m, p.n, p.d, p.gpr, magic, Y);
+  return hipGetLastError();
+}
+
 template <int B, int GW, bool OCT2, typename TX, typename TL>
 hipError_t sets_launch(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
                        const Problem& p, TX* Y, hipStream_t s) {
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   // u / ug == umulhi(u, magic) for u * ug < 2^32; ug == 1 is passed as 0
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
-  const int64_t E = (int64_t)p.gpr << p.b;
-  const size_t cells = (size_t)E * (OCT2 ? 512 : 256);
+  const size_t cells = (size_t)((int64_t)p.gpr << p.b) * (OCT2 ? 512 : 256);
   const size_t part = (size_t)DS_NW * 256 * 4;
-  const size_t lds = cells > part ? cells : part;
-  const dim3 grid((unsigned)((p.n + DS_ROWS - 1) / DS_ROWS));
-  const int64_t set_stride = p.n * E;
-  if (p.units() % 4 != 0) {
-    const auto kern = k_decode_sets<B, GW, OCT2, TX, TL, true>;
-    static const hipError_t prep = prepare_kernel((const void*)kern, lds);
-    if (prep != hipSuccess) return prep;
-    hipLaunchKernelGGL(kern, grid, dim3(DS_NW * 64), lds, s, X, idx, luts, lut_set, n_sets, set_stride, (int)p.m,
-                       p.n, p.d, p.gpr, magic, Y);
+  const bool xt = p.m >= DS_XT_MIN_M;
+  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)DS_NW * DS_XT_WAVE : 0);
+  const bool ragged = p.units() % 4 != 0;
+  if (xt)
+    return ragged ? sets_kernel<B, GW, OCT2, TX, TL, true, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, GW, OCT2, TX, TL, false, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+  if constexpr (OCT2) {
+    return hipErrorNotSupported;  // (more than 8 sets means more than 8 tokens: always the turn-around)
   } else {
-    const auto kern = k_decode_sets<B, GW, OCT2, TX, TL, false>;
-    static const hipError_t prep = prepare_kernel((const void*)kern, lds);
-    if (prep != hipSuccess) return prep;
-    hipLaunchKernelGGL(kern, grid, dim3(DS_NW * 64), lds, s, X, idx, luts, lut_set, n_sets, set_stride, (int)p.m,
-                       p.n, p.d, p.gpr, magic, Y);
+    return ragged ? sets_kernel<B, GW, OCT2, TX, TL, true, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, GW, OCT2, TX, TL, false, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
   }
-  return hipGetLastError();
 }
 
 template <int B, typename TX, typename TL>
@@ -463,13 +547,15 @@ hipError_t sets_t(const TX* X, const uint8_t* idx, const TL* luts, const int32_t
 }  // namespace
 
 bool decode_sets_supported(const Problem& p, int n_sets, bool scaled) {
-  if (scaled || p.m < 1 || p.m > 16 || n_sets < 1) return false;
+  // one token uses one set: the single-pass multi-set decode serves it with
+  // the single-set lookups (no parity halves, activations staged)
+  if (scaled || p.m < 2 || p.m > 16 || n_sets < 2) return false;
   const int64_t E = (int64_t)p.gpr << p.b;
   const int64_t bound = p.m < n_sets ? p.m : n_sets;
   const int64_t maxe = bound > 8 ? DS_MAX_ENTRIES2 : DS_MAX_ENTRIES;
-  // table units (cells x rows x 4-entry chunks) within two per thread
+  // table units (cells x rows x 4-entry chunks): one per thread
   const int64_t units = (bound > 8 ? 2 : 1) * 16 * (E / 4);
-  return E <= maxe && units <= 2 * DS_NW * 64 && p.d <= (int64_t(1) << 20);
+  return E <= maxe && units <= DS_NW * 64 && p.d <= (int64_t(1) << 20);
 }
 
 hipError_t launch_decode_sets(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
