@@ -328,6 +328,61 @@ def test_fwd_multi_selection_bit_exact(b):
         assert np.array_equal(got[t], W[:, cols[t]]), t
 
 
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("b,gpr,n,d,sets,n_sets", [
+    # eight sets in use: one 128-bit lookup per weight serves them all
+    (4, 8, 48, 4096, [0, 1, 2, 3, 4, 5, 6, 7], 8),
+    (2, 2, 40, 2752, [7, 6, 5, 4, 3, 2, 1, 0, 7, 6], 8),        # ragged 128-column slots
+    (3, 4, 33, 1536, [3, 1, 4, 1, 5, 0, 2, 6, 5, 3, 5], 7),
+    # more than eight sets: a second cell per (entry, row)
+    (4, 8, 64, 4096, list(range(16)), 16),
+    (4, 8, 70, 4096, [15 - t for t in range(16)], 16),
+    (2, 2, 40, 2752, [(5 * t) % 13 for t in range(13)], 13),    # ragged slots
+    (4, 1, 24, 1376, [(7 * t) % 16 for t in range(16)], 16),    # ragged slots, one group
+    (3, 4, 37, 1536, [(3 * t + 1) % 11 for t in range(12)], 11),
+    (4, 2, 16, 1024, [t % 9 for t in range(16)], 9),
+    # capacity above the sets in use (the pairs past them are not kept)
+    (4, 8, 32, 4096, [2, 2, 9, 9, 2, 9, 2, 2, 9, 9, 2, 9, 2, 9, 9, 2], 12),
+    (4, 8, 32, 4096, [1, 1, 1, 1, 1, 0, 0, 0], 8),
+    (2, 4, 24, 2048, [5, 3, 5, 3, 5, 3, 5, 3, 5, 3], 10),
+    # entry limits: 224 per row with at most 8 sets, 128 with more; beyond
+    # that, one round of lookups per set
+    (4, 14, 32, 14336, [0, 1, 2, 3, 4, 5], 6),
+    (3, 16, 32, 4096, list(range(12)), 12),
+    (4, 14, 32, 14336, list(range(10)), 10),
+    # out-of-range set indices (clamped) with two cells
+    (4, 8, 40, 4096, [-5, 0, 20, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 17], 16),
+])
+def test_fwd_multi_set_cells(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
+    """Set-interleaved tables (SpaLLM section 2.3, several adapters over one mapping): up to eight sets per
+    lookup and sixteen with two cells per (entry, row), activations loaded per lane below 8 tokens and
+    turned around in LDS from 8 on; the oracle takes the clamped set indices."""
+    clamped = [min(max(v, 0), n_sets - 1) for v in sets]
+    idx, luts, X = _multi_case(f"multicell/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}/{len(sets)}", n, d, b,
+                               gpr, len(sets), n_sets, x_dtype, lut_dtype)
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype))
+    want = oracle.forward_multi(syn.to_float64(X, x_dtype), idx, syn.to_float64(luts, lut_dtype), clamped, b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("m,n_sets", [(8, 8), (16, 16), (12, 16)])
+def test_fwd_multi_set_cells_selection_exact(b, m, n_sets):
+    """One-hot activation rows through the set-interleaved lookups (one cell, two cells): token t reads
+    W_{s(t)}[i, j_t] exactly, for every set slot and parity."""
+    gpr, n, d = 4, 40, 2048
+    idx, luts, _ = _multi_case(f"multicellsel/{b}/{m}/{n_sets}", n, d, b, gpr, 1, n_sets, "f16", "f16")
+    cols = np.random.default_rng(10 * b + m).choice(d, m, replace=False)
+    sets = [(5 * t + 3) % n_sets for t in range(m)]
+    X = np.zeros((m, d), dtype=np.float32)
+    X[np.arange(m), cols] = 1.0
+    got = to_f64(_fwd_multi(idx, luts, syn.to_storage(X, "f16"), sets, b, gpr, "f16", "f16"))
+    L = syn.to_float64(luts, "f16")
+    for t in range(m):
+        W = oracle.dequantize(idx, L[sets[t]], d, b, gpr)
+        assert np.array_equal(got[t], W[:, cols[t]]), t
+
+
 @pytest.mark.parametrize("b", [2, 3, 4])
 def test_fwd_identity_exact(b):
     """SpaLLM section 2.4: the identity sketched with the two values 0 and 1."""
