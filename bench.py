@@ -227,14 +227,21 @@ def bench_multi(torch, skm, steps, warmup):
         t = w.make(shape, b, m)
         X = dev(torch, t["X"], w.x_dtype)
         idx = dev(torch, t["idx_packed"], "u8")
-        luts = dev(torch, np.stack([syn.random_lut(f"bench-multi/{m}/{n_sets}/{s}", shape.n, w.gpr, b,
-                                                   w.lut_sigma, w.lut_dtype) for s in range(n_sets)]), w.lut_dtype)
+        luts_np = np.stack([syn.random_lut(f"bench-multi/{m}/{n_sets}/{s}", shape.n, w.gpr, b, w.lut_sigma,
+                                           w.lut_dtype) for s in range(n_sets)])
+        luts = dev(torch, luts_np, w.lut_dtype)
         sets = [tt % n_sets for tt in range(m)]
         lut_set = torch.tensor(sets, dtype=torch.int32, device="cuda:0")
         Y = torch.empty((m, shape.n), dtype=X.dtype, device="cuda:0")
         rot = Rotation(torch, idx, luts)
         total = time_launches(torch, lambda: skm.sketch_matmul_fwd_multi(X, *rot.next(), lut_set, b, w.gpr, out=Y),
                               steps, warmup)
+        # parity sample: every token on sampled rows (the rotated copies hold the same values)
+        rows = sample_ids(shape.n, 224, 70 + m + n_sets)
+        CHECKS.append({"name": f"decode_multi_lut_7b_attn.m{m}_sets{n_sets}", "kind": "fwdmulti", "X": t["X"],
+                       "idx": t["idx_packed"][rows], "lut": luts_np[:, rows], "sets": sets, "b": b, "gpr": w.gpr,
+                       "x_dtype": w.x_dtype, "lut_dtype": w.lut_dtype,
+                       "got": Y.float().cpu().numpy()[:, rows].astype(np.float64)})
         # one single-set launch per set, on that set's tokens
         Xs = [X[[tt for tt in range(m) if sets[tt] == s]].contiguous() for s in range(n_sets)]
         Ys = [torch.empty((x.shape[0], shape.n), dtype=X.dtype, device="cuda:0") for x in Xs]
@@ -654,6 +661,9 @@ def _score_checks(oracle, syn, checks):
         L64 = syn.to_float64(c["lut"], c["lut_dtype"]) if "lut" in c else None
         if c["kind"] == "fwd":
             want = oracle.forward(syn.to_float64(c["X"], c["x_dtype"]), c["idx"], L64, c["b"], c["gpr"])
+        elif c["kind"] == "fwdmulti":
+            want = oracle.forward_multi(syn.to_float64(c["X"], c["x_dtype"]), c["idx"], L64, c["sets"], c["b"],
+                                        c["gpr"])
         elif c["kind"] == "dx":
             d = c["idx"].shape[1] * 8 // c["b"]
             W = oracle.dequantize(c["idx"], L64, d, c["b"], c["gpr"])
