@@ -131,18 +131,19 @@ size_t sketch_matmul_fwd_workspace(int64_t m, int64_t n, int64_t d, int b, int g
  *            [0, n_sets) are clamped to that range
  *   Y[t][i] = sum_j X[t][j] * luts[lut_set[t]][i][j/G][idx[i][j]]
  * Decode-sized batches (1 <= m <= 16, tables of a 16-row block within the
- * decode limit) with a 16-bit dtype pair; other sizes, the fp32 pair and
- * (BF16, F16) rows of more than 32768 columns return SKM_EUNSUPPORTED. Row
- * exponents of the (BF16, F16) pair are found inside the kernel, so no
- * workspace is needed. The index stream is read from memory once and each set
- * that some token uses adds its tables. Table lookups: with (F16, F16),
- * (F16, BF16) and (BF16, BF16), m >= 2 and n_sets >= 2, when at most 224
- * table entries per row (gpr * 2^b) are used, or at most 128 when more than
- * 8 sets can occur (min(m, n_sets) > 8), the tables of all sets in use are
- * interleaved in LDS and one lookup serves up to 8 sets (n_sets == 1 is the
- * single-set forward); otherwise, and always with (BF16, F16), each set in
- * use takes one round of lookups (one per 32768 / d of its tokens when more
- * of them than that share the set). lut_set must
+ * decode limit) with a 16-bit dtype pair; other sizes, the fp32 pair and, for
+ * (BF16, F16), rows of more than 32768 columns with one token (or with more
+ * than 8 tokens and more than 128 table entries per row) return
+ * SKM_EUNSUPPORTED. Row exponents of the (BF16, F16) pair are found inside the
+ * kernel, so no workspace is needed. The index stream is read from memory once
+ * and each set that some token uses adds its tables. Table lookups: from two
+ * tokens on, with n_sets >= 2 (any n_sets for (BF16, F16)), when at most 224
+ * table entries per row (gpr * 2^b) are used, or at most 128 when more than 8
+ * sets can occur (min(m, n_sets) > 8), the tables of all sets in use are
+ * interleaved in LDS and one lookup serves up to 8 sets; n_sets == 1 with the
+ * other pairs is the single-set forward; otherwise each set in use takes one
+ * round of lookups (one per 32768 / d of its tokens when more of them than
+ * that share the set). lut_set must
  * be 4-byte aligned, the other pointers 16-byte aligned; Y must not overlap
  * any input. m == 0 returns OK.
  */

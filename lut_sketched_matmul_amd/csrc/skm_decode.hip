@@ -942,7 +942,12 @@ bool decode_stages_activations(const Problem& p, bool multi, int n_sets, bool sc
 }
 
 bool decode_multi_supported(const Problem& p, bool scaled) {
-  return decode_supported(p) && (!scaled || p.d <= DEC_XL_MAX);
+  // the prescaled pair stages its activations in the one-pass-per-set kernel
+  // (rows of at most 32768 columns); the set-interleaved kernel (m >= 2)
+  // finds its row exponents without staging, and takes every set count when
+  // the entries per row fit two cells (a set count above 8 needs that)
+  const int64_t E = (int64_t)p.gpr << p.b;
+  return decode_supported(p) && (!scaled || p.d <= DEC_XL_MAX || (p.m >= 2 && E <= (p.m > 8 ? 128 : 224)));
 }
 
 bool decode_supported(const Problem& p) {

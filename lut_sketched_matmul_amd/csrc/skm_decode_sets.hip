@@ -106,6 +106,19 @@ __device__ __forceinline__ u32x4 ds_convert(u32x4 v) {
   }
 }
 
+// 8 bf16 activations -> f16 with every value multiplied by sc (a power of two)
+// first: the per-row prescale of the (BF16, F16) pair (skm_common.h)
+__device__ __forceinline__ u32x4 ds_convert_scaled(u32x4 v, float sc) {
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = __builtin_bit_cast(float, v[k] << 16) * sc;
+    const float hi = __builtin_bit_cast(float, v[k] & 0xFFFF0000u) * sc;
+    o[k] = (uint32_t)bits16((half_t)lo) | ((uint32_t)bits16((half_t)hi) << 16);
+  }
+  return o;
+}
+
 // LDS read of one cell: GW sets' 16-bit values, GW / 2 dwords
 template <int GW>
 __device__ __forceinline__ void ds_cell(uint32_t addr, uint32_t* g) {
@@ -197,6 +210,9 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   constexpr int NP = (OCT2 ? 16 : GW) / 2;  // set pairs (accumulators)
   constexpr uint32_t ES = OCT2 ? 512u : 256u;  // bytes per entry
   typedef ds_mfma<TL> MF;
+  // (BF16, F16): each token row is prescaled by 2^-e before the f16
+  // conversion and its results multiplied by 2^e (skm_common.h)
+  constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   static_assert(GW == 2 || GW == 4 || GW == 8, "cell reads of 2, 4 or 8 sets");
   static_assert(!OCT2 || GW == 8, "a second cell only after a full first one");
 
@@ -290,14 +306,34 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
       }
     }
   }
+  // LDS above the cells (or the partial tiles, when larger): the XT buffers,
+  // then (SC) the largest magnitude of each token row
+  const uint32_t cells = (uint32_t)E * ES;
+  const uint32_t above = cells > NW * 1024u ? cells : NW * 1024u;
+  const uint32_t rmax = above + (XT ? NW * DS_XT_WAVE : 0u);
+  if constexpr (SC) {
+    // wave w < m scans token row w (wave-uniform branch)
+    if (wave < m) {
+      const TX* xr = X + (int64_t)wave * d;
+      uint32_t mx = 0u;
+      for (int64_t c = (int64_t)lane * 8; c < d; c += 512) {
+        const uint32_t v = absmax8_bf16(*reinterpret_cast<const u32x4*>(xr + c));
+        mx = mx > v ? mx : v;
+      }
+      mx = wave_max_to_lane63(mx);
+      if (lane == 63) *(ds_u32*)(uintptr_t)(rmax + (uint32_t)wave * 4u) = mx;
+    }
+  }
   // every load is consumed by now, the slots' (issued before the table
   // loads) included, or has landed
   __syncthreads();
 
   const uint32_t jc = (uint32_t)j * 16u;
+  // SC: 2^-e of this lane's A row (its token)
+  const float xsc = SC ? pow2f(-row_exp_of(*(const ds_u32*)(uintptr_t)(rmax + (uint32_t)tokc * 4u))) : 1.0f;
+  (void)xsc;
   // XT: this wave's buffer, above the cells and the partial tiles
-  const uint32_t cells = (uint32_t)E * ES;
-  const uint32_t xt_w = (cells > NW * 1024u ? cells : NW * 1024u) + (uint32_t)wave * DS_XT_WAVE;
+  const uint32_t xt_w = above + (uint32_t)wave * DS_XT_WAVE;
   const uint32_t xt_st = xt_w + (uint32_t)q * DS_XT_ROW + (uint32_t)j * 16u;
   const uint32_t xt_ld = xt_w + (uint32_t)j * DS_XT_ROW + (uint32_t)q * 64u;
   (void)xt_st;
@@ -368,8 +404,9 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
     // columns 8h..8h+7 of the unit in the compute dtype (dword i = columns
     // 8h + 2i, 8h + 2i + 1), read where first needed
     auto xq = [&](int h) -> u32x4 {
-      if constexpr (XT) return ds_convert<TX, TL>(*(const ds_u32x4*)(uintptr_t)(xt_ld + 16u * (uint32_t)h));
-      else return ds_convert<TX, TL>(Rc.x[h]);
+      const u32x4 v = XT ? *(const ds_u32x4*)(uintptr_t)(xt_ld + 16u * (uint32_t)h) : Rc.x[h];
+      if constexpr (SC) return ds_convert_scaled(v, xsc);
+      else return ds_convert<TX, TL>(v);
     };
     const uint32_t gk = OCT2 ? Rc.gk * 2u : Rc.gk;
     const uint32_t gk4 = __builtin_amdgcn_perm(0u, gk, 0u);  // gk (< 256) in all four bytes
@@ -485,6 +522,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < NW; ++wv) sum += red[wv * 256 + t];
+      if constexpr (SC) sum *= pow2f(row_exp_of(*(const ds_u32*)(uintptr_t)(rmax + (uint32_t)token * 4u)));
       Y[(int64_t)token * n + row0 + rr] = from_f32<TX>(sum);
     }
   }
@@ -511,7 +549,8 @@ hipError_t sets_launch(const TX* X, const uint8_t* idx, const TL* luts, const in
   const size_t cells = (size_t)((int64_t)p.gpr << p.b) * (OCT2 ? 512 : 256);
   const size_t part = (size_t)DS_NW * 256 * 4;
   const bool xt = p.m >= DS_XT_MIN_M;
-  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)DS_NW * DS_XT_WAVE : 0);
+  // + 16 row maxima of the (BF16, F16) prescale
+  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)DS_NW * DS_XT_WAVE : 0) + 64;
   const bool ragged = p.units() % 4 != 0;
   if (xt)
     return ragged ? sets_kernel<B, GW, OCT2, TX, TL, true, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
@@ -549,7 +588,8 @@ hipError_t sets_t(const TX* X, const uint8_t* idx, const TL* luts, const int32_t
 bool decode_sets_supported(const Problem& p, int n_sets, bool scaled) {
   // one token uses one set: the single-pass multi-set decode serves it with
   // the single-set lookups (no parity halves, activations staged)
-  if (scaled || p.m < 2 || p.m > 16 || n_sets < 2) return false;
+  // (the (BF16, F16) pair with one set: every token on set 0, still prescaled)
+  if (p.m < 2 || p.m > 16 || n_sets < 1 || (n_sets < 2 && !scaled)) return false;
   const int64_t E = (int64_t)p.gpr << p.b;
   const int64_t bound = p.m < n_sets ? p.m : n_sets;
   const int64_t maxe = bound > 8 ? DS_MAX_ENTRIES2 : DS_MAX_ENTRIES;
@@ -566,7 +606,7 @@ hipError_t launch_decode_sets(const void* X, int x_dtype, const uint8_t* idx, co
     return sets_t((const half_t*)X, idx, (const bf16_t*)luts, lut_set, n_sets, p, (half_t*)Y, s);
   if (x_dtype == DT_BF16 && lut_dtype == DT_BF16)
     return sets_t((const bf16_t*)X, idx, (const bf16_t*)luts, lut_set, n_sets, p, (bf16_t*)Y, s);
-  return hipErrorNotSupported;  // (BF16, F16) takes the prescaling multi-pass decode
+  return sets_t((const bf16_t*)X, idx, (const half_t*)luts, lut_set, n_sets, p, (bf16_t*)Y, s);  // (BF16, F16)
 }
 
 }  // namespace skm

@@ -97,6 +97,10 @@ def test_fwd_multi_rejects_bad_arguments(lib):
     assert fwd_multi(lib, sets=0x50000002) == EALIGN
     assert fwd_multi(lib, m=17) == EUNSUP               # decode-sized batches only
     assert fwd_multi(lib, xdt=0, ldt=0) == EUNSUP       # no fp32 path
+    # (BF16, F16) rows over 32768 columns: one token stages its row (at most 32768
+    # columns), and more than 8 tokens take two cells per entry (at most 128 entries)
+    assert fwd_multi(lib, xdt=2, ldt=1, m=1, d=36864) == EUNSUP
+    assert fwd_multi(lib, xdt=2, ldt=1, m=9, d=36864, gpr=9) == EUNSUP
     assert fwd_multi(lib, Y=0x50000000) == EALIAS       # output over the set array
     assert fwd_multi(lib, Y=C + 2048) == EALIAS         # output over the second table set
     assert fwd_multi(lib, m=0, X=0, Y=0, sets=0) == 0

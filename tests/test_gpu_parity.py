@@ -251,13 +251,16 @@ def _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype):
     (4, 4, 33, 16384, [1, 0, 1, 1, 0, 0, 1], 2),
     (4, 8, 16, 32768, [0, 0, 1], 2),       # one token per pass
     (4, 8, 32, 36864, [1, 0, 1], 2),       # no activation staging (one row exceeds it)
+    (4, 8, 32, 36864, [1], 2),             # the same with one token
     (3, 4, 24, 4096, [0] * 16, 1),         # one set: all 16 rows read from memory, one pass
 ])
 def test_fwd_multi(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     idx, luts, X = _multi_case(f"multi/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}", n, d, b, gpr, len(sets),
                                n_sets, x_dtype, lut_dtype)
-    if (x_dtype, lut_dtype) == ("bf16", "f16") and d > 32768:
-        # prescaled rows are staged in LDS, which holds at most 32768 columns of a row
+    if (x_dtype, lut_dtype) == ("bf16", "f16") and d > 32768 and len(sets) == 1:
+        # one prescaled token takes the kernel that stages its row in LDS, which
+        # holds at most 32768 columns (from two tokens on, the set-interleaved
+        # kernel finds the row exponents without staging)
         with pytest.raises(skm().SketchError) as e:
             _fwd_multi(idx, luts, X, sets, b, gpr, x_dtype, lut_dtype)
         assert e.value.status == -2
@@ -328,7 +331,7 @@ def test_fwd_multi_selection_bit_exact(b):
         assert np.array_equal(got[t], W[:, cols[t]]), t
 
 
-@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("f16", "bf16"), ("bf16", "bf16"), ("bf16", "f16")])
 @pytest.mark.parametrize("b,gpr,n,d,sets,n_sets", [
     # eight sets in use: one 128-bit lookup per weight serves them all
     (4, 8, 48, 4096, [0, 1, 2, 3, 4, 5, 6, 7], 8),
@@ -643,12 +646,18 @@ def test_decode_window_mixed_rows_bf16_f16(zero_row):
     assert max(_row_errs(got, want)) <= TOL16
 
 
-@pytest.mark.parametrize("sets,d", [([0, 1, 2, 1], 4096), ([1] * 12 + [0] * 4, 4096), ([0, 1, 0], 16384)])
-def test_fwd_multi_scales_bf16_f16(sets, d):
-    """Several table sets: token rows at their own scales, staged pass by pass; every row within the tolerance."""
+@pytest.mark.parametrize("sets,d,n_sets", [
+    ([0, 1, 2, 1], 4096, 3), ([1] * 12 + [0] * 4, 4096, 3), ([0, 1, 0], 16384, 3),
+    # rows longer than the staging holds, 8 and 16 set slots, one table set
+    ([2, 0, 1, 2, 1], 36864, 3), (list(range(8)), 2048, 8), ([15 - t for t in range(16)], 2048, 16),
+    ([0, 0, 0, 0, 0, 0], 4096, 1)])
+def test_fwd_multi_scales_bf16_f16(sets, d, n_sets):
+    """Several table sets: token rows at their own scales (2^-66 .. 2^30, prescaled per row by powers of two:
+    the row exponents come from the staged rows in the one-pass-per-set kernel and from a scan of each token
+    row in the set-interleaved one); every row within the tolerance."""
     b, gpr, n = 4, 8, 64
     m = len(sets)
-    idx, luts, _ = _multi_case(f"multiscale/{m}/{d}", n, d, b, gpr, 1, 3, "bf16", "f16")
+    idx, luts, _ = _multi_case(f"multiscale/{m}/{d}/{n_sets}", n, d, b, gpr, 1, n_sets, "bf16", "f16")
     X = _scaled_rows(f"multiscale/{m}/{d}/X", (m, d), [2.0 ** k for k in (-40, 17, -3, 30, -66, 8)])
     got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, "bf16", "f16"))
     want = oracle.forward_multi(syn.to_float64(X, "bf16"), idx, syn.to_float64(luts, "f16"), sets, b, gpr)
