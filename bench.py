@@ -214,20 +214,22 @@ def bench_fwd(torch, skm, w, shape, b, m, steps, warmup, rotate=True, check=None
 
 
 def bench_multi(torch, skm, steps, warmup):
-    """Decode with one table set per token over one shared index stream (the
-    7B attention projection, b=4): one multi-set launch against one
-    single-set launch per set on that set's tokens."""
+    """Decode with one table set per token over one shared index stream (b=4):
+    one multi-set launch against one single-set launch per set on that set's
+    tokens. The 7B attention projection (f16) and the 70B up projection (bf16
+    activations with f16 tables: the prescaled pair)."""
     from lut_sketched_matmul_amd import synthetic as syn
     from lut_sketched_matmul_amd import workloads as wl
-    w = wl.LLAMA2_7B_ATTN
-    shape = w.shapes[0]
     b = 4
     out = {}
-    for m, n_sets in ((4, 4), (16, 4), (16, 16)):
+    cases = [(wl.LLAMA2_7B_ATTN, 0, m, ns, "") for m, ns in ((4, 4), (16, 4), (16, 16))]
+    cases += [(wl.LLAMA3_70B_MLP, 0, m, ns, "70b_up_") for m, ns in ((4, 4), (16, 16))]
+    for w, si, m, n_sets, tag in cases:
+        shape = w.shapes[si]
         t = w.make(shape, b, m)
         X = dev(torch, t["X"], w.x_dtype)
         idx = dev(torch, t["idx_packed"], "u8")
-        luts_np = np.stack([syn.random_lut(f"bench-multi/{m}/{n_sets}/{s}", shape.n, w.gpr, b, w.lut_sigma,
+        luts_np = np.stack([syn.random_lut(f"bench-multi/{tag}{m}/{n_sets}/{s}", shape.n, w.gpr, b, w.lut_sigma,
                                            w.lut_dtype) for s in range(n_sets)])
         luts = dev(torch, luts_np, w.lut_dtype)
         sets = [tt % n_sets for tt in range(m)]
@@ -238,7 +240,7 @@ def bench_multi(torch, skm, steps, warmup):
                               steps, warmup)
         # parity sample: every token on sampled rows (the rotated copies hold the same values)
         rows = sample_ids(shape.n, 224, 70 + m + n_sets)
-        CHECKS.append({"name": f"decode_multi_lut_7b_attn.m{m}_sets{n_sets}", "kind": "fwdmulti", "X": t["X"],
+        CHECKS.append({"name": f"decode_multi_lut.{tag}m{m}_sets{n_sets}", "kind": "fwdmulti", "X": t["X"],
                        "idx": t["idx_packed"][rows], "lut": luts_np[:, rows], "sets": sets, "b": b, "gpr": w.gpr,
                        "x_dtype": w.x_dtype, "lut_dtype": w.lut_dtype,
                        "got": Y.float().cpu().numpy()[:, rows].astype(np.float64)})
@@ -255,7 +257,7 @@ def bench_multi(torch, skm, steps, warmup):
         nbytes = (shape.n * shape.d * b // 8 + n_sets * shape.n * w.gpr * (1 << b) * 2 + m * shape.d * 2
                   + m * shape.n * 2)
         ms, ms_sep = total / steps, total_sep / steps
-        out[f"m{m}_sets{n_sets}"] = {
+        out[f"{tag}m{m}_sets{n_sets}"] = {
             "shape": f"{shape.name} {shape.n}x{shape.d}", "b": b, "m": m, "n_sets": n_sets,
             "ms_per_launch": ms, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
             "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -718,8 +720,8 @@ def main():
         log("7B MLP b=2/3 decode: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in lb.items()))
     if "multilut" in want:
         ml = bench_multi(torch, skm, args.steps, args.warmup)
-        parts["decode_multi_lut_7b_attn"] = ml
-        log("multi-LUT decode 4096x4096: " + ", ".join(
+        parts["decode_multi_lut"] = ml
+        log("multi-LUT decode (4096x4096 f16; 70b_up: 28672x8192 bf16/f16): " + ", ".join(
             f"{k} {v['ms_per_launch'] * 1e3:.2f} us ({v['speedup_vs_one_launch_per_set']:.2f}x vs one launch per set)"
             for k, v in ml.items()))
     if "decode70b" in want:

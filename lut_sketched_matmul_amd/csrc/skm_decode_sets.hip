@@ -58,7 +58,10 @@ namespace skm {
 namespace {
 
 constexpr int DS_ROWS = 16;     // weight rows per block
-constexpr int DS_NW = 16;       // waves per block
+// waves per block: 16 when the grid has at most 384 blocks, else 8 (two
+// blocks share a CU, so one block's start-up hides behind the other's work)
+constexpr int DS_NW_MAX = 16;
+constexpr int64_t DS_NW16_MAX_BLOCKS = 384;
 constexpr int DS_MAX_ENTRIES = 224;   // table entries per row (entry byte: 8 bits)
 constexpr int DS_MAX_ENTRIES2 = 128;  // with two cells per (entry, row): doubled entry byte
 // XT: every wave turns its slot's [16 tokens][16 pieces of 16 bytes] around
@@ -196,8 +199,8 @@ __device__ __forceinline__ void ds_wait_vmcnt() {
 
 // GW: sets per cell read (2, 4 or 8); OCT2: a second cell per (entry, row)
 // for set slots 8..15 (GW == 8 only).
-template <int B, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
-__global__ void __launch_bounds__(DS_NW * 64)
+template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
+__global__ void __launch_bounds__(NW * 64, 16 / NW)
 k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ luts,
               const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride, int m, int64_t n, int64_t d,
               int gpr, uint32_t ug_magic, TX* __restrict__ Y) {
@@ -206,7 +209,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   // [NW][16][16] fp32 partial tiles in the same place; XT: the waves'
   // activation buffers above both.
   extern __shared__ uint32_t smem[];
-  constexpr int NW = DS_NW;
+  static_assert(NW == 8 || NW == 16, "8 or 16 waves");
   constexpr int NP = (OCT2 ? 16 : GW) / 2;  // set pairs (accumulators)
   constexpr uint32_t ES = OCT2 ? 512u : 256u;  // bytes per entry
   typedef ds_mfma<TL> MF;
@@ -269,7 +272,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
 
   // ---- table loads: unit (cell c, row jj, 4-entry chunk ec); rows vary
   // fastest, so a wave's cell writes cover 256 contiguous bytes per chunk
-  constexpr int UPT = 1;  // units per thread (the host checks the count)
+  constexpr int UPT = 16 / NW;  // units per thread (at most 1024 units: the host checks the count)
   const int EC = E >> 2;
   const int units = (OCT2 ? 2 : 1) * 16 * EC;
   u32x2 tv[UPT][GW];
@@ -313,15 +316,16 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   const uint32_t rmax = above + (XT ? NW * DS_XT_WAVE : 0u);
   if constexpr (SC) {
     // wave w < m scans token row w (wave-uniform branch)
-    if (wave < m) {
-      const TX* xr = X + (int64_t)wave * d;
+    // (wave-uniform loop: wave w takes rows w, w + NW)
+    for (int tr = wave; tr < m; tr += NW) {
+      const TX* xr = X + (int64_t)tr * d;
       uint32_t mx = 0u;
       for (int64_t c = (int64_t)lane * 8; c < d; c += 512) {
         const uint32_t v = absmax8_bf16(*reinterpret_cast<const u32x4*>(xr + c));
         mx = mx > v ? mx : v;
       }
       mx = wave_max_to_lane63(mx);
-      if (lane == 63) *(ds_u32*)(uintptr_t)(rmax + (uint32_t)wave * 4u) = mx;
+      if (lane == 63) *(ds_u32*)(uintptr_t)(rmax + (uint32_t)tr * 4u) = mx;
     }
   }
   // every load is consumed by now, the slots' (issued before the table
@@ -528,38 +532,38 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   }
 }
 
-template <int B, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
+template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
 hipError_t sets_kernel(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
                        const Problem& p, TX* Y, hipStream_t s, uint32_t magic, size_t lds) {
-  const auto kern = k_decode_sets<B, GW, OCT2, TX, TL, RAGGED, XT>;
+  const auto kern = k_decode_sets<B, NW, GW, OCT2, TX, TL, RAGGED, XT>;
   static const hipError_t prep = prepare_kernel((const void*)kern, lds);
   if (prep != hipSuccess) return prep;
   const dim3 grid((unsigned)((p.n + DS_ROWS - 1) / DS_ROWS));
-  hipLaunchKernelGGL(kern, grid, dim3(DS_NW * 64), lds, s, X, idx, luts, lut_set, n_sets, p.n * ((int64_t)p.gpr << p.b),
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, X, idx, luts, lut_set, n_sets, p.n * ((int64_t)p.gpr << p.b),
                      (int)p.m, p.n, p.d, p.gpr, magic, Y);
   return hipGetLastError();
 }
 
-template <int B, int GW, bool OCT2, typename TX, typename TL>
+template <int B, int NW, int GW, bool OCT2, typename TX, typename TL>
 hipError_t sets_launch(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
                        const Problem& p, TX* Y, hipStream_t s) {
   const uint32_t ug = (uint32_t)(p.group_cols() / 32);
   // u / ug == umulhi(u, magic) for u * ug < 2^32; ug == 1 is passed as 0
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
   const size_t cells = (size_t)((int64_t)p.gpr << p.b) * (OCT2 ? 512 : 256);
-  const size_t part = (size_t)DS_NW * 256 * 4;
+  const size_t part = (size_t)NW * 256 * 4;
   const bool xt = p.m >= DS_XT_MIN_M;
   // + 16 row maxima of the (BF16, F16) prescale
-  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)DS_NW * DS_XT_WAVE : 0) + 64;
+  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)NW * DS_XT_WAVE : 0) + 64;
   const bool ragged = p.units() % 4 != 0;
   if (xt)
-    return ragged ? sets_kernel<B, GW, OCT2, TX, TL, true, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
-                  : sets_kernel<B, GW, OCT2, TX, TL, false, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
   if constexpr (OCT2) {
     return hipErrorNotSupported;  // (more than 8 sets means more than 8 tokens: always the turn-around)
   } else {
-    return ragged ? sets_kernel<B, GW, OCT2, TX, TL, true, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
-                  : sets_kernel<B, GW, OCT2, TX, TL, false, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
   }
 }
 
@@ -567,10 +571,16 @@ template <int B, typename TX, typename TL>
 hipError_t sets_b(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
                   const Problem& p, TX* Y, hipStream_t s) {
   const int64_t bound = p.m < n_sets ? p.m : n_sets;  // distinct sets at most
-  if (bound <= 2) return sets_launch<B, 2, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
-  if (bound <= 4) return sets_launch<B, 4, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
-  if (bound <= 8) return sets_launch<B, 8, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
-  return sets_launch<B, 8, true>(X, idx, luts, lut_set, n_sets, p, Y, s);
+  if ((p.n + DS_ROWS - 1) / DS_ROWS > DS_NW16_MAX_BLOCKS) {
+    if (bound <= 2) return sets_launch<B, 8, 2, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+    if (bound <= 4) return sets_launch<B, 8, 4, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+    if (bound <= 8) return sets_launch<B, 8, 8, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+    return sets_launch<B, 8, 8, true>(X, idx, luts, lut_set, n_sets, p, Y, s);
+  }
+  if (bound <= 2) return sets_launch<B, 16, 2, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+  if (bound <= 4) return sets_launch<B, 16, 4, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+  if (bound <= 8) return sets_launch<B, 16, 8, false>(X, idx, luts, lut_set, n_sets, p, Y, s);
+  return sets_launch<B, 16, 8, true>(X, idx, luts, lut_set, n_sets, p, Y, s);
 }
 
 template <typename TX, typename TL>
@@ -595,7 +605,7 @@ bool decode_sets_supported(const Problem& p, int n_sets, bool scaled) {
   const int64_t maxe = bound > 8 ? DS_MAX_ENTRIES2 : DS_MAX_ENTRIES;
   // table units (cells x rows x 4-entry chunks): one per thread
   const int64_t units = (bound > 8 ? 2 : 1) * 16 * (E / 4);
-  return E <= maxe && units <= DS_NW * 64 && p.d <= (int64_t(1) << 20);
+  return E <= maxe && units <= DS_NW_MAX * 64 && p.d <= (int64_t(1) << 20);
 }
 
 hipError_t launch_decode_sets(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,

@@ -355,6 +355,10 @@ def test_fwd_multi_selection_bit_exact(b):
     (4, 14, 32, 14336, list(range(10)), 10),
     # out-of-range set indices (clamped) with two cells
     (4, 8, 40, 4096, [-5, 0, 20, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 17], 16),
+    # more than 384 row blocks: 8-wave blocks, two per CU
+    (4, 4, 6160, 512, [3, 1, 2, 0, 3, 1], 4),
+    (2, 1, 6176, 1024, [(5 * t + 2) % 16 for t in range(16)], 16),
+    (3, 2, 6150, 512, [4, 0, 1, 2, 3, 4, 0, 1, 2, 3], 5),
 ])
 def test_fwd_multi_set_cells(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     """Set-interleaved tables (SpaLLM section 2.3, several adapters over one mapping): up to eight sets per
