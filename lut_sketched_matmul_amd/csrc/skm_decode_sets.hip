@@ -50,6 +50,13 @@
 // Set slots: each wave computes the same schedule from lut_set: set indices
 // are clamped into [0, n_sets), the distinct sets are numbered in order of
 // first use, and lane k holds the set of slot k.
+//
+// Blocks have 16 waves, or 8 when the grid has more than 384 blocks (two
+// blocks then share a CU and one block's start-up hides behind the other's
+// work). With bf16 activations and f16 tables each token row is prescaled
+// by a power of two (skm_common.h): the waves find the rows' largest
+// magnitudes before the table barrier, the activations are converted scaled
+// and the sums scaled back.
 #include "skm_common.h"
 #include "skm_launch.h"
 
@@ -188,13 +195,6 @@ __device__ __forceinline__ void ds_load(DsSlot<B, TX>& R, int64_t s, int64_t S, 
     for (int h = 0; h < 4; ++h) R.x[h] = xp[h];
   }
   R.gk = (ug_magic ? __umulhi(u, ug_magic) : u) << B;
-}
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void ds_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // GW: sets per cell read (2, 4 or 8); OCT2: a second cell per (entry, row)
