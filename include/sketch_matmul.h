@@ -141,7 +141,9 @@ size_t sketch_matmul_fwd_workspace(int64_t m, int64_t n, int64_t d, int b, int g
  * table entries per row (gpr * 2^b) are used, or at most 128 when more than 8
  * sets can occur (min(m, n_sets) > 8), the tables of all sets in use are
  * interleaved in LDS and one lookup serves up to 8 sets; n_sets == 1 with the
- * other pairs is the single-set forward; otherwise each set in use takes one
+ * other pairs, and one token (m == 1, its row staged for (BF16, F16)), run the
+ * single-set forward on that set (read from lut_set on the device, so the
+ * results equal sketch_matmul_fwd's on that set); otherwise each set in use takes one
  * round of lookups (one per 32768 / d of its tokens when more of them than
  * that share the set). lut_set must
  * be 4-byte aligned, the other pointers 16-byte aligned; Y must not overlap

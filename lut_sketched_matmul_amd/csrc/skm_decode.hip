@@ -520,7 +520,15 @@ k_decode(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const
   // ---- prologue: table loads, activation loads (XL), first index loads, then
   // the LDS stores of the first two (their loads complete first). MULTI passes
   // find their tables, activations and first index batch loaded.
-  if constexpr (!MULTI) tab_load<B, NW, TL>(TR, lut, row_ok ? grow : n - 1, gpr, wave);
+  if constexpr (!MULTI) {
+    // one token of a multi-set call (lut_set given): the tables of its set
+    const TL* lut1 = lut;
+    if (lut_set) {
+      const int v = __builtin_amdgcn_readfirstlane(lut_set[0]);
+      lut1 = lut + (int64_t)(v < 0 ? 0 : (v >= n_sets ? n_sets - 1 : v)) * set_stride;
+    }
+    tab_load<B, NW, TL>(TR, lut1, row_ok ? grow : n - 1, gpr, wave);
+  }
   // (a chunk past m*d is neither loaded nor read: giving it a value would
   // merge it with the load at a branch, which waits for the load there)
   auto load_x = [&]() {
@@ -826,6 +834,7 @@ size_t decode_lds_bytes(int gpr, int64_t x_elems, bool mags, bool xt) {
 // Table sets for the MULTI kernel (a single set: lut_set == nullptr)
 struct SetArgs {
   const int32_t* lut_set = nullptr;
+  bool select = false;             // one token: the single-set kernel on set lut_set[0]
   int n_sets = 1;
   int64_t set_stride = 0;          // table elements per set
   const int32_t* rexp = nullptr;   // row exponents of X (prescaled pair without staging)
@@ -836,7 +845,7 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
                          uint32_t magic, const SetArgs& sa) {
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   // MULTI + XL stages one pass's tokens: at most min(m, DEC_XL_MAX / d) of them
-  const int64_t xl_m = sa.lut_set && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
+  const int64_t xl_m = sa.lut_set && !sa.select && p.m > DEC_XL_MAX / p.d ? DEC_XL_MAX / p.d : p.m;
   const size_t lds = decode_lds_bytes<B, NW>(p.gpr, XL ? xl_m * p.d : 0, SC && XL, XT);
   const dim3 grid((unsigned)((p.n + DEC_ROWS - 1) / DEC_ROWS));
   // element e of the staged activations lies in row e / d = umulhi(e, ceil(2^32 / d)), exact for e * d < 2^32
@@ -844,7 +853,7 @@ hipError_t decode_launch(const TX* X, const uint8_t* idx, const TL* lut, const P
   const uint32_t d_magic = p.d <= DEC_XL_MAX1 ? (uint32_t)(((uint64_t)1 << 32) / (uint64_t)p.d) + 1u : 0u;
   // (the gathers address the tables with absolute LDS addresses, see gaddr:
   // checked once per kernel, which also raises its LDS limit to 160 KB)
-  if (sa.lut_set) {
+  if (sa.lut_set && !sa.select) {
     if constexpr ((SC && !XL) || XT) {
       return hipErrorNotSupported;  // (the ABI routes no such call here)
     } else {
@@ -870,12 +879,13 @@ hipError_t decode_nw(const TX* X, const uint8_t* idx, const TL* lut, const Probl
   // one table set: stage the activations when all m rows fit. Several sets:
   // each pass stages its own tokens, so it suffices that one row fits (with a
   // single set in use, the m rows then take several passes)
-  const bool xl = decode_stages_activations(p, sa.lut_set != nullptr, sa.n_sets,
+  const bool multi = sa.lut_set && !sa.select;
+  const bool xl = decode_stages_activations(p, multi, sa.n_sets,
                                             scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t)));
   // Unstaged, one set: from 8 tokens on, the coalesced loads and the LDS
   // turn-around cost less than loading fragments directly (whose cost grows
   // with the distinct token rows a load touches); below, the direct loads.
-  const bool xt = !xl && !sa.lut_set && p.m >= DEC_XT_MIN_M;
+  const bool xt = !xl && !multi && p.m >= DEC_XT_MIN_M;
   if (p.units() % 4 != 0)
     return xl ? decode_launch<B, NW, TX, TL, true, true, false>(X, idx, lut, p, Y, s, magic, sa)
               : (xt ? decode_launch<B, NW, TX, TL, true, false, true>(X, idx, lut, p, Y, s, magic, sa)
@@ -965,11 +975,20 @@ hipError_t launch_decode(const void* X, int x_dtype, const uint8_t* idx, const v
 
 hipError_t launch_decode_multi(const void* X, int x_dtype, const uint8_t* idx, const void* luts, int lut_dtype,
                                const int32_t* lut_set, int n_sets, const Problem& p, void* Y, hipStream_t s) {
-  // one set: the single-set decode (every token on set 0); else
-  // set-interleaved tables whenever they apply (every pair but the
-  // prescaled one); otherwise one pass per set in use
+  // one set: the single-set decode (every token on set 0); one token: the
+  // single-set decode on that token's set (found on the device), when it
+  // needs no row exponents from a workspace; else set-interleaved tables
+  // whenever they apply; otherwise one pass per set in use
   const bool scaled = x_dtype == DT_BF16 && lut_dtype == DT_F16;
   if (n_sets == 1 && !scaled) return decode_dispatch(X, x_dtype, idx, luts, lut_dtype, p, Y, s, SetArgs{});
+  if (p.m == 1 && (!scaled || decode_stages_activations(p, false, 1, true))) {
+    SetArgs one;
+    one.lut_set = lut_set;
+    one.select = true;
+    one.n_sets = n_sets;
+    one.set_stride = p.n * p.gpr * p.k();
+    return decode_dispatch(X, x_dtype, idx, luts, lut_dtype, p, Y, s, one);
+  }
   if (decode_sets_supported(p, n_sets, scaled))
     return launch_decode_sets(X, x_dtype, idx, luts, lut_dtype, lut_set, n_sets, p, Y, s);
   SetArgs sa;

@@ -306,6 +306,18 @@ def test_fwd_multi_one_set_is_fwd(dt, m):
     assert oracle.rel_err(got, ref) <= 2.0 ** (-10 if dt == "f16" else -7), dt
 
 
+@pytest.mark.parametrize("x_dtype,lut_dtype", [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("setv,want_set", [(2, 2), (-1, 0), (7, 2)])
+def test_fwd_multi_one_token_is_fwd(x_dtype, lut_dtype, setv, want_set):
+    """One token uses one set: the multi-set call runs the single-set decode on the set it reads from lut_set
+    on the device (clamped), so its output equals the single-set forward on that set bit for bit."""
+    b, gpr, n, d = 4, 8, 80, 4096
+    idx, luts, X = _multi_case(f"multi1tok/{x_dtype}/{lut_dtype}", n, d, b, gpr, 1, 3, x_dtype, lut_dtype)
+    got = _fwd_multi(idx, luts, X, [setv], b, gpr, x_dtype, lut_dtype)
+    ref = skm().sketch_matmul_fwd(to_dev(X, x_dtype), to_dev(idx, "u8"), to_dev(luts[want_set], lut_dtype), b, gpr)
+    assert bool((got == ref).all())
+
+
 def test_fwd_multi_clamps_set_indices():
     b, gpr, n, d = 4, 4, 48, 1024
     sets, clamped = [-3, 0, 7, 1], [0, 0, 1, 1]
