@@ -40,12 +40,13 @@
 // Work split as in the single-set decode: wave w handles slots (4 units = 128
 // columns) w, w + NW, ..., lane (j, q) loads unit 4s+q of row j with one
 // index load, and the A fragments of token t = lane % 16 come from global
-// memory: below 8 tokens each lane loads its own 64 bytes, from 8 tokens on
-// the wave loads the slot's [16 tokens][256 bytes] with neighbouring lanes on
-// neighbouring 16-byte pieces and turns them around in a private LDS buffer
-// (a load whose lanes touch 16 separate rows is served piece by piece). The
-// waves' partial tiles are summed in LDS in wave order (deterministic) and
-// stored once.
+// memory through a turn-around: the wave loads the slot's [m tokens][256
+// bytes] in groups of four token rows (one 16-byte load per lane and group,
+// neighbouring lanes on neighbouring pieces), stores them in a private LDS
+// buffer and reads each lane's fragments back (loading per lane, 64 bytes of
+// the lane's own token, spreads one load over many rows, which the load
+// path serves piece by piece). The waves' partial tiles are summed in LDS in
+// wave order (deterministic) and stored once.
 //
 // Set slots: each wave computes the same schedule from lut_set: set indices
 // are clamped into [0, n_sets), the distinct sets are numbered in order of
@@ -71,11 +72,11 @@ constexpr int DS_NW_MAX = 16;
 constexpr int64_t DS_NW16_MAX_BLOCKS = 384;
 constexpr int DS_MAX_ENTRIES = 224;   // table entries per row (entry byte: 8 bits)
 constexpr int DS_MAX_ENTRIES2 = 128;  // with two cells per (entry, row): doubled entry byte
-// XT: every wave turns its slot's [16 tokens][16 pieces of 16 bytes] around
-// in a private LDS buffer, rows padded by one piece (conflict-free reads)
+// every wave turns its slot's [up to 16 tokens][16 pieces of 16 bytes]
+// around in a private LDS buffer, rows padded by one piece (conflict-free
+// reads)
 constexpr uint32_t DS_XT_ROW = 17 * 16;
 constexpr uint32_t DS_XT_WAVE = 16 * DS_XT_ROW;
-constexpr int DS_XT_MIN_M = 8;  // tokens from which the activations take the turn-around
 
 template <bool V> struct btag_ds { static constexpr bool value = V; };
 template <int V> struct ival_ds { static constexpr int value = V; };
@@ -157,7 +158,7 @@ struct DsSlot {
   bool ok;         // unit inside the row (RAGGED)
 };
 
-// Sources of the coalesced activation loads (XT): load i of a slot brings
+// Sources of the coalesced activation loads: load i of a slot brings
 // token min(4i + l/16, m-1) (element offset off[i]) at columns 128 s + c8,
 // c8 = 8 (l % 16), clamped to dcol = d - 8 when the row ends inside the slot.
 template <typename TX>
@@ -169,13 +170,12 @@ struct DsXt {
 };
 
 // Index and activation loads of slot s (clamped to the last slot, and to the
-// last unit with RAGGED, so every load is unconditional and in range).
-// Without XT, lane (token t, quarter q) loads its own 32 activations of unit
-// 4s+q; with XT, the wave's four loads cover the slot's [16 tokens][128
-// columns] with neighbouring lanes on neighbouring 16-byte pieces.
-template <int B, typename TX, bool RAGGED, bool XT>
+// last unit with RAGGED, so every load is unconditional and in range). The
+// wave's XT activation loads cover the slot's [4 XT tokens][128 columns] with
+// neighbouring lanes on neighbouring 16-byte pieces.
+template <int B, typename TX, bool RAGGED, int XT>
 __device__ __forceinline__ void ds_load(DsSlot<B, TX>& R, int64_t s, int64_t S, uint32_t U, uint32_t ug_magic,
-                                        int q, const uint8_t* rowp, const TX* xrow, const DsXt<TX>& xt) {
+                                        int q, const uint8_t* rowp, const DsXt<TX>& xt) {
   const int64_t sc = s < S ? s : S - 1;
   uint32_t u = 4u * (uint32_t)sc + (uint32_t)q;
   R.ok = true;
@@ -184,22 +184,16 @@ __device__ __forceinline__ void ds_load(DsSlot<B, TX>& R, int64_t s, int64_t S, 
     u = u < U ? u : U - 1u;
   }
   load_unit<B>(rowp, u, R.w);
-  if constexpr (XT) {
-    uint32_t col = 128u * (uint32_t)sc + xt.c8;
-    if constexpr (RAGGED) col = col < xt.dcol ? col : xt.dcol;
+  uint32_t col = 128u * (uint32_t)sc + xt.c8;
+  if constexpr (RAGGED) col = col < xt.dcol ? col : xt.dcol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.x[i] = *reinterpret_cast<const u32x4*>(xt.x + xt.off[i] + col);
-  } else {
-    const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (int64_t)u * 32);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) R.x[h] = xp[h];
-  }
+  for (int i = 0; i < XT; ++i) R.x[i] = *reinterpret_cast<const u32x4*>(xt.x + xt.off[i] + col);
   R.gk = (ug_magic ? __umulhi(u, ug_magic) : u) << B;
 }
 
 // GW: sets per cell read (2, 4 or 8); OCT2: a second cell per (entry, row)
 // for set slots 8..15 (GW == 8 only).
-template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
+template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, int XT>
 __global__ void __launch_bounds__(NW * 64, 16 / NW)
 k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, const TL* __restrict__ luts,
               const int32_t* __restrict__ lut_set, int n_sets, int64_t set_stride, int m, int64_t n, int64_t d,
@@ -218,6 +212,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   constexpr bool SC = scaled_pair(__is_same(TX, bf16_t), __is_same(TL, half_t));
   static_assert(GW == 2 || GW == 4 || GW == 8, "cell reads of 2, 4 or 8 sets");
   static_assert(!OCT2 || GW == 8, "a second cell only after a full first one");
+  static_assert(XT == 1 || XT == 2 || XT == 4, "turn-around loads: groups of four token rows");
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -232,9 +227,8 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   const uint32_t U = (uint32_t)(d / 32);
   const int64_t S = (U + 3) / 4;  // slots per row
   const uint8_t* rowp = idx_packed + (row_ok ? grow : n - 1) * (d * B / 8);
-  const TX* xrow = X + (int64_t)tokc * d;
   DsXt<TX> xts;
-  if constexpr (XT) {
+  {
     xts.x = X;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -253,8 +247,8 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   const int sv = lut_set[tl];
   int64_t s0 = wave;
   DsSlot<B, TX> R0, R1;
-  ds_load<B, TX, RAGGED, XT>(R0, s0, S, U, ug_magic, q, rowp, xrow, xts);
-  ds_load<B, TX, RAGGED, XT>(R1, s0 + NW, S, U, ug_magic, q, rowp, xrow, xts);
+  ds_load<B, TX, RAGGED, XT>(R0, s0, S, U, ug_magic, q, rowp, xts);
+  ds_load<B, TX, RAGGED, XT>(R1, s0 + NW, S, U, ug_magic, q, rowp, xts);
 
   // ---- set slots (every wave computes the same)
   const int setv = sv < 0 ? 0 : (sv >= n_sets ? n_sets - 1 : sv);
@@ -313,7 +307,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   // then (SC) the largest magnitude of each token row
   const uint32_t cells = (uint32_t)E * ES;
   const uint32_t above = cells > NW * 1024u ? cells : NW * 1024u;
-  const uint32_t rmax = above + (XT ? NW * DS_XT_WAVE : 0u);
+  const uint32_t rmax = above + NW * DS_XT_WAVE;
   if constexpr (SC) {
     // wave w < m scans token row w (wave-uniform branch)
     // (wave-uniform loop: wave w takes rows w, w + NW)
@@ -339,7 +333,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   // XT: this wave's buffer, above the cells and the partial tiles
   const uint32_t xt_w = above + (uint32_t)wave * DS_XT_WAVE;
   const uint32_t xt_st = xt_w + (uint32_t)q * DS_XT_ROW + (uint32_t)j * 16u;
-  const uint32_t xt_ld = xt_w + (uint32_t)j * DS_XT_ROW + (uint32_t)q * 64u;
+  const uint32_t xt_ld = xt_w + (uint32_t)tokc * DS_XT_ROW + (uint32_t)q * 64u;
   (void)xt_st;
   (void)xt_ld;
   // A fragment selectors: token's value into the half of its set's parity
@@ -398,17 +392,15 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
 
   auto compute = [&](auto npa, const DsSlot<B, TX>& Rc, int64_t s, auto tail) {
     if (decltype(tail)::value && s >= S) return;  // wave-uniform
-    if constexpr (XT) {
-      // a lane stores load i at row 4i + l/16, piece l%16, and reads its
-      // token's (row l%16) pieces 4q..4q+3: unit 4s+q, as a direct load
-      // would give (one wave's LDS accesses are carried out in order)
+    // a lane stores load i at row 4i + l/16, piece l%16, and reads its
+    // token's (row min(l%16, m-1)) pieces 4q..4q+3: unit 4s+q (one wave's
+    // LDS accesses are carried out in order)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(ds_u32x4*)(uintptr_t)(xt_st + (uint32_t)i * 4u * DS_XT_ROW) = Rc.x[i];
-    }
+    for (int i = 0; i < XT; ++i) *(ds_u32x4*)(uintptr_t)(xt_st + (uint32_t)i * 4u * DS_XT_ROW) = Rc.x[i];
     // columns 8h..8h+7 of the unit in the compute dtype (dword i = columns
     // 8h + 2i, 8h + 2i + 1), read where first needed
     auto xq = [&](int h) -> u32x4 {
-      const u32x4 v = XT ? *(const ds_u32x4*)(uintptr_t)(xt_ld + 16u * (uint32_t)h) : Rc.x[h];
+      const u32x4 v = *(const ds_u32x4*)(uintptr_t)(xt_ld + 16u * (uint32_t)h);
       if constexpr (SC) return ds_convert_scaled(v, xsc);
       else return ds_convert<TX, TL>(v);
     };
@@ -491,9 +483,9 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
     int64_t bi = 0;
     for (; bi + 2 < nb; bi += 2) {
       compute(npa, R0, s0, btag_ds<false>{});
-      ds_load<B, TX, RAGGED, XT>(R0, s0 + 2 * NW, S, U, ug_magic, q, rowp, xrow, xts);
+      ds_load<B, TX, RAGGED, XT>(R0, s0 + 2 * NW, S, U, ug_magic, q, rowp, xts);
       compute(npa, R1, s0 + NW, btag_ds<false>{});
-      ds_load<B, TX, RAGGED, XT>(R1, s0 + 3 * NW, S, U, ug_magic, q, rowp, xrow, xts);
+      ds_load<B, TX, RAGGED, XT>(R1, s0 + 3 * NW, S, U, ug_magic, q, rowp, xts);
       s0 += 2 * NW;
     }
     compute(npa, R0, s0, btag_ds<true>{});
@@ -532,7 +524,7 @@ k_decode_sets(const TX* __restrict__ X, const uint8_t* __restrict__ idx_packed, 
   }
 }
 
-template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, bool XT>
+template <int B, int NW, int GW, bool OCT2, typename TX, typename TL, bool RAGGED, int XT>
 hipError_t sets_kernel(const TX* X, const uint8_t* idx, const TL* luts, const int32_t* lut_set, int n_sets,
                        const Problem& p, TX* Y, hipStream_t s, uint32_t magic, size_t lds) {
   const auto kern = k_decode_sets<B, NW, GW, OCT2, TX, TL, RAGGED, XT>;
@@ -552,18 +544,21 @@ hipError_t sets_launch(const TX* X, const uint8_t* idx, const TL* luts, const in
   const uint32_t magic = ug == 1 ? 0u : (uint32_t)((((uint64_t)1) << 32) / ug + 1);
   const size_t cells = (size_t)((int64_t)p.gpr << p.b) * (OCT2 ? 512 : 256);
   const size_t part = (size_t)NW * 256 * 4;
-  const bool xt = p.m >= DS_XT_MIN_M;
-  // + 16 row maxima of the (BF16, F16) prescale
-  const size_t lds = (cells > part ? cells : part) + (xt ? (size_t)NW * DS_XT_WAVE : 0) + 64;
+  // + the waves' turn-around buffers + 16 row maxima of the (BF16, F16) prescale
+  const size_t lds = (cells > part ? cells : part) + (size_t)NW * DS_XT_WAVE + 64;
   const bool ragged = p.units() % 4 != 0;
-  if (xt)
-    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
-                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, true>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+  // turn-around loads: groups of four token rows, ceil(m / 4) rounded up to 1, 2 or 4
+  if (p.m > 8)
+    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, 4>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, 4>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
   if constexpr (OCT2) {
-    return hipErrorNotSupported;  // (more than 8 sets means more than 8 tokens: always the turn-around)
+    return hipErrorNotSupported;  // (more than 8 sets means more than 8 tokens)
   } else {
-    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
-                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, false>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+    if (p.m > 4)
+      return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, 2>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                    : sets_kernel<B, NW, GW, OCT2, TX, TL, false, 2>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
+    return ragged ? sets_kernel<B, NW, GW, OCT2, TX, TL, true, 1>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds)
+                  : sets_kernel<B, NW, GW, OCT2, TX, TL, false, 1>(X, idx, luts, lut_set, n_sets, p, Y, s, magic, lds);
   }
 }
 
