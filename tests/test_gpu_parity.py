@@ -374,8 +374,8 @@ def test_fwd_multi_selection_bit_exact(b):
 ])
 def test_fwd_multi_set_cells(x_dtype, lut_dtype, b, gpr, n, d, sets, n_sets):
     """Set-interleaved tables (SpaLLM section 2.3, several adapters over one mapping): up to eight sets per
-    lookup and sixteen with two cells per (entry, row), activations loaded per lane below 8 tokens and
-    turned around in LDS from 8 on; the oracle takes the clamped set indices."""
+    lookup and sixteen with two cells per (entry, row), activations turned around in LDS in one, two or four
+    groups of token rows; the oracle takes the clamped set indices."""
     clamped = [min(max(v, 0), n_sets - 1) for v in sets]
     idx, luts, X = _multi_case(f"multicell/{x_dtype}/{lut_dtype}/{b}/{gpr}/{n}/{d}/{n_sets}/{len(sets)}", n, d, b,
                                gpr, len(sets), n_sets, x_dtype, lut_dtype)
