@@ -289,6 +289,29 @@ def test_fwd_multi_random_patterns(seed):
     assert oracle.rel_err(got, want) <= TOL16, (b, d, gpr, m, n_sets, sets)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_fwd_multi_set_cells_random(seed):
+    """Seeded random batches for the set-interleaved lookups: 2-16 tokens over up to 20 sets (so 2-, 4- and
+    8-set lookups and two cells per entry), random and out-of-range set indices, every dtype pair, row counts
+    off the 16-row blocks and column counts off the 128-column slots."""
+    r = np.random.default_rng(5000 + seed)
+    b = int(r.choice([2, 3, 4]))
+    d, gpr = [(1024, 4), (1376, 1), (2752, 2), (2048, 8), (4096, 8), (1536, 4)][seed % 6]
+    if (gpr << b) > 128:
+        gpr = max(1, 128 >> b)
+        d = gpr * 32 * int(d // (gpr * 32))
+    m = int(r.integers(2, 17))
+    n_sets = int(r.integers(1, 21))
+    sets = r.integers(-2, n_sets + 2, m).tolist()
+    clamped = [min(max(v, 0), n_sets - 1) for v in sets]
+    n = int(r.integers(17, 120))
+    xdt, ldt = [("f16", "f16"), ("bf16", "f16"), ("f16", "bf16"), ("bf16", "bf16")][seed % 4]
+    idx, luts, X = _multi_case(f"cellrand/{seed}", n, d, b, gpr, m, n_sets, xdt, ldt)
+    got = to_f64(_fwd_multi(idx, luts, X, sets, b, gpr, xdt, ldt))
+    want = oracle.forward_multi(syn.to_float64(X, xdt), idx, syn.to_float64(luts, ldt), clamped, b, gpr)
+    assert oracle.rel_err(got, want) <= TOL16, (b, d, gpr, m, n_sets, sets)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("m", [5, 16])
 def test_fwd_multi_one_set_is_fwd(dt, m):
